@@ -1,0 +1,126 @@
+/*
+ * sla.h - C ABI of the MI355X (gfx950) SLA2 sparse-linear attention forward library.
+ *
+ * Method (SLA2: Sparse-Linear Attention with Learnable Routing and QAT):
+ *   - router, section 2.B: Q and K are mean-pooled over blocks of adjacent tokens, the
+ *     pooled vectors are multiplied by the learnable projections proj_q / proj_k, each
+ *     query block scores every key block with a dot product, and the top_k key blocks
+ *     are kept (ties go to the lower key-block index);
+ *   - sparse branch, sections 1 and 2.B: exact softmax attention (scale 1/sqrt(d)) of
+ *     each query block over the tokens of its routed key blocks;
+ *   - linear branch (SALAD page, section 2; SPLA page, section 2.2): ReLU-kernel linear
+ *     attention over the key blocks that were NOT routed, obtained as the total over all
+ *     key blocks minus the routed ones; O_l = phi(q) S_c / (phi(q) . z_c + 1e-6);
+ *   - mix, section 2.A: O = alpha (.) O_s + (1 - alpha) (.) O_l with a per-head,
+ *     per-channel ratio alpha;
+ *   - quantised sparse branch, section 2.C: sla_forward_fp8 runs the sparse branch on
+ *     OCP E4M3 operands (per 64-token-block absmax scales for Q, K, V; P per key tile and
+ *     query row); router, linear branch and mix are the same as in sla_forward.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays.
+ *     Q is [batch, heads, n_q, head_dim]; K and V are [batch, heads, n_kv, head_dim];
+ *     O is [batch, heads, n_q, head_dim]; the channel index is the fastest.
+ *   - Q, K, V have element type in_dtype (bf16 or f32); O has out_dtype.
+ *   - proj_q, proj_k: f32 [head_dim (in), head_dim (out)], shared by all batches and heads;
+ *     the pooled row vector x is mapped to x @ proj.
+ *   - alpha: f32 [heads, head_dim], values expected in [0, 1].
+ *   - block_idx: int32 [batch, heads, ceil(n_q/block), top_k], ascending within a row.
+ *   - Every pointer must be 16-byte aligned. The caller owns all memory; the library never
+ *     allocates, frees, copies between host and device, or synchronises.
+ *   - Work is enqueued on `stream`; calls return as soon as it is enqueued. A non-OK status
+ *     other than SLA_ERR_HIP means nothing was enqueued; after SLA_ERR_HIP (a launch was
+ *     refused) the outputs are undefined.
+ *   - The library keeps no mutable global state: concurrent calls on different streams
+ *     with separate workspaces are safe. Results are bit-reproducible for identical
+ *     inputs (no floating-point atomics).
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLA_OK = 0,
+  SLA_ERR_NULL = 1,        /* a required pointer is NULL                             */
+  SLA_ERR_SHAPE = 2,       /* a size is out of range (see sla_problem)               */
+  SLA_ERR_DTYPE = 3,       /* unknown dtype, or a dtype the entry point refuses      */
+  SLA_ERR_TOPK = 4,        /* top_k < 0 or top_k > ceil(n_kv / block)                */
+  SLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                       */
+  SLA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than sla_workspace_size()    */
+  SLA_ERR_UNSUPPORTED = 7, /* head_dim not in {64, 128}, block != 64, too many blocks */
+  SLA_ERR_HIP = 8          /* a kernel launch failed                                 */
+} sla_status;
+
+typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
+
+typedef struct {
+  int32_t batch;      /* >= 1                                                        */
+  int32_t heads;      /* >= 1                                                        */
+  int32_t n_q;        /* query tokens, >= 1                                          */
+  int32_t n_kv;       /* key/value tokens, >= 1; ceil(n_kv/block) <= 8064            */
+  int32_t head_dim;   /* 64 or 128                                                   */
+  int32_t block;      /* 64: size of both query blocks and key blocks                */
+  int32_t top_k;      /* key blocks kept per query block, 0 .. ceil(n_kv/block)      */
+  int32_t in_dtype;   /* sla_dtype of Q, K, V                                        */
+  int32_t out_dtype;  /* sla_dtype of O                                              */
+} sla_problem;
+
+/* Bytes of device workspace a call needs (fp8 = 0 for sla_forward / sla_route, 1 for
+ * sla_forward_fp8). Returns 0 if the problem is invalid. */
+size_t sla_workspace_size(const sla_problem* p, int fp8);
+
+/* Router only (SLA2 page, section 2.B): pool -> project -> score -> top-k.
+ * Writes block_idx (required). Pooling, projection and scores are computed in float64
+ * so that the selection is reproducible; ties go to the lower key-block index. */
+sla_status sla_route(const sla_problem* p, const void* q, const void* k,
+                     const float* proj_q, const float* proj_k, int32_t* block_idx,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Full forward with the bf16 sparse branch (SLA2 page, sections 2.A and 2.B).
+ * block_idx is optional (NULL: the selection stays in the workspace). */
+sla_status sla_forward(const sla_problem* p, const void* q, const void* k, const void* v,
+                       const float* proj_q, const float* proj_k, const float* alpha,
+                       void* o, int32_t* block_idx,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Full forward with the quantised (E4M3) sparse branch (SLA2 page, section 2.C).
+ * Same arguments as sla_forward; in_dtype must be SLA_BF16. The router and the linear
+ * branch are identical to sla_forward, so block_idx is too. */
+sla_status sla_forward_fp8(const sla_problem* p, const void* q, const void* k, const void* v,
+                           const float* proj_q, const float* proj_k, const float* alpha,
+                           void* o, int32_t* block_idx,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stages of a forward call, in launch order, for sla_forward_profiled. */
+enum {
+  SLA_STAGE_KV_SUMMARY = 0,  /* per-block phi(K)^T V, sum phi(K), pooled K, totals      */
+  SLA_STAGE_ROUTE = 1,       /* pooled Q, projections, block scores, top-k              */
+  SLA_STAGE_COMPLEMENT = 2,  /* per query block: total minus the selected summaries     */
+  SLA_STAGE_SPARSE = 3,      /* sparse attention + linear apply + alpha mix            */
+  SLA_NUM_STAGES = 4
+};
+
+/* Same as sla_forward (fp8 = 0) or sla_forward_fp8 (fp8 = 1), and additionally records
+ * events[2*s] before and events[2*s+1] after stage s on `stream` (caller-created events,
+ * 2*SLA_NUM_STAGES of them), so the caller can time each stage with
+ * hipEventElapsedTime after synchronising. NULL events: identical to the plain call. */
+sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void* k,
+                                const void* v, const float* proj_q, const float* proj_k,
+                                const float* alpha, void* o, int32_t* block_idx,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                int fp8, hipEvent_t* events);
+
+/* Static, NUL-terminated description of a status code. */
+const char* sla_status_string(sla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SLA_H */

@@ -1,0 +1,11 @@
+"""MI355X-native (gfx950) SLA2 sparse-linear attention forward.
+
+The computation lives in libsla.so (HIP kernels behind the C ABI of include/sla.h);
+``sla`` is its ctypes binding. The library is loaded on first use; every entry point raises if it is not built.
+"""
+from .sla import (SlaError, Problem, make_problem, workspace_size, sla_route, sla_forward,
+                  sla_forward_fp8, sla_forward_profiled, library, LIB_PATH, EXPORTS,
+                  STAGES)
+
+__all__ = ["SlaError", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
+           "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES"]

@@ -1,0 +1,161 @@
+// Shared device helpers for the gfx950 (CDNA4) SLA kernels: vector types, MFMA wrappers,
+// dtype conversions and the workspace plan shared by the host launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/sla.h"
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 64;          // query block = key block = 64 tokens
+constexpr float kEps = 1e-6f;       // linear-branch denominator epsilon
+constexpr int kMaxKeyBlocks = 8064;   // top-k keeps a row of 64-bit keys in 64 KB of LDS
+
+// ----------------------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// low / high bf16 of a packed 32-bit word
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (hardware round-to-nearest-even).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Two floats -> packed f16 pair (hardware round-to-nearest-even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ReLU on 8 packed bf16 values held in 4 dwords: a lane is zeroed when its sign bit is set
+// (this also maps -0 to +0, which does not change any product).
+__device__ __forceinline__ u32x4 relu_bf16x8(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t x = w[i];
+    uint32_t lo = (x & 0x8000u) ? 0u : (x & 0xffffu);
+    uint32_t hi = (x & 0x80000000u) ? 0u : (x & 0xffff0000u);
+    r[i] = lo | hi;
+  }
+  return r;
+}
+
+// ----------------------------------------------------------------------------- MFMA
+// 32x32x16 bf16 / f16, fp32 accumulate. Operand layout (64 lanes, 8 elements per lane):
+//   A[i][k]: lane i + 32*(k/8), element k%8;  B[k][j]: lane j + 32*(k/8), element k%8;
+//   C[i][j]: lane j + 32*((i/4)%2), element (i%4) + 4*(i/8).
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// LDS transposing read of 4 x 16-bit values. Within each group of 16 lanes, lane L
+// supplies the address of 4 consecutive 16-bit elements of row r0 + L/4 starting at
+// column c0 + 4*(L%4); lane i of the group receives column c0 + i of rows r0 .. r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
+  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+// Exchange with lane l ^ 32: returns the value held by the other half of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r[0]: lanes < 32 keep their own value, lanes >= 32 get lane l-32's;
+  // r[1]: lanes < 32 get lane l+32's, lanes >= 32 keep their own.
+  const int lane = threadIdx.x & 63;
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// Workgroup index remap so that consecutive logical indices run on the same XCD (the
+// dispatcher assigns workgroup w to XCD w % 8). Bijective for any n.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int nx = 8;
+  const int per = n / nx, rem = n % nx;
+  const int x = w % nx, slot = w / nx;
+  // XCD x owns logical range [start_x, start_x + cnt_x)
+  const int start = x * per + (x < rem ? x : rem);
+  const int cnt = per + (x < rem ? 1 : 0);
+  return slot < cnt ? start + slot : w;
+}
+
+// ----------------------------------------------------------------------------- workspace
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Plan {
+  int B, H, BH, nq, nkv, D, nbq, nbk, k, nchunk;
+  bool in_bf16, out_bf16;
+  // byte offsets into the workspace
+  size_t qbar, kbar, qt, kt, scores, idx;        // router
+  size_t v16, sblk, zblk, spart, zpart, stot, ztot, sc, zc;   // linear branch
+  size_t q8, k8, v8, sq8, sk8, sv8;             // fp8 sparse branch
+  size_t total_route, total_fwd, total_fp8;
+};
+
+constexpr int kSummaryChunk = 8;  // key blocks per partial-total chunk
+
+inline Plan make_plan(const sla_problem& p) {
+  Plan s{};
+  s.B = p.batch; s.H = p.heads; s.BH = p.batch * p.heads;
+  s.nq = p.n_q; s.nkv = p.n_kv; s.D = p.head_dim;
+  s.nbq = (p.n_q + kBlock - 1) / kBlock;
+  s.nbk = (p.n_kv + kBlock - 1) / kBlock;
+  s.k = p.top_k;
+  s.nchunk = (s.nbk + kSummaryChunk - 1) / kSummaryChunk;
+  s.in_bf16 = p.in_dtype == SLA_BF16;
+  s.out_bf16 = p.out_dtype == SLA_BF16;
+  const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  s.qbar = take(BH * nbq * D * 8);
+  s.kbar = take(BH * nbk * D * 8);
+  s.qt = take(BH * nbq * D * 8);
+  s.kt = take(BH * nbk * D * 8);
+  s.scores = take(BH * nbq * nbk * 8);
+  s.idx = take(BH * nbq * (size_t)(s.k > 0 ? s.k : 1) * 4);
+  s.total_route = off;
+  s.v16 = take(BH * nbk * kBlock * D * 2);
+  s.sblk = take(BH * nbk * D * D * 2);
+  s.zblk = take(BH * nbk * D * 4);
+  s.spart = take(BH * (size_t)s.nchunk * D * D * 4);
+  s.zpart = take(BH * (size_t)s.nchunk * D * 4);
+  s.stot = take(BH * D * D * 4);
+  s.ztot = take(BH * D * 4);
+  s.sc = take(BH * nbq * D * D * 2);
+  s.zc = take(BH * nbq * D * 4);
+  s.total_fwd = off;
+  s.q8 = take(BH * nbq * kBlock * D);
+  s.k8 = take(BH * nbk * kBlock * D);
+  s.v8 = take(BH * nbk * kBlock * D);
+  s.sq8 = take(BH * nbq * 4);
+  s.sk8 = take(BH * nbk * 4);
+  s.sv8 = take(BH * nbk * 4);
+  s.total_fp8 = off;
+  return s;
+}
+
+}  // namespace sla

@@ -1,0 +1,23 @@
+// Host-side launchers of the SLA kernels (one translation unit per kernel family).
+#pragma once
+#include "common.h"
+
+namespace sla {
+
+// Router: pool Q (and K if pool_k), project, score, top-k -> idx.
+hipError_t launch_route(const Plan& s, const void* q, const void* k, const float* pq,
+                        const float* pk, int32_t* idx, char* ws, bool pool_k, hipStream_t st);
+
+// Linear branch, part 1 (independent of routing): per key block phi(K)^T V, sum phi(K),
+// pooled K means, f16 copy of V, and the per-head totals.
+hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, char* ws, hipStream_t st);
+
+// Linear branch, part 2: complement = total - selected, per query block.
+hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);
+
+// Sparse branch (bf16 MFMA for Q K^T, f16 MFMA for P V) with the linear apply and the
+// alpha mix fused into its epilogue.
+hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                         const float* alpha, void* o, char* ws, hipStream_t st);
+
+}  // namespace sla

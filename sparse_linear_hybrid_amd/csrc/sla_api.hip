@@ -1,0 +1,137 @@
+// C ABI entry points (include/sla.h): argument validation, workspace plan and the launch
+// sequence. Validation happens before anything is enqueued.
+#include "common.h"
+#include "kernels.h"
+
+using namespace sla;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sla_status check_problem(const sla_problem* p) {
+  if (!p) return SLA_ERR_NULL;
+  if (p->batch < 1 || p->heads < 1 || p->n_q < 1 || p->n_kv < 1) return SLA_ERR_SHAPE;
+  if (p->in_dtype != SLA_F32 && p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  if (p->out_dtype != SLA_F32 && p->out_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return SLA_ERR_UNSUPPORTED;
+  if (p->block != kBlock) return SLA_ERR_UNSUPPORTED;
+  const long long nbq = (p->n_q + kBlock - 1) / kBlock;
+  const long long nbk = (p->n_kv + kBlock - 1) / kBlock;
+  if (nbk > kMaxKeyBlocks) return SLA_ERR_UNSUPPORTED;
+  // grid sizes: one workgroup per (batch*head, query block) must fit a 1-D grid
+  const long long rows = (long long)p->batch * p->heads * nbq;
+  if (rows > 0x7fffffffLL || (long long)p->batch * p->heads > 65535) return SLA_ERR_SHAPE;
+  if (p->top_k < 0 || p->top_k > nbk) return SLA_ERR_TOPK;
+  return SLA_OK;
+}
+
+sla_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!x) return SLA_ERR_NULL;
+  for (const void* x : ps)
+    if (!aligned16(x)) return SLA_ERR_ALIGN;
+  return SLA_OK;
+}
+
+sla_status forward_impl(const sla_problem* p, const void* q, const void* k, const void* v,
+                        const float* proj_q, const float* proj_k, const float* alpha, void* o,
+                        int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, bool fp8, hipEvent_t* ev) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  if (fp8 && p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  st = check_ptrs({q, k, v, proj_q, proj_k, alpha, o});
+  if (st != SLA_OK) return st;
+  if (block_idx && !aligned16(block_idx)) return SLA_ERR_ALIGN;
+  const Plan s = make_plan(*p);
+  const size_t need = fp8 ? s.total_fp8 : s.total_fwd;
+  if (!workspace || workspace_bytes < need) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  if (fp8) return SLA_ERR_UNSUPPORTED;   // quantised sparse kernel: not built yet
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
+  auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
+  if (mark(2 * SLA_STAGE_KV_SUMMARY) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_kv_summary(s, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_KV_SUMMARY + 1) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_ROUTE) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_ROUTE + 1) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_COMPLEMENT) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_complement(s, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_COMPLEMENT + 1) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_SPARSE) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_sparse(s, q, k, idx, alpha, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_SPARSE + 1) != hipSuccess) return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sla_workspace_size(const sla_problem* p, int fp8) {
+  if (check_problem(p) != SLA_OK) return 0;
+  const Plan s = make_plan(*p);
+  return fp8 ? s.total_fp8 : s.total_fwd;
+}
+
+sla_status sla_route(const sla_problem* p, const void* q, const void* k, const float* proj_q,
+                     const float* proj_k, int32_t* block_idx, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  st = check_ptrs({q, k, proj_q, proj_k, block_idx});
+  if (st != SLA_OK) return st;
+  const Plan s = make_plan(*p);
+  if (!workspace || workspace_bytes < s.total_route) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  if (launch_route(s, q, k, proj_q, proj_k, block_idx, static_cast<char*>(workspace),
+                   /*pool_k=*/true, stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
+sla_status sla_forward(const sla_problem* p, const void* q, const void* k, const void* v,
+                       const float* proj_q, const float* proj_k, const float* alpha, void* o,
+                       int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
+                      workspace_bytes, stream, false, nullptr);
+}
+
+sla_status sla_forward_fp8(const sla_problem* p, const void* q, const void* k, const void* v,
+                           const float* proj_q, const float* proj_k, const float* alpha, void* o,
+                           int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
+                      workspace_bytes, stream, true, nullptr);
+}
+
+sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void* k,
+                                const void* v, const float* proj_q, const float* proj_k,
+                                const float* alpha, void* o, int32_t* block_idx,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                int fp8, hipEvent_t* events) {
+  return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
+                      workspace_bytes, stream, fp8 != 0, events);
+}
+
+const char* sla_status_string(sla_status s) {
+  switch (s) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_NULL: return "a required pointer is NULL";
+    case SLA_ERR_SHAPE: return "a size is out of range";
+    case SLA_ERR_DTYPE: return "unsupported dtype";
+    case SLA_ERR_TOPK: return "top_k out of range";
+    case SLA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SLA_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,187 @@
+"""ctypes binding of libsla.so (include/sla.h).
+
+Argument marshalling only: tensors are passed as device pointers, the current torch stream
+as the HIP stream, and every step of the computation runs in the library's HIP kernels.
+Device memory for outputs and the workspace is allocated with torch (the library itself
+never allocates). There is no fallback: the library is loaded on first use and a missing
+library raises ImportError there.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsla.so")
+
+SLA_F32, SLA_BF16 = 0, 1
+STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE",
+          4: "SLA_ERR_TOPK", 5: "SLA_ERR_ALIGN", 6: "SLA_ERR_WORKSPACE",
+          7: "SLA_ERR_UNSUPPORTED", 8: "SLA_ERR_HIP"}
+EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
+           "sla_forward_profiled", "sla_status_string")
+STAGES = ("kv_summary", "route", "complement", "sparse")
+
+
+class SlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({library().sla_status_string(status).decode()})")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("n_q", ctypes.c_int32),
+                ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sparse_linear_hybrid_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)
+    pp = ctypes.POINTER(Problem)
+    lib.sla_workspace_size.argtypes = [pp, ctypes.c_int]
+    lib.sla_workspace_size.restype = sz
+    lib.sla_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_route.restype = ctypes.c_int
+    for name in ("sla_forward", "sla_forward_fp8"):
+        f = getattr(lib, name)
+        f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    lib.sla_forward_profiled.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                         ctypes.c_int, vp]
+    lib.sla_forward_profiled.restype = ctypes.c_int
+    lib.sla_status_string.argtypes = [ctypes.c_int]
+    lib.sla_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libsla.so (loaded on first use; raises ImportError if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return SLA_BF16
+    if t == torch.float32:
+        return SLA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, top_k: int, block: int = 64,
+                 out_dtype: torch.dtype = torch.float32) -> Problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [batch, heads, tokens, head_dim]")
+    B, H, nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
+    return Problem(B, H, nq, k.shape[2], d, block, top_k, _dtype_code(q.dtype),
+                   _dtype_code(out_dtype))
+
+
+def workspace_size(p: Problem, fp8: bool = False) -> int:
+    return int(library().sla_workspace_size(ctypes.byref(p), int(fp8)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(p: Problem, fp8: bool, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    need = workspace_size(p, fp8)
+    if need == 0:
+        raise SlaError(2, "sla_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def sla_route(q, k, proj_q, proj_k, top_k: int, block: int = 64,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Router: int32 block indices [B, H, ceil(n_q/block), top_k], ascending per row."""
+    p = make_problem(q, k, top_k, block)
+    ws = _workspace(p, False, q.device, workspace)
+    idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                      device=q.device)
+    st = library().sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k), _ptr(idx),
+                        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_route")
+    return idx
+
+
+def _forward(name: str, q, k, v, proj_q, proj_k, alpha, top_k: int, block: int,
+             out_dtype: torch.dtype, return_idx: bool, workspace, out) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    p = make_problem(q, k, top_k, block, out_dtype)
+    fp8 = name == "sla_forward_fp8"
+    ws = _workspace(p, fp8, q.device, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    idx = None
+    if return_idx:
+        idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                          device=q.device)
+    st = getattr(library(), name)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                             _ptr(proj_k), _ptr(alpha), _ptr(out), _ptr(idx), _ptr(ws),
+                             ctypes.c_size_t(ws.numel()), _stream(q.device))
+    if st != 0:
+        raise SlaError(st, name)
+    return out, idx
+
+
+def sla_forward(q, k, v, proj_q, proj_k, alpha, top_k: int, block: int = 64,
+                out_dtype: torch.dtype = torch.float32, return_idx: bool = True,
+                workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """SLA2 forward (bf16 sparse branch). Returns (O, block_idx or None)."""
+    return _forward("sla_forward", q, k, v, proj_q, proj_k, alpha, top_k, block, out_dtype,
+                    return_idx, workspace, out)
+
+
+def sla_forward_fp8(q, k, v, proj_q, proj_k, alpha, top_k: int, block: int = 64,
+                    out_dtype: torch.dtype = torch.float32, return_idx: bool = True,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """SLA2 forward with the E4M3 sparse branch. Returns (O, block_idx or None)."""
+    return _forward("sla_forward_fp8", q, k, v, proj_q, proj_k, alpha, top_k, block, out_dtype,
+                    return_idx, workspace, out)
+
+
+def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8: bool = False,
+                         block: int = 64, out_dtype: torch.dtype = torch.float32,
+                         workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None):
+    """sla_forward / sla_forward_fp8 that also records ``events`` (2 per stage, in the order
+    of STAGES: before, after) on the current stream. ``events``: ctypes array of
+    hipEvent_t handles created by the caller. Returns O."""
+    p = make_problem(q, k, top_k, block, out_dtype)
+    ws = _workspace(p, fp8, q.device, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                                   _ptr(proj_k), _ptr(alpha), _ptr(out), None, _ptr(ws),
+                                   ctypes.c_size_t(ws.numel()), _stream(q.device), int(fp8),
+                                   events)
+    if st != 0:
+        raise SlaError(st, "sla_forward_profiled")
+    return out
