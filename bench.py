@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the SLA2 sparse-linear attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video95]
+
+One step is one full forward (router, linear summaries, complement, sparse attention with
+the fused linear apply and mix) over the workload's synthetic inputs, which are resident in
+HBM before timing starts. Prints ONE JSON line with the latency, the roofline of the
+dominant kernel (the sparse-attention kernel, timed with HIP events that the library
+records around it on the same stream), the dense-attention baseline on the same GPU and
+the CPU oracle baseline.
+
+Other modes:
+    --profile            only warm-up + K plain forward calls and a 1 GiB copy (short runs
+                         under rocprofv3; the copy calibrates the memory counters)
+    --summarize-pmc DIR  turn rocprofv3 --pmc CSV output into profiles/*_traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-linear attn fwd latency (ms) + effective TFLOP/s and % MFMA/HBM peak"
+PEAK_BF16 = 2.5e15
+PEAK_FP8 = 5.0e15
+PEAK_HBM = 8.0e12
+SPARSE_SOURCES = ["sparse_linear_hybrid_amd/csrc/sparse.hip", "sparse_linear_hybrid_amd/csrc/common.h"]
+TRAFFIC_FILE = "profiles/sparse_attn_{workload}_traffic.json"
+COPY_BYTES = 1 << 30
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# --------------------------------------------------------------------------- algorithmic work
+def work(p, fp8=False):
+    """Algorithmic FLOPs / bytes of each stage for problem p (see the design notes)."""
+    BH, d, b = p.batch * p.heads, p.head_dim, 64
+    pairs = BH * p.nbq * p.top_k
+    sparse_flops = pairs * 4 * b * b * d + BH * p.nbq * 2 * b * d * d   # QK^T + PV + apply
+    elt = 2 if p.dtype == "bf16" else 4
+    kv_bytes = (2 * BH * p.n_kv * d * elt                  # read K, V
+                + BH * p.nbk * d * d * 2                  # write S_j (bf16)
+                + BH * p.nbk * b * d * 2)                 # write f16 V
+    dense_flops = 4 * BH * p.n_q * p.n_kv * d
+    return {"pairs": pairs, "sparse_flops": sparse_flops, "kv_summary_bytes": kv_bytes,
+            "dense_flops": dense_flops}
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(x, n_heads_sample=4):
+    """The oracle, as it stands, on a bounded sample: n complete heads of the workload;
+    scaled to the whole workload (all heads) in ms."""
+    import numpy as np
+    from oracle import sla_oracle as so
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    except Exception:   # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    p = x.problem
+    pairs = [(b, h) for b in range(p.batch) for h in range(p.heads)][:n_heads_sample]
+    t0 = time.perf_counter()
+    so.forward(x, heads=pairs)
+    dt = time.perf_counter() - t0
+    total = p.batch * p.heads
+    return {"value": dt * 1e3 * total / len(pairs), "unit": "ms", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(pairs)} of {total} (batch, head) pairs computed in full "
+                      f"({dt:.1f} s), scaled to all pairs"}
+
+
+# --------------------------------------------------------------------------- traffic summary
+def read_traffic(workload):
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != sources_sha(SPARSE_SOURCES):
+        return None          # the kernel changed since the counters were taken
+    return rec.get("traffic_bytes_per_launch")
+
+
+def summarize_pmc(fetch_dir, write_dir, workload):
+    """profiles/sparse_attn_<workload>_traffic.json from two rocprofv3 --pmc runs."""
+    def rows(d):
+        out = []
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                out += list(csv.DictReader(f))
+        return out
+
+    def per_kernel(rs, counter):
+        acc = {}
+        for r in rs:
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+        return acc
+
+    def pick(acc, needle):
+        for k, v in acc.items():
+            if needle in k:
+                return sum(v) / len(v)
+        return None
+
+    f = per_kernel(rows(fetch_dir), "FETCH_SIZE")
+    w = per_kernel(rows(write_dir), "WRITE_SIZE")
+    sp_f, sp_w = pick(f, "sparse_attn_kernel"), pick(w, "sparse_attn_kernel")
+    cp_f = pick(f, "copy") or pick(f, "elementwise")
+    cp_w = pick(w, "copy") or pick(w, "elementwise")
+    sf = (cp_f * 1024) / COPY_BYTES if cp_f else None       # KiB counted per real byte read
+    sw = (cp_w * 1024) / COPY_BYTES if cp_w else None
+    rec = {
+        "workload": workload,
+        "source_sha256": sources_sha(SPARSE_SOURCES),
+        "fetch_kib_per_launch": sp_f, "write_kib_per_launch": sp_w,
+        "copy_fetch_kib": cp_f, "copy_write_kib": cp_w, "copy_bytes": COPY_BYTES,
+        "fetch_scale": sf, "write_scale": sw,
+        "traffic_bytes_per_launch": (sp_f * 1024 / sf + sp_w * 1024 / sw)
+        if (sp_f and sp_w and sf and sw) else None,
+    }
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video95")
+    ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each (batch, head) is independent; sharding is described in the design "
+              "notes, not built). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import ctypes
+    import numpy as np
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import sparse_linear_hybrid_amd as sla
+    from workloads import make_inputs, sha256_of
+
+    fp8 = args.workload.endswith("_fp8")
+    dev = torch.device("cuda:0")
+    x = make_inputs(args.workload)
+    p = x.problem
+
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k, v, pq, pk, al = (t(a) for a in (x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha))
+    prob = sla.make_problem(q, k, p.top_k)
+    ws = torch.empty(sla.workspace_size(prob, fp8), dtype=torch.uint8, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    fwd_fn = sla.sla_forward_fp8 if fp8 else sla.sla_forward
+
+    def fwd():
+        fwd_fn(q, k, v, pq, pk, al, p.top_k, return_idx=False, workspace=ws, out=out)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+
+    if args.profile:
+        for _ in range(args.steps):
+            fwd()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": args.workload, "steps": args.steps}))
+        return 0
+
+    # ---------------------------------------------------------------- timed region
+    K = args.steps
+    nst = len(sla.STAGES)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(K)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    handles = [(ctypes.c_void_p * (2 * nst))(*[e.cuda_event for e in row]) for row in evs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        sla.sla_forward_profiled(q, k, v, pq, pk, al, p.top_k, handles[s], fp8=fp8,
+                                 workspace=ws, out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / K
+    stage_ms = {name: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
+                                     for s in range(K)]))
+                for i, name in enumerate(sla.STAGES)}
+
+    w = work(p, fp8)
+    sparse_s = stage_ms["sparse"] * 1e-3
+    peak = PEAK_FP8 if fp8 else PEAK_BF16
+    achieved = w["sparse_flops"] / sparse_s
+    roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / peak, "traffic": read_traffic(args.workload),
+                "kernel": "sparse_attn_kernel", "flops_per_launch": w["sparse_flops"],
+                "avg_launch_ms": stage_ms["sparse"]}
+    kernels = {
+        "stage_ms": stage_ms,
+        "kv_summary_GBps": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / 1e9,
+        "kv_summary_hbm_frac": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM,
+    }
+
+    # ---------------------------------------------------------------- dense baselines
+    dense = None
+    if not args.no_dense:
+        dense = {}
+        try:
+            f = torch.nn.functional.scaled_dot_product_attention
+            if p.dtype == "bf16":
+                for _ in range(2):
+                    f(q, k, v)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = 5
+                a.record()
+                for _ in range(n):
+                    f(q, k, v)
+                b.record()
+                torch.cuda.synchronize()
+                dense["sdpa_bf16_ms"] = a.elapsed_time(b) / n
+        except Exception as ex:  # noqa: BLE001
+            dense["sdpa_error"] = str(ex)[:200]
+        try:
+            all_k = p.nbk
+            ones = torch.ones_like(al)
+            ws2 = torch.empty(sla.workspace_size(sla.make_problem(q, k, all_k), False),
+                              dtype=torch.uint8, device=dev)
+            sla.sla_forward(q, k, v, pq, pk, ones, all_k, return_idx=False, workspace=ws2, out=out)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 3
+            a.record()
+            for _ in range(n):
+                sla.sla_forward(q, k, v, pq, pk, ones, all_k, return_idx=False, workspace=ws2,
+                                out=out)
+            b.record()
+            torch.cuda.synchronize()
+            dense["own_all_blocks_ms"] = a.elapsed_time(b) / n
+            del ws2
+        except Exception as ex:  # noqa: BLE001
+            dense["own_error"] = str(ex)[:200]
+        best = min([v_ for k_, v_ in dense.items() if k_.endswith("_ms")] or [float("nan")])
+        dense["best_dense_ms"] = best
+        dense["speedup_vs_best_dense"] = best / ms
+
+    cpu = None if args.no_cpu else cpu_baseline(x)
+
+    line = {
+        "metric": METRIC, "value": ms, "unit": "ms", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/bf16" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": p.name, "batch": p.batch, "heads": p.heads, "n_q": p.n_q,
+                   "n_kv": p.n_kv, "head_dim": p.head_dim, "block": p.block,
+                   "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
+                   "grid": "x".join(map(str, p.grid)) if p.grid else None,
+                   "parallelism": "single GPU"},
+        "effective_tflops": w["dense_flops"] / (ms * 1e-3) / 1e12,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "dense": dense,
+        "kernels": kernels,
+        "inputs_sha256": sha256_of(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

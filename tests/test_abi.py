@@ -1,0 +1,115 @@
+"""Host-side tests of the C ABI: symbols, validation and workspace sizing.
+
+No compute is launched here: every call below is rejected by argument validation, which
+runs before anything is enqueued, so the fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+sla = pytest.importorskip("sparse_linear_hybrid_amd")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sla.LIB_PATH):
+        pytest.fail("libsla.so is not built (run __graft_entry__.build())")
+    return sla.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sla_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("sla_route", "sla_forward", "sla_forward_fp8", "sla_workspace_size",
+              "sla_status_string", "sla_forward_profiled"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(sla.EXPORTS) == set(declared_functions())
+
+
+def prob(**kw):
+    base = dict(batch=1, heads=2, n_q=300, n_kv=700, head_dim=128, block=64, top_k=3,
+                in_dtype=1, out_dtype=0)
+    base.update(kw)
+    return sla.Problem(**base)
+
+
+FAKE = 0x100000          # aligned, never dereferenced (every call fails validation first)
+MISALIGNED = 0x100004
+
+
+def call_forward(lib, p, q=FAKE, k=FAKE, v=FAKE, pq=FAKE, pk=FAKE, al=FAKE, o=FAKE, idx=None,
+                 ws=FAKE, ws_bytes=0, fn="sla_forward"):
+    vp = ctypes.c_void_p
+    pp = ctypes.byref(p) if p is not None else None
+    return getattr(lib, fn)(pp, vp(q), vp(k), vp(v), vp(pq), vp(pk), vp(al), vp(o), vp(idx),
+                            vp(ws), ctypes.c_size_t(ws_bytes), vp(0))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), "SLA_ERR_SHAPE"), (dict(n_q=0), "SLA_ERR_SHAPE"),
+    (dict(n_kv=-5), "SLA_ERR_SHAPE"), (dict(in_dtype=7), "SLA_ERR_DTYPE"),
+    (dict(out_dtype=3), "SLA_ERR_DTYPE"), (dict(head_dim=96), "SLA_ERR_UNSUPPORTED"),
+    (dict(block=32), "SLA_ERR_UNSUPPORTED"), (dict(top_k=-1), "SLA_ERR_TOPK"),
+    (dict(top_k=12), "SLA_ERR_TOPK"), (dict(n_kv=64 * 8065), "SLA_ERR_UNSUPPORTED"),
+])
+def test_problem_validation(lib, kw, status):
+    code = {v: k for k, v in sla.sla.STATUS.items()}[status]
+    assert call_forward(lib, prob(**kw)) == code
+    assert lib.sla_workspace_size(ctypes.byref(prob(**kw)), 0) == 0
+
+
+def test_pointer_validation(lib):
+    p = prob()
+    assert call_forward(lib, None) == 1
+    assert call_forward(lib, p, q=0) == 1
+    assert call_forward(lib, p, al=0) == 1
+    assert call_forward(lib, p, o=MISALIGNED) == 5
+    assert call_forward(lib, p, idx=MISALIGNED) == 5
+    # valid problem and pointers but no / too small workspace
+    assert call_forward(lib, p, ws=0, ws_bytes=1 << 40) == 6
+    need = lib.sla_workspace_size(ctypes.byref(p), 0)
+    assert call_forward(lib, p, ws_bytes=need - 1) == 6
+    # the fp8 entry point accepts only bf16 inputs
+    assert call_forward(lib, prob(in_dtype=0), fn="sla_forward_fp8") == 3
+    assert call_forward(lib, p, fn="sla_forward_fp8", ws_bytes=need) == 6   # fp8 needs more
+
+
+def test_route_validation(lib):
+    vp = ctypes.c_void_p
+    p = prob()
+    r = lib.sla_route(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(0), vp(FAKE),
+                      ctypes.c_size_t(1 << 30), vp(0))
+    assert r == 1    # block_idx is required
+    r = lib.sla_route(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                      ctypes.c_size_t(0), vp(0))
+    assert r == 6
+
+
+def test_workspace_size_monotone(lib):
+    def ws(**kw):
+        return lib.sla_workspace_size(ctypes.byref(prob(**kw)), 0)
+    base = ws()
+    assert base > 0
+    assert ws(n_q=3000) > base and ws(n_kv=7000) > base and ws(heads=4) > base
+    assert lib.sla_workspace_size(ctypes.byref(prob()), 1) > base
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        assert lib.sla_status_string(code).decode()
+    assert lib.sla_status_string(99) == b"unknown status"
