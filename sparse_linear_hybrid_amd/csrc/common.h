@@ -110,7 +110,7 @@ struct Plan {
   int B, H, BH, nq, nkv, D, nbq, nbk, k, nchunk;
   bool in_bf16, out_bf16;
   // byte offsets into the workspace
-  size_t qbar, kbar, qt, kt, scores, idx;        // router
+  size_t qt, kt, scores, idx;                    // router
   size_t v16, sblk, zblk, spart, zpart, stot, ztot, sc, zc;   // linear branch
   size_t q8, k8, v8, sq8, sk8, sv8;             // fp8 sparse branch
   size_t total_route, total_fwd, total_fp8;
@@ -131,8 +131,6 @@ inline Plan make_plan(const sla_problem& p) {
   const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  s.qbar = take(BH * nbq * D * 8);
-  s.kbar = take(BH * nbk * D * 8);
   s.qt = take(BH * nbq * D * 8);
   s.kt = take(BH * nbk * D * 8);
   s.scores = take(BH * nbq * nbk * 8);

@@ -4,13 +4,14 @@
 
 namespace sla {
 
-// Router: pool Q (and K if pool_k), project, score, top-k -> idx.
+// Router: pool + project Q (and K if pool_k), score, top-k -> idx.
 hipError_t launch_route(const Plan& s, const void* q, const void* k, const float* pq,
                         const float* pk, int32_t* idx, char* ws, bool pool_k, hipStream_t st);
 
 // Linear branch, part 1 (independent of routing): per key block phi(K)^T V, sum phi(K),
-// pooled K means, f16 copy of V, and the per-head totals.
-hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, char* ws, hipStream_t st);
+// the projected pooled K (for the router), an f16 copy of V, and the per-head totals.
+hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk, char* ws,
+                             hipStream_t st);
 
 // Linear branch, part 2: complement = total - selected, per query block.
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);

@@ -62,45 +62,34 @@ __device__ __forceinline__ void block_mean_finish(double (&acc)[8], int nrows, d
   __syncthreads();
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, double* __restrict__ mean,
-                                                   int n, int nb) {
-  __shared__ double lds[256 / (D / 8) * D];
-  const int j = blockIdx.x, bh = blockIdx.y;
-  const int row0 = j * kBlock;
-  const int nrows = min(kBlock, n - row0);
-  double acc[8];
-  block_sum_partial<T, D>(x + (size_t)bh * n * D, row0, nrows, acc);
-  block_mean_finish<D>(acc, nrows, lds, mean + ((size_t)bh * nb + j) * D);
-}
+// Pool + project for PB consecutive blocks of one (batch, head): block means over the
+// valid tokens (float64 sums, exact for bf16 data) and x~ = mean @ P in float64. Reading P
+// once per PB blocks keeps the projection off the critical path.
+constexpr int PB = 8;
 
-// ----------------------------------------------------------------------------- projection
-// out[row][c] = sum_r in[row][r] * P[r][c] in float64; 16 rows per workgroup, one thread
-// per output channel.
-template <int D>
-__global__ __launch_bounds__(D) void project_kernel(const double* __restrict__ in,
-                                                    const float* __restrict__ P,
-                                                    double* __restrict__ out, int rows) {
-  constexpr int R = 16;
-  __shared__ double xs[R][D];
-  const int row0 = blockIdx.x * R;
-  const int c = threadIdx.x;
-  for (int rr = 0; rr < R; ++rr) {
-    const int row = row0 + rr;
-    xs[rr][c] = row < rows ? in[(size_t)row * D + c] : 0.0;
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_project_kernel(const T* __restrict__ x,
+                                                           const float* __restrict__ P,
+                                                           double* __restrict__ out, int n, int nb) {
+  constexpr int RPP = 256 / (D / 8);
+  __shared__ double part[RPP * D];
+  __shared__ double means[PB][D];
+  const int j0 = blockIdx.x * PB, bh = blockIdx.y;
+  const int nblk = min(PB, nb - j0);
+  const T* xb = x + (size_t)bh * n * D;
+  const int t = threadIdx.x;
+  for (int b = 0; b < nblk; ++b) {
+    const int row0 = (j0 + b) * kBlock;
+    const int nrows = min(kBlock, n - row0);
+    double acc[8];
+    block_sum_partial<T, D>(xb, row0, nrows, acc);
+    block_mean_finish<D>(acc, nrows, part, &means[b][0]);
   }
-  __syncthreads();
-  double acc[R];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) acc[rr] = 0.0;
-  for (int r = 0; r < D; ++r) {
-    const double p = (double)P[r * D + c];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) acc[rr] = fma(xs[rr][r], p, acc[rr]);
-  }
-  for (int rr = 0; rr < R; ++rr) {
-    const int row = row0 + rr;
-    if (row < rows) out[(size_t)row * D + c] = acc[rr];
+  for (int b = t / D; b < nblk; b += 256 / D) {
+    const int c = t % D;
+    double acc = 0.0;
+    for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)P[r * D + c], acc);
+    out[((size_t)bh * nb + j0 + b) * D + c] = acc;
   }
 }
 
@@ -260,27 +249,24 @@ template <int D>
 static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, const float* pq,
                                  const float* pk, int32_t* idx, char* ws, bool pool_k,
                                  hipStream_t st) {
-  double* qbar = reinterpret_cast<double*>(ws + s.qbar);
-  double* kbar = reinterpret_cast<double*>(ws + s.kbar);
   double* qt = reinterpret_cast<double*>(ws + s.qt);
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   double* sc = reinterpret_cast<double*>(ws + s.scores);
+  const dim3 gq((s.nbq + PB - 1) / PB, s.BH), gk((s.nbk + PB - 1) / PB, s.BH);
   if (s.in_bf16) {
-    hipLaunchKernelGGL((pool_kernel<uint16_t, D>), dim3(s.nbq, s.BH), dim3(256), 0, st,
-                       (const uint16_t*)q, qbar, s.nq, s.nbq);
+    hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gq, dim3(256), 0, st,
+                       (const uint16_t*)q, pq, qt, s.nq, s.nbq);
     if (pool_k)
-      hipLaunchKernelGGL((pool_kernel<uint16_t, D>), dim3(s.nbk, s.BH), dim3(256), 0, st,
-                         (const uint16_t*)k, kbar, s.nkv, s.nbk);
+      hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gk, dim3(256), 0, st,
+                         (const uint16_t*)k, pk, kt, s.nkv, s.nbk);
   } else {
-    hipLaunchKernelGGL((pool_kernel<float, D>), dim3(s.nbq, s.BH), dim3(256), 0, st,
-                       (const float*)q, qbar, s.nq, s.nbq);
+    hipLaunchKernelGGL((pool_project_kernel<float, D>), gq, dim3(256), 0, st, (const float*)q,
+                       pq, qt, s.nq, s.nbq);
     if (pool_k)
-      hipLaunchKernelGGL((pool_kernel<float, D>), dim3(s.nbk, s.BH), dim3(256), 0, st,
-                         (const float*)k, kbar, s.nkv, s.nbk);
+      hipLaunchKernelGGL((pool_project_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k,
+                         pk, kt, s.nkv, s.nbk);
   }
-  const int rq = s.BH * s.nbq, rk = s.BH * s.nbk;
-  hipLaunchKernelGGL((project_kernel<D>), dim3((rq + 15) / 16), dim3(D), 0, st, qbar, pq, qt, rq);
-  hipLaunchKernelGGL((project_kernel<D>), dim3((rk + 15) / 16), dim3(D), 0, st, kbar, pk, kt, rk);
+  const int rq = s.BH * s.nbq;
   hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
                      dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk);
   if (s.k > 0) {

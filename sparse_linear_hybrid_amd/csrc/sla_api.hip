@@ -53,7 +53,7 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
   if (mark(2 * SLA_STAGE_KV_SUMMARY) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_kv_summary(s, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_kv_summary(s, k, v, proj_k, ws, stream) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_KV_SUMMARY + 1) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_ROUTE) != hipSuccess) return SLA_ERR_HIP;
   if (launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream) != hipSuccess)

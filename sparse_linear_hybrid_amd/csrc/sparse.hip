@@ -2,28 +2,28 @@
 // blocks) with the linear-branch apply and the alpha mix (section 2.A) fused into the
 // epilogue.
 //
-// One workgroup of two waves per (batch*head, query block). Both waves hold all 64 query
-// rows; wave w takes keys 32w .. 32w+31 of every routed 64-key tile, so each K/V element
-// staged in LDS is read by exactly one wave. Each wave keeps its own running max, row sum
-// and output partial (an online softmax over its half of the keys); the two partials are
-// merged once at the end.
+// A workgroup handles QB consecutive query blocks of one (batch, head) with 2*QB waves;
+// wave w owns the 32 query rows 32*(w%2) .. +31 of query block w/2 and all 64 keys of each
+// key tile, so every softmax row lives in one wave. The workgroup walks the ascending union
+// of its query blocks' selections: neighbouring query blocks mostly select the same key
+// blocks, so each shared K/V tile is staged in LDS once for all of them; a wave skips the
+// tiles its own query block did not select.
 //
-// Everything is computed transposed so that no register shuffles are needed:
-//   S^T (keys x queries) = K Q^T            bf16 MFMA 32x32x16, fp32 accumulate
-//   O^T (channels x queries) += V^T P^T     f16 MFMA 32x32x16 (P in [0, 2^8], f16 keeps
-//                                            11 significant bits), fp32 accumulate
-// The S^T accumulator layout (lane = query column, 16 key rows per lane) is exactly the
-// B-operand layout P^T needs, up to a fixed permutation of the keys inside each 16-key
+// Per tile and wave, everything is computed transposed so that no register shuffles are
+// needed:
+//   S^T (64 keys x 32 queries) = K Q^T        bf16 MFMA 32x32x16, fp32 accumulate
+//   O^T (d x 32 queries)     += V^T P^T       f16 MFMA 32x32x16 (P in [0, 2^8]), fp32
+// The S^T accumulator layout (lane = query column, 16 key rows per lane per 32-key half) is
+// the B-operand layout P^T needs, up to a fixed permutation of the keys inside each 16-key
 // step; the V^T operand is read from the row-major V tile with transposing LDS reads in the
-// same permuted key order.
+// same permuted key order. LDS rows are XOR-swizzled in 16-byte chunks so that both the K
+// fragment reads and the transposing V reads are free of bank conflicts.
 //
-// Epilogue: O_s = O / l; O_l^T = S_c^T phi(Q)^T / (phi(Q) . z_c + eps) on bf16 MFMA (the
-// phi(Q)^T operand is the register-resident Q fragment with ReLU applied);
+// Epilogue per wave: O_s = O / l; O_l^T = S_c^T phi(Q)^T / (phi(Q) . z_c + eps) on bf16 MFMA
+// (phi(Q)^T is the register-resident Q fragment with ReLU applied);
 // O = alpha O_s + (1 - alpha) O_l.
 #include "common.h"
 #include "kernels.h"
-
-#include <type_traits>
 
 namespace sla {
 
@@ -33,15 +33,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;      // finite "minus infinity" for running maxima
 constexpr float kRescaleSlack = 8.0f;    // keep a stale max while p <= 2^8
 
-// P^T-matched V^T fragment: lane row x0 + lane%32; reduction slot e holds key
-// k0 + 4h + e (e < 4) or k0 + 8 + 4h + (e - 4) (e >= 4), h = lane / 32.
-__device__ __forceinline__ u32x4 frag_tr_perm(const uint16_t* M, int stride, int x0, int k0) {
+// Element offset of (row, col) in a swizzled LDS tile with D 16-bit columns per row: the
+// 16-byte chunk index is XORed with the row (mod chunks per row).
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int CH = D / 8;
+  return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
+}
+
+// P^T-matched V^T fragment from a swizzled row-major [key][channel] tile: lane row (channel)
+// x0 + lane%32; reduction slot e holds key k0 + 4h + e (e < 4) or k0 + 8 + 4h + (e - 4)
+// (e >= 4), h = lane / 32.
+template <int D>
+__device__ __forceinline__ u32x4 vt_frag(const uint16_t* M, int x0, int k0) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, L = lane & 15;
   const int row = k0 + 4 * (g >> 1) + (L >> 2);
   const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const u32x2 lo = lds_read_tr16(M + row * stride + col);
-  const u32x2 hi = lds_read_tr16(M + (row + 8) * stride + col);
+  const u32x2 lo = lds_read_tr16(M + swz<D>(row, col));
+  const u32x2 hi = lds_read_tr16(M + swz<D>(row + 8, col));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -49,12 +59,12 @@ struct SparseArgs {
   const void* q;
   const void* k;
   const uint16_t* v16;     // f16 [BH][nbk*64][D], rows beyond n_kv are zero
-  const int32_t* idx;      // [BH][nbq][top_k]
+  const int32_t* idx;      // [BH][nbq][top_k], ascending
   const uint16_t* sc;      // bf16 S_c^T [BH][nbq][D(c)][D(r)]
   const float* zc;         // [BH][nbq][D]
   const float* alpha;      // [H][D]
   void* out;
-  int nq, nkv, nbq, nbk, topk, H, total;
+  int nq, nkv, nbq, nbk, topk, H, ngroups, total;
 };
 
 template <typename T>
@@ -77,291 +87,263 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t h = pack_bf16(x[2 * e], x[2 * e + 1]);
-    hi[e] = h;
-    lo[e] = pack_bf16(x[2 * e] - bf16_lo(h), x[2 * e + 1] - bf16_hi(h));
+    const uint32_t hv = pack_bf16(x[2 * e], x[2 * e + 1]);
+    hi[e] = hv;
+    lo[e] = pack_bf16(x[2 * e] - bf16_lo(hv), x[2 * e + 1] - bf16_hi(hv));
   }
 }
 
-template <typename T, int D, bool OUT_BF16>
-__global__ __launch_bounds__(128) void sparse_attn_kernel(SparseArgs a) {
+template <typename T, int D, int QB, bool OUT_BF16>
+__global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
-  constexpr int LS = D + 8;             // padded LDS row, elements
-  constexpr int KS = D / 16;            // 16-channel reduction steps for Q K^T
-  constexpr int CT = D / 32;            // 32-channel tiles of the output
-  constexpr int TPR = D / 8;            // 16-byte chunks per row
-  constexpr int CPT = 64 * TPR / 128;   // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[SPLIT ? 2 : 1][SPLIT ? 64 * LS : 8];
+  constexpr int NT = 128 * QB;             // threads
+  constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
+  constexpr int CT = D / 32;               // 32-channel tiles of the output
+  constexpr int CH = D / 8;                // 16-byte chunks per row
+  constexpr int CPT = 64 * CH / NT;        // chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Kl[SPLIT ? 2 : 1][SPLIT ? 64 * D : 8];
 
   const int wid = xcd_remap(blockIdx.x, a.total);
-  const int bh = wid / a.nbq, i = wid % a.nbq;
+  const int bh = wid / a.ngroups, grp = wid % a.ngroups;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
-  const int q0 = i * kBlock;
-  const T* qb = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
+  const int qb = wv >> 1;                       // this wave's query block within the group
+  const int iq = grp * QB + qb;                 // its query block index
+  const bool active = iq < a.nbq;
+  const int qrow0 = iq * kBlock + 32 * (wv & 1);
+  const T* qb_ptr = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* kb = reinterpret_cast<const T*>(a.k) + (size_t)bh * a.nkv * D;
   const uint16_t* vb = a.v16 + (size_t)bh * a.nbk * kBlock * D;
-  const int32_t* sel = a.idx + ((size_t)bh * a.nbq + i) * a.topk;
+  const int k = a.topk;
 
-  // Q^T fragments (B operand): lane column q = 32 t + l32, channels 16 s + 8 h .. +7
-  u32x4 qf[2][KS];
-  u32x4 ql[2][SPLIT ? KS : 1];
+  // selection lists of the group's query blocks (absent blocks have empty lists)
+  const int32_t* selp[QB];
+  int nsel[QB], ptr[QB];
 #pragma unroll
-  for (int tq = 0; tq < 2; ++tq) {
-    const int q = q0 + 32 * tq + l32;
+  for (int b = 0; b < QB; ++b) {
+    const int ib = grp * QB + b;
+    selp[b] = a.idx + ((size_t)bh * a.nbq + (ib < a.nbq ? ib : 0)) * k;
+    nsel[b] = ib < a.nbq ? k : 0;
+    ptr[b] = 0;
+  }
+  // next element of the ascending union: key block and membership flags
+  auto next_union = [&](int& j, int& flags) {
+    j = 0x7fffffff;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (ptr[b] < nsel[b]) j = min(j, selp[b][ptr[b]]);
+    flags = 0;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (ptr[b] < nsel[b] && selp[b][ptr[b]] == j) { flags |= 1 << b; ++ptr[b]; }
+    return flags != 0;
+  };
+
+  // Q^T fragments (B operand): lane column q = qrow0 + l32, channels 16 s + 8 h .. +7
+  u32x4 qf[KS];
+  u32x4 ql[SPLIT ? KS : 1];
+  {
+    const int q = qrow0 + l32;
+    const bool ok = active && q < a.nq;
+    const int qc = ok ? q : 0;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qf[tq][s] = u32x4{0, 0, 0, 0};
       if constexpr (SPLIT) {
-        ql[tq][s] = u32x4{0, 0, 0, 0};
-        if (q < a.nq)
-          load_split_bf16x8(reinterpret_cast<const float*>(qb) + (size_t)q * D + 16 * s + 8 * h,
-                            qf[tq][s], ql[tq][s]);
+        load_split_bf16x8(reinterpret_cast<const float*>(qb_ptr) + (size_t)qc * D + 16 * s + 8 * h,
+                          qf[s], ql[s]);
+        if (!ok) ql[s] = u32x4{0, 0, 0, 0};
       } else {
-        if (q < a.nq) qf[tq][s] = load_bf16x8(qb + (size_t)q * D + 16 * s + 8 * h);
+        qf[s] = load_bf16x8(qb_ptr + (size_t)qc * D + 16 * s + 8 * h);
       }
+      if (!ok) qf[s] = u32x4{0, 0, 0, 0};
     }
   }
 
-  f32x16 o[CT][2];
+  f32x16 o[CT];
 #pragma unroll
-  for (int c = 0; c < CT; ++c) o[c][0] = o[c][1] = f32x16{};
-  float m[2] = {kNegBig, kNegBig};
-  float l[2] = {0.f, 0.f};
+  for (int c = 0; c < CT; ++c) o[c] = f32x16{};
+  float m = kNegBig, l = 0.f;
   const float qk_scale = kLog2e / sqrtf((float)D);
 
-  // tile staging: registers -> LDS
+  // tile staging: registers -> swizzled LDS (branch-free: rows beyond n_kv read a valid row
+  // and are zeroed)
   u32x4 kreg[CPT], vreg[CPT], klreg[SPLIT ? CPT : 1];
   auto load_tile = [&](int j) {
     const int row0 = j * kBlock;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int cidx = t + 128 * u;
-      const int r = cidx / TPR, c8 = cidx % TPR;
-      kreg[u] = u32x4{0, 0, 0, 0};
+      const int id = t + NT * u;
+      const int r = id / CH, c = id % CH;
+      const bool ok = row0 + r < a.nkv;
+      const size_t goff = (size_t)(ok ? row0 + r : a.nkv - 1) * D + c * 8;
       if constexpr (SPLIT) {
-        klreg[u] = u32x4{0, 0, 0, 0};
-        if (row0 + r < a.nkv)
-          load_split_bf16x8(reinterpret_cast<const float*>(kb) + (size_t)(row0 + r) * D + c8 * 8,
-                            kreg[u], klreg[u]);
+        load_split_bf16x8(reinterpret_cast<const float*>(kb) + goff, kreg[u], klreg[u]);
+        if (!ok) klreg[u] = u32x4{0, 0, 0, 0};
       } else {
-        if (row0 + r < a.nkv) kreg[u] = load_bf16x8(kb + (size_t)(row0 + r) * D + c8 * 8);
+        kreg[u] = load_bf16x8(kb + goff);
       }
-      vreg[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)(row0 + r) * D + c8 * 8);
+      if (!ok) kreg[u] = u32x4{0, 0, 0, 0};
+      vreg[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)(row0 + r) * D + c * 8);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
-      const int cidx = t + 128 * u;
-      const int r = cidx / TPR, c8 = cidx % TPR;
-      *reinterpret_cast<u32x4*>(&Ks[buf][r * LS + c8 * 8]) = kreg[u];
-      *reinterpret_cast<u32x4*>(&Vs[buf][r * LS + c8 * 8]) = vreg[u];
-      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(&Kl[buf][r * LS + c8 * 8]) = klreg[u];
+      const int id = t + NT * u;
+      const int r = id / CH, c = id % CH;
+      const int off = swz<D>(r, c * 8);
+      *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kreg[u];
+      *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vreg[u];
+      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(&Kl[buf][off]) = klreg[u];
     }
   };
 
-  const int ntiles = a.topk;
-  if (ntiles > 0) {
-    load_tile(sel[0]);
+  int j_cur, f_cur;
+  bool have = next_union(j_cur, f_cur);
+  if (have) {
+    load_tile(j_cur);
     store_tile(0);
-    __syncthreads();
   }
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int buf = tt & 1;
-    const int j = sel[tt];
-    if (tt + 1 < ntiles) load_tile(sel[tt + 1]);
-    const uint16_t* Kt = Ks[buf];
-    const uint16_t* Vt = Vs[buf];
-
-    // S^T tile: rows = keys 32 wv + (0..31), columns = queries
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  __syncthreads();
+  int buf = 0;
+  while (have) {
+    int j_nxt, f_nxt;
+    const bool have_nxt = next_union(j_nxt, f_nxt);
+    if (have_nxt) load_tile(j_nxt);
+    if ((f_cur >> qb) & 1) {
+      const uint16_t* Kt = Ks[buf];
+      const uint16_t* Vt = Vs[buf];
+      // S^T: two 32-key halves
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int off = (32 * wv + l32) * LS + 16 * ks + 8 * h;
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
-      s[0] = mfma_bf16(af, qf[0][ks], s[0]);
-      s[1] = mfma_bf16(af, qf[1][ks], s[1]);
-      if constexpr (SPLIT) {
-        const u32x4 al = *reinterpret_cast<const u32x4*>(&Kl[buf][off]);
-        s[0] = mfma_bf16(af, ql[0][ks], s[0]);
-        s[1] = mfma_bf16(af, ql[1][ks], s[1]);
-        s[0] = mfma_bf16(al, qf[0][ks], s[0]);
-        s[1] = mfma_bf16(al, qf[1][ks], s[1]);
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
+          const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
+          s[mt] = mfma_bf16(af, qf[ks], s[mt]);
+          if constexpr (SPLIT) {
+            const u32x4 al = *reinterpret_cast<const u32x4*>(&Kl[buf][off]);
+            s[mt] = mfma_bf16(af, ql[ks], s[mt]);
+            s[mt] = mfma_bf16(al, qf[ks], s[mt]);
+          }
+        }
       }
-    }
-    // key validity (only the last key block can be partial)
-    const int key_base = j * kBlock + 32 * wv;
-    const bool partial = key_base + 32 > a.nkv;
-    float mx[2];
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
+      // scale, mask the tail of a partial last key block, row max over the 64 keys
+      const bool partial = (j_cur + 1) * kBlock > a.nkv;
       float r = kNegBig;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float z = s[tq][e] * qk_scale;
-        if (partial) {
-          const int key = key_base + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= a.nkv) z = -INFINITY;
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float z = s[mt][e] * qk_scale;
+          if (partial) {
+            const int key = j_cur * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+            z = key < a.nkv ? z : -INFINITY;
+          }
+          s[mt][e] = z;
+          r = fmaxf(r, z);
         }
-        s[tq][e] = z;
-        r = fmaxf(r, z);
       }
-      mx[tq] = fmaxf(r, swap_halves(r));
-    }
-    const bool grow = (mx[0] > m[0] + kRescaleSlack) || (mx[1] > m[1] + kRescaleSlack);
-    if (__ballot(grow)) {
+      r = fmaxf(r, swap_halves(r));
+      if (__ballot(r > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, r);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        l *= corr;
 #pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const float mn = fmaxf(m[tq], mx[tq]);
-        const float corr = exp2f(m[tq] - mn);
-        l[tq] *= corr;
-#pragma unroll
-        for (int c = 0; c < CT; ++c) o[c][tq] *= corr;
-        m[tq] = mn;
+        for (int c = 0; c < CT; ++c) o[c] *= corr;
+        m = mn;
       }
-    }
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      float p[16];
+      u32x4 pf[4];
       float rs = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(s[tq][e] - m[tq]);
-        rs += p[e];
+      for (int mt = 0; mt < 2; ++mt) {
+        float p[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(s[mt][e] - m);
+          rs += p[e];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          pf[2 * mt + hh] = u32x4{pack_f16(p[8 * hh + 0], p[8 * hh + 1]), pack_f16(p[8 * hh + 2], p[8 * hh + 3]),
+                                  pack_f16(p[8 * hh + 4], p[8 * hh + 5]), pack_f16(p[8 * hh + 6], p[8 * hh + 7])};
       }
-      l[tq] += rs;
+      l += rs;
+      // O^T += V^T P^T over the 64 keys (four 16-key steps)
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss)
-        pf[tq][ss] = u32x4{pack_f16(p[8 * ss + 0], p[8 * ss + 1]), pack_f16(p[8 * ss + 2], p[8 * ss + 3]),
-                           pack_f16(p[8 * ss + 4], p[8 * ss + 5]), pack_f16(p[8 * ss + 6], p[8 * ss + 7])};
-    }
-    // O^T += V^T P^T over this wave's 32 keys (two 16-key steps)
+      for (int c = 0; c < CT; ++c) {
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-#pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        const u32x4 vf = frag_tr_perm(Vt, LS, 32 * c, 32 * wv + 16 * ss);
-        o[c][0] = mfma_f16(vf, pf[0][ss], o[c][0]);
-        o[c][1] = mfma_f16(vf, pf[1][ss], o[c][1]);
-      }
-    }
-    if (tt + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---------------------------------------------------------------- merge the two waves
-  float* xl = reinterpret_cast<float*>(&Ks[0][0]);   // LDS reuse after the loop
-  // [wave][tq][32] maxima and sums
-  l[0] += swap_halves(l[0]);
-  l[1] += swap_halves(l[1]);
-  if (h == 0) {
-    xl[(wv * 2 + 0) * 32 + l32] = m[0];
-    xl[(wv * 2 + 1) * 32 + l32] = m[1];
-    xl[128 + (wv * 2 + 0) * 32 + l32] = l[0];
-    xl[128 + (wv * 2 + 1) * 32 + l32] = l[1];
-  }
-  // Exchange the output channel half this wave does not keep: wave w keeps tiles
-  // [w*HALF, (w+1)*HALF). Tile indices are compile-time constants in each branch so the
-  // accumulators stay in registers.
-  constexpr int HALF = CT / 2;
-  float* xo = xl + 256;   // [wave][HALF][2][16][64]
-  const int other = 1 - wv;
-  auto give = [&](auto keep_tag) {
-    constexpr int GIVE0 = HALF - decltype(keep_tag)::value;
-#pragma unroll
-    for (int c = 0; c < HALF; ++c)
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          xo[(((wv * HALF + c) * 2 + tq) * 16 + e) * 64 + lane] = o[GIVE0 + c][tq][e];
-  };
-  if (wv == 0) give(std::integral_constant<int, 0>{});
-  else give(std::integral_constant<int, HALF>{});
-  __syncthreads();
-  auto finish = [&](auto keep_tag) {
-    constexpr int KEEP0 = decltype(keep_tag)::value;
-    float fs[2], fo[2], inv_l[2];
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      const float mo = xl[(other * 2 + tq) * 32 + l32];
-      const float lo_ = xl[128 + (other * 2 + tq) * 32 + l32];
-      const float M = fmaxf(m[tq], mo);
-      fs[tq] = exp2f(m[tq] - M);
-      fo[tq] = exp2f(mo - M);
-      const float L = l[tq] * fs[tq] + lo_ * fo[tq];
-      inv_l[tq] = L > 0.f ? 1.f / L : 0.f;
-    }
-
-    // ------------------------------------------------------------ linear apply + mix
-    const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + i) * D * D;
-    const float* zcb = a.zc + ((size_t)bh * a.nbq + i) * D;
-    // phi(Q) . z_c per query column: this lane holds channels 16 s + 8 h .. +7
-    float den[2];
-#pragma unroll
-    for (int tq = 0; tq < 2; ++tq) {
-      float d = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h);
-        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h + 4);
-        const u32x4 w = qf[tq][s];
-        d += fmaxf(bf16_lo(w[0]), 0.f) * z0[0] + fmaxf(bf16_hi(w[0]), 0.f) * z0[1] +
-             fmaxf(bf16_lo(w[1]), 0.f) * z0[2] + fmaxf(bf16_hi(w[1]), 0.f) * z0[3] +
-             fmaxf(bf16_lo(w[2]), 0.f) * z1[0] + fmaxf(bf16_hi(w[2]), 0.f) * z1[1] +
-             fmaxf(bf16_lo(w[3]), 0.f) * z1[2] + fmaxf(bf16_hi(w[3]), 0.f) * z1[3];
-      }
-      d += swap_halves(d);
-      den[tq] = 1.f / (d + kEps);
-    }
-    const float* al = a.alpha + (size_t)(bh % a.H) * D;
-#pragma unroll
-    for (int cc = 0; cc < HALF; ++cc) {
-      const int c = KEEP0 + cc;
-      f32x16 lin[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 af =
-            *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
-        lin[0] = mfma_bf16(af, relu_bf16x8(qf[0][s]), lin[0]);
-        lin[1] = mfma_bf16(af, relu_bf16x8(qf[1][s]), lin[1]);
-      }
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const int q = q0 + 32 * tq + l32;
-        if (q >= a.nq) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int ch = 32 * c + 8 * g + 4 * h;
-          const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
-          float r[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ix = 4 * g + e;
-            const float other_o = xo[(((other * HALF + cc) * 2 + tq) * 16 + ix) * 64 + lane];
-            const float os = (o[KEEP0 + cc][tq][ix] * fs[tq] + other_o * fo[tq]) * inv_l[tq];
-            const float ol = lin[tq][ix] * den[tq];
-            r[e] = alv[e] * os + (1.f - alv[e]) * ol;
-          }
-          if constexpr (OUT_BF16) {
-            uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-          } else {
-            float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-            *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
-          }
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4 vf = vt_frag<D>(Vt, 32 * c, 16 * kk);
+          o[c] = mfma_f16(vf, pf[kk], o[c]);
         }
       }
     }
-  };
-  if (wv == 0) finish(std::integral_constant<int, 0>{});
-  else finish(std::integral_constant<int, HALF>{});
+    if (have_nxt) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    j_cur = j_nxt;
+    f_cur = f_nxt;
+    have = have_nxt;
+  }
+  if (!active) return;   // no barrier follows
+
+  // ---------------------------------------------------------------- epilogue
+  l += swap_halves(l);
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
+  const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
+  // phi(Q) . z_c for this lane's query: this lane holds channels 16 s + 8 h .. +7
+  float d = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h);
+    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h + 4);
+    const u32x4 w = qf[s];
+    d += fmaxf(bf16_lo(w[0]), 0.f) * z0[0] + fmaxf(bf16_hi(w[0]), 0.f) * z0[1] +
+         fmaxf(bf16_lo(w[1]), 0.f) * z0[2] + fmaxf(bf16_hi(w[1]), 0.f) * z0[3] +
+         fmaxf(bf16_lo(w[2]), 0.f) * z1[0] + fmaxf(bf16_hi(w[2]), 0.f) * z1[1] +
+         fmaxf(bf16_lo(w[3]), 0.f) * z1[2] + fmaxf(bf16_hi(w[3]), 0.f) * z1[3];
+  }
+  d += swap_halves(d);
+  const float inv_den = 1.f / (d + kEps);
+  const float* al = a.alpha + (size_t)(bh % a.H) * D;
+  const int q = qrow0 + l32;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    f32x16 lin = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 af =
+          *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
+      lin = mfma_bf16(af, relu_bf16x8(qf[s]), lin);
+    }
+    if (q < a.nq) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = 32 * c + 8 * g + 4 * h;
+        const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ix = 4 * g + e;
+          r[e] = alv[e] * (o[c][ix] * inv_l) + (1.f - alv[e]) * (lin[ix] * inv_den);
+        }
+        if constexpr (OUT_BF16) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+        } else {
+          float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+        }
+      }
+    }
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, int QB>
 hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
   SparseArgs a;
@@ -374,12 +356,22 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
   a.alpha = alpha;
   a.out = o;
   a.nq = s.nq; a.nkv = s.nkv; a.nbq = s.nbq; a.nbk = s.nbk; a.topk = s.k; a.H = s.H;
-  a.total = s.BH * s.nbq;
+  a.ngroups = (s.nbq + QB - 1) / QB;
+  a.total = s.BH * a.ngroups;
   if (s.out_bf16)
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, true>), dim3(a.total), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
   else
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, false>), dim3(a.total), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, false>), dim3(a.total), dim3(128 * QB), 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_sparse_D(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                           const float* alpha, void* o, char* ws, hipStream_t st) {
+  // Pair neighbouring query blocks when there are enough of them to fill the GPU.
+  if (s.nbq >= 2 && (long long)s.BH * s.nbq >= 1024)
+    return launch_sparse_T<T, D, 2>(s, q, k, idx, alpha, o, ws, st);
+  return launch_sparse_T<T, D, 1>(s, q, k, idx, alpha, o, ws, st);
 }
 
 }  // namespace
@@ -387,11 +379,11 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
 hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int32_t* idx,
                          const float* alpha, void* o, char* ws, hipStream_t st) {
   if (s.in_bf16) {
-    if (s.D == 128) return launch_sparse_T<uint16_t, 128>(s, q, k, idx, alpha, o, ws, st);
-    return launch_sparse_T<uint16_t, 64>(s, q, k, idx, alpha, o, ws, st);
+    if (s.D == 128) return launch_sparse_D<uint16_t, 128>(s, q, k, idx, alpha, o, ws, st);
+    return launch_sparse_D<uint16_t, 64>(s, q, k, idx, alpha, o, ws, st);
   }
-  if (s.D == 128) return launch_sparse_T<float, 128>(s, q, k, idx, alpha, o, ws, st);
-  return launch_sparse_T<float, 64>(s, q, k, idx, alpha, o, ws, st);
+  if (s.D == 128) return launch_sparse_D<float, 128>(s, q, k, idx, alpha, o, ws, st);
+  return launch_sparse_D<float, 64>(s, q, k, idx, alpha, o, ws, st);
 }
 
 }  // namespace sla
