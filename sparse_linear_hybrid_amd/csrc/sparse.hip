@@ -13,6 +13,8 @@
 // needed:
 //   S^T (64 keys x 32 queries) = K Q^T        bf16 MFMA 32x32x16, fp32 accumulate
 //   O^T (d x 32 queries)     += V^T P^T       f16 MFMA 32x32x16 (P in [0, 2^8]), fp32
+// Softmax runs in base 2 with the 1/sqrt(d) scale folded into the exponent's FMA; the row
+// sum adds the f16-rounded P actually used by the P.V product.
 // The S^T accumulator layout (lane = query column, 16 key rows per lane per 32-key half) is
 // the B-operand layout P^T needs, up to a fixed permutation of the keys inside each 16-key
 // step; the V^T operand is read from the row-major V tile with transposing LDS reads in the
@@ -24,6 +26,8 @@
 // O = alpha O_s + (1 - alpha) O_l.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace sla {
 
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
     ptr[b] = 0;
   }
   // next element of the ascending union: key block and membership flags
-  auto next_union = [&](int& j, int& flags) {
+  auto next_union = [&](int& j, int& flags) __attribute__((always_inline)) {
     j = 0x7fffffff;
 #pragma unroll
     for (int b = 0; b < QB; ++b)
@@ -166,28 +170,25 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   float m = kNegBig, l = 0.f;
   const float qk_scale = kLog2e / sqrtf((float)D);
 
-  // tile staging: registers -> swizzled LDS (branch-free: rows beyond n_kv read a valid row
-  // and are zeroed)
+  // tile staging: registers -> swizzled LDS. Rows beyond n_kv read row n_kv-1: their logits
+  // are masked to -inf, so the values never contribute.
   u32x4 kreg[CPT], vreg[CPT], klreg[SPLIT ? CPT : 1];
-  auto load_tile = [&](int j) {
+  auto load_tile = [&](int j) __attribute__((always_inline)) {
     const int row0 = j * kBlock;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int id = t + NT * u;
       const int r = id / CH, c = id % CH;
-      const bool ok = row0 + r < a.nkv;
-      const size_t goff = (size_t)(ok ? row0 + r : a.nkv - 1) * D + c * 8;
+      const size_t goff = (size_t)min(row0 + r, a.nkv - 1) * D + c * 8;
       if constexpr (SPLIT) {
         load_split_bf16x8(reinterpret_cast<const float*>(kb) + goff, kreg[u], klreg[u]);
-        if (!ok) klreg[u] = u32x4{0, 0, 0, 0};
       } else {
         kreg[u] = load_bf16x8(kb + goff);
       }
-      if (!ok) kreg[u] = u32x4{0, 0, 0, 0};
       vreg[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)(row0 + r) * D + c * 8);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int id = t + NT * u;
@@ -199,6 +200,80 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
     }
   };
 
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+  // One routed tile for this wave: scores, online softmax (base 2, running max m kept in
+  // scaled units), P.V accumulation.
+  auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j)
+                          __attribute__((always_inline)) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
+        sacc[mt] = mfma_bf16(af, qf[ks], sacc[mt]);
+        if constexpr (SPLIT) {
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&Klo[off]);
+          sacc[mt] = mfma_bf16(af, ql[ks], sacc[mt]);
+          sacc[mt] = mfma_bf16(alo, qf[ks], sacc[mt]);
+        }
+      }
+    }
+    // mask the tail of a partial last key block (uniform, rare)
+    if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          sacc[mt][e] = key < a.nkv ? sacc[mt][e] : -INFINITY;
+        }
+    }
+    float r = kNegBig;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[mt][e]);
+    r = fmaxf(r, swap_halves(r)) * qk_scale;      // row max in scaled (log2) units
+    if (__ballot(r > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, r);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
+      l *= corr;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] *= corr;
+      m = mn;
+    }
+    u32x4 pf[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e = 8 * hh + 2 * e2;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e], qk_scale, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e + 1], qk_scale, -m));
+          const uint32_t pk = pack_f16(p0, p1);
+          pf[2 * mt + hh][e2] = pk;
+          rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, rs, false);
+        }
+      }
+    }
+    l += rs;
+    // O^T += V^T P^T over the 64 keys (four 16-key steps), independent accumulators inner
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 vf = vt_frag<D>(Vt, 32 * c, 16 * kk);
+        o[c] = mfma_f16(vf, pf[kk], o[c]);
+      }
+    }
+  };
+
   int j_cur, f_cur;
   bool have = next_union(j_cur, f_cur);
   if (have) {
@@ -206,87 +281,23 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
     store_tile(0);
   }
   __syncthreads();
-  int buf = 0;
-  while (have) {
+  // Loop unrolled by two so that the LDS buffer of each half is a compile-time constant.
+  auto step = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bufc)::value;
     int j_nxt, f_nxt;
     const bool have_nxt = next_union(j_nxt, f_nxt);
     if (have_nxt) load_tile(j_nxt);
-    if ((f_cur >> qb) & 1) {
-      const uint16_t* Kt = Ks[buf];
-      const uint16_t* Vt = Vs[buf];
-      // S^T: two 32-key halves
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
-          const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
-          s[mt] = mfma_bf16(af, qf[ks], s[mt]);
-          if constexpr (SPLIT) {
-            const u32x4 al = *reinterpret_cast<const u32x4*>(&Kl[buf][off]);
-            s[mt] = mfma_bf16(af, ql[ks], s[mt]);
-            s[mt] = mfma_bf16(al, qf[ks], s[mt]);
-          }
-        }
-      }
-      // scale, mask the tail of a partial last key block, row max over the 64 keys
-      const bool partial = (j_cur + 1) * kBlock > a.nkv;
-      float r = kNegBig;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float z = s[mt][e] * qk_scale;
-          if (partial) {
-            const int key = j_cur * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-            z = key < a.nkv ? z : -INFINITY;
-          }
-          s[mt][e] = z;
-          r = fmaxf(r, z);
-        }
-      }
-      r = fmaxf(r, swap_halves(r));
-      if (__ballot(r > m + kRescaleSlack)) {
-        const float mn = fmaxf(m, r);
-        const float corr = __builtin_amdgcn_exp2f(m - mn);
-        l *= corr;
-#pragma unroll
-        for (int c = 0; c < CT; ++c) o[c] *= corr;
-        m = mn;
-      }
-      u32x4 pf[4];
-      float rs = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        float p[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s[mt][e] - m);
-          rs += p[e];
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          pf[2 * mt + hh] = u32x4{pack_f16(p[8 * hh + 0], p[8 * hh + 1]), pack_f16(p[8 * hh + 2], p[8 * hh + 3]),
-                                  pack_f16(p[8 * hh + 4], p[8 * hh + 5]), pack_f16(p[8 * hh + 6], p[8 * hh + 7])};
-      }
-      l += rs;
-      // O^T += V^T P^T over the 64 keys (four 16-key steps)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x4 vf = vt_frag<D>(Vt, 32 * c, 16 * kk);
-          o[c] = mfma_f16(vf, pf[kk], o[c]);
-        }
-      }
-    }
-    if (have_nxt) store_tile(buf ^ 1);
+    if ((f_cur >> qb) & 1) compute_tile(Ks[B], Kl[SPLIT ? B : 0], Vs[B], j_cur);
+    if (have_nxt) store_tile(B ^ 1);
     __syncthreads();
-    buf ^= 1;
     j_cur = j_nxt;
     f_cur = f_nxt;
     have = have_nxt;
+  };
+  while (have) {
+    step(std::integral_constant<int, 0>{});
+    if (!have) break;
+    step(std::integral_constant<int, 1>{});
   }
   if (!active) return;   // no barrier follows
 
