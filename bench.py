@@ -13,7 +13,12 @@ the CPU oracle baseline.
 Other modes:
     --profile            only warm-up + K plain forward calls and a 1 GiB copy (short runs
                          under rocprofv3; the copy calibrates the memory counters)
-    --summarize-pmc DIR  turn rocprofv3 --pmc CSV output into profiles/*_traffic.json
+    --summarize-pmc FETCH_DIR WRITE_DIR
+                         turn two rocprofv3 --pmc CSV outputs (FETCH_SIZE, WRITE_SIZE) into
+                         profiles/sparse_attn_<workload>_traffic.json
+    --summarize-trace DIR OUT "COMMAND"
+                         turn rocprofv3 --kernel-trace --stats CSV output into a short text
+                         summary (per-kernel calls and average duration) with its command
 """
 from __future__ import annotations
 
@@ -114,17 +119,18 @@ def summarize_pmc(fetch_dir, write_dir, workload):
             acc.setdefault(name, []).append(float(r["Counter_Value"]))
         return acc
 
-    def pick(acc, needle):
-        for k, v in acc.items():
-            if needle in k:
-                return sum(v) / len(v)
-        return None
+    def pick(acc, needle, how="mean"):
+        vals = [x for k, v in acc.items() if needle in k for x in v]
+        if not vals:
+            return None
+        return max(vals) if how == "max" else sum(vals) / len(vals)
 
     f = per_kernel(rows(fetch_dir), "FETCH_SIZE")
     w = per_kernel(rows(write_dir), "WRITE_SIZE")
     sp_f, sp_w = pick(f, "sparse_attn_kernel"), pick(w, "sparse_attn_kernel")
-    cp_f = pick(f, "copy") or pick(f, "elementwise")
-    cp_w = pick(w, "copy") or pick(w, "elementwise")
+    # the calibration copy is the largest copy dispatch of the run (1 GiB device to device)
+    cp_f = pick(f, "copy", "max")
+    cp_w = pick(w, "copy", "max")
     sf = (cp_f * 1024) / COPY_BYTES if cp_f else None       # KiB counted per real byte read
     sw = (cp_w * 1024) / COPY_BYTES if cp_w else None
     rec = {
@@ -135,11 +141,31 @@ def summarize_pmc(fetch_dir, write_dir, workload):
         "fetch_scale": sf, "write_scale": sw,
         "traffic_bytes_per_launch": (sp_f * 1024 / sf + sp_w * 1024 / sw)
         if (sp_f and sp_w and sf and sw) else None,
+        "per_kernel_fetch_kib": {k.split("(")[0][-60:]: sum(v) / len(v) for k, v in f.items()},
+        "per_kernel_write_kib": {k.split("(")[0][-60:]: sum(v) / len(v) for k, v in w.items()},
     }
     path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
     with open(path, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec))
+
+
+def summarize_trace(d, out, command):
+    """Short text summary of rocprofv3 --kernel-trace --stats CSV output."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "#",
+             f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'total_%':>8s}"]
+    for r in rows:
+        name = r.get("Name", "")
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:70]
+        lines.append(f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):8.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # --------------------------------------------------------------------------- main
@@ -153,8 +179,12 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
         return 0
