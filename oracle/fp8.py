@@ -6,21 +6,24 @@ SLA2 page, section 2.C: the sparse branch is quantised to low precision (INT8 or
 the forward pass uses the quantised attention. The router, the linear branch and the mix
 are unquantised, exactly as in ``sla_oracle``.
 
-Readings (the pages give no format details):
+Readings (the pages give no format details; the fp8 workload asks for per-64x128-block
+absmax scales on Q K^T and a per-tile scale on P.V):
 * Format: OCP E4M3FN (bias 7, 3 mantissa bits, finite max 448, no infinities, one NaN
   pattern per sign). Rounding: to nearest, ties to even, saturating at +-448.
-* Q, K and V are quantised per (b, h, 64-token block) with the block's absolute maximum
-  over its valid tokens and all channels: r = fp32(448 / absmax), s = fp32(absmax / 448)
-  (r = s = 1 when absmax is 0); x8 = E4M3(fp32(x * r)); the dequantised value is x8 * s.
-* Logits of a (query block i, key block j) tile: z = s_Q(i) s_K(j) (Q8_i K8_j^T) / sqrt(d).
-* P is quantised per key tile and query row: with t the row's largest logit inside the
-  tile, P8 = E4M3(448 * exp(z - t)) and the row's dequantisation weight for that tile is
-  exp(t - m)/448, where m is the row's largest logit over all selected tiles. The tile's
-  largest element therefore maps exactly to 448.
-* O_s = sum_j exp(t_j - m)/448 * s_V(j) * (P8_j V8_j) / sum_j sum_keys exp(z - m): the
-  normaliser uses the unquantised probabilities.
+* Q, K and V are quantised per (b, h, 64-token block) with a power-of-two scale derived
+  from the block's absolute maximum over its valid tokens and all channels (an E8M0 block
+  scale): s = 2^e with e the smallest integer such that 448 * 2^e >= absmax (e = 0 when
+  the block is all zero); x8 = E4M3(x * 2^-e), which is an exact scaling followed by one
+  rounding; the dequantised value is x8 * s.
+* Logits of a (query block i, key tile j) pair: z = s_Q(i) s_K(j) (Q8_i K8_j^T) / sqrt(d);
+  y = z * log2(e) (base-2 units).
+* P is quantised per key tile and query row: with T = floor(max over the tile's keys of y),
+  P8 = E4M3(2^7 * 2^(y - T)) (values in (0, 256), the row's largest in [128, 256)), and the
+  tile contributes 2^(T - 7) * s_V(j) * (P8 V8_j): every per-row weight is a power of two.
+* O_s = sum_j 2^(T_j - 7) s_V(j) (P8_j V8_j) / sum_j sum_keys 2^y: the normaliser uses the
+  unquantised probabilities.
 This form does not depend on the order in which tiles are visited: an online softmax that
-visits the selected tiles in any order and rescales by exp(m_old - m_new) gives the same
+keeps its running maximum on integers and rescales by exact powers of two gives the same
 value in exact arithmetic.
 """
 from __future__ import annotations
@@ -63,29 +66,31 @@ def e4m3_round(x: np.ndarray) -> np.ndarray:
     return np.where(np.isnan(x), np.nan, np.copysign(r, x))
 
 
-def f32(x):
-    """Round to IEEE binary32 (numpy float32 arithmetic is correctly rounded)."""
-    return np.float32(x)
+def block_scale_exponent(amax: float) -> int:
+    """Smallest integer e with 448 * 2^e >= amax (0 for an all-zero block)."""
+    if amax == 0:
+        return 0
+    _, ex = math.frexp(amax / E4M3_MAX)      # amax/448 = f * 2^ex, f in [0.5, 1)
+    e = ex
+    while E4M3_MAX * math.ldexp(1.0, e - 1) >= amax:   # exact comparisons (powers of two)
+        e -= 1
+    while E4M3_MAX * math.ldexp(1.0, e) < amax:
+        e += 1
+    return e
 
 
 def quantise_blocks(x: np.ndarray, block: int):
-    """Per-block E4M3 quantisation of one (b, h) tensor x [N, d] (float64 holding fp32-exact
-    values). Returns (x8 values [N, d] float64, s [Nb] float64)."""
+    """Per-block E4M3 quantisation of one (b, h) tensor x [N, d] (float64 holding the exact
+    stored values). Returns (x8 values [N, d] float64, s [Nb] float64 powers of two)."""
     n = x.shape[0]
     nb = n_blocks(n, block)
     x8 = np.empty_like(x)
     s = np.empty(nb)
     for j in range(nb):
         sl = block_slice(j, n, block)
-        amax = np.float32(np.abs(x[sl]).max())
-        if amax == 0:
-            r32, s32 = np.float32(1.0), np.float32(1.0)
-        else:
-            r32 = f32(np.float32(E4M3_MAX) / amax)
-            s32 = f32(amax / np.float32(E4M3_MAX))
-        scaled = (x[sl].astype(np.float32) * r32).astype(np.float32)   # fp32 product
-        x8[sl] = e4m3_round(scaled.astype(np.float64))
-        s[j] = float(s32)
+        e = block_scale_exponent(float(np.abs(x[sl]).max()))
+        x8[sl] = e4m3_round(x[sl] * math.ldexp(1.0, -e))
+        s[j] = math.ldexp(1.0, e)
     return x8, s
 
 
@@ -96,20 +101,21 @@ def sparse_rows_fp8(q8_rows: np.ndarray, sq: float, k8: np.ndarray, sk: np.ndarr
     if len(sel) == 0:
         return np.zeros((q8_rows.shape[0], d))
     tau = 1.0 / math.sqrt(d)
-    z_tiles = []
+    log2e = 1.0 / math.log(2.0)
+    ys, Ts = [], []
     for j in sel:
         sl = block_slice(j, n, block)
-        z_tiles.append(sq * sk[j] * tau * (q8_rows @ k8[sl].T))
-    m = np.max(np.stack([zt.max(axis=1) for zt in z_tiles], axis=1), axis=1)   # [rows]
+        y = sq * sk[j] * tau * (q8_rows @ k8[sl].T) * log2e
+        ys.append(y)
+        Ts.append(np.floor(y.max(axis=1)))
+    G = np.max(np.stack(Ts, axis=1), axis=1)         # common reference, avoids overflow
     num = np.zeros((q8_rows.shape[0], d))
     den = np.zeros(q8_rows.shape[0])
-    for j, zt in zip(sel, z_tiles):
+    for j, y, T in zip(sel, ys, Ts):
         sl = block_slice(j, n, block)
-        t = zt.max(axis=1)
-        p8 = e4m3_round(E4M3_MAX * np.exp(zt - t[:, None]))
-        w = np.exp(t - m) / E4M3_MAX
-        num += (w * sv[j])[:, None] * (p8 @ v8[sl])
-        den += np.exp(zt - m[:, None]).sum(axis=1)
+        p8 = e4m3_round(np.exp2(7.0 + y - T[:, None]))
+        num += (np.exp2(T - 7.0 - G) * sv[j])[:, None] * (p8 @ v8[sl])
+        den += np.exp2(y - G[:, None]).sum(axis=1)
     return num / den[:, None]
 
 

@@ -65,27 +65,37 @@ def test_e4m3_round_is_nearest_even_saturating():
     assert same.all(), x[~same][:10]
 
 
+def test_block_scale_exponent_closed_form():
+    """e is the smallest integer with 448 * 2^e >= absmax."""
+    cases = {448.0: 0, 449.0: 1, 224.0: -1, 224.5: 0, 896.0: 1, 1.0: -8, 1.75: -8,
+             1.7500001: -7, 3.5: -7, 0.0: 0, 448.0 * 2.0 ** -20: -20}
+    for amax, e in cases.items():
+        assert fp8.block_scale_exponent(amax) == e, amax
+
+
 def test_quantise_blocks_scales_and_bounds():
     x = RNG.standard_normal((3 * 64 + 10, 16)).astype(np.float32).astype(np.float64)
     x[70, 3] = -9.5                                               # block 1 absmax
     x8, s = fp8.quantise_blocks(x, 64)
     assert s.shape == (4,)
-    assert np.float32(s[1]) == np.float32(np.float32(9.5) / np.float32(448))
-    assert x8[70, 3] == -448.0                                    # absmax maps to -448
-    assert np.all(np.abs(x8) <= 448.0)
-    # every code is an E4M3 value and dequantisation is within half a step of x
-    assert np.array_equal(fp8.e4m3_round(x8), x8)
+    assert s[1] == 2.0 ** -5                                      # 448/64 = 7 < 9.5 <= 14
+    assert x8[70, 3] == -320.0      # 9.5 * 32 = 304: midway between 288 and 320, ties to even
     for j in range(4):
         sl = so.block_slice(j, x.shape[0], 64)
-        err = np.abs(x8[sl] * s[j] - x[sl])
+        e = np.log2(s[j])
+        assert e == int(e)                                        # power of two
+        amax = np.abs(x[sl]).max()
+        assert 224.0 < amax / s[j] <= 448.0                       # smallest such power
+        assert np.array_equal(fp8.e4m3_round(x8[sl]), x8[sl])     # every code is E4M3
+        err = np.abs(x8[sl] * s[j] - x[sl])                       # half a step, relative
         assert np.all(err <= np.abs(x[sl]) * 2.0 ** -4 + 2.0 ** -10 * s[j] + 1e-12)
     z8, zs = fp8.quantise_blocks(np.zeros((64, 4)), 64)
     assert zs[0] == 1.0 and not z8.any()
 
 
 def test_fp8_equal_logits_give_mean_of_dequantised_v():
-    """A tile whose logits are all equal has P8 = 448 everywhere, so O_s is the plain mean of
-    the dequantised values."""
+    """A tile whose logits are all equal has P8 = 128 everywhere (T = 0), so O_s is the
+    plain mean of the dequantised values."""
     d, b = 8, 64
     q8 = fp8.e4m3_round(RNG.standard_normal((4, d)) * 50)
     k8 = np.zeros((b, d))
@@ -95,14 +105,13 @@ def test_fp8_equal_logits_give_mean_of_dequantised_v():
 
 
 def test_fp8_two_keys_ln2_apart():
-    """Logits ln 2 apart give p = (1, 1/2): both exact in E4M3 after scaling by 448, so the
-    output is the exact 2/3 : 1/3 average of the dequantised values."""
+    """Logits ln 2 apart give p = (1, 1/2): 128 and 64 after scaling, both exact in E4M3,
+    so the output is the exact 2/3 : 1/3 average of the dequantised values."""
     d = 4
     tau = 1 / math.sqrt(d)
     target = math.log(2.0)
     q8 = np.array([[1.0, 0.0, 0.0, 0.0]])
-    # scale s_K chosen so that the logits are exactly 0 and -ln 2 with k8 = 0 and -1
-    sk = target / tau
+    sk = target / tau          # logits exactly 0 and -ln 2 with k8 = 0 and -1
     k8 = np.zeros((2, d))
     k8[1, 0] = -1.0
     v8 = np.array([[3.0, 1.0, 0.0, 2.0], [0.5, -1.0, 4.0, 2.0]])
@@ -113,19 +122,16 @@ def test_fp8_two_keys_ln2_apart():
 def test_fp8_identity_quantisation_within_p_rounding_bound():
     """With E4M3-exact inputs whose block absmax is 448 every scale is 1, the logits are the
     exact ones, and the only difference to exact attention comes from rounding P to E4M3:
-    at most 2^-4 of sum p|v| / sum p."""
+    at most 2^-4 of sum p|v| / sum p (plus the subnormal step for p below 2^-13)."""
     d, b, n = 16, 64, 256
-    def exact_block(shape):
-        x = fp8.e4m3_round(RNG.standard_normal(shape) * 8)
+    def exact_block(shape, scale):
+        x = fp8.e4m3_round(RNG.standard_normal(shape) * scale)
         for j in range(shape[0] // b):
             x[j * b, 0] = 448.0
         return x
-    q = exact_block((n, d)) / 64
-    q = fp8.e4m3_round(q)
-    for j in range(n // b):
-        q[j * b, 0] = 448.0
-    k = exact_block((n, d))
-    v = exact_block((n, d))
+    q = exact_block((n, d), 0.125)
+    k = exact_block((n, d), 8)
+    v = exact_block((n, d), 8)
     q8, sq = fp8.quantise_blocks(q, b)
     k8, sk = fp8.quantise_blocks(k, b)
     v8, sv = fp8.quantise_blocks(v, b)
@@ -137,32 +143,35 @@ def test_fp8_identity_quantisation_within_p_rounding_bound():
     toks = np.concatenate([np.arange(j * b, (j + 1) * b) for j in sel])
     lg = q[:b] @ k[toks].T / math.sqrt(d)
     p = np.exp(lg - lg.max(1, keepdims=True))
-    bound = 2.0 ** -4 * (p @ np.abs(v[toks])) / p.sum(1, keepdims=True)
+    bound = (2.0 ** -4 * (p @ np.abs(v[toks])) + 2.0 ** -13 * np.abs(v[toks]).sum(0).max()) \
+        / p.sum(1, keepdims=True)
     assert np.all(np.abs(o8 - ex) <= bound + 1e-12)
     assert np.abs(o8 - ex).max() > 0          # P rounding does act
 
 
 def test_fp8_visit_order_free_definition_matches_online_form():
-    """The order-free definition equals an online softmax visiting the tiles in ascending order
-    (written out independently here), so either schedule may implement it."""
+    """The order-free definition equals an online softmax (written out independently here)
+    that keeps an integer running maximum and rescales by exact powers of two, visiting the
+    tiles in ascending or in descending order."""
     d, b = 8, 64
     q8 = fp8.e4m3_round(RNG.standard_normal((8, d)) * 30)
     k8 = fp8.e4m3_round(RNG.standard_normal((4 * b, d)) * 30)
     v8 = fp8.e4m3_round(RNG.standard_normal((4 * b, d)) * 30)
-    sk = np.array([0.01, 0.02, 0.015, 0.03])
-    sv = np.array([0.1, 0.2, 0.3, 0.4])
-    sq, sel = 0.02, [0, 1, 3]
+    sk = np.array([2.0 ** -6, 2.0 ** -5, 2.0 ** -7, 2.0 ** -4])
+    sv = np.array([0.125, 0.25, 0.5, 1.0])
+    sq, sel = 2.0 ** -5, [0, 1, 3]
     got = fp8.sparse_rows_fp8(q8, sq, k8, sk, v8, sv, sel, b)
-    m = np.full(8, -np.inf)
-    acc = np.zeros((8, d))
-    lsum = np.zeros(8)
-    for j in sel:
-        z = sq * sk[j] / math.sqrt(d) * (q8 @ k8[j * b:(j + 1) * b].T)
-        t = z.max(1)
-        mn = np.maximum(m, t)
-        c = np.exp(m - mn)
-        p8 = fp8.e4m3_round(448 * np.exp(z - t[:, None]))
-        acc = acc * c[:, None] + (np.exp(t - mn) / 448 * sv[j])[:, None] * (p8 @ v8[j * b:(j + 1) * b])
-        lsum = lsum * c + np.exp(z - mn[:, None]).sum(1)
-        m = mn
-    assert np.allclose(got, acc / lsum[:, None], rtol=1e-12, atol=1e-14)
+    for order in (sel, sel[::-1]):
+        m = np.full(8, -np.inf)
+        acc = np.zeros((8, d))
+        lsum = np.zeros(8)
+        for j in order:
+            y = sq * sk[j] / math.sqrt(d) * (q8 @ k8[j * b:(j + 1) * b].T) / math.log(2)
+            T = np.floor(y.max(1))
+            mn = np.maximum(m, np.ceil(y.max(1)))
+            c = np.exp2(m - mn)
+            p8 = fp8.e4m3_round(np.exp2(7 + y - T[:, None]))
+            acc = acc * c[:, None] + (np.exp2(T - 7 - mn) * sv[j])[:, None] * (p8 @ v8[j * b:(j + 1) * b])
+            lsum = lsum * c + np.exp2(y - mn[:, None]).sum(1)
+            m = mn
+        assert np.allclose(got, acc / lsum[:, None], rtol=1e-12, atol=1e-14)
