@@ -117,6 +117,25 @@ sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void*
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 int fp8, hipEvent_t* events);
 
+/* Workspace regions that tests and diagnostics may read back after a call. */
+typedef enum {
+  SLA_WS_Q8 = 0,        /* bf16 holding the E4M3 values of Q [B*H][ceil(n_q/64)*64][d] */
+  SLA_WS_K8 = 1,        /* bf16 holding the E4M3 values of K [B*H][ceil(n_kv/64)*64][d]*/
+  SLA_WS_V8 = 2,        /* uint8  E4M3 V   [B*H][ceil(n_kv/64)][head_dim][64], keys in
+                           the P8 operand order (see sparse.hip)                    */
+  SLA_WS_EQ = 3,        /* int32 block exponents of Q  [B*H][ceil(n_q/64)]           */
+  SLA_WS_EK = 4,        /* int32 block exponents of K  [B*H][ceil(n_kv/64)]          */
+  SLA_WS_EV = 5,        /* int32 block exponents of V  [B*H][ceil(n_kv/64)]          */
+  SLA_WS_SCORES = 6,    /* float64 block scores [B*H][ceil(n_q/64)][ceil(n_kv/64)]   */
+  SLA_WS_SC = 7,        /* bf16 S_c^T per query block [B*H][ceil(n_q/64)][d][d]      */
+  SLA_WS_ZC = 8         /* fp32 z_c per query block [B*H][ceil(n_q/64)][d]           */
+} sla_ws_region;
+
+/* Byte offset and size of a workspace region for problem p (fp8 selects the sla_forward_fp8
+ * layout). Returns SLA_ERR_SHAPE / SLA_ERR_NULL on invalid arguments. Host only. */
+sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,
+                                size_t* bytes);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sla_status_string(sla_status s);
 

@@ -5,7 +5,7 @@ The computation lives in libsla.so (HIP kernels behind the C ABI of include/sla.
 """
 from .sla import (SlaError, Problem, make_problem, workspace_size, sla_route, sla_forward,
                   sla_forward_fp8, sla_forward_profiled, library, LIB_PATH, EXPORTS,
-                  STAGES)
+                  STAGES, workspace_region, WS_REGIONS)
 
 __all__ = ["SlaError", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
-           "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES"]
+           "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES", "workspace_region", "WS_REGIONS"]

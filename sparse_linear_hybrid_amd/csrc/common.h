@@ -146,8 +146,8 @@ inline Plan make_plan(const sla_problem& p) {
   s.sc = take(BH * nbq * D * D * 2);
   s.zc = take(BH * nbq * D * 4);
   s.total_fwd = off;
-  s.q8 = take(BH * nbq * kBlock * D);
-  s.k8 = take(BH * nbk * kBlock * D);
+  s.q8 = take(BH * nbq * kBlock * D * 2);   // E4M3 values held as bf16
+  s.k8 = take(BH * nbk * kBlock * D * 2);
   s.v8 = take(BH * nbk * kBlock * D);
   s.sq8 = take(BH * nbq * 4);
   s.sk8 = take(BH * nbk * 4);

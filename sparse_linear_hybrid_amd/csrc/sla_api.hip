@@ -48,7 +48,6 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   const size_t need = fp8 ? s.total_fp8 : s.total_fwd;
   if (!workspace || workspace_bytes < need) return SLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SLA_ERR_ALIGN;
-  if (fp8) return SLA_ERR_UNSUPPORTED;   // quantised sparse kernel: not built yet
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
@@ -63,7 +62,12 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   if (launch_complement(s, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_COMPLEMENT + 1) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_SPARSE) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_sparse(s, q, k, idx, alpha, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (fp8) {
+    if (launch_quant(s, q, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+    if (launch_sparse_fp8(s, q, idx, alpha, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  } else if (launch_sparse(s, q, k, idx, alpha, o, ws, stream) != hipSuccess) {
+    return SLA_ERR_HIP;
+  }
   if (mark(2 * SLA_STAGE_SPARSE + 1) != hipSuccess) return SLA_ERR_HIP;
   return SLA_OK;
 }
@@ -117,6 +121,29 @@ sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void*
                                 int fp8, hipEvent_t* events) {
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
                       workspace_bytes, stream, fp8 != 0, events);
+}
+
+sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,
+                                size_t* bytes) {
+  const sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  if (!offset || !bytes) return SLA_ERR_NULL;
+  const Plan s = make_plan(*p);
+  const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk;
+  switch (region) {
+    case SLA_WS_Q8: *offset = s.q8; *bytes = BH * nbq * kBlock * D * 2; break;
+    case SLA_WS_K8: *offset = s.k8; *bytes = BH * nbk * kBlock * D * 2; break;
+    case SLA_WS_V8: *offset = s.v8; *bytes = BH * nbk * kBlock * D; break;
+    case SLA_WS_EQ: *offset = s.sq8; *bytes = BH * nbq * 4; break;
+    case SLA_WS_EK: *offset = s.sk8; *bytes = BH * nbk * 4; break;
+    case SLA_WS_EV: *offset = s.sv8; *bytes = BH * nbk * 4; break;
+    case SLA_WS_SCORES: *offset = s.scores; *bytes = BH * nbq * nbk * 8; break;
+    case SLA_WS_SC: *offset = s.sc; *bytes = BH * nbq * D * D * 2; break;
+    case SLA_WS_ZC: *offset = s.zc; *bytes = BH * nbq * D * 4; break;
+    default: return SLA_ERR_SHAPE;
+  }
+  if (region <= SLA_WS_EV && !fp8) return SLA_ERR_SHAPE;
+  return SLA_OK;
 }
 
 const char* sla_status_string(sla_status s) {

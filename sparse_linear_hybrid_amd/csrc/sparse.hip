@@ -69,6 +69,13 @@ struct SparseArgs {
   const float* alpha;      // [H][D]
   void* out;
   int nq, nkv, nbq, nbk, topk, H, ngroups, total;
+  // quantised branch only
+  const uint16_t* q8;      // E4M3 values as bf16 [BH][nbq*64][D]
+  const uint16_t* k8;      // E4M3 values as bf16 [BH][nbk*64][D]
+  const uint8_t* v8;       // E4M3 [BH][nbk][D][64], keys in P8 slot order
+  const int32_t* eq;       // block exponents [BH][nbq]
+  const int32_t* ek;       // [BH][nbk]
+  const int32_t* ev;       // [BH][nbk]
 };
 
 template <typename T>
@@ -354,7 +361,267 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   }
 }
 
-template <typename T, int D, int QB>
+// ------------------------------------------------------------------------------------
+// Quantised sparse branch (SLA2 page, section 2.C). Same structure as sparse_attn_kernel,
+// on E4M3 operands with power-of-two block scales:
+//   S^T = K8 Q8^T                   bf16 MFMA 32x32x16 on the E4M3 values (held exactly in
+//                                   bf16; every product is exact and the sum is accumulated
+//                                   in fp32), logits y = S * 2^(eQ+eK) log2(e)/sqrt(d)
+//   per (row, tile): T = floor(max y), P8 = E4M3(2^(y - T + 7)) in (0, 256)
+//   O^T += 2^(T - 7 - m + eV) (V8^T P8^T)   fp8 MFMA 32x32x64 with the power-of-two weight
+//                                           applied by the MFMA's E8M0 scale on P8
+// The logits do not use the fp8 MFMA: on gfx950 it keeps only about 12-13 significant bits
+// when products of very different magnitude are summed, and the exponential turns that into
+// errors of several percent for logits of a few hundred. For P.V the same relative error
+// is harmless (it stays about 1e-4 of sum p |v|).
+// m is the row's running maximum kept on integers, so every rescale is an exact power of
+// two; the row sum uses the unquantised probabilities. In the 32x32x64 MFMA each lane half
+// holds 32 of the 64 reduction elements; the two 32-element scale blocks take their E8M0
+// scale from lanes x and x+32, which here always carry the same value.
+template <int D, int QB, bool OUT_BF16>
+__global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(SparseArgs a) {
+  constexpr int NT = 128 * QB;
+  constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
+  constexpr int CT = D / 32;
+  constexpr int CH = D / 8;                // 16-byte chunks per K row
+  constexpr int VROW = 64 + 16;            // padded LDS row of the V8 tile (bytes)
+  constexpr int KPT = 64 * CH / NT;        // K chunks per thread per tile
+  constexpr int VPT = D * 64 / 16 / NT;    // V8 chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
+  __shared__ __attribute__((aligned(16))) uint8_t V8s[2][D * VROW];
+
+  const int wid = xcd_remap(blockIdx.x, a.total);
+  const int bh = wid / a.ngroups, grp = wid % a.ngroups;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int qb = wv >> 1;
+  const int iq = grp * QB + qb;
+  const bool active = iq < a.nbq;
+  const int qrow0 = iq * kBlock + 32 * (wv & 1);
+  const uint16_t* k8b = a.k8 + (size_t)bh * a.nbk * kBlock * D;
+  const uint8_t* v8b = a.v8 + (size_t)bh * a.nbk * kBlock * D;
+  const int k = a.topk;
+
+  const int32_t* selp[QB];
+  int nsel[QB], ptr[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int ib = grp * QB + b;
+    selp[b] = a.idx + ((size_t)bh * a.nbq + (ib < a.nbq ? ib : 0)) * k;
+    nsel[b] = ib < a.nbq ? k : 0;
+    ptr[b] = 0;
+  }
+  auto next_union = [&](int& j, int& flags) __attribute__((always_inline)) {
+    j = 0x7fffffff;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (ptr[b] < nsel[b]) j = min(j, selp[b][ptr[b]]);
+    flags = 0;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (ptr[b] < nsel[b] && selp[b][ptr[b]] == j) { flags |= 1 << b; ++ptr[b]; }
+    return flags != 0;
+  };
+
+  // Q8^T fragments (B operand): lane column q, channels 16 s + 8 h .. +7
+  u32x4 qf8[KS];
+  {
+    const int q = qrow0 + l32;
+    const int qc = (active && q < a.nq) ? q : 0;
+    const uint16_t* src = a.q8 + ((size_t)bh * a.nbq * kBlock + qc) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf8[s] = *reinterpret_cast<const u32x4*>(src + 16 * s + 8 * h);
+  }
+  const int eq = active ? a.eq[(size_t)bh * a.nbq + iq] : 0;
+  const float base_scale = kLog2e / sqrtf((float)D);
+
+  f32x16 o[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) o[c] = f32x16{};
+  float m = -16384.f;     // running maximum (an integer), far below any logit
+  float l = 0.f;
+
+  u32x4 kreg[KPT], vreg[VPT];
+  auto load_tile = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+      kreg[u] = *reinterpret_cast<const u32x4*>(k8b + (size_t)j * kBlock * D + (t + NT * u) * 8);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u)
+      vreg[u] = *reinterpret_cast<const u32x4*>(v8b + (size_t)j * kBlock * D + (t + NT * u) * 16);
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int id = t + NT * u, r = id / CH, c = id % CH;
+      *reinterpret_cast<u32x4*>(&Ks[buf][swz<D>(r, c * 8)]) = kreg[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int id = t + NT * u, vr = id / 4, vc = id % 4;
+      *reinterpret_cast<u32x4*>(&V8s[buf][vr * VROW + vc * 16]) = vreg[u];
+    }
+  };
+  auto frag32 = [&](const uint8_t* p) __attribute__((always_inline)) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  auto compute_tile = [&](const uint16_t* Kt, const uint8_t* Vt, int j) __attribute__((always_inline)) {
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(32 * mt + l32, 16 * ks + 8 * h)]);
+        sacc[mt] = mfma_bf16(af, qf8[ks], sacc[mt]);
+      }
+    }
+    const float cj = ldexpf(base_scale, eq + a.ek[(size_t)bh * a.nbk + j]);
+    if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          sacc[mt][e] = key < a.nkv ? sacc[mt][e] : -INFINITY;
+        }
+    }
+    float r = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[mt][e]);
+    r = fmaxf(r, swap_halves(r)) * cj;          // row max of y over the tile
+    const float T = floorf(r);
+    if (__ballot(r > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, ceilf(r));
+      const float corr = ldexpf(1.f, (int)fmaxf(m - mn, -200.f));
+      l *= corr;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] *= corr;
+      m = mn;
+    }
+    // P8 = E4M3(2^(y - T + 7)); slot 16 mt + e of this lane half holds accumulator element e
+    // of key tile half mt
+    const int wexp = (int)(T - 7.f - m) + a.ev[(size_t)bh * a.nbk + j];
+    const bool live = wexp >= -127;   // weights below 2^-127 contribute nothing in fp32
+    i32x8 pf8;
+    float rs = 0.f;
+    const float off = 7.f - T;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int mt = w >> 2, e0 = 4 * (w & 3);
+      float p4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p4[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e0 + i], cj, off));
+        rs += p4[i];
+      }
+      int pk = 0;
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], pk, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
+      pf8[w] = live ? pk : 0;
+    }
+    l += ldexpf(rs, (int)(T - 7.f - m));
+    const int sb = min(max(127 + wexp, 0), 254);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      const i32x8 vf = frag32(&Vt[(32 * c + l32) * VROW + 32 * h]);
+      o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf8, o[c], 0, 0, 0, 127, 0, sb);
+    }
+  };
+
+  int j_cur, f_cur;
+  bool have = next_union(j_cur, f_cur);
+  if (have) {
+    load_tile(j_cur);
+    store_tile(0);
+  }
+  __syncthreads();
+  auto step = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bufc)::value;
+    int j_nxt, f_nxt;
+    const bool have_nxt = next_union(j_nxt, f_nxt);
+    if (have_nxt) load_tile(j_nxt);
+    if ((f_cur >> qb) & 1) compute_tile(Ks[B], V8s[B], j_cur);
+    if (have_nxt) store_tile(B ^ 1);
+    __syncthreads();
+    j_cur = j_nxt;
+    f_cur = f_nxt;
+    have = have_nxt;
+  };
+  while (have) {
+    step(std::integral_constant<int, 0>{});
+    if (!have) break;
+    step(std::integral_constant<int, 1>{});
+  }
+  if (!active) return;
+
+  // ---------------------------------------------------------------- epilogue (as bf16)
+  l += swap_halves(l);
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + (size_t)bh * a.nq * D;
+  u32x4 qf[KS];
+  {
+    const int q = qrow0 + l32;
+    const bool ok = q < a.nq;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = ok ? *reinterpret_cast<const u32x4*>(qsrc + (size_t)q * D + 16 * s + 8 * h)
+                 : u32x4{0, 0, 0, 0};
+  }
+  const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
+  const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
+  float d = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h);
+    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h + 4);
+    const u32x4 w = qf[s];
+    d += fmaxf(bf16_lo(w[0]), 0.f) * z0[0] + fmaxf(bf16_hi(w[0]), 0.f) * z0[1] +
+         fmaxf(bf16_lo(w[1]), 0.f) * z0[2] + fmaxf(bf16_hi(w[1]), 0.f) * z0[3] +
+         fmaxf(bf16_lo(w[2]), 0.f) * z1[0] + fmaxf(bf16_hi(w[2]), 0.f) * z1[1] +
+         fmaxf(bf16_lo(w[3]), 0.f) * z1[2] + fmaxf(bf16_hi(w[3]), 0.f) * z1[3];
+  }
+  d += swap_halves(d);
+  const float inv_den = 1.f / (d + kEps);
+  const float* al = a.alpha + (size_t)(bh % a.H) * D;
+  const int q = qrow0 + l32;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    f32x16 lin = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 af =
+          *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
+      lin = mfma_bf16(af, relu_bf16x8(qf[s]), lin);
+    }
+    if (q < a.nq) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ch = 32 * c + 8 * g + 4 * h;
+        const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ix = 4 * g + e;
+          r[e] = alv[e] * (o[c][ix] * inv_l) + (1.f - alv[e]) * (lin[ix] * inv_den);
+        }
+        if constexpr (OUT_BF16) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+        } else {
+          float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, int QB, bool FP8>
 hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
   SparseArgs a;
@@ -369,20 +636,33 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
   a.nq = s.nq; a.nkv = s.nkv; a.nbq = s.nbq; a.nbk = s.nbk; a.topk = s.k; a.H = s.H;
   a.ngroups = (s.nbq + QB - 1) / QB;
   a.total = s.BH * a.ngroups;
-  if (s.out_bf16)
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
-  else
-    hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, false>), dim3(a.total), dim3(128 * QB), 0, st, a);
+  a.q8 = reinterpret_cast<const uint16_t*>(ws + s.q8);
+  a.k8 = reinterpret_cast<const uint16_t*>(ws + s.k8);
+  a.v8 = reinterpret_cast<const uint8_t*>(ws + s.v8);
+  a.eq = reinterpret_cast<const int32_t*>(ws + s.sq8);
+  a.ek = reinterpret_cast<const int32_t*>(ws + s.sk8);
+  a.ev = reinterpret_cast<const int32_t*>(ws + s.sv8);
+  if constexpr (FP8) {
+    if (s.out_bf16)
+      hipLaunchKernelGGL((sparse_attn_fp8_kernel<D, QB, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
+    else
+      hipLaunchKernelGGL((sparse_attn_fp8_kernel<D, QB, false>), dim3(a.total), dim3(128 * QB), 0, st, a);
+  } else {
+    if (s.out_bf16)
+      hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
+    else
+      hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, false>), dim3(a.total), dim3(128 * QB), 0, st, a);
+  }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8 = false>
 hipError_t launch_sparse_D(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
   // Pair neighbouring query blocks when there are enough of them to fill the GPU.
   if (s.nbq >= 2 && (long long)s.BH * s.nbq >= 1024)
-    return launch_sparse_T<T, D, 2>(s, q, k, idx, alpha, o, ws, st);
-  return launch_sparse_T<T, D, 1>(s, q, k, idx, alpha, o, ws, st);
+    return launch_sparse_T<T, D, 2, FP8>(s, q, k, idx, alpha, o, ws, st);
+  return launch_sparse_T<T, D, 1, FP8>(s, q, k, idx, alpha, o, ws, st);
 }
 
 }  // namespace
@@ -395,6 +675,12 @@ hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int3
   }
   if (s.D == 128) return launch_sparse_D<float, 128>(s, q, k, idx, alpha, o, ws, st);
   return launch_sparse_D<float, 64>(s, q, k, idx, alpha, o, ws, st);
+}
+
+hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
+                             const float* alpha, void* o, char* ws, hipStream_t st) {
+  if (s.D == 128) return launch_sparse_D<uint16_t, 128, true>(s, q, nullptr, idx, alpha, o, ws, st);
+  return launch_sparse_D<uint16_t, 64, true>(s, q, nullptr, idx, alpha, o, ws, st);
 }
 
 }  // namespace sla

@@ -22,7 +22,8 @@ STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE"
           4: "SLA_ERR_TOPK", 5: "SLA_ERR_ALIGN", 6: "SLA_ERR_WORKSPACE",
           7: "SLA_ERR_UNSUPPORTED", 8: "SLA_ERR_HIP"}
 EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
-           "sla_forward_profiled", "sla_status_string")
+           "sla_forward_profiled", "sla_workspace_region", "sla_status_string")
+WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
 STAGES = ("kv_summary", "route", "complement", "sparse")
 
 
@@ -58,6 +59,10 @@ def _load() -> ctypes.CDLL:
     lib.sla_forward_profiled.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                          ctypes.c_int, vp]
     lib.sla_forward_profiled.restype = ctypes.c_int
+    lib.sla_workspace_region.argtypes = [pp, ctypes.c_int, ctypes.c_int,
+                                         ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.sla_workspace_region.restype = ctypes.c_int
     lib.sla_status_string.argtypes = [ctypes.c_int]
     lib.sla_status_string.restype = ctypes.c_char_p
     return lib
@@ -185,3 +190,13 @@ def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8
     if st != 0:
         raise SlaError(st, "sla_forward_profiled")
     return out
+
+
+def workspace_region(p: Problem, name: str, fp8: bool = False) -> Tuple[int, int]:
+    """(byte offset, byte size) of a named workspace region (see WS_REGIONS)."""
+    off, size = ctypes.c_size_t(), ctypes.c_size_t()
+    st = library().sla_workspace_region(ctypes.byref(p), int(fp8), WS_REGIONS[name],
+                                        ctypes.byref(off), ctypes.byref(size))
+    if st != 0:
+        raise SlaError(st, "sla_workspace_region")
+    return off.value, size.value

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle                                   # noqa: E402
 from oracle import sla_oracle as so             # noqa: E402
-from workloads import make_custom, make_inputs  # noqa: E402
+from workloads import make_custom, make_inputs, bf16_bits_to_f32  # noqa: E402
 from tests.gpu_helpers import to_device, check_masks, max_err_over_rms  # noqa: E402
 
 TOL = 2e-2
@@ -177,3 +177,109 @@ def test_video90_full(sla):
 def test_longctx_full(sla):
     x = make_inputs("longctx")
     _sampled_check(sla, x, blocks_per_head=1, heads=[(0, 0), (3, 31)])
+
+
+# ----------------------------------------------------------------------------- fp8 branch
+TOL_FP8 = 6e-2
+
+
+def run_forward_fp8(sla, x, out_dtype=torch.float32):
+    q, k, v, pq, pk, al = to_device(x)
+    out, idx = sla.sla_forward_fp8(q, k, v, pq, pk, al, x.problem.top_k, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), idx.cpu().numpy()
+
+
+FP8_CASES = [
+    (1, 2, 256, 256, 128, 2, "smooth"),
+    (1, 2, 300, 300, 128, 3, "smooth"),     # ragged tail
+    (2, 1, 200, 520, 64, 4, "normal"),      # d = 64, n_q != n_kv
+    (1, 1, 64, 1000, 128, 5, "normal"),
+]
+
+
+@pytest.mark.parametrize("B,H,nq,nkv,d,top_k,kind", FP8_CASES)
+def test_fp8_small(sla, B, H, nq, nkv, d, top_k, kind):
+    x = make_custom(B, H, nq, nkv, d, top_k, dtype="bf16", kind=kind, seed=nq + 3 * d)
+    print(f"fp8 case B={B} H={H} nq={nq} nkv={nkv} d={d} k={top_k} {kind}", flush=True)
+    out, idx = run_forward_fp8(sla, x)
+    ref, ref_idx = oracle.forward_fp8(x)
+    check_masks(idx, oracle.sla_oracle.route_full(x), top_k)
+    err, rms = max_err_over_rms(out, ref)
+    print(f"  max-abs/rms {err:.3e}")
+    assert err <= TOL_FP8, f"max-abs/rms {err:.3e}"
+
+
+def test_fp8_masks_equal_bf16_masks(sla):
+    x = make_custom(1, 2, 320, 448, 128, 3, dtype="bf16", kind="smooth", seed=12)
+    _, i8 = run_forward_fp8(sla, x)
+    _, i16 = run_forward(sla, x)
+    assert np.array_equal(i8, i16)
+
+
+@pytest.mark.slow
+def test_video95_fp8_full(sla):
+    x = make_inputs("video95_fp8")
+    out, idx = run_forward_fp8(sla, x)
+    routes = oracle.sla_oracle.route_full(x)
+    rows, near = check_masks(idx, routes, x.problem.top_k)
+    rng = np.random.default_rng(1)
+    p = x.problem
+    refs, gots = [], []
+    for h in (0, 7, 11):
+        blocks = rng.choice(p.nbq, size=2, replace=False)
+        rws = np.concatenate([np.arange(i * 64, i * 64 + 64) for i in blocks])
+        ref, _ = oracle.forward_fp8(x, heads=[(0, h)], rows=rws)
+        refs.append(ref[0, h, rws])
+        gots.append(out[0, h, rws])
+    err, rms = max_err_over_rms(np.concatenate(gots), np.concatenate(refs))
+    print(f"video95_fp8: rows={rows} near_tie={near} max-abs/rms={err:.3e} rms={rms:.4f}")
+    assert err <= TOL_FP8
+
+
+def _v8_key_order():
+    """Key stored at each byte position of a V8 tile row (the P8 operand order)."""
+    order = np.empty(64, np.int64)
+    for hh in range(2):
+        for slot in range(32):
+            order[32 * hh + slot] = 32 * (slot // 16) + 8 * ((slot % 16) // 4) + 4 * hh + slot % 4
+    return order
+
+
+@pytest.mark.parametrize("nq,nkv,d", [(256, 320, 128), (200, 130, 64)])
+def test_fp8_quantiser_bit_exact(sla, nq, nkv, d):
+    """E4M3 values and block exponents of Q, K, V equal the oracle's quantisation exactly
+    (Q and K are held as bf16, V as E4M3 bytes)."""
+    from oracle import fp8 as ofp8
+    x = make_custom(1, 2, nq, nkv, d, 2, dtype="bf16", kind="smooth", seed=31)
+    q, k, v, pq, pk, al = to_device(x)
+    prob = sla.make_problem(q, k, 2)
+    ws = torch.zeros(sla.workspace_size(prob, True), dtype=torch.uint8, device="cuda")
+    sla.sla_forward_fp8(q, k, v, pq, pk, al, 2, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+
+    def region(name, dtype):
+        off, size = sla.workspace_region(prob, name, fp8=True)
+        return wsh[off:off + size].view(dtype)
+
+    nbq, nbk = prob.n_q // 64 + (prob.n_q % 64 > 0), -(-nkv // 64)
+    q8 = region("q8", np.uint16).reshape(2, nbq * 64, d)
+    k8 = region("k8", np.uint16).reshape(2, nbk * 64, d)
+    v8 = region("v8", np.uint8).reshape(2, nbk, d, 64)
+    eq = region("eq", np.int32).reshape(2, nbq)
+    ek = region("ek", np.int32).reshape(2, nbk)
+    ev = region("ev", np.int32).reshape(2, nbk)
+    order = _v8_key_order()
+    for h in range(2):
+        for name, g8, ge, n in (("q", q8, eq, nq), ("k", k8, ek, nkv)):
+            want, s = ofp8.quantise_blocks(x.as_f64(name)[0, h], 64)
+            assert np.array_equal(ge[h], np.log2(s).astype(np.int32)), name
+            assert np.array_equal(bf16_bits_to_f32(g8[h, :n]).astype(np.float64), want), name
+            assert not g8[h, n:].any()
+        want, s = ofp8.quantise_blocks(x.as_f64("v")[0, h], 64)
+        assert np.array_equal(ev[h], np.log2(s).astype(np.int32))
+        got = np.zeros((nbk * 64, d))
+        for j in range(nbk):
+            got[j * 64 + order] = ofp8.e4m3_decode(v8[h, j]).T
+        assert np.array_equal(got[:nkv], want)
