@@ -56,14 +56,25 @@ def work(p, fp8=False):
     """Algorithmic FLOPs / bytes of each stage for problem p (see the design notes)."""
     BH, d, b = p.batch * p.heads, p.head_dim, 64
     pairs = BH * p.nbq * p.top_k
-    sparse_flops = pairs * 4 * b * b * d + BH * p.nbq * 2 * b * d * d   # QK^T + PV + apply
+    qk_flops = pairs * 2 * b * b * d
+    pv_flops = pairs * 2 * b * b * d
+    apply_flops = BH * p.nbq * 2 * b * d * d
+    sparse_flops = qk_flops + pv_flops + apply_flops
+    # MFMA-time floor of the sparse kernel: the quantised branch runs P.V at the fp8 rate and
+    # Q K^T and the linear apply at the bf16 rate
+    if fp8:
+        floor_s = (qk_flops + apply_flops) / PEAK_BF16 + pv_flops / PEAK_FP8
+    else:
+        floor_s = sparse_flops / PEAK_BF16
     elt = 2 if p.dtype == "bf16" else 4
     kv_bytes = (2 * BH * p.n_kv * d * elt                  # read K, V
                 + BH * p.nbk * d * d * 2                  # write S_j (bf16)
                 + BH * p.nbk * b * d * 2)                 # write f16 V
     dense_flops = 4 * BH * p.n_q * p.n_kv * d
+    quant_bytes = BH * (p.n_q + p.n_kv) * d * (2 + 2) + BH * p.n_kv * d * (2 + 1)
     return {"pairs": pairs, "sparse_flops": sparse_flops, "kv_summary_bytes": kv_bytes,
-            "dense_flops": dense_flops}
+            "dense_flops": dense_flops, "sparse_peak": sparse_flops / floor_s,
+            "quant_bytes": quant_bytes}
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -259,17 +270,20 @@ def main():
 
     w = work(p, fp8)
     sparse_s = stage_ms["sparse"] * 1e-3
-    peak = PEAK_FP8 if fp8 else PEAK_BF16
+    peak = w["sparse_peak"]
     achieved = w["sparse_flops"] / sparse_s
     roofline = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak, "traffic": read_traffic(args.workload),
-                "kernel": "sparse_attn_kernel", "flops_per_launch": w["sparse_flops"],
+                "kernel": "sparse_attn_fp8_kernel" if fp8 else "sparse_attn_kernel",
+                "flops_per_launch": w["sparse_flops"],
                 "avg_launch_ms": stage_ms["sparse"]}
     kernels = {
         "stage_ms": stage_ms,
         "kv_summary_GBps": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / 1e9,
         "kv_summary_hbm_frac": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM,
     }
+    if fp8:
+        kernels["quant_GBps"] = w["quant_bytes"] / (stage_ms["quant"] * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- dense baselines
     dense = None

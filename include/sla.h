@@ -103,8 +103,9 @@ enum {
   SLA_STAGE_KV_SUMMARY = 0,  /* per-block phi(K)^T V, sum phi(K), pooled K, totals      */
   SLA_STAGE_ROUTE = 1,       /* pooled Q, projections, block scores, top-k              */
   SLA_STAGE_COMPLEMENT = 2,  /* per query block: total minus the selected summaries     */
-  SLA_STAGE_SPARSE = 3,      /* sparse attention + linear apply + alpha mix            */
-  SLA_NUM_STAGES = 4
+  SLA_STAGE_QUANT = 3,       /* E4M3 quantisation of Q, K, V (fp8 only; empty otherwise) */
+  SLA_STAGE_SPARSE = 4,      /* sparse attention + linear apply + alpha mix            */
+  SLA_NUM_STAGES = 5
 };
 
 /* Same as sla_forward (fp8 = 0) or sla_forward_fp8 (fp8 = 1), and additionally records

@@ -61,9 +61,11 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   if (mark(2 * SLA_STAGE_COMPLEMENT) != hipSuccess) return SLA_ERR_HIP;
   if (launch_complement(s, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_COMPLEMENT + 1) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_QUANT) != hipSuccess) return SLA_ERR_HIP;
+  if (fp8 && launch_quant(s, q, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (mark(2 * SLA_STAGE_QUANT + 1) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_SPARSE) != hipSuccess) return SLA_ERR_HIP;
   if (fp8) {
-    if (launch_quant(s, q, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
     if (launch_sparse_fp8(s, q, idx, alpha, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
   } else if (launch_sparse(s, q, k, idx, alpha, o, ws, stream) != hipSuccess) {
     return SLA_ERR_HIP;

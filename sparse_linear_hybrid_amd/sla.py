@@ -24,7 +24,7 @@ STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE"
 EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_profiled", "sla_workspace_region", "sla_status_string")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
-STAGES = ("kv_summary", "route", "complement", "sparse")
+STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
 
 
 class SlaError(RuntimeError):

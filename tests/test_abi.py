@@ -113,3 +113,19 @@ def test_status_strings(lib):
     for code in range(9):
         assert lib.sla_status_string(code).decode()
     assert lib.sla_status_string(99) == b"unknown status"
+
+
+def test_stage_names_follow_header_enum():
+    text = open(HEADER).read()
+    vals = {m.group(1).lower(): int(m.group(2))
+            for m in re.finditer(r"SLA_STAGE_(\w+)\s*=\s*(\d+)", text)}
+    n = int(re.search(r"SLA_NUM_STAGES\s*=\s*(\d+)", text).group(1))
+    assert sorted(vals.values()) == list(range(n))
+    assert tuple(sorted(vals, key=vals.get)) == sla.STAGES
+
+
+def test_workspace_regions_follow_header_enum(lib):
+    text = open(HEADER).read()
+    vals = {m.group(1).lower(): int(m.group(2))
+            for m in re.finditer(r"SLA_WS_(\w+)\s*=\s*(\d+)", text)}
+    assert vals == dict(sla.WS_REGIONS)
