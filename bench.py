@@ -138,14 +138,15 @@ def summarize_pmc(fetch_dir, write_dir, workload):
 
     f = per_kernel(rows(fetch_dir), "FETCH_SIZE")
     w = per_kernel(rows(write_dir), "WRITE_SIZE")
-    sp_f, sp_w = pick(f, "sparse_attn_kernel"), pick(w, "sparse_attn_kernel")
+    kname = "sparse_attn_fp8_kernel" if workload.endswith("_fp8") else "sparse_attn_kernel"
+    sp_f, sp_w = pick(f, kname), pick(w, kname)
     # the calibration copy is the largest copy dispatch of the run (1 GiB device to device)
     cp_f = pick(f, "copy", "max")
     cp_w = pick(w, "copy", "max")
     sf = (cp_f * 1024) / COPY_BYTES if cp_f else None       # KiB counted per real byte read
     sw = (cp_w * 1024) / COPY_BYTES if cp_w else None
     rec = {
-        "workload": workload,
+        "workload": workload, "kernel": kname,
         "source_sha256": sources_sha(SPARSE_SOURCES),
         "fetch_kib_per_launch": sp_f, "write_kib_per_launch": sp_w,
         "copy_fetch_kib": cp_f, "copy_write_kib": cp_w, "copy_bytes": COPY_BYTES,

@@ -81,6 +81,47 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
   return __builtin_bit_cast(u32x2, t);
 }
 
+// Raw buffer descriptor over `bytes` bytes from `base` (stride 0): loads at offsets >= bytes
+// return 0 without touching memory.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes from offset voff land at
+// LDS byte address lds + 16*l (lds is wave-uniform). Written as asm so that the compiler's
+// own wait insertion does not drain these loads before every LDS read; every consumer waits
+// explicitly (wait_vmem*, barrier_vmem_n). The instruction writes no VGPR, so nothing of the
+// compiler's register allocation is left in flight. M0 is set here and used by nothing else
+// in the kernels that call this; an SALU write of M0 needs one wait state before a load
+// into LDS reads it.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
+}
+// Wait until every vector-memory load of this wave, including loads into LDS, has landed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory loads of this wave are still in flight (they complete
+// in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for loops whose only LDS writes are loads into LDS: first wait until at
+// most N vector-memory loads of this wave are in flight, then s_barrier. Unlike
+// __syncthreads() it does not drain every outstanding load; the LDS reads before it have all
+// been consumed by then. One asm block, so no memory access moves across it.
+template <int N>
+__device__ __forceinline__ void barrier_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Exchange with lane l ^ 32: returns the value held by the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) {
   uint32_t u = __float_as_uint(x);

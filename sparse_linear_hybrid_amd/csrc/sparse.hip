@@ -45,6 +45,94 @@ __device__ __forceinline__ int swz(int row, int col) {
   return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
 }
 
+// Swizzle of the V tile. A transposing V^T read has each group of 16 lanes touch 4
+// consecutive key rows x 2 adjacent chunks (and each 32 lanes 4 rows x 4 chunks); XORing
+// the chunk index with f(row % 4) spreads those accesses over distinct banks whether the LDS
+// serves 128 or 256 bytes per clock. Rows are bijective, so the row-wise tile writes stay
+// conflict-free as well.
+template <int D>
+__device__ __forceinline__ int swzv_f(int row) {
+  const int r = row & 3;
+  return D == 128 ? (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) : 2 * r;
+}
+template <int D>
+__device__ __forceinline__ int swzv(int row, int col) {
+  constexpr int CH = D / 8;
+  return row * D + ((((col >> 3) ^ swzv_f<D>(row)) & (CH - 1)) << 3) + (col & 7);
+}
+
+// Ascending walk over the union of QB ascending selection lists. Each list is held 64
+// entries at a time in a VGPR (lane l: entry base + l) and read with readlane, so the walk
+// costs no memory round trip per step.
+template <int QB>
+struct UnionWalk {
+  const int32_t* selp[QB];
+  int nsel[QB], ptr[QB], base[QB], head[QB];
+  int selv[QB];
+
+  __device__ __forceinline__ void reload(int b) {
+    const int lane = threadIdx.x & 63;
+    selv[b] = base[b] + lane < nsel[b] ? selp[b][base[b] + lane] : 0;
+  }
+  __device__ __forceinline__ int read(int b) {
+    if (ptr[b] - base[b] >= 64) {
+      base[b] += 64;
+      reload(b);
+    }
+    return __builtin_amdgcn_readlane(selv[b], ptr[b] - base[b]);
+  }
+  __device__ __forceinline__ void init(const int32_t* idx, int bh, int nbq, int grp, int k) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int ib = grp * QB + b;
+      selp[b] = idx + ((size_t)bh * nbq + (ib < nbq ? ib : 0)) * k;
+      nsel[b] = ib < nbq ? k : 0;
+      ptr[b] = 0;
+      base[b] = 0;
+      reload(b);
+      head[b] = nsel[b] > 0 ? __builtin_amdgcn_readlane(selv[b], 0) : 0x7fffffff;
+    }
+  }
+  // next key block of the union and the mask of lists that contain it
+  __device__ __forceinline__ bool next_direct(int& j, int& flags) {
+    j = 0x7fffffff;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) j = min(j, head[b]);
+    flags = 0;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (head[b] == j && j != 0x7fffffff) {
+        flags |= 1 << b;
+        ++ptr[b];
+        head[b] = ptr[b] < nsel[b] ? read(b) : 0x7fffffff;
+      }
+    return flags != 0;
+  }
+
+  // The walk is buffered 64 union entries at a time (lane i: entry i, key block | flags<<24,
+  // -1 past the end), so the per-step read is a readlane and any list reload, with its wait
+  // on all outstanding loads, happens once per 64 steps.
+  int uvec = -1, upos = 64;
+  __device__ __forceinline__ void fill() {
+#pragma unroll 1
+    for (int i = 0; i < 64; ++i) {
+      int j, f;
+      const bool ok = next_direct(j, f);
+      const int e = ok ? (j | (f << 24)) : -1;
+      uvec = (int)(threadIdx.x & 63) == i ? e : uvec;
+    }
+    upos = 0;
+  }
+  __device__ __forceinline__ bool next(int& j, int& flags) {
+    if (upos == 64) fill();
+    const int e = __builtin_amdgcn_readlane(uvec, upos);
+    ++upos;
+    j = e & 0xffffff;
+    flags = e < 0 ? 0 : e >> 24;
+    return e >= 0;
+  }
+};
+
 // P^T-matched V^T fragment from a swizzled row-major [key][channel] tile: lane row (channel)
 // x0 + lane%32; reduction slot e holds key k0 + 4h + e (e < 4) or k0 + 8 + 4h + (e - 4)
 // (e >= 4), h = lane / 32.
@@ -54,8 +142,8 @@ __device__ __forceinline__ u32x4 vt_frag(const uint16_t* M, int x0, int k0) {
   const int g = lane >> 4, L = lane & 15;
   const int row = k0 + 4 * (g >> 1) + (L >> 2);
   const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const u32x2 lo = lds_read_tr16(M + swz<D>(row, col));
-  const u32x2 hi = lds_read_tr16(M + swz<D>(row + 8, col));
+  const u32x2 lo = lds_read_tr16(M + swzv<D>(row, col));
+  const u32x2 hi = lds_read_tr16(M + swzv<D>(row + 8, col));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -107,14 +195,17 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
 template <typename T, int D, int QB, bool OUT_BF16>
 __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
+  constexpr bool DMA = !SPLIT;             // bf16 inputs: K/V tiles go global -> LDS directly
   constexpr int NT = 128 * QB;             // threads
+  constexpr int NW = 2 * QB;               // waves
   constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
   constexpr int CT = D / 32;               // 32-channel tiles of the output
   constexpr int CH = D / 8;                // 16-byte chunks per row
-  constexpr int CPT = 64 * CH / NT;        // chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Kl[SPLIT ? 2 : 1][SPLIT ? 64 * D : 8];
+  constexpr int CPT = SPLIT ? 64 * CH / NT : 1;   // chunks per thread per tile (register path)
+  constexpr int KPW = 64 * D * 2 / 1024 / NW;     // 1-KB pieces per wave per tile (LDS DMA)
+  constexpr int TILE = 64 * D;             // elements of one K or V tile
+  // LDS DMA path: K ring of 3 tiles, then V ring of 2. Register path: K[2], V[2], Klo[2].
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(DMA ? 5 : 6) * TILE];
 
   const int wid = xcd_remap(blockIdx.x, a.total);
   const int bh = wid / a.ngroups, grp = wid % a.ngroups;
@@ -126,30 +217,9 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   const T* qb_ptr = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
   const T* kb = reinterpret_cast<const T*>(a.k) + (size_t)bh * a.nkv * D;
   const uint16_t* vb = a.v16 + (size_t)bh * a.nbk * kBlock * D;
-  const int k = a.topk;
 
-  // selection lists of the group's query blocks (absent blocks have empty lists)
-  const int32_t* selp[QB];
-  int nsel[QB], ptr[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int ib = grp * QB + b;
-    selp[b] = a.idx + ((size_t)bh * a.nbq + (ib < a.nbq ? ib : 0)) * k;
-    nsel[b] = ib < a.nbq ? k : 0;
-    ptr[b] = 0;
-  }
-  // next element of the ascending union: key block and membership flags
-  auto next_union = [&](int& j, int& flags) __attribute__((always_inline)) {
-    j = 0x7fffffff;
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-      if (ptr[b] < nsel[b]) j = min(j, selp[b][ptr[b]]);
-    flags = 0;
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-      if (ptr[b] < nsel[b] && selp[b][ptr[b]] == j) { flags |= 1 << b; ++ptr[b]; }
-    return flags != 0;
-  };
+  UnionWalk<QB> walk;
+  walk.init(a.idx, bh, a.nbq, grp, a.topk);
 
   // Q^T fragments (B operand): lane column q = qrow0 + l32, channels 16 s + 8 h .. +7
   u32x4 qf[KS];
@@ -177,8 +247,38 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   float m = kNegBig, l = 0.f;
   const float qk_scale = kLog2e / sqrtf((float)D);
 
-  // tile staging: registers -> swizzled LDS. Rows beyond n_kv read row n_kv-1: their logits
-  // are masked to -inf, so the values never contribute.
+  // LDS DMA: piece u of wave w is 1 KB of the swizzled tile (elements 512 (KPW w + u) ..);
+  // lane l lands at element +8 l, i.e. row r, physical chunk p, so it fetches the logical
+  // chunk that the swizzle puts there.
+  uint32_t koff[DMA ? KPW : 1], voff[DMA ? KPW : 1];
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  if constexpr (DMA) {
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
+      const int e = (wv * KPW + u) * 512 + lane * 8;
+      const int r = e / D, pch = (e % D) / 8;
+      koff[u] = (uint32_t)(r * D * 2 + ((pch ^ r) & (CH - 1)) * 16);
+      voff[u] = (uint32_t)(r * D * 2 + ((pch ^ swzv_f<D>(r)) & (CH - 1)) * 16);
+    }
+  }
+  // j < 0: an absent tile; the loads then cover an empty range (no memory access) so that
+  // every step issues the same number of loads, which the vmcnt waits below rely on.
+  auto stage_k = [&](int j, uint16_t* slot) __attribute__((always_inline)) {
+    const int row0 = j < 0 ? 0 : j * kBlock;
+    const uint32_t bytes = j < 0 ? 0u : (uint32_t)(min(kBlock, a.nkv - row0) * D * 2);
+    const auto r = make_rsrc(kb + (size_t)row0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) load_lds16(r, lds_addr(slot) + (wvs * KPW + u) * 1024, koff[u]);
+  };
+  auto stage_v = [&](int j, uint16_t* slot) __attribute__((always_inline)) {
+    const int row0 = j < 0 ? 0 : j * kBlock;
+    const auto r = make_rsrc(vb + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D * 2));
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) load_lds16(r, lds_addr(slot) + (wvs * KPW + u) * 1024, voff[u]);
+  };
+
+  // Register path (fp32 inputs): rows beyond n_kv read row n_kv-1; their logits are masked
+  // to -inf, so the values never contribute.
   u32x4 kreg[CPT], vreg[CPT], klreg[SPLIT ? CPT : 1];
   auto load_tile = [&](int j) __attribute__((always_inline)) {
     const int row0 = j * kBlock;
@@ -187,11 +287,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       const int id = t + NT * u;
       const int r = id / CH, c = id % CH;
       const size_t goff = (size_t)min(row0 + r, a.nkv - 1) * D + c * 8;
-      if constexpr (SPLIT) {
-        load_split_bf16x8(reinterpret_cast<const float*>(kb) + goff, kreg[u], klreg[u]);
-      } else {
-        kreg[u] = load_bf16x8(kb + goff);
-      }
+      load_split_bf16x8(reinterpret_cast<const float*>(kb) + goff, kreg[u], klreg[u]);
       vreg[u] = *reinterpret_cast<const u32x4*>(vb + (size_t)(row0 + r) * D + c * 8);
     }
   };
@@ -201,78 +297,90 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       const int id = t + NT * u;
       const int r = id / CH, c = id % CH;
       const int off = swz<D>(r, c * 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][off]) = kreg[u];
-      *reinterpret_cast<u32x4*>(&Vs[buf][off]) = vreg[u];
-      if constexpr (SPLIT) *reinterpret_cast<u32x4*>(&Kl[buf][off]) = klreg[u];
+      *reinterpret_cast<u32x4*>(&smem[buf * TILE + off]) = kreg[u];
+      *reinterpret_cast<u32x4*>(&smem[(2 + buf) * TILE + swzv<D>(r, c * 8)]) = vreg[u];
+      *reinterpret_cast<u32x4*>(&smem[(4 + buf) * TILE + off]) = klreg[u];
     }
   };
 
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
-  // One routed tile for this wave: scores, online softmax (base 2, running max m kept in
-  // scaled units), P.V accumulation.
-  auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j)
-                          __attribute__((always_inline)) {
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // One routed tile for this wave, in two 32-key halves so that the MFMAs of one half run
+  // while the VALU works on the other:
+  //   S0 = K[0:32] Q^T; rescale check of half 0;
+  //   S1 = K[32:64] Q^T            alongside  P0 = exp2(S0 - m) (f16), row sums;
+  //   rescale check of half 1;
+  //   O^T += V[0:32]^T P0^T        alongside  P1 = exp2(S1 - m), row sums;
+  //   O^T += V[32:64]^T P1^T.
+  // The online softmax runs in base 2 with the running max m in scaled units; the rescale of
+  // O and l happens only when a half's max exceeds m by more than the slack (a uniform
+  // branch, so each straight-line stretch between the checks can be interleaved). P0 is
+  // formed before half 1 is checked and added to O after it, so a rescale at half 1 scales
+  // P0 as well.
+  u32x4 pf[4];
+  auto qk_half = [&](const uint16_t* Kt, const uint16_t* Klo, int mt, f32x16& sh)
+                     __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
-        sacc[mt] = mfma_bf16(af, qf[ks], sacc[mt]);
-        if constexpr (SPLIT) {
-          const u32x4 alo = *reinterpret_cast<const u32x4*>(&Klo[off]);
-          sacc[mt] = mfma_bf16(af, ql[ks], sacc[mt]);
-          sacc[mt] = mfma_bf16(alo, qf[ks], sacc[mt]);
-        }
+      const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
+      const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[off]);
+      sh = mfma_bf16(af, qf[ks], sh);
+      if constexpr (SPLIT) {
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(&Klo[off]);
+        sh = mfma_bf16(af, ql[ks], sh);
+        sh = mfma_bf16(alo, qf[ks], sh);
       }
     }
-    // mask the tail of a partial last key block (uniform, rare)
+  };
+  // tail mask and rescale check of one half (its row max over 32 keys, both lane halves)
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+  auto check_half = [&](f32x16& sh, int mt, int j) __attribute__((always_inline)) {
     if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          sacc[mt][e] = key < a.nkv ? sacc[mt][e] : -INFINITY;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        sh[e] = key < a.nkv ? sh[e] : -INFINITY;
+      }
     }
     float r = kNegBig;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[mt][e]);
-    r = fmaxf(r, swap_halves(r)) * qk_scale;      // row max in scaled (log2) units
+    for (int e = 0; e < 16; ++e) r = fmaxf(r, sh[e]);
+    r = fmaxf(r, swap_halves(r)) * qk_scale;
     if (__ballot(r > m + kRescaleSlack)) {
       const float mn = fmaxf(m, r);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
       l *= corr;
 #pragma unroll
       for (int c = 0; c < CT; ++c) o[c] *= corr;
+      if (mt == 1) {
+        const _Float16 ch = (_Float16)corr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          pf[kk] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, pf[kk]) * ch);
+      }
       m = mn;
     }
-    u32x4 pf[4];
+  };
+  // P^T fragments pf[2 mt], pf[2 mt + 1] of one half and its row-sum contribution
+  auto exp_half = [&](const f32x16& sh, int mt) __attribute__((always_inline)) {
     float rs = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e = 8 * hh + 2 * e2;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e], qk_scale, -m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e + 1], qk_scale, -m));
-          const uint32_t pk = pack_f16(p0, p1);
-          pf[2 * mt + hh][e2] = pk;
-          rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, rs, false);
-        }
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e = 8 * hh + 2 * e2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e], qk_scale, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e + 1], qk_scale, -m));
+        const uint32_t pk = pack_f16(p0, p1);
+        pf[2 * mt + hh][e2] = pk;
+        rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, rs, false);
       }
     }
     l += rs;
-    // O^T += V^T P^T over the 64 keys (four 16-key steps), independent accumulators inner
+  };
+  // O^T += V^T P^T over the 32 keys of one half (two 16-key steps)
+  auto pv_half = [&](const uint16_t* Vt, int mt) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 2 * mt; kk < 2 * mt + 2; ++kk) {
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
         const u32x4 vf = vt_frag<D>(Vt, 32 * c, 16 * kk);
@@ -280,31 +388,75 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       }
     }
   };
-
-  int j_cur, f_cur;
-  bool have = next_union(j_cur, f_cur);
-  if (have) {
-    load_tile(j_cur);
-    store_tile(0);
-  }
-  __syncthreads();
-  // Loop unrolled by two so that the LDS buffer of each half is a compile-time constant.
-  auto step = [&](auto bufc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bufc)::value;
-    int j_nxt, f_nxt;
-    const bool have_nxt = next_union(j_nxt, f_nxt);
-    if (have_nxt) load_tile(j_nxt);
-    if ((f_cur >> qb) & 1) compute_tile(Ks[B], Kl[SPLIT ? B : 0], Vs[B], j_cur);
-    if (have_nxt) store_tile(B ^ 1);
-    __syncthreads();
-    j_cur = j_nxt;
-    f_cur = f_nxt;
-    have = have_nxt;
+  auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j)
+                          __attribute__((always_inline)) {
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    qk_half(Kt, Klo, 0, s0);
+    check_half(s0, 0, j);
+    qk_half(Kt, Klo, 1, s1);
+    exp_half(s0, 0);
+    check_half(s1, 1, j);
+    pv_half(Vt, 0);
+    exp_half(s1, 1);
+    pv_half(Vt, 1);
   };
-  while (have) {
-    step(std::integral_constant<int, 0>{});
-    if (!have) break;
-    step(std::integral_constant<int, 1>{});
+
+  if constexpr (DMA) {
+    // Ring pipeline. Step s computes tile s while V(s+1) and K(s+2) load (issued in that
+    // order), then waits until at most the K(s+2) loads are in flight and meets the others
+    // at one barrier: V(s+1) and K(s+1) have then landed. A K slot is rewritten two steps
+    // after its Q K^T and a V slot one step after its P.V, both behind that barrier, so K
+    // loads get two steps to land and V loads one.
+    uint16_t* const kring = smem;
+    uint16_t* const vring = smem + 3 * TILE;
+    int j0, f0, j1, f1;
+    bool have0 = walk.next(j0, f0);
+    bool have1 = walk.next(j1, f1);
+    stage_k(have0 ? j0 : -1, kring);
+    stage_k(have1 ? j1 : -1, kring + TILE);
+    stage_v(have0 ? j0 : -1, vring);
+    barrier_vmem_n<0>();
+    int ks = 0, vs = 0;
+    while (have0) {
+      int j2, f2;
+      const bool have2 = walk.next(j2, f2);
+      const int ks2 = ks == 0 ? 2 : ks - 1;          // (ks + 2) % 3
+      stage_v(have1 ? j1 : -1, vring + (vs ^ 1) * TILE);
+      stage_k(have2 ? j2 : -1, kring + ks2 * TILE);
+      if ((f0 >> qb) & 1) compute_tile(kring + ks * TILE, nullptr, vring + vs * TILE, j0);
+      barrier_vmem_n<KPW>();
+      j0 = j1; f0 = f1; have0 = have1;
+      j1 = j2; f1 = f2; have1 = have2;
+      ks = ks == 2 ? 0 : ks + 1;
+      vs ^= 1;
+    }
+  } else {
+    int j_cur, f_cur;
+    bool have = walk.next(j_cur, f_cur);
+    if (have) {
+      load_tile(j_cur);
+      store_tile(0);
+    }
+    __syncthreads();
+    // Loop unrolled by two so that the LDS buffer of each half is a compile-time constant.
+    auto step = [&](auto bufc) __attribute__((always_inline)) {
+      constexpr int B = decltype(bufc)::value;
+      int j_nxt, f_nxt;
+      const bool have_nxt = walk.next(j_nxt, f_nxt);
+      if (have_nxt) load_tile(j_nxt);
+      if ((f_cur >> qb) & 1)
+        compute_tile(smem + B * TILE, smem + (4 + B) * TILE, smem + (2 + B) * TILE, j_cur);
+      if (have_nxt) store_tile(B ^ 1);
+      __syncthreads();
+      j_cur = j_nxt;
+      f_cur = f_nxt;
+      have = have_nxt;
+    };
+    while (have) {
+      step(std::integral_constant<int, 0>{});
+      if (!have) break;
+      step(std::integral_constant<int, 1>{});
+    }
   }
   if (!active) return;   // no barrier follows
 
@@ -399,28 +551,8 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(Spars
   const int qrow0 = iq * kBlock + 32 * (wv & 1);
   const uint16_t* k8b = a.k8 + (size_t)bh * a.nbk * kBlock * D;
   const uint8_t* v8b = a.v8 + (size_t)bh * a.nbk * kBlock * D;
-  const int k = a.topk;
-
-  const int32_t* selp[QB];
-  int nsel[QB], ptr[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int ib = grp * QB + b;
-    selp[b] = a.idx + ((size_t)bh * a.nbq + (ib < a.nbq ? ib : 0)) * k;
-    nsel[b] = ib < a.nbq ? k : 0;
-    ptr[b] = 0;
-  }
-  auto next_union = [&](int& j, int& flags) __attribute__((always_inline)) {
-    j = 0x7fffffff;
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-      if (ptr[b] < nsel[b]) j = min(j, selp[b][ptr[b]]);
-    flags = 0;
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-      if (ptr[b] < nsel[b] && selp[b][ptr[b]] == j) { flags |= 1 << b; ++ptr[b]; }
-    return flags != 0;
-  };
+  UnionWalk<QB> walk;
+  walk.init(a.idx, bh, a.nbq, grp, a.topk);
 
   // Q8^T fragments (B operand): lane column q, channels 16 s + 8 h .. +7
   u32x4 qf8[KS];
@@ -534,7 +666,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(Spars
   };
 
   int j_cur, f_cur;
-  bool have = next_union(j_cur, f_cur);
+  bool have = walk.next(j_cur, f_cur);
   if (have) {
     load_tile(j_cur);
     store_tile(0);
@@ -543,7 +675,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(Spars
   auto step = [&](auto bufc) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
     int j_nxt, f_nxt;
-    const bool have_nxt = next_union(j_nxt, f_nxt);
+    const bool have_nxt = walk.next(j_nxt, f_nxt);
     if (have_nxt) load_tile(j_nxt);
     if ((f_cur >> qb) & 1) compute_tile(Ks[B], V8s[B], j_cur);
     if (have_nxt) store_tile(B ^ 1);

@@ -119,6 +119,30 @@ def test_planted_ties_lowest_index(sla):
     assert ref[0][0].near_tie.any(), "the planted duplicates should create boundary ties"
 
 
+@pytest.mark.parametrize("boost", [0.0, 6.0, 40.0])
+def test_max_rises_inside_a_tile(sla, boost):
+    """Keys 32..63 of every key block lean towards the queries, so the running maximum jumps
+    between the two halves of a tile (by more than the rescale slack for the larger boosts)
+    as well as between tiles; the online softmax must stay exact in every case."""
+    from workloads import Inputs, bf16_round_bits
+    x = make_custom(1, 2, 256, 384, 128, 3, dtype="bf16", kind="normal", seed=17)
+    q = x.as_f64("q")
+    k = x.as_f64("k")
+    for h in range(2):
+        u = q[0, h].mean(axis=0)
+        u /= np.linalg.norm(u)
+        second = (np.arange(k.shape[2]) % 64) >= 32
+        k[0, h, second] += boost * u
+    k_bits = bf16_round_bits(k.astype(np.float32))
+    y = Inputs(x.problem, x.q, k_bits, x.v, x.proj_q, x.proj_k, x.alpha, dict(x.meta))
+    out, idx = run_forward(sla, y)
+    ref, _ = oracle.forward(y)
+    check_masks(idx, oracle.sla_oracle.route_full(y), 3)
+    err, _ = max_err_over_rms(out, ref)
+    print(f"  boost {boost}: max-abs/rms {err:.3e}")
+    assert err <= TOL, f"max-abs/rms {err:.3e}"
+
+
 def test_deterministic(sla):
     x = make_custom(1, 2, 256, 256, 128, 3, dtype="bf16", kind="smooth", seed=8)
     a, ia = run_forward(sla, x)
