@@ -215,28 +215,69 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // summary, C[n][i] = sum_j M[i][j] S_j[n] with M the 0/1 selection matrix, computed as an
 // MFMA product over steps of CK key blocks (M is exact in bf16), then S_c = S_tot - C.
 // The tile's selections are first scattered into an LDS bitmap (one bit per query block and
-// key block of a window of WIN key blocks) together with a per-step occupancy bitmap, so
-// steps that no query block of the tile selects are skipped; the summaries of the next
-// occupied step are prefetched into registers while the current step runs. Query tiles
-// sharing a column slice are consecutive workgroups (same XCD), so each S_j slice comes
-// from HBM about once.
+// key block of a window of up to 32 * MAXW key blocks; one 32-bit word per query block and
+// step), and the steps that no query block of the tile selects are skipped. The summary
+// slices of a step (CK rows of CN bf16) are loaded straight into a CBUF-deep LDS ring, two
+// steps ahead of their use. Each wave owns 64 of the CN columns and all CQ query blocks:
+// per step it reads 4 A fragments (summaries, transposing LDS reads) and builds 8 B
+// fragments (bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a column slice
+// are consecutive workgroups (same XCD), so each S_j slice comes from HBM about once.
 constexpr int CQ = 128;    // query blocks per workgroup
-constexpr int CN = 128;    // summary columns per workgroup
-constexpr int CK = 32;     // key blocks per step (two 16-deep MFMA reductions)
-constexpr int WIN = 2048;  // key blocks per bitmap window
+constexpr int CN = 256;    // summary columns per workgroup (64 per wave)
+constexpr int CK = 32;     // key blocks per step = bits per bitmap word
+constexpr int CBUF = 3;    // steps in the LDS ring
+constexpr int MAXW = 30;   // bitmap words per query block and window (window <= 960 blocks)
+constexpr int RING_BYTES = CBUF * CK * CN * 2;
+
+// Dynamic LDS of complement_kernel for a window of `ww` words: ring, bitmap (ww + 1 words
+// per query block: the odd row length keeps the per-lane word reads on distinct banks) and
+// four 64-bit step-occupancy masks.
+inline size_t complement_lds_bytes(int ww) {
+  return (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
+}
+
+// Swizzle of a ring row (CN bf16 = 32 chunks of 16 bytes): chunk c of row r sits at
+// c ^ f(r % 4), which keeps the transposing fragment reads (4 rows x 2 or 4 adjacent chunks
+// per 16 or 32 lanes) on distinct banks.
+__device__ __forceinline__ int ring_f(int r) {
+  const int q = r & 3;
+  return ((q & 1) ? 6 : 0) ^ ((q & 2) ? 10 : 0);
+}
+// A fragment from a ring step buffer M[j][n]: lane owns n = x0 + lane%32 and the 8 key
+// blocks k0 + 8*(lane/32) .. +7.
+__device__ __forceinline__ u32x4 ring_frag(const uint16_t* M, int x0, int k0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (L >> 2);
+  const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
+  const int off = ((((col >> 3) ^ ring_f(row)) & 31) << 3) + (col & 7);
+  const u32x2 lo = lds_read_tr16(M + row * CN + off);
+  const u32x2 hi = lds_read_tr16(M + (row + 4) * CN + off);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+// bf16 0/1 B fragment from 8 selection bits (bit e -> element e)
+__device__ __forceinline__ u32x4 bits_to_bf16x8(uint32_t m8) {
+  u32x4 b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t x = (m8 >> (2 * e)) & 3u;
+    b[e] = ((x * 0x8001u) & 0x10001u) * 0x3F80u;   // bit 0 -> low half, bit 1 -> high half
+  }
+  return b;
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void complement_kernel(
+__global__ __launch_bounds__(256, 2) void complement_kernel(
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ sblk,
     const float* __restrict__ stot, uint16_t* __restrict__ sc, int nbq, int nbk, int k,
-    int nqt, int total) {
+    int nqt, int total, int ww) {
   constexpr int NCS = D * D / CN;      // column slices per (batch, head)
-  constexpr int SS = CN + 8;           // padded LDS row of staged summaries
-  constexpr int WW = WIN / 32 + 1;     // bitmap words per query block (+1: no bank conflicts)
-  constexpr int NSTEP = WIN / CK;      // steps per window
-  __shared__ uint32_t bits[CQ * WW];
-  __shared__ uint32_t occ[NSTEP / 32];
-  __shared__ __attribute__((aligned(16))) uint16_t Ss[2][CK * SS];
+  constexpr int LPW = CK * CN * 2 / 1024 / 4;   // 1-KB ring loads per wave per step
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+  uint16_t* ring = reinterpret_cast<uint16_t*>(dyn);
+  const int WW = ww + 1;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(dyn + RING_BYTES);
+  uint64_t* occw = reinterpret_cast<uint64_t*>(bits + CQ * WW + (CQ * WW & 1));
 
   const int wid = xcd_remap(blockIdx.x, total);
   const int qt = wid % nqt;
@@ -257,65 +298,89 @@ __global__ __launch_bounds__(256) void complement_kernel(
   }
   const int nq_tile = min(CQ, nbq - qt * CQ);
   const int32_t* sel0 = idx + ((size_t)bh * nbq + qt * CQ) * k;
-  // staging: thread t loads summary rows t/16 and 16 + t/16 of a step, 8 columns at (t%16)*8
-  const int sr = t >> 4, sc8 = t & 15;
-  const uint16_t* sbase = sblk + (size_t)bh * nbk * D * D + col0 + sc8 * 8;
 
-  f32x16 acc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-  for (int win0 = 0; win0 < nbk; win0 += WIN) {
+  // ring loads: wave w moves pieces LPW w .. LPW w + LPW - 1 (1 KB = 2 rows of 512 bytes);
+  // lane l lands at row 2 piece + l / 32, physical chunk l % 32, and fetches the logical
+  // chunk that the swizzle puts there
+  uint32_t roff[LPW];
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) {
+    const int r = 2 * (LPW * w + u) + (lane >> 5), pch = lane & 31;
+    roff[u] = (uint32_t)((size_t)r * D * D * 2 + ((pch ^ ring_f(r)) & 31) * 16);
+  }
+  const int ws = __builtin_amdgcn_readfirstlane(w);
+  const uint16_t* sbase = sblk + (size_t)bh * nbk * D * D + col0;
+  auto stage = [&](int j0, int slot) __attribute__((always_inline)) {   // j0 < 0: nothing
+    const uint32_t bytes = j0 < 0 ? 0u : (uint32_t)min(CK, nbk - j0) * D * D * 2;
+    const i32x4 r = make_rsrc(sbase + (size_t)(j0 < 0 ? 0 : j0) * D * D, bytes);
+    const uint32_t dst = lds_addr(ring + slot * CK * CN) + ws * LPW * 1024;
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) load_lds16(r, dst + u * 1024, roff[u]);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int tq = 0; tq < 4; ++tq)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[tq][nt] = f32x16{};
+
+  const int win = ww * CK;
+  for (int win0 = 0; win0 < nbk; win0 += win) {
+    const int nstep = min(ww, (nbk - win0 + CK - 1) / CK);
+    barrier_vmem_n<0>();   // the previous window's (empty) ring loads have all landed
     for (int e = t; e < CQ * WW; e += 256) bits[e] = 0u;
-    if (t < NSTEP / 32) occ[t] = 0u;
     __syncthreads();
     for (int e = t; e < nq_tile * k; e += 256) {
       const int j = sel0[e] - win0;
-      if (j >= 0 && j < WIN) {
-        const int il = e / k;
-        atomicOr(&bits[il * WW + (j >> 5)], 1u << (j & 31));
-        atomicOr(&occ[(j / CK) >> 5], 1u << ((j / CK) & 31));
-      }
+      if (j >= 0 && j < win) atomicOr(&bits[(e / k) * WW + (j >> 5)], 1u << (j & 31));
     }
     __syncthreads();
-    // occupied steps of this window, in order
-    auto next_step = [&](int from) {
-      for (int st = from; st < NSTEP; ++st)
-        if ((occ[st >> 5] >> (st & 31)) & 1u) return st;
-      return NSTEP;
+    // occupied steps: wave w ORs the words of its 32 query blocks, lane = step
+    {
+      uint32_t v = 0;
+      if (lane < nstep)
+        for (int il = 32 * w; il < min(32 * w + 32, nq_tile); ++il) v |= bits[il * WW + lane];
+      const uint64_t bal = __ballot(v != 0);
+      if (lane == 0) occw[w] = bal;
+    }
+    __syncthreads();
+    const uint64_t occ = occw[0] | occw[1] | occw[2] | occw[3];
+    auto next_after = [&](int st) -> int {   // first occupied step > st, or -1
+      const uint64_t rest = st >= 63 ? 0ull : occ & ~((2ull << st) - 1ull);
+      return rest ? __builtin_ctzll(rest) : -1;
     };
-    auto load_step = [&](int st, u32x4& r0, u32x4& r1) {
-      const int ja = win0 + st * CK + sr, jb = ja + 16;
-      r0 = ja < nbk ? *reinterpret_cast<const u32x4*>(sbase + (size_t)ja * D * D) : u32x4{0, 0, 0, 0};
-      r1 = jb < nbk ? *reinterpret_cast<const u32x4*>(sbase + (size_t)jb * D * D) : u32x4{0, 0, 0, 0};
-    };
-    int st = next_step(0);
-    u32x4 r0, r1;
-    if (st < NSTEP) load_step(st, r0, r1);
-    int buf = 0;
-    while (st < NSTEP) {
-      *reinterpret_cast<u32x4*>(&Ss[buf][sr * SS + sc8 * 8]) = r0;
-      *reinterpret_cast<u32x4*>(&Ss[buf][(sr + 16) * SS + sc8 * 8]) = r1;
-      __syncthreads();
-      const int nst = next_step(st + 1);
-      if (nst < NSTEP) load_step(nst, r0, r1);
+    int s_cur = occ ? __builtin_ctzll(occ) : -1;
+    int s_ld = s_cur;
+    stage(s_ld < 0 ? -1 : win0 + s_ld * CK, 0);
+    s_ld = s_ld < 0 ? -1 : next_after(s_ld);
+    stage(s_ld < 0 ? -1 : win0 + s_ld * CK, 1);
+    s_ld = s_ld < 0 ? -1 : next_after(s_ld);
+    barrier_vmem_n<0>();
+    int slot = 0;
+    while (s_cur >= 0) {
+      stage(s_ld < 0 ? -1 : win0 + s_ld * CK, slot == 0 ? 2 : slot - 1);
+      s_ld = s_ld < 0 ? -1 : next_after(s_ld);
+      const uint16_t* M = ring + slot * CK * CN;
+      uint32_t word[4];
+#pragma unroll
+      for (int tq = 0; tq < 4; ++tq) word[tq] = bits[(32 * tq + l32) * WW + s_cur];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x4 a = frag_tr(Ss[buf], SS, 32 * w, 16 * kk);
-        const int bit0 = st * CK + 16 * kk + 8 * h;          // first key block of the slot
+        const u32x4 a0 = ring_frag(M, 64 * w, 16 * kk);
+        const u32x4 a1 = ring_frag(M, 64 * w + 32, 16 * kk);
 #pragma unroll
         for (int tq = 0; tq < 4; ++tq) {
-          const uint32_t word = bits[(32 * tq + l32) * WW + (bit0 >> 5)];
-          const uint32_t m8 = (word >> (bit0 & 31)) & 0xffu;
-          u32x4 b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            b[e] = ((m8 >> (2 * e)) & 1u ? 0x3F80u : 0u) | ((m8 >> (2 * e + 1)) & 1u ? 0x3F800000u : 0u);
-          acc[tq] = mfma_bf16(a, b, acc[tq]);
+          const u32x4 b = bits_to_bf16x8((word[tq] >> (16 * kk + 8 * h)) & 0xffu);
+          acc[tq][0] = mfma_bf16(a0, b, acc[tq][0]);
+          acc[tq][1] = mfma_bf16(a1, b, acc[tq][1]);
         }
       }
-      buf ^= 1;
-      st = nst;
+      barrier_vmem_n<LPW>();   // the next step's slices have landed; its slot is free
+      s_cur = next_after(s_cur);
+      slot = slot == 2 ? 0 : slot + 1;
     }
-    __syncthreads();   // bitmap reuse in the next window
   }
+  wait_vmem();   // no load into LDS outlives the workgroup
   // S_c = S_tot - C; lane column = query block, rows = 4-column runs
 #pragma unroll
   for (int tq = 0; tq < 4; ++tq) {
@@ -324,13 +389,15 @@ __global__ __launch_bounds__(256) void complement_kernel(
     uint16_t* dst = sc + ((size_t)bh * nbq + i) * D * D + col0;
     const float* tot = stot + (size_t)bh * D * D + col0;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int n = 32 * w + 8 * g + 4 * h;
-      const f32x4 tv = *reinterpret_cast<const f32x4*>(tot + n);
-      *reinterpret_cast<u32x2*>(dst + n) =
-          u32x2{pack_bf16(tv[0] - acc[tq][4 * g], tv[1] - acc[tq][4 * g + 1]),
-                pack_bf16(tv[2] - acc[tq][4 * g + 2], tv[3] - acc[tq][4 * g + 3])};
-    }
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = 64 * w + 32 * nt + 8 * g + 4 * h;
+        const f32x4 tv = *reinterpret_cast<const f32x4*>(tot + n);
+        *reinterpret_cast<u32x2*>(dst + n) =
+            u32x2{pack_bf16(tv[0] - acc[tq][nt][4 * g], tv[1] - acc[tq][nt][4 * g + 1]),
+                  pack_bf16(tv[2] - acc[tq][nt][4 * g + 2], tv[3] - acc[tq][nt][4 * g + 3])};
+      }
   }
 }
 
@@ -386,11 +453,13 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
   const int nqt = (s.nbq + CQ - 1) / CQ;
   const int ncs = s.D * s.D / CN;
   const int total = s.BH * ncs * nqt;
+  const int ww = min(MAXW, (s.nbk + CK - 1) / CK);
+  const size_t lds = complement_lds_bytes(ww);
   auto go = [&](auto kern, auto zkern) {
-    hipLaunchKernelGGL(kern, dim3(total), dim3(256), 0, st, idx,
+    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, idx,
                        reinterpret_cast<const uint16_t*>(ws + s.sblk),
                        reinterpret_cast<const float*>(ws + s.stot),
-                       reinterpret_cast<uint16_t*>(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total);
+                       reinterpret_cast<uint16_t*>(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww);
     hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
                        reinterpret_cast<const float*>(ws + s.zblk),
                        reinterpret_cast<const float*>(ws + s.ztot),

@@ -430,6 +430,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       ks = ks == 2 ? 0 : ks + 1;
       vs ^= 1;
     }
+    wait_vmem();   // no load into LDS outlives the workgroup
   } else {
     int j_cur, f_cur;
     bool have = walk.next(j_cur, f_cur);
