@@ -214,29 +214,30 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // Complement, summary part: for a tile of CQ query blocks and CN columns n of the d x d
 // summary, C[n][i] = sum_j M[i][j] S_j[n] with M the 0/1 selection matrix, computed as an
 // MFMA product over steps of CK key blocks (M is exact in bf16), then S_c = S_tot - C.
-// The tile's selections are first scattered into an LDS bitmap (one bit per query block and
-// key block of a window of up to 32 * MAXW key blocks; one 32-bit word per query block and
-// step), and the steps that no query block of the tile selects are skipped. The summary
-// slices of a step (CK rows of CN bf16) are loaded straight into a CBUF-deep LDS ring, two
-// steps ahead of their use. Each wave owns 64 of the CN columns and all CQ query blocks:
-// per step it reads 4 A fragments (summaries, transposing LDS reads) and builds 8 B
-// fragments (bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a column slice
-// are consecutive workgroups (same XCD), so each S_j slice comes from HBM about once.
-constexpr int CQ = 128;    // query blocks per workgroup
-constexpr int CN = 256;    // summary columns per workgroup (64 per wave)
+// Each thread first turns one query block's ascending selection list into an LDS bitmap
+// row (one 32-bit word per step of a window of up to 32 * MAXW key blocks), and steps that
+// no query block of the tile selects are skipped. The summary slices of a step (CK rows of
+// CN bf16) are loaded straight into a CBUF-deep LDS ring, two steps ahead of their use.
+// Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
+// reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
+// builds 4 B fragments (its bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a
+// column slice are consecutive workgroups (same XCD), so each S_j slice comes from HBM
+// about once and from L2 ceil(n_blocks / CQ) times.
+constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
+constexpr int CN = 128;    // summary columns per workgroup
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
 constexpr int CBUF = 3;    // steps in the LDS ring
 constexpr int MAXW = 30;   // bitmap words per query block and window (window <= 960 blocks)
 constexpr int RING_BYTES = CBUF * CK * CN * 2;
 
 // Dynamic LDS of complement_kernel for a window of `ww` words: ring, bitmap (ww + 1 words
-// per query block: the odd row length keeps the per-lane word reads on distinct banks) and
-// four 64-bit step-occupancy masks.
+// per query block: the odd row length keeps the per-lane word accesses on distinct banks)
+// and four 64-bit step-occupancy masks.
 inline size_t complement_lds_bytes(int ww) {
   return (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
 }
 
-// Swizzle of a ring row (CN bf16 = 32 chunks of 16 bytes): chunk c of row r sits at
+// Swizzle of a ring row (CN bf16 = 16 chunks of 16 bytes): chunk c of row r sits at
 // c ^ f(r % 4), which keeps the transposing fragment reads (4 rows x 2 or 4 adjacent chunks
 // per 16 or 32 lanes) on distinct banks.
 __device__ __forceinline__ int ring_f(int r) {
@@ -250,7 +251,7 @@ __device__ __forceinline__ u32x4 ring_frag(const uint16_t* M, int x0, int k0) {
   const int g = lane >> 4, L = lane & 15;
   const int row = k0 + 8 * (g >> 1) + (L >> 2);
   const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const int off = ((((col >> 3) ^ ring_f(row)) & 31) << 3) + (col & 7);
+  const int off = ((((col >> 3) ^ ring_f(row)) & 15) << 3) + (col & 7);
   const u32x2 lo = lds_read_tr16(M + row * CN + off);
   const u32x2 hi = lds_read_tr16(M + (row + 4) * CN + off);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   uint16_t* ring = reinterpret_cast<uint16_t*>(dyn);
   const int WW = ww + 1;
   uint32_t* bits = reinterpret_cast<uint32_t*>(dyn + RING_BYTES);
-  uint64_t* occw = reinterpret_cast<uint64_t*>(bits + CQ * WW + (CQ * WW & 1));
+  uint64_t* occw = reinterpret_cast<uint64_t*>(bits + CQ * WW);
 
   const int wid = xcd_remap(blockIdx.x, total);
   const int qt = wid % nqt;
@@ -296,17 +297,20 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     }
     return;
   }
-  const int nq_tile = min(CQ, nbq - qt * CQ);
-  const int32_t* sel0 = idx + ((size_t)bh * nbq + qt * CQ) * k;
+  // this thread's query block and its selection list
+  const int qi = qt * CQ + t;
+  const int32_t* my_sel = idx + ((size_t)bh * nbq + min(qi, nbq - 1)) * k;
+  const int my_n = qi < nbq ? k : 0;
+  int my_p = 0;
 
-  // ring loads: wave w moves pieces LPW w .. LPW w + LPW - 1 (1 KB = 2 rows of 512 bytes);
-  // lane l lands at row 2 piece + l / 32, physical chunk l % 32, and fetches the logical
+  // ring loads: wave w moves pieces LPW w .. LPW w + LPW - 1 (1 KB = 4 rows of 256 bytes);
+  // lane l lands at row 4 piece + l / 16, physical chunk l % 16, and fetches the logical
   // chunk that the swizzle puts there
   uint32_t roff[LPW];
 #pragma unroll
   for (int u = 0; u < LPW; ++u) {
-    const int r = 2 * (LPW * w + u) + (lane >> 5), pch = lane & 31;
-    roff[u] = (uint32_t)((size_t)r * D * D * 2 + ((pch ^ ring_f(r)) & 31) * 16);
+    const int r = 4 * (LPW * w + u) + (lane >> 4), pch = lane & 15;
+    roff[u] = (uint32_t)((size_t)r * D * D * 2 + ((pch ^ ring_f(r)) & 15) * 16);
   }
   const int ws = __builtin_amdgcn_readfirstlane(w);
   const uint16_t* sbase = sblk + (size_t)bh * nbk * D * D + col0;
@@ -318,33 +322,62 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     for (int u = 0; u < LPW; ++u) load_lds16(r, dst + u * 1024, roff[u]);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int tq = 0; tq < 4; ++tq)
+  for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) acc[tq][nt] = f32x16{};
+    for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = f32x16{};
 
   const int win = ww * CK;
   for (int win0 = 0; win0 < nbk; win0 += win) {
     const int nstep = min(ww, (nbk - win0 + CK - 1) / CK);
-    barrier_vmem_n<0>();   // the previous window's (empty) ring loads have all landed
-    for (int e = t; e < CQ * WW; e += 256) bits[e] = 0u;
-    __syncthreads();
-    for (int e = t; e < nq_tile * k; e += 256) {
-      const int j = sel0[e] - win0;
-      if (j >= 0 && j < win) atomicOr(&bits[(e / k) * WW + (j >> 5)], 1u << (j & 31));
-    }
-    __syncthreads();
-    // occupied steps: wave w ORs the words of its 32 query blocks, lane = step
+    barrier_vmem_n<0>();   // the previous window's ring and bitmap are no longer in use
+    // bitmap row of this thread's query block (the list is ascending: one pass per window;
+    // entries are fetched 16 at a time so that their loads overlap)
+    uint64_t my_occ = 0;
     {
-      uint32_t v = 0;
-      if (lane < nstep)
-        for (int il = 32 * w; il < min(32 * w + 32, nq_tile); ++il) v |= bits[il * WW + lane];
-      const uint64_t bal = __ballot(v != 0);
-      if (lane == 0) occw[w] = bal;
+      int word_i = 0;
+      uint32_t word = 0;
+      bool more = my_p < my_n;
+      while (more) {
+        int e16[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) e16[u] = my_p + u < my_n ? my_sel[my_p + u] : 0x7fffffff;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int j = e16[u] - win0;          // e16 = INT_MAX past the end: j >= win
+          if (more && j < win) {
+            ++my_p;
+            while (word_i < (j >> 5)) {
+              bits[t * WW + word_i] = word;
+              my_occ |= (uint64_t)(word != 0) << word_i;
+              word = 0;
+              ++word_i;
+            }
+            word |= 1u << (j & 31);
+          } else {
+            more = false;
+          }
+        }
+        more = more && my_p < my_n;
+      }
+      for (; word_i < ww; ++word_i) {
+        bits[t * WW + word_i] = word;
+        my_occ |= (uint64_t)(word != 0) << word_i;
+        word = 0;
+      }
     }
+    // union of the occupancy masks over the workgroup
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)my_occ, o, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(my_occ >> 32), o, 64);
+      my_occ |= ((uint64_t)hi << 32) | lo;
+    }
+    if (lane == 0) occw[w] = my_occ;
     __syncthreads();
-    const uint64_t occ = occw[0] | occw[1] | occw[2] | occw[3];
+    const uint64_t occ = (occw[0] | occw[1] | occw[2] | occw[3]) &
+                         (nstep >= 64 ? ~0ull : ((1ull << nstep) - 1ull));
     auto next_after = [&](int st) -> int {   // first occupied step > st, or -1
       const uint64_t rest = st >= 63 ? 0ull : occ & ~((2ull << st) - 1ull);
       return rest ? __builtin_ctzll(rest) : -1;
@@ -361,18 +394,19 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       stage(s_ld < 0 ? -1 : win0 + s_ld * CK, slot == 0 ? 2 : slot - 1);
       s_ld = s_ld < 0 ? -1 : next_after(s_ld);
       const uint16_t* M = ring + slot * CK * CN;
-      uint32_t word[4];
+      uint32_t word[2];
 #pragma unroll
-      for (int tq = 0; tq < 4; ++tq) word[tq] = bits[(32 * tq + l32) * WW + s_cur];
+      for (int tq = 0; tq < 2; ++tq) word[tq] = bits[(64 * w + 32 * tq + l32) * WW + s_cur];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const u32x4 a0 = ring_frag(M, 64 * w, 16 * kk);
-        const u32x4 a1 = ring_frag(M, 64 * w + 32, 16 * kk);
+        u32x4 a[4];
 #pragma unroll
-        for (int tq = 0; tq < 4; ++tq) {
+        for (int nt = 0; nt < 4; ++nt) a[nt] = ring_frag(M, 32 * nt, 16 * kk);
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
           const u32x4 b = bits_to_bf16x8((word[tq] >> (16 * kk + 8 * h)) & 0xffu);
-          acc[tq][0] = mfma_bf16(a0, b, acc[tq][0]);
-          acc[tq][1] = mfma_bf16(a1, b, acc[tq][1]);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = mfma_bf16(a[nt], b, acc[tq][nt]);
         }
       }
       barrier_vmem_n<LPW>();   // the next step's slices have landed; its slot is free
@@ -381,23 +415,36 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     }
   }
   wait_vmem();   // no load into LDS outlives the workgroup
-  // S_c = S_tot - C; lane column = query block, rows = 4-column runs
+  // S_c = S_tot - C, staged through LDS (the ring and bitmap are free now) so that every
+  // query block's CN columns go out as contiguous 16-byte stores. Per half tq, wave w
+  // stages its 32 query blocks x CN columns; 16-byte chunk c of staged row q sits at
+  // c ^ (q % 16).
+  __syncthreads();
+  const float* tot = stot + (size_t)bh * D * D + col0;
+  uint16_t* stg = reinterpret_cast<uint16_t*>(dyn) + w * 32 * CN;
 #pragma unroll
-  for (int tq = 0; tq < 4; ++tq) {
-    const int i = qt * CQ + 32 * tq + l32;
-    if (i >= nbq) continue;
-    uint16_t* dst = sc + ((size_t)bh * nbq + i) * D * D + col0;
-    const float* tot = stot + (size_t)bh * D * D + col0;
+  for (int tq = 0; tq < 2; ++tq) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = 64 * w + 32 * nt + 8 * g + 4 * h;
+        const int n = 32 * nt + 8 * g + 4 * h;
         const f32x4 tv = *reinterpret_cast<const f32x4*>(tot + n);
-        *reinterpret_cast<u32x2*>(dst + n) =
+        const int off = l32 * CN + ((((n >> 3) ^ l32) & 15) << 3) + (n & 7);
+        *reinterpret_cast<u32x2*>(stg + off) =
             u32x2{pack_bf16(tv[0] - acc[tq][nt][4 * g], tv[1] - acc[tq][nt][4 * g + 1]),
                   pack_bf16(tv[2] - acc[tq][nt][4 * g + 2], tv[3] - acc[tq][nt][4 * g + 3])};
       }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {           // 4 rows of 16 chunks per pass
+      const int q = 4 * u + (lane >> 4), c = lane & 15;
+      const int i = qt * CQ + 64 * w + 32 * tq + q;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + q * CN + (((c ^ q) & 15) << 3));
+      if (i < nbq) *reinterpret_cast<u32x4*>(sc + ((size_t)bh * nbq + i) * D * D + col0 + c * 8) = v;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
