@@ -199,14 +199,24 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
                                                             const float* __restrict__ zpart,
                                                             float* __restrict__ stot,
                                                             float* __restrict__ ztot, int nchunk) {
+  // chunk partials are added in chunk order (deterministic); loads go out 8 at a time
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
+  const float* src = spart + (size_t)bh * nchunk * D * D + e;
   float s = 0.f;
-  for (int c = 0; c < nchunk; ++c) s += spart[((size_t)bh * nchunk + c) * D * D + e];
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * D * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; c < nchunk; ++c) s += src[(size_t)c * D * D];
   stot[(size_t)bh * D * D + e] = s;
   if (blockIdx.x == 0 && threadIdx.x < D) {
     float z = 0.f;
-    for (int c = 0; c < nchunk; ++c) z += zpart[((size_t)bh * nchunk + c) * D + threadIdx.x];
+    for (int cc = 0; cc < nchunk; ++cc) z += zpart[((size_t)bh * nchunk + cc) * D + threadIdx.x];
     ztot[(size_t)bh * D + threadIdx.x] = z;
   }
 }
@@ -462,8 +472,18 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
     return;
   }
   const int32_t* sel = idx + ((size_t)bh * nbq + i) * k;
+  const float* zb = zblk + (size_t)bh * nbk * D + r;
+  // selected blocks are added in list order (deterministic); loads go out 8 at a time
   float z = 0.f;
-  for (int s = 0; s < k; ++s) z += zblk[((size_t)bh * nbk + sel[s]) * D + r];
+  int s = 0;
+  for (; s + 8 <= k; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = zb[(size_t)sel[s + u] * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) z += v[u];
+  }
+  for (; s < k; ++s) z += zb[(size_t)sel[s] * D];
   out[r] = ztot[(size_t)bh * D + r] - z;
 }
 

@@ -11,85 +11,118 @@
 namespace sla {
 
 // ----------------------------------------------------------------------------- pooling
-// Sum of one 64-token block into per-thread partials: each thread owns 8 consecutive
-// channels of rows r0, r0 + RPP, ... (RPP = rows covered by the 256 threads per pass).
-template <typename T, int D>
-__device__ __forceinline__ void block_sum_partial(const T* __restrict__ x, int row0, int nrows,
-                                                  double (&acc)[8]) {
-  constexpr int TPR = D / 8;           // threads per row
-  constexpr int RPP = 256 / TPR;       // rows per pass
-  const int t = threadIdx.x;
-  const int cg = t % TPR, r = t / TPR;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int rr = r; rr < nrows; rr += RPP) {
-    const T* p = x + (size_t)(row0 + rr) * D + cg * 8;
-    if constexpr (sizeof(T) == 2) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += (double)bf16_lo(w[e]);
-        acc[2 * e + 1] += (double)bf16_hi(w[e]);
-      }
-    } else {
-      f32x4 a = *reinterpret_cast<const f32x4*>(p);
-      f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += (double)a[e];
-        acc[4 + e] += (double)b[e];
-      }
-    }
-  }
-}
-
-// Combine the per-thread partials (fixed order) and write the mean over nrows tokens.
-template <int D>
-__device__ __forceinline__ void block_mean_finish(double (&acc)[8], int nrows, double* lds,
-                                                  double* __restrict__ out) {
-  constexpr int TPR = D / 8;
-  constexpr int RPP = 256 / TPR;
-  const int t = threadIdx.x;
-  const int cg = t % TPR, r = t / TPR;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) lds[r * D + cg * 8 + e] = acc[e];
-  __syncthreads();
-  if (t < D) {
-    double s = 0.0;
-    for (int rr = 0; rr < RPP; ++rr) s += lds[rr * D + t];
-    out[t] = s / (double)nrows;
-  }
-  __syncthreads();
-}
-
 // Pool + project for PB consecutive blocks of one (batch, head): block means over the
-// valid tokens (float64 sums, exact for bf16 data) and x~ = mean @ P in float64. Reading P
-// once per PB blocks keeps the projection off the critical path.
+// valid tokens (float64 sums, exact for bf16 data, so the summation order does not matter)
+// and x~ = mean @ P in float64. The loads of G blocks are issued together; each thread sums
+// its rows of 8 channels, the rows of a wave are combined with lane exchanges and the four
+// waves through LDS. Each thread then projects one output channel for PB * D / 256 of the
+// blocks, reading P once per PB blocks.
 constexpr int PB = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_project_kernel(const T* __restrict__ x,
                                                            const float* __restrict__ P,
                                                            double* __restrict__ out, int n, int nb) {
-  constexpr int RPP = 256 / (D / 8);
-  __shared__ double part[RPP * D];
+  constexpr int TPR = D / 8;            // threads per row (8 channels each)
+  constexpr int RPP = 256 / TPR;        // rows per pass of the workgroup
+  constexpr int LPB = kBlock / RPP;     // rows per thread and block
+  constexpr int G = 4;                  // blocks whose loads are in flight together
+  __shared__ double part[4][G][D];
   __shared__ double means[PB][D];
   const int j0 = blockIdx.x * PB, bh = blockIdx.y;
   const int nblk = min(PB, nb - j0);
   const T* xb = x + (size_t)bh * n * D;
-  const int t = threadIdx.x;
-  for (int b = 0; b < nblk; ++b) {
-    const int row0 = (j0 + b) * kBlock;
-    const int nrows = min(kBlock, n - row0);
-    double acc[8];
-    block_sum_partial<T, D>(xb, row0, nrows, acc);
-    block_mean_finish<D>(acc, nrows, part, &means[b][0]);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int cg = t % TPR, r = t / TPR;
+  for (int b0 = 0; b0 < nblk; b0 += G) {
+    double acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] = 0.0;
+    }
+    if constexpr (sizeof(T) == 2) {
+      u32x4 raw[G][LPB];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int u = 0; u < LPB; ++u) {
+          const int row = (j0 + b0 + g) * kBlock + r + RPP * u;
+          raw[g][u] = (b0 + g < nblk && row < n)
+                          ? *reinterpret_cast<const u32x4*>(xb + (size_t)row * D + cg * 8)
+                          : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int u = 0; u < LPB; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[g][2 * e] += (double)bf16_lo(raw[g][u][e]);
+            acc[g][2 * e + 1] += (double)bf16_hi(raw[g][u][e]);
+          }
+    } else {
+      f32x4 raw[G][LPB][2];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int u = 0; u < LPB; ++u) {
+          const int row = (j0 + b0 + g) * kBlock + r + RPP * u;
+          const bool ok = b0 + g < nblk && row < n;
+          const float* p = xb + (size_t)(ok ? row : 0) * D + cg * 8;
+          raw[g][u][0] = ok ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
+          raw[g][u][1] = ok ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int u = 0; u < LPB; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[g][e] += (double)raw[g][u][0][e];
+            acc[g][4 + e] += (double)raw[g][u][1][e];
+          }
+    }
+    // rows of one wave: lanes with the same channel group differ by multiples of TPR
+#pragma unroll
+    for (int o = TPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, 64);
+    if (lane < TPR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[w][g][cg * 8 + e] = acc[g][e];
+    }
+    __syncthreads();
+    for (int e = t; e < G * D; e += 256) {
+      const int g = e / D, c = e % D;
+      if (b0 + g < nblk) {
+        const int nrows = min(kBlock, n - (j0 + b0 + g) * kBlock);
+        means[b0 + g][c] = (part[0][g][c] + part[1][g][c] + part[2][g][c] + part[3][g][c]) /
+                           (double)nrows;
+      }
+    }
+    __syncthreads();
   }
-  for (int b = t / D; b < nblk; b += 256 / D) {
-    const int c = t % D;
-    double acc = 0.0;
-    for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)P[r * D + c], acc);
-    out[((size_t)bh * nb + j0 + b) * D + c] = acc;
+  // (means are visible: the last pooling round ended with a barrier)
+  constexpr int NBT = PB * D / 256;     // blocks per thread
+  const int c = t % D, b0 = t / D;      // blocks b0, b0 + 256/D, ...
+  double acc[NBT];
+#pragma unroll
+  for (int u = 0; u < NBT; ++u) acc[u] = 0.0;
+#pragma unroll 8
+  for (int rr = 0; rr < D; ++rr) {
+    const double pv = (double)P[rr * D + c];
+#pragma unroll
+    for (int u = 0; u < NBT; ++u) acc[u] = fma(means[b0 + u * (256 / D)][rr], pv, acc[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < NBT; ++u) {
+    const int b = b0 + u * (256 / D);
+    if (b < nblk) out[((size_t)bh * nb + j0 + b) * D + c] = acc[u];
   }
 }
 
@@ -114,15 +147,29 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int c0 = 0; c0 < D; c0 += C) {
-    // 64 rows x 32 channels per operand = 2048 values, 8 per thread
-    for (int e = t; e < T * C; e += 256) {
-      const int r = e / C, cc = e % C;
+  // 64 rows x 32 channels per operand and chunk = 2048 values, 8 per thread; the next
+  // chunk is fetched into registers while the current one is multiplied
+  constexpr int PER = T * C / 256;
+  double ra[PER], rb[PER];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = t + 256 * u, r = e / C, cc = e % C;
       const int gi = i0 + r, gj = j0 + r;
-      As[cc][r] = gi < nbq ? qb[(size_t)gi * D + c0 + cc] : 0.0;
-      Bs[cc][r] = gj < nbk ? kb[(size_t)gj * D + c0 + cc] : 0.0;
+      ra[u] = gi < nbq ? qb[(size_t)gi * D + c0 + cc] : 0.0;
+      rb[u] = gj < nbk ? kb[(size_t)gj * D + c0 + cc] : 0.0;
+    }
+  };
+  fetch(0);
+  for (int c0 = 0; c0 < D; c0 += C) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = t + 256 * u, r = e / C, cc = e % C;
+      As[cc][r] = ra[u];
+      Bs[cc][r] = rb[u];
     }
     __syncthreads();
+    if (c0 + C < D) fetch(c0 + C);
 #pragma unroll 4
     for (int cc = 0; cc < C; ++cc) {
       double a[4], b[4];
@@ -208,32 +255,36 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ sco
     const int L = 63 - __clzll(ge);           // highest lane whose suffix reaches `remaining`
     uint32_t above = __shfl(suf - own, L, 64);
     int digit = 0;
+    uint32_t cnt = 0;
     if (lane == L) {
       uint32_t acc = above;
       digit = 4 * L;
       for (int b = 3; b >= 0; --b) {
-        if (acc + h[b] >= (uint32_t)remaining) { digit = 4 * L + b; break; }
+        if (acc + h[b] >= (uint32_t)remaining) { digit = 4 * L + b; cnt = h[b]; break; }
         acc += h[b];
       }
       above = acc;
     }
     digit = __shfl(digit, L, 64);
     above = __shfl(above, L, 64);
+    cnt = __shfl(cnt, L, 64);
     remaining -= (int)above;
     prefix |= (uint64_t)digit << shift;
     mask |= 255ull << shift;
     __syncthreads();
+    if (cnt == (uint32_t)remaining) break;   // the whole bucket is kept: no further digits
   }
-  // prefix == T, the k-th largest key; `remaining` keys equal to T are to be kept.
-  const uint64_t T = prefix;
+  // Keys whose masked value exceeds `prefix` are kept, and of those equal to it under the
+  // mask the first `remaining` in index order (all of them when the loop stopped early;
+  // after all 8 digits the mask is complete and these are exact ties, lowest index first).
   int written = 0, eq_seen = 0;
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
   for (int base = 0; base < nbk; base += 64) {
     const int j = base + lane;
     const bool valid = j < nbk;
-    const uint64_t key = valid ? keys[j] : 0ull;
-    const bool gt = valid && key > T;
-    const bool eq = valid && key == T;
+    const uint64_t key = valid ? (keys[j] & mask) : 0ull;
+    const bool gt = valid && key > prefix;
+    const bool eq = valid && key == prefix;
     const unsigned long long eqb = __ballot(eq);
     const int eq_rank = eq_seen + __popcll(eqb & lt_mask);
     const bool sel = gt || (eq && eq_rank < remaining);
