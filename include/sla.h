@@ -137,6 +137,49 @@ typedef enum {
 sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,
                                 size_t* bytes);
 
+/* ---------------------------------------------------------------- key/value summary cache
+ * Decode path (SPLA page, section 2.2: the linear term of the unselected key blocks is the
+ * total over all blocks minus that of the selected ones; SLA2 page, section 2.B: the router
+ * only needs the pooled, projected keys). The cache keeps, per (batch, head), the totals
+ * S_tot = sum_t phi(k_t)^T v_t (fp32, stored transposed [d(c)][d(r)]), z_tot = sum_t phi(k_t)
+ * (fp32) and the projected block means k~_j (fp64) of every key block:
+ *   bytes [0, B*H*d*d*4)                S_tot^T [B*H][d][d]
+ *   then (256-byte aligned)             z_tot   [B*H][d]
+ *   then (256-byte aligned)             k~      [ceil(n_kv/64)][B*H][d]  (block-major)
+ * The layout only grows at its end with n_kv, so a cache allocated for the final length
+ * serves every shorter one. Only bf16 inputs are supported on this path. */
+
+/* Bytes of the cache for p->n_kv tokens. 0 if the problem is invalid. */
+size_t sla_kv_cache_size(const sla_problem* p);
+
+/* Workspace bytes sla_kv_cache_update needs for an update from n_done tokens (>= 256). */
+size_t sla_kv_cache_workspace_size(const sla_problem* p, int32_t n_done);
+
+/* Bring the cache from the first n_done tokens of K and V to all p->n_kv tokens: adds the
+ * new tokens' phi(k)^T v and phi(k) to the totals (n_done = 0 initialises them) and
+ * recomputes k~ of every key block holding a new token from all its valid tokens (proj_k:
+ * as in sla_forward). K, V: [batch, heads, n_kv, head_dim] bf16, the first n_done tokens
+ * unchanged since the last update. Device pointers, 16-byte aligned. Calls on one cache
+ * must be ordered (same stream). Returns SLA_ERR_DTYPE for fp32 inputs, SLA_ERR_SHAPE if
+ * n_done is outside [0, n_kv]. */
+sla_status sla_kv_cache_update(const sla_problem* p, const void* k, const void* v,
+                               const float* proj_k, int32_t n_done, void* cache,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of sla_forward_cached. 0 if the problem is invalid. */
+size_t sla_cached_workspace_size(const sla_problem* p);
+
+/* The forward of sla_forward computed against a summary cache that covers all p->n_kv tokens
+ * (routing against the cached k~; the linear branch from the cached totals minus the
+ * selected blocks' summaries, which are formed from the K/V tiles the exact branch reads).
+ * Same outputs and conventions as sla_forward; no proj_k argument (it is in the cache). The
+ * work per call scales with the selected blocks, not with n_kv: meant for few query blocks
+ * per head (decode chunks). bf16 inputs only. */
+sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k, const void* v,
+                              const float* proj_q, const float* alpha, const void* cache,
+                              void* o, int32_t* block_idx, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sla_status_string(sla_status s);
 

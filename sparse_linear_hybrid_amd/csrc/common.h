@@ -197,4 +197,62 @@ inline Plan make_plan(const sla_problem& p) {
   return s;
 }
 
+// ----------------------------------------------------------------------------- summary cache
+// Key/value summary cache (caller-owned, see sla_kv_cache_update): S_tot^T [BH][D(c)][D(r)]
+// fp32, z_tot [BH][D] fp32, then k~ [nbk][BH][D] fp64. k~ is block-major so that the layout
+// only grows at its end as tokens are appended.
+struct CachePlan {
+  size_t stot, ztot, kt, bytes;
+};
+inline CachePlan make_cache_plan(const Plan& s) {
+  CachePlan c{};
+  const size_t BH = s.BH, D = s.D;
+  c.stot = 0;
+  c.ztot = align_up(BH * D * D * 4, 256);
+  c.kt = align_up(c.ztot + BH * D * 4, 256);
+  c.bytes = c.kt + (size_t)s.nbk * BH * D * 8;
+  return c;
+}
+// Chunks of kSummaryChunk key blocks that an update from n_done tokens to s.nkv touches.
+inline int cache_update_chunks(const Plan& s, int n_done) {
+  const int nblocks = s.nbk - n_done / kBlock;
+  return nblocks > 0 ? (nblocks + kSummaryChunk - 1) / kSummaryChunk : 0;
+}
+inline size_t cache_update_zpart_offset(const Plan& s, int n_done) {
+  return align_up((size_t)s.BH * cache_update_chunks(s, n_done) * s.D * s.D * 4, 256);
+}
+inline size_t cache_update_ws_bytes(const Plan& s, int n_done) {
+  return cache_update_zpart_offset(s, n_done) +
+         (size_t)s.BH * cache_update_chunks(s, n_done) * s.D * 4;
+}
+
+// Workspace of the cached forward: router buffers, then the per-part partial results of
+// the decode kernel.
+constexpr int kMaxDecodeParts = 32;
+struct DecodePlan {
+  int nsplit;
+  size_t qt, scores, idx, pml, po, ps, pz, bytes;
+};
+inline DecodePlan make_decode_plan(const Plan& s) {
+  DecodePlan d{};
+  const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk;
+  // enough parts to give the GPU about 1024 workgroups, each with at least 4 key blocks
+  int ns = (int)((1024 + BH * nbq - 1) / (BH * nbq));
+  ns = ns < s.k / 4 ? ns : s.k / 4;
+  ns = ns < kMaxDecodeParts ? ns : kMaxDecodeParts;
+  d.nsplit = ns < 1 ? 1 : ns;
+  const size_t parts = BH * nbq * d.nsplit;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  d.qt = take(BH * nbq * D * 8);
+  d.scores = take(BH * nbq * nbk * 8);
+  d.idx = take(BH * nbq * (size_t)(s.k > 0 ? s.k : 1) * 4);
+  d.pml = take(parts * kBlock * 2 * 4);
+  d.po = take(parts * kBlock * D * 4);
+  d.ps = take(parts * D * D * 4);
+  d.pz = take(parts * D * 4);
+  d.bytes = off;
+  return d;
+}
+
 }  // namespace sla

@@ -29,4 +29,18 @@ hipError_t launch_quant(const Plan& s, const void* q, const void* k, const void*
 hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
                              const float* alpha, void* o, char* ws, hipStream_t st);
 
+// Summary cache: bring k~, S_tot, z_tot from the first n_done tokens to s.nkv tokens.
+hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,
+                                  int n_done, char* cache, char* ws, hipStream_t st);
+
+// Router against cached k~ (k~ of block j of head bh at kt + bh * kbh + j * kj).
+hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, const double* kt,
+                               size_t kbh, size_t kj, int32_t* idx, double* qt, double* sc,
+                               hipStream_t st);
+
+// Cached forward: exact branch and selected-block summaries per part, then the combine.
+hipError_t launch_decode(const Plan& s, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const float* alpha, const char* cache, void* o,
+                         char* ws, hipStream_t st);
+
 }  // namespace sla

@@ -35,12 +35,17 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
   return pack_f16(fminf(fmaxf(a, -m), m), fminf(fmaxf(b, -m), m));
 }
 
-template <typename T, int D>
+// One pass over the key blocks jbase, jbase+1, ... (kSummaryChunk per workgroup): the
+// projected pooled K of each block (all its valid tokens) goes to kt + bh*kbh + j*kj, and
+// phi(K)^T V, sum phi(K) over the tokens t0 <= t < nkv go into the chunk's partial totals.
+// BLOCKS: also store each block's S_j^T, z_j and its f16 copy of V (the full forward; then
+// jbase = t0 = 0). Without BLOCKS this is the key/value summary cache update.
+template <typename T, int D, bool BLOCKS>
 __global__ __launch_bounds__(256) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
-    double* __restrict__ kt, uint16_t* __restrict__ v16, uint16_t* __restrict__ sblk,
-    float* __restrict__ zblk, float* __restrict__ spart, float* __restrict__ zpart, int nkv,
-    int nbk) {
+    double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
+    uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
+    float* __restrict__ zpart, int nkv, int nbk, int jbase, int t0) {
   constexpr int LS = D + 8;                  // padded LDS row (elements)
   constexpr int TPR = D / 8, RPP = 256 / TPR;
   constexpr int CPT = 64 * TPR / 256;        // 16-byte chunks per thread per tensor
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
-  const int j0 = chunk * kSummaryChunk, j1 = min(j0 + kSummaryChunk, nbk);
+  const int j0 = jbase + chunk * kSummaryChunk, j1 = min(j0 + kSummaryChunk, nbk);
   const T* kb = k + (size_t)bh * nkv * D;
   const T* vb = v + (size_t)bh * nkv * D;
   const int mt = (NT == 4) ? w : (w >> 1);   // this wave's 32-row tile of S_j (rows r)
@@ -92,7 +97,8 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
     for (int u = 0; u < CPT; ++u) {
       const int cidx = t + 256 * u;
       const int r = cidx / TPR, c8 = cidx % TPR;
-      const bool ok = r < nrows;
+      const bool ok = r < nrows;                 // valid token: pooled
+      const bool ok_sum = ok && row0 + r >= t0;  // and counted in the summaries
       float kf[8], vf[8];
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -109,20 +115,24 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        kf[e] = ok ? kf[e] : 0.f;
-        vf[e] = ok ? vf[e] : 0.f;
-        pacc[e] += (double)kf[e];
+        pacc[e] += ok ? (double)kf[e] : 0.0;
+        kf[e] = ok_sum ? kf[e] : 0.f;
+        vf[e] = ok_sum ? vf[e] : 0.f;
       }
-      u32x4 kw, vw, v16w;
+      u32x4 kw, vw;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         kw[e] = pack_bf16(kf[2 * e], kf[2 * e + 1]);
         vw[e] = pack_bf16(vf[2 * e], vf[2 * e + 1]);
-        v16w[e] = f16_sat_pack(vf[2 * e], vf[2 * e + 1]);
       }
       *reinterpret_cast<u32x4*>(&Ks[r * LS + c8 * 8]) = kw;
       *reinterpret_cast<u32x4*>(&Vs[r * LS + c8 * 8]) = vw;
-      *reinterpret_cast<u32x4*>(&v16[((size_t)bh * nbk * kBlock + row0 + r) * D + c8 * 8]) = v16w;
+      if constexpr (BLOCKS) {
+        u32x4 v16w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v16w[e] = f16_sat_pack(vf[2 * e], vf[2 * e + 1]);
+        *reinterpret_cast<u32x4*>(&v16[((size_t)bh * nbk * kBlock + row0 + r) * D + c8 * 8]) = v16w;
+      }
     }
     {
       const int cg = t % TPR, r = t / TPR;
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
       for (int e = 0; e < 4; ++e) zl += bf16_lo(af[s4][e]) + bf16_hi(af[s4][e]);
     }
     zl += swap_halves(zl);
-    if (((NT == 4) || (w & 1) == 0) && h == 0) {
+    if (BLOCKS && ((NT == 4) || (w & 1) == 0) && h == 0) {
       zblk[((size_t)bh * nbk + j) * D + 32 * mt + l32] = zl;
     }
     zp += zl;
@@ -158,14 +168,16 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) acc = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), acc);
       part[u] += acc;
-      // store S_j^T[c][r] (bf16): lane column c = 32 nt + l32, rows r in runs of 4
-      const int c = 32 * nt + l32;
-      uint16_t* dst = sblk + (((size_t)bh * nbk + j) * D + c) * D;
+      if constexpr (BLOCKS) {
+        // store S_j^T[c][r] (bf16): lane column c = 32 nt + l32, rows r in runs of 4
+        const int c = 32 * nt + l32;
+        uint16_t* dst = sblk + (((size_t)bh * nbk + j) * D + c) * D;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 32 * mt + 8 * q + 4 * h;
-        *reinterpret_cast<u32x2*>(dst + r) =
-            u32x2{pack_bf16(acc[4 * q], acc[4 * q + 1]), pack_bf16(acc[4 * q + 2], acc[4 * q + 3])};
+        for (int q = 0; q < 4; ++q) {
+          const int r = 32 * mt + 8 * q + 4 * h;
+          *reinterpret_cast<u32x2*>(dst + r) = u32x2{pack_bf16(acc[4 * q], acc[4 * q + 1]),
+                                                     pack_bf16(acc[4 * q + 2], acc[4 * q + 3])};
+        }
       }
     }
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
@@ -175,7 +187,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
     const int c = t % D;
     double acc = 0.0;
     for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)Pk[r * D + c], acc);
-    kt[((size_t)bh * nbk + j0 + b) * D + c] = acc;
+    kt[(size_t)bh * kbh + (size_t)(j0 + b) * kj + c] = acc;
   }
   // chunk partial totals (fp32, layout [c][r])
 #pragma unroll
@@ -198,12 +210,14 @@ template <int D>
 __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restrict__ spart,
                                                             const float* __restrict__ zpart,
                                                             float* __restrict__ stot,
-                                                            float* __restrict__ ztot, int nchunk) {
-  // chunk partials are added in chunk order (deterministic); loads go out 8 at a time
+                                                            float* __restrict__ ztot, int nchunk,
+                                                            int accumulate) {
+  // chunk partials are added in chunk order (deterministic), onto the previous totals when
+  // accumulating (summary cache update); loads go out 8 at a time
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const float* src = spart + (size_t)bh * nchunk * D * D + e;
-  float s = 0.f;
+  float s = accumulate ? stot[(size_t)bh * D * D + e] : 0.f;
   int c = 0;
   for (; c + 8 <= nchunk; c += 8) {
     float v[8];
@@ -215,7 +229,7 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
   for (; c < nchunk; ++c) s += src[(size_t)c * D * D];
   stot[(size_t)bh * D * D + e] = s;
   if (blockIdx.x == 0 && threadIdx.x < D) {
-    float z = 0.f;
+    float z = accumulate ? ztot[(size_t)bh * D + threadIdx.x] : 0.f;
     for (int cc = 0; cc < nchunk; ++cc) z += zpart[((size_t)bh * nchunk + cc) * D + threadIdx.x];
     ztot[(size_t)bh * D + threadIdx.x] = z;
   }
@@ -497,17 +511,47 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   float* spart = reinterpret_cast<float*>(ws + s.spart);
   float* zpart = reinterpret_cast<float*>(ws + s.zpart);
   const dim3 grid(s.nchunk, s.BH);
+  const size_t kbh = (size_t)s.nbk * D, kj = D;
   if (s.in_bf16)
-    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D>), grid, dim3(256), 0, st,
-                       (const uint16_t*)k, (const uint16_t*)v, pk, kt, v16, sblk, zblk, spart,
-                       zpart, s.nkv, s.nbk);
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true>), grid, dim3(256), 0, st,
+                       (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
+                       spart, zpart, s.nkv, s.nbk, 0, 0);
   else
-    hipLaunchKernelGGL((kv_summary_kernel<float, D>), grid, dim3(256), 0, st, (const float*)k,
-                       (const float*)v, pk, kt, v16, sblk, zblk, spart, zpart, s.nkv, s.nbk);
+    hipLaunchKernelGGL((kv_summary_kernel<float, D, true>), grid, dim3(256), 0, st,
+                       (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
+                       zpart, s.nkv, s.nbk, 0, 0);
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
-                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk);
+                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const void* v,
+                                           const float* pk, int n_done, const CachePlan& c,
+                                           char* cache, char* ws, hipStream_t st) {
+  const int jbase = n_done / kBlock;
+  const int nchunk = cache_update_chunks(s, n_done);
+  if (nchunk == 0) return hipSuccess;
+  double* kt = reinterpret_cast<double*>(cache + c.kt);
+  float* spart = reinterpret_cast<float*>(ws);
+  float* zpart = reinterpret_cast<float*>(ws + cache_update_zpart_offset(s, n_done));
+  const dim3 grid(nchunk, s.BH);
+  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false>), grid, dim3(256), 0, st,
+                     (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
+                     (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
+                     jbase, n_done);
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
+                     zpart, reinterpret_cast<float*>(cache + c.stot),
+                     reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,
+                                  int n_done, char* cache, char* ws, hipStream_t st) {
+  const CachePlan c = make_cache_plan(s);
+  if (s.D == 128) return launch_kv_cache_update_T<128>(s, k, v, pk, n_done, c, cache, ws, st);
+  return launch_kv_cache_update_T<64>(s, k, v, pk, n_done, c, cache, ws, st);
 }
 
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk,

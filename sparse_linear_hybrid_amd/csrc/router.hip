@@ -130,16 +130,18 @@ __global__ __launch_bounds__(256) void pool_project_kernel(const T* __restrict__
 // scores[bh][i][j] = sum_c qt[bh][i][c] * kt[bh][j][c]; float64, 64x64 output tile per
 // 256-thread workgroup, 4x4 outputs per thread, channel chunks of 32 staged in LDS.
 template <int D>
+// k~ of key block j of (batch, head) bh is at kt + bh * kbh + j * kj.
 __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ qt,
                                                     const double* __restrict__ kt,
-                                                    double* __restrict__ scores, int nbq, int nbk) {
+                                                    double* __restrict__ scores, int nbq, int nbk,
+                                                    size_t kbh, size_t kj) {
   constexpr int T = 64, C = 32;
   __shared__ double As[C][T + 1];
   __shared__ double Bs[C][T + 1];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
   const double* qb = qt + (size_t)bh * nbq * D;
-  const double* kb = kt + (size_t)bh * nbk * D;
+  const double* kb = kt + (size_t)bh * kbh;
   const int t = threadIdx.x;
   const int ty = t / 16, tx = t % 16;
   double acc[4][4];
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
       const int e = t + 256 * u, r = e / C, cc = e % C;
       const int gi = i0 + r, gj = j0 + r;
       ra[u] = gi < nbq ? qb[(size_t)gi * D + c0 + cc] : 0.0;
-      rb[u] = gj < nbk ? kb[(size_t)gj * D + c0 + cc] : 0.0;
+      rb[u] = gj < nbk ? kb[(size_t)gj * kj + c0 + cc] : 0.0;
     }
   };
   fetch(0);
@@ -297,33 +299,47 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ sco
 
 // ----------------------------------------------------------------------------- launchers
 template <int D>
+static void launch_pool_q(const Plan& s, const void* q, const float* pq, double* qt,
+                          hipStream_t st) {
+  const dim3 gq((s.nbq + PB - 1) / PB, s.BH);
+  if (s.in_bf16)
+    hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gq, dim3(256), 0, st,
+                       (const uint16_t*)q, pq, qt, s.nq, s.nbq);
+  else
+    hipLaunchKernelGGL((pool_project_kernel<float, D>), gq, dim3(256), 0, st, (const float*)q,
+                       pq, qt, s.nq, s.nbq);
+}
+
+template <int D>
+static void launch_select(const Plan& s, const double* qt, const double* kt, size_t kbh,
+                          size_t kj, double* sc, int32_t* idx, hipStream_t st) {
+  const int rq = s.BH * s.nbq;
+  hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
+                     dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk, kbh, kj);
+  if (s.k > 0) {
+    const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
+    hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, rq, s.nbk, s.k);
+  }
+}
+
+template <int D>
 static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, const float* pq,
                                  const float* pk, int32_t* idx, char* ws, bool pool_k,
                                  hipStream_t st) {
   double* qt = reinterpret_cast<double*>(ws + s.qt);
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   double* sc = reinterpret_cast<double*>(ws + s.scores);
-  const dim3 gq((s.nbq + PB - 1) / PB, s.BH), gk((s.nbk + PB - 1) / PB, s.BH);
-  if (s.in_bf16) {
-    hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gq, dim3(256), 0, st,
-                       (const uint16_t*)q, pq, qt, s.nq, s.nbq);
-    if (pool_k)
+  launch_pool_q<D>(s, q, pq, qt, st);
+  if (pool_k) {
+    const dim3 gk((s.nbk + PB - 1) / PB, s.BH);
+    if (s.in_bf16)
       hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gk, dim3(256), 0, st,
                          (const uint16_t*)k, pk, kt, s.nkv, s.nbk);
-  } else {
-    hipLaunchKernelGGL((pool_project_kernel<float, D>), gq, dim3(256), 0, st, (const float*)q,
-                       pq, qt, s.nq, s.nbq);
-    if (pool_k)
+    else
       hipLaunchKernelGGL((pool_project_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k,
                          pk, kt, s.nkv, s.nbk);
   }
-  const int rq = s.BH * s.nbq;
-  hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
-                     dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk);
-  if (s.k > 0) {
-    const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
-    hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, rq, s.nbk, s.k);
-  }
+  launch_select<D>(s, qt, kt, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
   return hipGetLastError();
 }
 
@@ -331,6 +347,19 @@ hipError_t launch_route(const Plan& s, const void* q, const void* k, const float
                         const float* pk, int32_t* idx, char* ws, bool pool_k, hipStream_t st) {
   if (s.D == 128) return launch_route_T<128>(s, q, k, pq, pk, idx, ws, pool_k, st);
   return launch_route_T<64>(s, q, k, pq, pk, idx, ws, pool_k, st);
+}
+
+hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, const double* kt,
+                               size_t kbh, size_t kj, int32_t* idx, double* qt, double* sc,
+                               hipStream_t st) {
+  if (s.D == 128) {
+    launch_pool_q<128>(s, q, pq, qt, st);
+    launch_select<128>(s, qt, kt, kbh, kj, sc, idx, st);
+  } else {
+    launch_pool_q<64>(s, q, pq, qt, st);
+    launch_select<64>(s, qt, kt, kbh, kj, sc, idx, st);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace sla

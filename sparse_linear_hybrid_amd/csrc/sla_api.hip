@@ -148,6 +148,67 @@ sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_
   return SLA_OK;
 }
 
+size_t sla_kv_cache_size(const sla_problem* p) {
+  if (check_problem(p) != SLA_OK) return 0;
+  return make_cache_plan(make_plan(*p)).bytes;
+}
+
+size_t sla_kv_cache_workspace_size(const sla_problem* p, int32_t n_done) {
+  if (check_problem(p) != SLA_OK || n_done < 0 || n_done > p->n_kv) return 0;
+  const size_t b = cache_update_ws_bytes(make_plan(*p), n_done);
+  return b > 0 ? b : 256;
+}
+
+sla_status sla_kv_cache_update(const sla_problem* p, const void* k, const void* v,
+                               const float* proj_k, int32_t n_done, void* cache,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  if (p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  if (n_done < 0 || n_done > p->n_kv) return SLA_ERR_SHAPE;
+  st = check_ptrs({k, v, proj_k, cache});
+  if (st != SLA_OK) return st;
+  const Plan s = make_plan(*p);
+  if (!workspace || workspace_bytes < cache_update_ws_bytes(s, n_done)) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  if (launch_kv_cache_update(s, k, v, proj_k, n_done, static_cast<char*>(cache),
+                             static_cast<char*>(workspace), stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
+size_t sla_cached_workspace_size(const sla_problem* p) {
+  if (check_problem(p) != SLA_OK) return 0;
+  return make_decode_plan(make_plan(*p)).bytes;
+}
+
+sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k, const void* v,
+                              const float* proj_q, const float* alpha, const void* cache,
+                              void* o, int32_t* block_idx, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  if (p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  st = check_ptrs({q, k, v, proj_q, alpha, cache, o});
+  if (st != SLA_OK) return st;
+  if (block_idx && !aligned16(block_idx)) return SLA_ERR_ALIGN;
+  const Plan s = make_plan(*p);
+  const DecodePlan d = make_decode_plan(s);
+  if (!workspace || workspace_bytes < d.bytes) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  const char* cc = static_cast<const char*>(cache);
+  const CachePlan c = make_cache_plan(s);
+  int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + d.idx);
+  if (launch_route_cached(s, q, proj_q, reinterpret_cast<const double*>(cc + c.kt),
+                          (size_t)s.D, (size_t)s.BH * s.D, idx,
+                          reinterpret_cast<double*>(ws + d.qt),
+                          reinterpret_cast<double*>(ws + d.scores), stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  if (launch_decode(s, q, k, v, idx, alpha, cc, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
 const char* sla_status_string(sla_status s) {
   switch (s) {
     case SLA_OK: return "ok";

@@ -22,7 +22,9 @@ STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE"
           4: "SLA_ERR_TOPK", 5: "SLA_ERR_ALIGN", 6: "SLA_ERR_WORKSPACE",
           7: "SLA_ERR_UNSUPPORTED", 8: "SLA_ERR_HIP"}
 EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
-           "sla_forward_profiled", "sla_workspace_region", "sla_status_string")
+           "sla_forward_profiled", "sla_workspace_region", "sla_status_string",
+           "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
+           "sla_cached_workspace_size", "sla_forward_cached")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
 STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
 
@@ -65,6 +67,16 @@ def _load() -> ctypes.CDLL:
     lib.sla_workspace_region.restype = ctypes.c_int
     lib.sla_status_string.argtypes = [ctypes.c_int]
     lib.sla_status_string.restype = ctypes.c_char_p
+    lib.sla_kv_cache_size.argtypes = [pp]
+    lib.sla_kv_cache_size.restype = sz
+    lib.sla_kv_cache_workspace_size.argtypes = [pp, ctypes.c_int32]
+    lib.sla_kv_cache_workspace_size.restype = sz
+    lib.sla_kv_cache_update.argtypes = [pp, vp, vp, vp, ctypes.c_int32, vp, vp, sz, vp]
+    lib.sla_kv_cache_update.restype = ctypes.c_int
+    lib.sla_cached_workspace_size.argtypes = [pp]
+    lib.sla_cached_workspace_size.restype = sz
+    lib.sla_forward_cached.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_forward_cached.restype = ctypes.c_int
     return lib
 
 
@@ -200,3 +212,60 @@ def workspace_region(p: Problem, name: str, fp8: bool = False) -> Tuple[int, int
     if st != 0:
         raise SlaError(st, "sla_workspace_region")
     return off.value, size.value
+
+
+# ----------------------------------------------------------------------------- summary cache
+def kv_cache_size(p: Problem) -> int:
+    """Bytes of the key/value summary cache for p.n_kv tokens (see include/sla.h)."""
+    return int(library().sla_kv_cache_size(ctypes.byref(p)))
+
+
+def sla_kv_cache_update(k, v, proj_k, cache: torch.Tensor, n_done: int = 0, block: int = 64,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Bring ``cache`` (uint8 device tensor of at least kv_cache_size bytes) from the first
+    n_done tokens of k, v to all of them (n_done = 0 builds it). Returns ``cache``."""
+    p = make_problem(k, k, 0, block)
+    if cache.numel() < kv_cache_size(p):
+        raise ValueError("cache tensor too small")
+    need = int(library().sla_kv_cache_workspace_size(ctypes.byref(p), int(n_done)))
+    if need == 0:
+        raise SlaError(2, "sla_kv_cache_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    st = library().sla_kv_cache_update(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(proj_k),
+                                       int(n_done), _ptr(cache), _ptr(workspace),
+                                       ctypes.c_size_t(workspace.numel()), _stream(k.device))
+    if st != 0:
+        raise SlaError(st, "sla_kv_cache_update")
+    return cache
+
+
+def cached_workspace_size(p: Problem) -> int:
+    return int(library().sla_cached_workspace_size(ctypes.byref(p)))
+
+
+def sla_forward_cached(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor, block: int = 64,
+                       out_dtype: torch.dtype = torch.float32, return_idx: bool = True,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None):
+    """SLA2 forward against a summary cache covering all of k, v. Returns (O, block_idx or
+    None)."""
+    p = make_problem(q, k, top_k, block, out_dtype)
+    need = cached_workspace_size(p)
+    if need == 0:
+        raise SlaError(2, "sla_cached_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    idx = None
+    if return_idx:
+        idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                          device=q.device)
+    st = library().sla_forward_cached(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                                      _ptr(alpha), _ptr(cache), _ptr(out), _ptr(idx),
+                                      _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                      _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_forward_cached")
+    return out, idx

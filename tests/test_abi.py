@@ -129,3 +129,54 @@ def test_workspace_regions_follow_header_enum(lib):
     vals = {m.group(1).lower(): int(m.group(2))
             for m in re.finditer(r"SLA_WS_(\w+)\s*=\s*(\d+)", text)}
     assert vals == dict(sla.WS_REGIONS)
+
+
+def test_kv_cache_layout_and_growth(lib):
+    """The cache is S_tot^T, z_tot, then k~ block-major: its size grows only with the number
+    of key blocks, by B*H*d*8 bytes per block."""
+    def size(**kw):
+        return lib.sla_kv_cache_size(ctypes.byref(prob(**kw)))
+    BH, d = 2, 128
+    base = size(n_kv=640)
+    stot = BH * d * d * 4
+    ztot_end = -(-stot // 256) * 256 + BH * d * 4
+    assert base == -(-ztot_end // 256) * 256 + 10 * BH * d * 8
+    assert size(n_kv=641) - base == BH * d * 8
+    assert size(n_kv=700) == size(n_kv=704)
+    assert size(n_kv=0) == 0
+
+
+def test_kv_cache_update_validation(lib):
+    vp = ctypes.c_void_p
+    p = prob(n_kv=700)
+
+    def upd(prob_=p, n_done=0, k=FAKE, cache=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lib.sla_kv_cache_update(ctypes.byref(prob_), vp(k), vp(FAKE), vp(FAKE),
+                                       ctypes.c_int32(n_done), vp(cache), vp(ws),
+                                       ctypes.c_size_t(ws_bytes), vp(0))
+    assert upd(prob_=prob(in_dtype=0)) == 3            # bf16 only
+    assert upd(n_done=-1) == 2 and upd(n_done=701) == 2
+    assert upd(k=0) == 1 and upd(cache=0) == 1
+    assert upd(cache=MISALIGNED) == 5
+    need = lib.sla_kv_cache_workspace_size(ctypes.byref(p), 0)
+    assert need >= 256
+    assert upd(ws_bytes=need - 1) == 6
+    # an update from 640 tokens touches only the last two key blocks
+    assert lib.sla_kv_cache_workspace_size(ctypes.byref(p), 640) < need
+    assert lib.sla_kv_cache_workspace_size(ctypes.byref(p), 701) == 0
+
+
+def test_forward_cached_validation(lib):
+    vp = ctypes.c_void_p
+    p = prob()
+
+    def fwd(prob_=p, q=FAKE, cache=FAKE, ws_bytes=1 << 40, idx=None):
+        return lib.sla_forward_cached(ctypes.byref(prob_), vp(q), vp(FAKE), vp(FAKE), vp(FAKE),
+                                      vp(FAKE), vp(cache), vp(FAKE), vp(idx), vp(FAKE),
+                                      ctypes.c_size_t(ws_bytes), vp(0))
+    assert fwd(prob_=prob(in_dtype=0)) == 3
+    assert fwd(prob_=prob(top_k=12)) == 4
+    assert fwd(q=0) == 1 and fwd(cache=0) == 1
+    assert fwd(idx=MISALIGNED) == 5
+    need = lib.sla_cached_workspace_size(ctypes.byref(p))
+    assert need > 0 and fwd(ws_bytes=need - 1) == 6
