@@ -180,6 +180,95 @@ def summarize_trace(d, out, command):
     print("\n".join(lines))
 
 
+# --------------------------------------------------------------------------- decode path
+def bench_cached(args, sla, x, q, k, v, pq, pk, al, out):
+    """sla_forward_cached against a cache built before timing (the key/value summary lives
+    with the KV cache); one step = one cached forward."""
+    import numpy as np
+    import torch
+    from workloads import sha256_of
+    p = x.problem
+    dev = q.device
+    kprob = sla.make_problem(k, k, 0)
+    cache = torch.empty(sla.kv_cache_size(kprob), dtype=torch.uint8, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sla.sla_kv_cache_update(k, v, pk, cache)                   # warm-up build
+    torch.cuda.synchronize()
+    a.record()
+    sla.sla_kv_cache_update(k, v, pk, cache)
+    b.record()
+    torch.cuda.synchronize()
+    build_ms = a.elapsed_time(b)
+    ws = torch.empty(sla.cached_workspace_size(sla.make_problem(q, k, p.top_k)),
+                     dtype=torch.uint8, device=dev)
+
+    def fwd():
+        sla.sla_forward_cached(q, k, v, pq, al, p.top_k, cache, return_idx=False, workspace=ws,
+                               out=out)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    if args.profile:
+        for _ in range(args.steps):
+            fwd()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": args.workload, "cached": True, "steps": args.steps}))
+        return 0
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        fwd()
+        e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / K
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    BH, d = p.batch * p.heads, p.head_dim
+    # bytes the method has to move: the selected K/V tiles, Q, O, the cached k~ (router)
+    # and S_tot, z_tot
+    sel_bytes = BH * p.nbq * p.top_k * 2 * 64 * d * 2
+    alg_bytes = (sel_bytes + BH * p.n_q * d * (2 + 4) + p.nbk * BH * d * 8 + BH * (d * d + d) * 4)
+    achieved = alg_bytes / (call_ms * 1e-3)
+    dense = None
+    if not args.no_dense:
+        f = torch.nn.functional.scaled_dot_product_attention
+        for _ in range(2):
+            f(q, k, v)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(3):
+            f(q, k, v)
+        b.record()
+        torch.cuda.synchronize()
+        sdpa = a.elapsed_time(b) / 3
+        dense = {"sdpa_bf16_ms": sdpa, "speedup_vs_sdpa": sdpa / ms}
+    line = {
+        "metric": METRIC, "value": ms, "unit": "ms", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": p.name, "path": "sla_forward_cached", "batch": p.batch,
+                   "heads": p.heads, "n_q": p.n_q, "n_kv": p.n_kv, "head_dim": d,
+                   "block": p.block, "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
+                     "kernel": "sla_forward_cached (whole call: route, decode, combine)",
+                     "bytes_per_call": alg_bytes, "avg_call_ms": call_ms},
+        "cpu_baseline": None,
+        "kv_cache_build_ms": build_ms,
+        "dense": dense,
+        "inputs_sha256": sha256_of(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line))
+    return 0
+
+
 # --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -190,6 +279,9 @@ def main():
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cached", action="store_true",
+                    help="time sla_forward_cached against a prebuilt key/value summary cache "
+                         "(the decode path); the cache build is timed separately")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     args = ap.parse_args()
@@ -227,8 +319,10 @@ def main():
 
     q, k, v, pq, pk, al = (t(a) for a in (x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha))
     prob = sla.make_problem(q, k, p.top_k)
-    ws = torch.empty(sla.workspace_size(prob, fp8), dtype=torch.uint8, device=dev)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    if args.cached:
+        return bench_cached(args, sla, x, q, k, v, pq, pk, al, out)
+    ws = torch.empty(sla.workspace_size(prob, fp8), dtype=torch.uint8, device=dev)
     fwd_fn = sla.sla_forward_fp8 if fp8 else sla.sla_forward
 
     def fwd():

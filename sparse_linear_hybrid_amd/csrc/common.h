@@ -213,10 +213,12 @@ inline CachePlan make_cache_plan(const Plan& s) {
   c.bytes = c.kt + (size_t)s.nbk * BH * D * 8;
   return c;
 }
-// Chunks of kSummaryChunk key blocks that an update from n_done tokens to s.nkv touches.
+// Key blocks per workgroup of a cache update, and the chunks an update from n_done tokens
+// to s.nkv touches (larger chunks than the forward's: fewer partial totals to add up).
+constexpr int kCacheChunk = 64;
 inline int cache_update_chunks(const Plan& s, int n_done) {
   const int nblocks = s.nbk - n_done / kBlock;
-  return nblocks > 0 ? (nblocks + kSummaryChunk - 1) / kSummaryChunk : 0;
+  return nblocks > 0 ? (nblocks + kCacheChunk - 1) / kCacheChunk : 0;
 }
 inline size_t cache_update_zpart_offset(const Plan& s, int n_done) {
   return align_up((size_t)s.BH * cache_update_chunks(s, n_done) * s.D * s.D * 4, 256);

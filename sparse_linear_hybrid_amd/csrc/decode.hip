@@ -18,7 +18,8 @@
 //
 // decode_combine_kernel: merges the parts into O_s, forms S_c = S_tot - S_sel and
 // z_c = z_tot - z_sel (zero when every key block is selected), then
-// O_l = phi(Q) S_c / (phi(Q) . z_c + eps) and O = alpha O_s + (1 - alpha) O_l.
+// O_l = phi(Q) S_c / (phi(Q) . z_c + eps) and O = alpha O_s + (1 - alpha) O_l; one workgroup
+// per 32 output channels.
 #include "common.h"
 #include "kernels.h"
 
@@ -86,7 +87,7 @@ struct DecodeArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void decode_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeArgs a) {
   constexpr int KS = D / 16;               // 16-channel steps of Q K^T
   constexpr int CT = D / 32;               // 32-channel tiles
   constexpr int CH = D / 8;                // 16-byte chunks per row
@@ -320,24 +321,29 @@ struct CombineArgs {
 };
 
 
+// One workgroup per (batch*head, query block, 32-channel tile ct of the output): S_c^T rows
+// c in the tile (all d columns r), z_c, the merge weights of the parts, then for the two
+// 32-row query tiles (waves 0 and 1) O_l^T = S_c^T phi(Q)^T and the mix.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
-  constexpr int KS = D / 16, CT = D / 32;
+  constexpr int KS = D / 16;
   constexpr int SR = D + 8;                        // padded LDS row of S_c^T (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Sc[D * SR];
+  __shared__ __attribute__((aligned(16))) uint16_t Sc[32 * SR];
   __shared__ float zc[D];
-  __shared__ float wgt[kMaxDecodeParts][kBlock];         // per part and row: exp2(m_p - M) / L
+  __shared__ float wgt[kMaxDecodeParts][kBlock];   // per part and row: exp2(m_p - M) / L
   const int bq = blockIdx.x;                       // bh * nbq + iq
+  const int ct = blockIdx.y;
   const int bh = bq / a.nbq, iq = bq % a.nbq;
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int t = threadIdx.x, wv = t >> 6, h = (t & 63) >> 5, l32 = t & 31;
   const size_t p0 = (size_t)bq * a.nsplit;
   const bool empty_c = a.topk >= a.nbk;            // every block selected: no complement
 
-  // S_c^T = S_tot^T - sum_p S_sel,p^T (bf16), z_c likewise
-  for (int e4 = t; e4 < D * D / 4; e4 += 256) {
-    f32x4 sv = *reinterpret_cast<const f32x4*>(a.stot + (size_t)bh * D * D + 4 * e4);
+  // rows c = 32 ct .. 32 ct + 31 of S_c^T = S_tot^T - sum_p S_sel,p^T (bf16); z_c
+  for (int e4 = t; e4 < 32 * D / 4; e4 += 256) {
+    const size_t off = (size_t)32 * ct * D + 4 * e4;
+    f32x4 sv = *reinterpret_cast<const f32x4*>(a.stot + (size_t)bh * D * D + off);
     for (int p = 0; p < a.nsplit; ++p) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(a.ps + (p0 + p) * D * D + 4 * e4);
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(a.ps + (p0 + p) * D * D + off);
       sv -= pv;
     }
     if (empty_c) sv = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -362,50 +368,47 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
       wgt[p][t] = __builtin_amdgcn_exp2f(a.pml[((p0 + p) * kBlock + t) * 2] - M) * inv;
   }
   __syncthreads();
+  if (wv >= 2) return;
 
   const float* al = a.alpha + (size_t)(bh % a.H) * D;
-  // output tiles: (channel tile ct, query tile qt); wave w takes tiles w, w + 4, ...
-  for (int tile = wv; tile < 2 * CT; tile += 4) {
-    const int ct = tile % CT, qt = tile / CT;
-    const int qr = 32 * qt + l32;                  // row within the query block
-    const int q = iq * kBlock + qr;
-    const uint16_t* qsrc = a.q + ((size_t)bh * a.nq + (q < a.nq ? q : 0)) * D;
-    f32x16 lin = f32x16{};
-    float d = 0.f;
+  const int qr = 32 * wv + l32;                    // row within the query block
+  const int q = iq * kBlock + qr;
+  const uint16_t* qsrc = a.q + ((size_t)bh * a.nq + (q < a.nq ? q : 0)) * D;
+  f32x16 lin = f32x16{};
+  float d = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 qw = q < a.nq ? *reinterpret_cast<const u32x4*>(qsrc + 16 * s + 8 * h)
-                                : u32x4{0, 0, 0, 0};
-      const u32x4 qr8 = relu_bf16x8(qw);
+  for (int s = 0; s < KS; ++s) {
+    const u32x4 qw = q < a.nq ? *reinterpret_cast<const u32x4*>(qsrc + 16 * s + 8 * h)
+                              : u32x4{0, 0, 0, 0};
+    const u32x4 qr8 = relu_bf16x8(qw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      d += bf16_lo(qr8[e]) * zc[16 * s + 8 * h + 2 * e] + bf16_hi(qr8[e]) * zc[16 * s + 8 * h + 2 * e + 1];
+    const u32x4 af = *reinterpret_cast<const u32x4*>(&Sc[l32 * SR + 16 * s + 8 * h]);
+    lin = mfma_bf16(af, qr8, lin);
+  }
+  d += swap_halves(d);
+  const float inv_den = 1.f / (d + kEps);
+  if (q < a.nq) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int ch = 32 * ct + 8 * g + 4 * h;
+      f32x4 os = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < a.nsplit; ++p) {
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(a.po + ((p0 + p) * kBlock + qr) * D + ch);
+        os += pv * wgt[p][qr];
+      }
+      const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
+      float r[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        d += bf16_lo(qr8[e]) * zc[16 * s + 8 * h + 2 * e] + bf16_hi(qr8[e]) * zc[16 * s + 8 * h + 2 * e + 1];
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&Sc[(32 * ct + l32) * SR + 16 * s + 8 * h]);
-      lin = mfma_bf16(af, qr8, lin);
-    }
-    d += swap_halves(d);
-    const float inv_den = 1.f / (d + kEps);
-    if (q < a.nq) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ch = 32 * ct + 8 * g + 4 * h;
-        f32x4 os = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int p = 0; p < a.nsplit; ++p) {
-          const f32x4 pv = *reinterpret_cast<const f32x4*>(a.po + ((p0 + p) * kBlock + qr) * D + ch);
-          os += pv * wgt[p][qr];
-        }
-        const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          r[e] = alv[e] * os[e] + (1.f - alv[e]) * (lin[4 * g + e] * inv_den);
-        if constexpr (OUT_BF16) {
-          uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-        } else {
-          float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-          *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
-        }
+        r[e] = alv[e] * os[e] + (1.f - alv[e]) * (lin[4 * g + e] * inv_den);
+      if constexpr (OUT_BF16) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+      } else {
+        float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
       }
     }
   }
@@ -437,10 +440,11 @@ hipError_t launch_decode_T(const Plan& s, const DecodePlan& d, const void* q, co
   b.pml = a.pml; b.po = a.po; b.ps = a.ps; b.pz = a.pz;
   b.out = o;
   b.nq = s.nq; b.nbq = s.nbq; b.nbk = s.nbk; b.topk = s.k; b.nsplit = d.nsplit; b.H = s.H;
+  const dim3 grid(s.BH * s.nbq, D / 32);
   if (s.out_bf16)
-    hipLaunchKernelGGL((decode_combine_kernel<D, true>), dim3(s.BH * s.nbq), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((decode_combine_kernel<D, true>), grid, dim3(256), 0, st, b);
   else
-    hipLaunchKernelGGL((decode_combine_kernel<D, false>), dim3(s.BH * s.nbq), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((decode_combine_kernel<D, false>), grid, dim3(256), 0, st, b);
   return hipGetLastError();
 }
 

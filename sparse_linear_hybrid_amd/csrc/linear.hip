@@ -35,12 +35,12 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
   return pack_f16(fminf(fmaxf(a, -m), m), fminf(fmaxf(b, -m), m));
 }
 
-// One pass over the key blocks jbase, jbase+1, ... (kSummaryChunk per workgroup): the
+// One pass over the key blocks jbase, jbase+1, ... (CHUNK per workgroup): the
 // projected pooled K of each block (all its valid tokens) goes to kt + bh*kbh + j*kj, and
 // phi(K)^T V, sum phi(K) over the tokens t0 <= t < nkv go into the chunk's partial totals.
 // BLOCKS: also store each block's S_j^T, z_j and its f16 copy of V (the full forward; then
 // jbase = t0 = 0). Without BLOCKS this is the key/value summary cache update.
-template <typename T, int D, bool BLOCKS>
+template <typename T, int D, bool BLOCKS, int CHUNK>
 __global__ __launch_bounds__(256) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
@@ -55,11 +55,11 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LS];
   __shared__ double pool_lds[RPP * D];
-  __shared__ double means[kSummaryChunk][D];
+  __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
-  const int j0 = jbase + chunk * kSummaryChunk, j1 = min(j0 + kSummaryChunk, nbk);
+  const int j0 = jbase + chunk * CHUNK, j1 = min(j0 + CHUNK, nbk);
   const T* kb = k + (size_t)bh * nkv * D;
   const T* vb = v + (size_t)bh * nkv * D;
   const int mt = (NT == 4) ? w : (w >> 1);   // this wave's 32-row tile of S_j (rows r)
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
     if (t < D) {
       double sm = 0.0;
       for (int rr = 0; rr < RPP; ++rr) sm += pool_lds[rr * D + t];
-      means[j - j0][t] = sm / (double)nrows;
+      means[(j - j0) % kSummaryChunk][t] = sm / (double)nrows;
     }
     // S_j[r][c] = sum_m relu(K[m][r]) V[m][c]: M = r, N = c, reduction over the 64 keys;
     // z_j[r] = sum_m relu(K[m][r]) from the same A fragments.
@@ -181,13 +181,18 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
       }
     }
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
-  }
-  // projected pooled K for the router: k~ = mean @ P_k (float64)
-  for (int b = t / D; b < j1 - j0; b += 256 / D) {
-    const int c = t % D;
-    double acc = 0.0;
-    for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)Pk[r * D + c], acc);
-    kt[(size_t)bh * kbh + (size_t)(j0 + b) * kj + c] = acc;
+    // projected pooled K of each finished group of kSummaryChunk blocks: k~ = mean @ P_k
+    // (float64; means are visible after the barrier above)
+    if ((j - j0) % kSummaryChunk == kSummaryChunk - 1 || j + 1 == j1) {
+      const int g0 = j - (j - j0) % kSummaryChunk;
+      for (int b = t / D; b <= j - g0; b += 256 / D) {
+        const int c = t % D;
+        double acc = 0.0;
+        for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)Pk[r * D + c], acc);
+        kt[(size_t)bh * kbh + (size_t)(g0 + b) * kj + c] = acc;
+      }
+      __syncthreads();   // means are rewritten by the next group
+    }
   }
   // chunk partial totals (fp32, layout [c][r])
 #pragma unroll
@@ -513,11 +518,11 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   const dim3 grid(s.nchunk, s.BH);
   const size_t kbh = (size_t)s.nbk * D, kj = D;
   if (s.in_bf16)
-    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
                        spart, zpart, s.nkv, s.nbk, 0, 0);
   else
-    hipLaunchKernelGGL((kv_summary_kernel<float, D, true>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
                        zpart, s.nkv, s.nbk, 0, 0);
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
@@ -537,7 +542,7 @@ static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const v
   float* spart = reinterpret_cast<float*>(ws);
   float* zpart = reinterpret_cast<float*>(ws + cache_update_zpart_offset(s, n_done));
   const dim3 grid(nchunk, s.BH);
-  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false>), grid, dim3(256), 0, st,
+  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false, kCacheChunk>), grid, dim3(256), 0, st,
                      (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
                      (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
                      jbase, n_done);

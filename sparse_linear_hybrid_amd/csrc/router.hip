@@ -199,6 +199,41 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
   }
 }
 
+// Scores for few query blocks (nbq <= kFewRows): one workgroup per 64 key blocks of a head;
+// four threads share a key block (32 channels each, contiguous 256-byte loads), the query
+// rows sit in LDS, and the four partial dot products are added with lane exchanges.
+constexpr int kFewRows = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void score_few_kernel(const double* __restrict__ qt,
+                                                        const double* __restrict__ kt,
+                                                        double* __restrict__ scores, int nbq,
+                                                        int nbk, size_t kbh, size_t kj) {
+  constexpr int CPT = D / 4;               // channels per thread
+  __shared__ double qs[kFewRows][D];
+  const int bh = blockIdx.y;
+  const int t = threadIdx.x, c4 = t & 3;
+  const int j = blockIdx.x * 64 + (t >> 2);
+  for (int e = t; e < nbq * D; e += 256) qs[e / D][e % D] = qt[((size_t)bh * nbq) * D + e];
+  double kv[CPT];
+  const double* src = kt + (size_t)bh * kbh + (size_t)(j < nbk ? j : 0) * kj + CPT * c4;
+#pragma unroll
+  for (int u = 0; u < CPT; u += 2) {
+    const double2 w = *reinterpret_cast<const double2*>(src + u);
+    kv[u] = w.x;
+    kv[u + 1] = w.y;
+  }
+  __syncthreads();
+  for (int i = 0; i < nbq; ++i) {
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) acc = fma(qs[i][CPT * c4 + u], kv[u], acc);
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (c4 == 0 && j < nbk) scores[((size_t)bh * nbq + i) * nbk + j] = acc;
+  }
+}
+
 // ----------------------------------------------------------------------------- top-k
 // Order-preserving 64-bit key of a float64 score: larger score -> larger key. -0 is
 // folded into +0 (they compare equal), NaN ranks below everything.
@@ -314,8 +349,12 @@ template <int D>
 static void launch_select(const Plan& s, const double* qt, const double* kt, size_t kbh,
                           size_t kj, double* sc, int32_t* idx, hipStream_t st) {
   const int rq = s.BH * s.nbq;
-  hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
-                     dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk, kbh, kj);
+  if (s.nbq <= kFewRows)
+    hipLaunchKernelGGL((score_few_kernel<D>), dim3((s.nbk + 63) / 64, s.BH), dim3(256), 0, st, qt,
+                       kt, sc, s.nbq, s.nbk, kbh, kj);
+  else
+    hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
+                       dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk, kbh, kj);
   if (s.k > 0) {
     const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
     hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, rq, s.nbk, s.k);
