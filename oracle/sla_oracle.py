@@ -16,6 +16,9 @@ What is computed (per batch b and head h, independently):
 * Linear branch (SALAD page, section 2 "Ramos Paralelos": kernel feature map such as
   ReLU, linear cost; SPLA page, section 2.2: the linear term covers exactly the blocks the
   sparse part did not select).
+* Training-free router (SPLA page, section 2.1), selectable instead of the learnable one:
+  the block score is the second-order Taylor estimate of the block's attention mass
+  around its mean key with a diagonal covariance (``taylor_scores``).
 
 Readings taken where the pages are silent (each listed in the design notes):
   block b for queries and keys; pool over valid tokens only; project after pooling with
@@ -116,6 +119,41 @@ def route_head(q: np.ndarray, k: np.ndarray, proj_q: np.ndarray, proj_k: np.ndar
     return Route(idx, s, gaps, gaps < 1e-12 * scale)
 
 
+# ----------------------------------------------------------------------------- Taylor router
+def block_variances(x: np.ndarray, block: int) -> np.ndarray:
+    """Per block and channel, the population variance of x over the block's valid tokens
+    (the diagonal of the block's key covariance). x: [N, d] -> [ceil(N/b), d]."""
+    n = x.shape[0]
+    out = []
+    for j in range(n_blocks(n, block)):
+        xb = x[block_slice(j, n, block)]
+        dev = xb - xb.mean(axis=0)
+        out.append((dev * dev).mean(axis=0))
+    return np.stack(out)
+
+
+def taylor_scores(q_bar: np.ndarray, k_bar: np.ndarray, k_var: np.ndarray) -> np.ndarray:
+    """Training-free block score (SPLA page, section 2.1): the expected exponential
+    attention score of a query over a block's keys, expanded to second order around the
+    block mean with the covariance taken diagonal, exp(tau q.k_bar)(1 + tau^2 q^T diag(var)
+    q / 2), with the attention scale tau = 1/sqrt(d). Returned as its logarithm,
+    tau q.k_bar + log1p(tau^2 (q*q).var / 2), which ranks the blocks identically and does not
+    overflow. q_bar: [Nq, d] (pooled queries, no projection); k_bar, k_var: [Nk, d]."""
+    d = q_bar.shape[1]
+    tau = 1.0 / math.sqrt(d)
+    return tau * (q_bar @ k_bar.T) + np.log1p(0.5 * tau * tau * ((q_bar * q_bar) @ k_var.T))
+
+
+def route_head_taylor(q: np.ndarray, k: np.ndarray, block: int, top_k: int) -> Route:
+    """Training-free router of one (b, h): pool Q and K (means), block variances of K,
+    Taylor score, top-k with the same tie rule and output order as route_head."""
+    s = taylor_scores(pool_blocks(q, block), pool_blocks(k, block), block_variances(k, block))
+    idx = select_topk(s, top_k)
+    gaps = boundary_gaps(s, top_k)
+    scale = np.abs(s).max(axis=1) if s.size else np.zeros(s.shape[0])
+    return Route(idx, s, gaps, gaps < 1e-12 * scale)
+
+
 def selection_mask(idx: np.ndarray, nbk: int) -> np.ndarray:
     """0/1 matrix M[i, j] = 1 iff key block j is routed to query block i."""
     m = np.zeros((idx.shape[0], nbk), dtype=np.float64)
@@ -191,15 +229,19 @@ class HeadResult:
 
 
 def forward_head(q, k, v, proj_q, proj_k, alpha_h, block: int, top_k: int,
-                 rows: Optional[np.ndarray] = None) -> HeadResult:
+                 rows: Optional[np.ndarray] = None, router: str = "learnable") -> HeadResult:
     """SLA2 forward of one (b, h).
 
     ``rows``: optional query-token indices to evaluate (the router always runs in full);
-    unevaluated rows of the returned arrays are NaN.
+    unevaluated rows of the returned arrays are NaN. ``router``: "learnable" (SLA2 page,
+    section 2.B) or "taylor" (SPLA page, section 2.1; the projections are not used).
     """
     nq, d = q.shape
     nkv = k.shape[0]
-    r = route_head(q, k, proj_q, proj_k, block, top_k)
+    if router == "taylor":
+        r = route_head_taylor(q, k, block, top_k)
+    else:
+        r = route_head(q, k, proj_q, proj_k, block, top_k)
     nbk = n_blocks(nkv, block)
     M = selection_mask(r.idx, nbk)
     S, z = block_summaries(k, v, block)
@@ -229,7 +271,7 @@ def route(inputs) -> np.ndarray:
     return out
 
 
-def route_full(inputs):
+def route_full(inputs, router: str = "learnable"):
     """Router results for every (b, h) as a nested list of Route objects."""
     p = inputs.problem
     pq = inputs.proj_q.astype(np.float64)
@@ -240,7 +282,10 @@ def route_full(inputs):
         for h in range(p.heads):
             q = _head(inputs, "q", b, h)
             k = _head(inputs, "k", b, h)
-            row.append(route_head(q, k, pq, pk, p.block, p.top_k))
+            if router == "taylor":
+                row.append(route_head_taylor(q, k, p.block, p.top_k))
+            else:
+                row.append(route_head(q, k, pq, pk, p.block, p.top_k))
         res.append(row)
     return res
 
@@ -253,11 +298,12 @@ def _head(inputs, name, b, h) -> np.ndarray:
 
 
 def forward(inputs, heads: Optional[Sequence[tuple]] = None,
-            rows: Optional[np.ndarray] = None):
+            rows: Optional[np.ndarray] = None, router: str = "learnable"):
     """SLA2 forward for all (or selected) (b, h) pairs.
 
     Returns (out [B, H, Nq, d] float64 with NaN where not evaluated, idx [B, H, Nbq, k]).
-    ``heads``: optional list of (b, h) pairs to evaluate; ``rows``: optional query rows.
+    ``heads``: optional list of (b, h) pairs to evaluate; ``rows``: optional query rows;
+    ``router``: "learnable" or "taylor".
     """
     p = inputs.problem
     pq = inputs.proj_q.astype(np.float64)
@@ -268,7 +314,8 @@ def forward(inputs, heads: Optional[Sequence[tuple]] = None,
     pairs = heads if heads is not None else [(b, h) for b in range(p.batch) for h in range(p.heads)]
     for b, h in pairs:
         r = forward_head(_head(inputs, "q", b, h), _head(inputs, "k", b, h),
-                         _head(inputs, "v", b, h), pq, pk, al[h], p.block, p.top_k, rows)
+                         _head(inputs, "v", b, h), pq, pk, al[h], p.block, p.top_k, rows,
+                         router)
         out[b, h] = r.out
         idx[b, h] = r.route.idx
     return out, idx
