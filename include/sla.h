@@ -98,6 +98,24 @@ sla_status sla_forward_fp8(const sla_problem* p, const void* q, const void* k, c
                            void* o, int32_t* block_idx,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Training-free router (SPLA page, section 2.1: block selection from a second-order Taylor
+ * expansion of the attention objective around the block mean, covariance taken diagonal).
+ * Query block i and key block j score
+ *     tau * (qbar_i . kbar_j) + log1p(tau^2 / 2 * sum_c qbar_ic^2 var_jc),   tau = 1/sqrt(d),
+ * the logarithm of exp(tau qbar.kbar)(1 + tau^2 qbar^T diag(var) qbar / 2), with qbar, kbar
+ * the block means over valid tokens and var the per-channel population variance of the key
+ * block (all float64); no projections. Top-k, tie rule and output order as sla_route.
+ * Same workspace as sla_route. */
+sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,
+                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* sla_forward with the training-free router instead of the learnable one (no proj_q, proj_k).
+ * Same workspace as sla_forward (fp8 = 0). */
+sla_status sla_forward_taylor(const sla_problem* p, const void* q, const void* k, const void* v,
+                              const float* alpha, void* o, int32_t* block_idx, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Stages of a forward call, in launch order, for sla_forward_profiled. */
 enum {
   SLA_STAGE_KV_SUMMARY = 0,  /* per-block phi(K)^T V, sum phi(K), pooled K, totals      */

@@ -151,7 +151,7 @@ struct Plan {
   int B, H, BH, nq, nkv, D, nbq, nbk, k, nchunk;
   bool in_bf16, out_bf16;
   // byte offsets into the workspace
-  size_t qt, kt, scores, idx;                    // router
+  size_t qt, kt, scores, idx, kvar;              // router (kvar: training-free router)
   size_t v16, sblk, zblk, spart, zpart, stot, ztot, sc, zc;   // linear branch
   size_t q8, k8, v8, sq8, sk8, sv8;             // fp8 sparse branch
   size_t total_route, total_fwd, total_fp8;
@@ -176,6 +176,7 @@ inline Plan make_plan(const sla_problem& p) {
   s.kt = take(BH * nbk * D * 8);
   s.scores = take(BH * nbq * nbk * 8);
   s.idx = take(BH * nbq * (size_t)(s.k > 0 ? s.k : 1) * 4);
+  s.kvar = take(BH * nbk * D * 8);
   s.total_route = off;
   s.v16 = take(BH * nbk * kBlock * D * 2);
   s.sblk = take(BH * nbk * D * D * 2);

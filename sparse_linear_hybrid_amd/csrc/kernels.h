@@ -29,6 +29,11 @@ hipError_t launch_quant(const Plan& s, const void* q, const void* k, const void*
 hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
                              const float* alpha, void* o, char* ws, hipStream_t st);
 
+// Training-free router (SPLA page, section 2.1): block means of Q and K, variances of K,
+// second-order Taylor scores, top-k -> idx.
+hipError_t launch_route_taylor(const Plan& s, const void* q, const void* k, int32_t* idx,
+                               char* ws, hipStream_t st);
+
 // Summary cache: bring k~, S_tot, z_tot from the first n_done tokens to s.nkv tokens.
 hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,
                                   int n_done, char* cache, char* ws, hipStream_t st);

@@ -39,7 +39,8 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // projected pooled K of each block (all its valid tokens) goes to kt + bh*kbh + j*kj, and
 // phi(K)^T V, sum phi(K) over the tokens t0 <= t < nkv go into the chunk's partial totals.
 // BLOCKS: also store each block's S_j^T, z_j and its f16 copy of V (the full forward; then
-// jbase = t0 = 0). Without BLOCKS this is the key/value summary cache update.
+// jbase = t0 = 0). Without BLOCKS this is the key/value summary cache update. Pk = nullptr
+// (the training-free router) skips k~.
 template <typename T, int D, bool BLOCKS, int CHUNK>
 __global__ __launch_bounds__(256) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
     // projected pooled K of each finished group of kSummaryChunk blocks: k~ = mean @ P_k
     // (float64; means are visible after the barrier above)
-    if ((j - j0) % kSummaryChunk == kSummaryChunk - 1 || j + 1 == j1) {
+    if (Pk != nullptr && ((j - j0) % kSummaryChunk == kSummaryChunk - 1 || j + 1 == j1)) {
       const int g0 = j - (j - j0) % kSummaryChunk;
       for (int b = t / D; b <= j - g0; b += 256 / D) {
         const int c = t % D;

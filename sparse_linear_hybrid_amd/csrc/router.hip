@@ -126,33 +126,149 @@ __global__ __launch_bounds__(256) void pool_project_kernel(const T* __restrict__
   }
 }
 
+// Block means and (optionally) per-channel population variances of G = 4 consecutive blocks
+// of one (batch, head), float64, two passes over the register-held tokens (the training-free
+// router's block statistics, SPLA page, section 2.1). Only valid tokens count.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_stats_kernel(const T* __restrict__ x,
+                                                         double* __restrict__ mean_out,
+                                                         double* __restrict__ var_out, int n,
+                                                         int nb) {
+  constexpr int TPR = D / 8, RPP = 256 / TPR, LPB = kBlock / RPP, G = 4;
+  __shared__ double part[4][G][D];
+  __shared__ double mean[G][D];
+  const int j0 = blockIdx.x * G, bh = blockIdx.y;
+  const int nblk = min(G, nb - j0);
+  const T* xb = x + (size_t)bh * n * D;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  const int cg = t % TPR, r = t / TPR;
+  float xv[G][LPB][8];
+  bool ok[G][LPB];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int u = 0; u < LPB; ++u) {
+      const int row = (j0 + g) * kBlock + r + RPP * u;
+      ok[g][u] = g < nblk && row < n;
+      const size_t off = (size_t)(ok[g][u] ? row : 0) * D + cg * 8;
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 wv = ok[g][u] ? *reinterpret_cast<const u32x4*>(xb + off) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[g][u][2 * e] = bf16_lo(wv[e]);
+          xv[g][u][2 * e + 1] = bf16_hi(wv[e]);
+        }
+      } else {
+        const f32x4 a = ok[g][u] ? *reinterpret_cast<const f32x4*>(xb + off) : f32x4{0, 0, 0, 0};
+        const f32x4 b = ok[g][u] ? *reinterpret_cast<const f32x4*>(xb + off + 4) : f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[g][u][e] = a[e];
+          xv[g][u][4 + e] = b[e];
+        }
+      }
+    }
+  auto reduce_rows = [&](double (&acc)[G][8]) {   // sum over all rows of the workgroup -> part
+#pragma unroll
+    for (int o = TPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], o, 64);
+    if (lane < TPR) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[w][g][cg * 8 + e] = acc[g][e];
+    }
+    __syncthreads();
+  };
+  double acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double sm = 0.0;
+#pragma unroll
+      for (int u = 0; u < LPB; ++u) sm += ok[g][u] ? (double)xv[g][u][e] : 0.0;
+      acc[g][e] = sm;
+    }
+  reduce_rows(acc);
+  for (int e = t; e < G * D; e += 256) {
+    const int g = e / D, c = e % D;
+    if (g < nblk) {
+      const int nrows = min(kBlock, n - (j0 + g) * kBlock);
+      const double m = (part[0][g][c] + part[1][g][c] + part[2][g][c] + part[3][g][c]) /
+                       (double)nrows;
+      mean[g][c] = m;
+      mean_out[((size_t)bh * nb + j0 + g) * D + c] = m;
+    }
+  }
+  if (var_out == nullptr) return;
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double m = g < nblk ? mean[g][cg * 8 + e] : 0.0;
+      double sq = 0.0;
+#pragma unroll
+      for (int u = 0; u < LPB; ++u) {
+        const double dv = (double)xv[g][u][e] - m;
+        sq += ok[g][u] ? dv * dv : 0.0;
+      }
+      acc[g][e] = sq;
+    }
+  reduce_rows(acc);
+  for (int e = t; e < G * D; e += 256) {
+    const int g = e / D, c = e % D;
+    if (g < nblk) {
+      const int nrows = min(kBlock, n - (j0 + g) * kBlock);
+      var_out[((size_t)bh * nb + j0 + g) * D + c] =
+          (part[0][g][c] + part[1][g][c] + part[2][g][c] + part[3][g][c]) / (double)nrows;
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------- scores
 // scores[bh][i][j] = sum_c qt[bh][i][c] * kt[bh][j][c]; float64, 64x64 output tile per
 // 256-thread workgroup, 4x4 outputs per thread, channel chunks of 32 staged in LDS.
-template <int D>
 // k~ of key block j of (batch, head) bh is at kt + bh * kbh + j * kj.
+// TAYLOR (training-free router, SPLA page, section 2.1): qt holds the block means of Q, kt
+// those of K and kv the variances of K (same strides); the score is
+// tau q.k + log1p(tau^2 (q*q).var / 2) with tau = 1/sqrt(d).
+template <int D, bool TAYLOR>
 __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ qt,
                                                     const double* __restrict__ kt,
+                                                    const double* __restrict__ kv,
                                                     double* __restrict__ scores, int nbq, int nbk,
                                                     size_t kbh, size_t kj) {
   constexpr int T = 64, C = 32;
   __shared__ double As[C][T + 1];
   __shared__ double Bs[C][T + 1];
+  __shared__ double Vs[TAYLOR ? C : 1][TAYLOR ? T + 1 : 1];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
   const double* qb = qt + (size_t)bh * nbq * D;
   const double* kb = kt + (size_t)bh * kbh;
+  const double* vb = TAYLOR ? kv + (size_t)bh * kbh : nullptr;
   const int t = threadIdx.x;
   const int ty = t / 16, tx = t % 16;
-  double acc[4][4];
+  double acc[4][4], acc2[TAYLOR ? 4 : 1][TAYLOR ? 4 : 1];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+  if constexpr (TAYLOR) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc2[a][b] = 0.0;
+  }
   // 64 rows x 32 channels per operand and chunk = 2048 values, 8 per thread; the next
   // chunk is fetched into registers while the current one is multiplied
   constexpr int PER = T * C / 256;
-  double ra[PER], rb[PER];
+  double ra[PER], rb[PER], rv[TAYLOR ? PER : 1];
   auto fetch = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -160,6 +276,7 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
       const int gi = i0 + r, gj = j0 + r;
       ra[u] = gi < nbq ? qb[(size_t)gi * D + c0 + cc] : 0.0;
       rb[u] = gj < nbk ? kb[(size_t)gj * kj + c0 + cc] : 0.0;
+      if constexpr (TAYLOR) rv[u] = gj < nbk ? vb[(size_t)gj * kj + c0 + cc] : 0.0;
     }
   };
   fetch(0);
@@ -169,6 +286,7 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
       const int e = t + 256 * u, r = e / C, cc = e % C;
       As[cc][r] = ra[u];
       Bs[cc][r] = rb[u];
+      if constexpr (TAYLOR) Vs[cc][r] = rv[u];
     }
     __syncthreads();
     if (c0 + C < D) fetch(c0 + C);
@@ -184,9 +302,19 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int w = 0; w < 4; ++w) acc[u][w] = fma(a[u], b[w], acc[u][w]);
+      if constexpr (TAYLOR) {
+        double vv[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) vv[w] = Vs[cc][tx + 16 * w];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc2[u][w] = fma(a[u] * a[u], vv[w], acc2[u][w]);
+      }
     }
     __syncthreads();
   }
+  const double tau = 1.0 / sqrt((double)D);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int gi = i0 + ty + 16 * u;
@@ -194,7 +322,9 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int gj = j0 + tx + 16 * w;
-      if (gj < nbk) scores[((size_t)bh * nbq + gi) * nbk + gj] = acc[u][w];
+      double sc = acc[u][w];
+      if constexpr (TAYLOR) sc = tau * acc[u][w] + log1p(0.5 * tau * tau * acc2[u][w]);
+      if (gj < nbk) scores[((size_t)bh * nbq + gi) * nbk + gj] = sc;
     }
   }
 }
@@ -204,9 +334,10 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
 // rows sit in LDS, and the four partial dot products are added with lane exchanges.
 constexpr int kFewRows = 8;
 
-template <int D>
+template <int D, bool TAYLOR>
 __global__ __launch_bounds__(256) void score_few_kernel(const double* __restrict__ qt,
                                                         const double* __restrict__ kt,
+                                                        const double* __restrict__ kv,
                                                         double* __restrict__ scores, int nbq,
                                                         int nbk, size_t kbh, size_t kj) {
   constexpr int CPT = D / 4;               // channels per thread
@@ -215,21 +346,36 @@ __global__ __launch_bounds__(256) void score_few_kernel(const double* __restrict
   const int t = threadIdx.x, c4 = t & 3;
   const int j = blockIdx.x * 64 + (t >> 2);
   for (int e = t; e < nbq * D; e += 256) qs[e / D][e % D] = qt[((size_t)bh * nbq) * D + e];
-  double kv[CPT];
-  const double* src = kt + (size_t)bh * kbh + (size_t)(j < nbk ? j : 0) * kj + CPT * c4;
+  double kvals[CPT], vvals[TAYLOR ? CPT : 1];
+  const size_t roff = (size_t)bh * kbh + (size_t)(j < nbk ? j : 0) * kj + CPT * c4;
 #pragma unroll
   for (int u = 0; u < CPT; u += 2) {
-    const double2 w = *reinterpret_cast<const double2*>(src + u);
-    kv[u] = w.x;
-    kv[u + 1] = w.y;
+    const double2 w = *reinterpret_cast<const double2*>(kt + roff + u);
+    kvals[u] = w.x;
+    kvals[u + 1] = w.y;
+    if constexpr (TAYLOR) {
+      const double2 z = *reinterpret_cast<const double2*>(kv + roff + u);
+      vvals[u] = z.x;
+      vvals[u + 1] = z.y;
+    }
   }
   __syncthreads();
+  const double tau = 1.0 / sqrt((double)D);
   for (int i = 0; i < nbq; ++i) {
-    double acc = 0.0;
+    double acc = 0.0, acc2 = 0.0;
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) acc = fma(qs[i][CPT * c4 + u], kv[u], acc);
+    for (int u = 0; u < CPT; ++u) {
+      const double qv = qs[i][CPT * c4 + u];
+      acc = fma(qv, kvals[u], acc);
+      if constexpr (TAYLOR) acc2 = fma(qv * qv, vvals[u], acc2);
+    }
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
+    if constexpr (TAYLOR) {
+      acc2 += __shfl_xor(acc2, 1, 64);
+      acc2 += __shfl_xor(acc2, 2, 64);
+      acc = tau * acc + log1p(0.5 * tau * tau * acc2);
+    }
     if (c4 == 0 && j < nbk) scores[((size_t)bh * nbq + i) * nbk + j] = acc;
   }
 }
@@ -345,16 +491,27 @@ static void launch_pool_q(const Plan& s, const void* q, const float* pq, double*
                        pq, qt, s.nq, s.nbq);
 }
 
+// kv != nullptr: training-free (Taylor) scores with the key variances kv
 template <int D>
-static void launch_select(const Plan& s, const double* qt, const double* kt, size_t kbh,
-                          size_t kj, double* sc, int32_t* idx, hipStream_t st) {
+static void launch_select(const Plan& s, const double* qt, const double* kt, const double* kv,
+                          size_t kbh, size_t kj, double* sc, int32_t* idx, hipStream_t st) {
   const int rq = s.BH * s.nbq;
-  if (s.nbq <= kFewRows)
-    hipLaunchKernelGGL((score_few_kernel<D>), dim3((s.nbk + 63) / 64, s.BH), dim3(256), 0, st, qt,
-                       kt, sc, s.nbq, s.nbk, kbh, kj);
-  else
-    hipLaunchKernelGGL((score_kernel<D>), dim3((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH),
-                       dim3(256), 0, st, qt, kt, sc, s.nbq, s.nbk, kbh, kj);
+  const dim3 gf((s.nbk + 63) / 64, s.BH), gt((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH);
+  if (s.nbq <= kFewRows) {
+    if (kv)
+      hipLaunchKernelGGL((score_few_kernel<D, true>), gf, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
+                         s.nbk, kbh, kj);
+    else
+      hipLaunchKernelGGL((score_few_kernel<D, false>), gf, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
+                         s.nbk, kbh, kj);
+  } else {
+    if (kv)
+      hipLaunchKernelGGL((score_kernel<D, true>), gt, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
+                         s.nbk, kbh, kj);
+    else
+      hipLaunchKernelGGL((score_kernel<D, false>), gt, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
+                         s.nbk, kbh, kj);
+  }
   if (s.k > 0) {
     const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
     hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, rq, s.nbk, s.k);
@@ -378,8 +535,37 @@ static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, co
       hipLaunchKernelGGL((pool_project_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k,
                          pk, kt, s.nkv, s.nbk);
   }
-  launch_select<D>(s, qt, kt, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
+  launch_select<D>(s, qt, kt, nullptr, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_route_taylor_T(const Plan& s, const void* q, const void* k,
+                                        int32_t* idx, char* ws, hipStream_t st) {
+  double* qt = reinterpret_cast<double*>(ws + s.qt);
+  double* kt = reinterpret_cast<double*>(ws + s.kt);
+  double* kv = reinterpret_cast<double*>(ws + s.kvar);
+  double* sc = reinterpret_cast<double*>(ws + s.scores);
+  const dim3 gq((s.nbq + 3) / 4, s.BH), gk((s.nbk + 3) / 4, s.BH);
+  if (s.in_bf16) {
+    hipLaunchKernelGGL((pool_stats_kernel<uint16_t, D>), gq, dim3(256), 0, st, (const uint16_t*)q,
+                       qt, nullptr, s.nq, s.nbq);
+    hipLaunchKernelGGL((pool_stats_kernel<uint16_t, D>), gk, dim3(256), 0, st, (const uint16_t*)k,
+                       kt, kv, s.nkv, s.nbk);
+  } else {
+    hipLaunchKernelGGL((pool_stats_kernel<float, D>), gq, dim3(256), 0, st, (const float*)q, qt,
+                       nullptr, s.nq, s.nbq);
+    hipLaunchKernelGGL((pool_stats_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k, kt,
+                       kv, s.nkv, s.nbk);
+  }
+  launch_select<D>(s, qt, kt, kv, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_taylor(const Plan& s, const void* q, const void* k, int32_t* idx,
+                               char* ws, hipStream_t st) {
+  if (s.D == 128) return launch_route_taylor_T<128>(s, q, k, idx, ws, st);
+  return launch_route_taylor_T<64>(s, q, k, idx, ws, st);
 }
 
 hipError_t launch_route(const Plan& s, const void* q, const void* k, const float* pq,
@@ -393,10 +579,10 @@ hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, co
                                hipStream_t st) {
   if (s.D == 128) {
     launch_pool_q<128>(s, q, pq, qt, st);
-    launch_select<128>(s, qt, kt, kbh, kj, sc, idx, st);
+    launch_select<128>(s, qt, kt, nullptr, kbh, kj, sc, idx, st);
   } else {
     launch_pool_q<64>(s, q, pq, qt, st);
-    launch_select<64>(s, qt, kt, kbh, kj, sc, idx, st);
+    launch_select<64>(s, qt, kt, nullptr, kbh, kj, sc, idx, st);
   }
   return hipGetLastError();
 }

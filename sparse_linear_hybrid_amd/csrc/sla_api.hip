@@ -34,14 +34,15 @@ sla_status check_ptrs(std::initializer_list<const void*> ps) {
   return SLA_OK;
 }
 
+// taylor: the training-free router (proj_q / proj_k unused and may be NULL)
 sla_status forward_impl(const sla_problem* p, const void* q, const void* k, const void* v,
                         const float* proj_q, const float* proj_k, const float* alpha, void* o,
                         int32_t* block_idx, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool fp8, hipEvent_t* ev) {
+                        hipStream_t stream, bool fp8, hipEvent_t* ev, bool taylor = false) {
   sla_status st = check_problem(p);
   if (st != SLA_OK) return st;
   if (fp8 && p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
-  st = check_ptrs({q, k, v, proj_q, proj_k, alpha, o});
+  st = taylor ? check_ptrs({q, k, v, alpha, o}) : check_ptrs({q, k, v, proj_q, proj_k, alpha, o});
   if (st != SLA_OK) return st;
   if (block_idx && !aligned16(block_idx)) return SLA_ERR_ALIGN;
   const Plan s = make_plan(*p);
@@ -52,11 +53,16 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
   if (mark(2 * SLA_STAGE_KV_SUMMARY) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_kv_summary(s, k, v, proj_k, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  if (launch_kv_summary(s, k, v, taylor ? nullptr : proj_k, ws, stream) != hipSuccess)
+    return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_KV_SUMMARY + 1) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_ROUTE) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream) != hipSuccess)
+  if (taylor) {
+    if (launch_route_taylor(s, q, k, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
+  } else if (launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream) !=
+             hipSuccess) {
     return SLA_ERR_HIP;
+  }
   if (mark(2 * SLA_STAGE_ROUTE + 1) != hipSuccess) return SLA_ERR_HIP;
   if (mark(2 * SLA_STAGE_COMPLEMENT) != hipSuccess) return SLA_ERR_HIP;
   if (launch_complement(s, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
@@ -123,6 +129,28 @@ sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void*
                                 int fp8, hipEvent_t* events) {
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
                       workspace_bytes, stream, fp8 != 0, events);
+}
+
+sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,
+                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  st = check_ptrs({q, k, block_idx});
+  if (st != SLA_OK) return st;
+  const Plan s = make_plan(*p);
+  if (!workspace || workspace_bytes < s.total_route) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  if (launch_route_taylor(s, q, k, block_idx, static_cast<char*>(workspace), stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
+sla_status sla_forward_taylor(const sla_problem* p, const void* q, const void* k, const void* v,
+                              const float* alpha, void* o, int32_t* block_idx, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(p, q, k, v, nullptr, nullptr, alpha, o, block_idx, workspace,
+                      workspace_bytes, stream, false, nullptr, /*taylor=*/true);
 }
 
 sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,

@@ -24,7 +24,8 @@ STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE"
 EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_profiled", "sla_workspace_region", "sla_status_string",
            "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
-           "sla_cached_workspace_size", "sla_forward_cached")
+           "sla_cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
+           "sla_forward_taylor")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
 STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
 
@@ -77,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.sla_cached_workspace_size.restype = sz
     lib.sla_forward_cached.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sla_forward_cached.restype = ctypes.c_int
+    lib.sla_route_taylor.argtypes = [pp, vp, vp, vp, vp, sz, vp]
+    lib.sla_route_taylor.restype = ctypes.c_int
+    lib.sla_forward_taylor.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_forward_taylor.restype = ctypes.c_int
     return lib
 
 
@@ -268,4 +273,40 @@ def sla_forward_cached(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor, 
                                       _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_forward_cached")
+    return out, idx
+
+
+# ----------------------------------------------------------------------------- Taylor router
+def sla_route_taylor(q, k, top_k: int, block: int = 64,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Training-free router: int32 block indices [B, H, ceil(n_q/block), top_k]."""
+    p = make_problem(q, k, top_k, block)
+    ws = _workspace(p, False, q.device, workspace)
+    idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                      device=q.device)
+    st = library().sla_route_taylor(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws),
+                                    ctypes.c_size_t(ws.numel()), _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_route_taylor")
+    return idx
+
+
+def sla_forward_taylor(q, k, v, alpha, top_k: int, block: int = 64,
+                       out_dtype: torch.dtype = torch.float32, return_idx: bool = True,
+                       workspace: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None):
+    """SLA2 forward with the training-free router. Returns (O, block_idx or None)."""
+    p = make_problem(q, k, top_k, block, out_dtype)
+    ws = _workspace(p, False, q.device, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    idx = None
+    if return_idx:
+        idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                          device=q.device)
+    st = library().sla_forward_taylor(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(out), _ptr(idx), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                      _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_forward_taylor")
     return out, idx

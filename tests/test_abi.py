@@ -182,3 +182,23 @@ def test_forward_cached_validation(lib):
     assert fwd(idx=MISALIGNED) == 5
     need = lib.sla_cached_workspace_size(ctypes.byref(p))
     assert need > 0 and fwd(ws_bytes=need - 1) == 6
+
+
+def test_taylor_entry_points_validation(lib):
+    vp = ctypes.c_void_p
+    p = prob()
+    need = lib.sla_workspace_size(ctypes.byref(p), 0)
+    r = lib.sla_route_taylor(ctypes.byref(p), vp(FAKE), vp(FAKE), vp(0), vp(FAKE),
+                             ctypes.c_size_t(need), vp(0))
+    assert r == 1    # block_idx is required
+    r = lib.sla_route_taylor(ctypes.byref(prob(top_k=12)), vp(FAKE), vp(FAKE), vp(FAKE),
+                             vp(FAKE), ctypes.c_size_t(need), vp(0))
+    assert r == 4
+
+    def fwd(prob_=p, q=FAKE, al=FAKE, ws_bytes=need):
+        return lib.sla_forward_taylor(ctypes.byref(prob_), vp(q), vp(FAKE), vp(FAKE), vp(al),
+                                      vp(FAKE), vp(None), vp(FAKE), ctypes.c_size_t(ws_bytes),
+                                      vp(0))
+    assert fwd(q=0) == 1 and fwd(al=0) == 1
+    assert fwd(ws_bytes=need - 1) == 6
+    assert fwd(prob_=prob(head_dim=96)) == 7
