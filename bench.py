@@ -254,7 +254,7 @@ def bench_cached(args, sla, x, q, k, v, pq, pk, al, out):
         "config": {"workload": p.name, "path": "sla_forward_cached", "batch": p.batch,
                    "heads": p.heads, "n_q": p.n_q, "n_kv": p.n_kv, "head_dim": d,
                    "block": p.block, "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
-                   "parallelism": "single GPU"},
+                   "router": args.router, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
                      "kernel": "sla_forward_cached (whole call: route, decode, combine)",
@@ -282,6 +282,8 @@ def main():
     ap.add_argument("--cached", action="store_true",
                     help="time sla_forward_cached against a prebuilt key/value summary cache "
                          "(the decode path); the cache build is timed separately")
+    ap.add_argument("--router", choices=("learnable", "taylor"), default="learnable",
+                    help="taylor: time sla_forward_taylor (training-free second-order router)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     args = ap.parse_args()
@@ -323,10 +325,19 @@ def main():
     if args.cached:
         return bench_cached(args, sla, x, q, k, v, pq, pk, al, out)
     ws = torch.empty(sla.workspace_size(prob, fp8), dtype=torch.uint8, device=dev)
-    fwd_fn = sla.sla_forward_fp8 if fp8 else sla.sla_forward
+    taylor = args.router == "taylor"
+    if taylor and fp8:
+        print("the Taylor router is timed on the bf16 forward only", file=sys.stderr)
+        return 2
 
     def fwd():
-        fwd_fn(q, k, v, pq, pk, al, p.top_k, return_idx=False, workspace=ws, out=out)
+        if taylor:
+            sla.sla_forward_taylor(q, k, v, al, p.top_k, return_idx=False, workspace=ws, out=out)
+        elif fp8:
+            sla.sla_forward_fp8(q, k, v, pq, pk, al, p.top_k, return_idx=False, workspace=ws,
+                                out=out)
+        else:
+            sla.sla_forward(q, k, v, pq, pk, al, p.top_k, return_idx=False, workspace=ws, out=out)
 
     for _ in range(args.warmup):
         fwd()
@@ -355,7 +366,7 @@ def main():
     t0 = time.perf_counter()
     for s in range(K):
         sla.sla_forward_profiled(q, k, v, pq, pk, al, p.top_k, handles[s], fp8=fp8,
-                                 workspace=ws, out=out)
+                                 workspace=ws, out=out, taylor=taylor)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -434,7 +445,7 @@ def main():
                    "n_kv": p.n_kv, "head_dim": p.head_dim, "block": p.block,
                    "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
                    "grid": "x".join(map(str, p.grid)) if p.grid else None,
-                   "parallelism": "single GPU"},
+                   "router": args.router, "parallelism": "single GPU"},
         "effective_tflops": w["dense_flops"] / (ms * 1e-3) / 1e12,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -126,15 +126,23 @@ enum {
   SLA_NUM_STAGES = 5
 };
 
-/* Same as sla_forward (fp8 = 0) or sla_forward_fp8 (fp8 = 1), and additionally records
- * events[2*s] before and events[2*s+1] after stage s on `stream` (caller-created events,
- * 2*SLA_NUM_STAGES of them), so the caller can time each stage with
- * hipEventElapsedTime after synchronising. NULL events: identical to the plain call. */
+/* Forward variants that sla_forward_profiled can run. */
+enum {
+  SLA_PROFILE_FP8 = 1,     /* the sla_forward_fp8 path                                   */
+  SLA_PROFILE_TAYLOR = 2   /* the sla_forward_taylor path (proj_q, proj_k ignored)       */
+};
+
+/* Same as sla_forward (flags = 0), sla_forward_fp8 (flags = SLA_PROFILE_FP8) or
+ * sla_forward_taylor (flags = SLA_PROFILE_TAYLOR), and additionally records events[2*s]
+ * before and events[2*s+1] after stage s on `stream` (caller-created events,
+ * 2*SLA_NUM_STAGES of them), so the caller can time each stage with hipEventElapsedTime
+ * after synchronising. NULL events: identical to the plain call. Any other flags value
+ * (including both bits together) returns SLA_ERR_UNSUPPORTED. */
 sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void* k,
                                 const void* v, const float* proj_q, const float* proj_k,
                                 const float* alpha, void* o, int32_t* block_idx,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                int fp8, hipEvent_t* events);
+                                int flags, hipEvent_t* events);
 
 /* Workspace regions that tests and diagnostics may read back after a call. */
 typedef enum {

@@ -126,9 +126,12 @@ sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void*
                                 const void* v, const float* proj_q, const float* proj_k,
                                 const float* alpha, void* o, int32_t* block_idx,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                int fp8, hipEvent_t* events) {
+                                int flags, hipEvent_t* events) {
+  if (flags != 0 && flags != SLA_PROFILE_FP8 && flags != SLA_PROFILE_TAYLOR)
+    return SLA_ERR_UNSUPPORTED;
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
-                      workspace_bytes, stream, fp8 != 0, events);
+                      workspace_bytes, stream, flags == SLA_PROFILE_FP8, events,
+                      flags == SLA_PROFILE_TAYLOR);
 }
 
 sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,

@@ -28,6 +28,9 @@ EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_taylor")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
 STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
+# flags of sla_forward_profiled
+PROFILE_FP8 = 1
+PROFILE_TAYLOR = 2
 
 
 class SlaError(RuntimeError):
@@ -192,18 +195,24 @@ def sla_forward_fp8(q, k, v, proj_q, proj_k, alpha, top_k: int, block: int = 64,
 def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8: bool = False,
                          block: int = 64, out_dtype: torch.dtype = torch.float32,
                          workspace: Optional[torch.Tensor] = None,
-                         out: Optional[torch.Tensor] = None):
-    """sla_forward / sla_forward_fp8 that also records ``events`` (2 per stage, in the order
-    of STAGES: before, after) on the current stream. ``events``: ctypes array of
-    hipEvent_t handles created by the caller. Returns O."""
+                         out: Optional[torch.Tensor] = None, taylor: bool = False):
+    """sla_forward / sla_forward_fp8 / sla_forward_taylor (``taylor=True``: proj_q and proj_k
+    are ignored) that also records ``events`` (2 per stage, in the order of STAGES: before,
+    after) on the current stream. ``events``: ctypes array of hipEvent_t handles created by
+    the caller. Returns O."""
+    if fp8 and taylor:
+        raise ValueError("the fp8 and Taylor-router variants are separate paths")
     p = make_problem(q, k, top_k, block, out_dtype)
     ws = _workspace(p, fp8, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
-                                   _ptr(proj_k), _ptr(alpha), _ptr(out), None, _ptr(ws),
-                                   ctypes.c_size_t(ws.numel()), _stream(q.device), int(fp8),
-                                   events)
+    flags = PROFILE_FP8 if fp8 else (PROFILE_TAYLOR if taylor else 0)
+    pq = None if taylor else _ptr(proj_q)
+    pk = None if taylor else _ptr(proj_k)
+    st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), pq, pk,
+                                        _ptr(alpha), _ptr(out), None, _ptr(ws),
+                                        ctypes.c_size_t(ws.numel()), _stream(q.device), flags,
+                                        events)
     if st != 0:
         raise SlaError(st, "sla_forward_profiled")
     return out

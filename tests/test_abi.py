@@ -202,3 +202,13 @@ def test_taylor_entry_points_validation(lib):
     assert fwd(q=0) == 1 and fwd(al=0) == 1
     assert fwd(ws_bytes=need - 1) == 6
     assert fwd(prob_=prob(head_dim=96)) == 7
+
+
+@pytest.mark.parametrize("flags", [3, 4, -1])
+def test_profiled_rejects_unknown_flags(lib, flags):
+    vp = ctypes.c_void_p
+    p = prob()
+    need = lib.sla_workspace_size(ctypes.byref(p), 1)
+    r = lib.sla_forward_profiled(ctypes.byref(p), *[vp(FAKE)] * 7, vp(None), vp(FAKE),
+                                 ctypes.c_size_t(need), vp(0), flags, vp(None))
+    assert r == 7

@@ -100,3 +100,20 @@ def test_video95_taylor_full(sla):
     err, rms = max_err_over_rms(np.concatenate(gots), np.concatenate(refs))
     print(f"video95 taylor: rows={rows} near_tie={near} max-abs/rms={err:.3e}")
     assert err <= TOL
+
+
+def test_profiled_taylor_matches_plain(sla):
+    """The stage-timed Taylor forward enqueues the same work as sla_forward_taylor."""
+    import ctypes
+    x = make_custom(1, 2, 640, 1000, 128, 5, dtype="bf16", kind="smooth", seed=71)
+    q, k, v, pq, pk, al = to_device(x)
+    out, _ = sla.sla_forward_taylor(q, k, v, al, 5)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(sla.STAGES))]
+    for e in evs:
+        e.record()                      # torch creates the HIP event on its first record
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    out2 = sla.sla_forward_profiled(q, k, v, None, None, al, 5, handles, taylor=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(len(sla.STAGES)))
