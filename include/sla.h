@@ -72,9 +72,16 @@ typedef struct {
   int32_t out_dtype;  /* sla_dtype of O                                              */
 } sla_problem;
 
-/* Bytes of device workspace a call needs (fp8 = 0 for sla_forward / sla_route, 1 for
- * sla_forward_fp8). Returns 0 if the problem is invalid. */
-size_t sla_workspace_size(const sla_problem* p, int fp8);
+/* Workspace layouts (the `variant` of sla_workspace_size and sla_workspace_region). */
+enum {
+  SLA_VARIANT_FORWARD = 0,  /* sla_forward, sla_route, sla_route_taylor, sla_forward_taylor */
+  SLA_VARIANT_FP8 = 1,      /* sla_forward_fp8                                            */
+  SLA_VARIANT_PISA = 2      /* sla_forward_pisa                                           */
+};
+
+/* Bytes of device workspace a call of that variant needs. Returns 0 if the problem is
+ * invalid or the variant unknown. */
+size_t sla_workspace_size(const sla_problem* p, int variant);
 
 /* Router only (SLA2 page, section 2.B): pool -> project -> score -> top-k.
  * Writes block_idx (required). Pooling, projection and scores are computed in float64
@@ -116,7 +123,24 @@ sla_status sla_forward_taylor(const sla_problem* p, const void* q, const void* k
                               const float* alpha, void* o, int32_t* block_idx, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
-/* Stages of a forward call, in launch order, for sla_forward_profiled. */
+/* Piecewise exact-or-approximate forward (PISA page, "Piecewise Sparse Attention", core
+ * algorithm), routed by the learnable router of sla_forward (same proj_q, proj_k, same
+ * block_idx). Every key block enters one softmax normalisation: the routed blocks exactly,
+ * every other block j through its centroid kbar_j (block mean of the valid keys), value sum
+ * Vsum_j and token count n_j, plus one global first-order matrix
+ * H_bar = mean over all key blocks of H_j = sum_n (k_n - kbar_j)^T v_n. For query row q of
+ * query block i, with a_j = exp(tau q . kbar_j), tau = 1/sqrt(d), and U the blocks not routed
+ * to i:
+ *     N = sum_{routed tokens} e^{tau q.k} v + sum_{j in U} a_j Vsum_j + tau (q H_bar) sum_U a_j
+ *     D = sum_{routed tokens} e^{tau q.k}   + sum_{j in U} a_j n_j,          O = N / D.
+ * There is no alpha and no separate linear branch. Workspace: SLA_VARIANT_PISA. */
+sla_status sla_forward_pisa(const sla_problem* p, const void* q, const void* k, const void* v,
+                            const float* proj_q, const float* proj_k, void* o,
+                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Stages of a forward call, in launch order, for sla_forward_profiled. For the piecewise
+ * forward KV_SUMMARY is its per-block statistics pass and COMPLEMENT its tail kernel. */
 enum {
   SLA_STAGE_KV_SUMMARY = 0,  /* per-block phi(K)^T V, sum phi(K), pooled K, totals      */
   SLA_STAGE_ROUTE = 1,       /* pooled Q, projections, block scores, top-k              */
@@ -129,15 +153,17 @@ enum {
 /* Forward variants that sla_forward_profiled can run. */
 enum {
   SLA_PROFILE_FP8 = 1,     /* the sla_forward_fp8 path                                   */
-  SLA_PROFILE_TAYLOR = 2   /* the sla_forward_taylor path (proj_q, proj_k ignored)       */
+  SLA_PROFILE_TAYLOR = 2,  /* the sla_forward_taylor path (proj_q, proj_k ignored)       */
+  SLA_PROFILE_PISA = 4     /* the sla_forward_pisa path (alpha ignored)                  */
 };
 
-/* Same as sla_forward (flags = 0), sla_forward_fp8 (flags = SLA_PROFILE_FP8) or
- * sla_forward_taylor (flags = SLA_PROFILE_TAYLOR), and additionally records events[2*s]
+/* Same as sla_forward (flags = 0), sla_forward_fp8 (flags = SLA_PROFILE_FP8),
+ * sla_forward_taylor (flags = SLA_PROFILE_TAYLOR) or sla_forward_pisa
+ * (flags = SLA_PROFILE_PISA), and additionally records events[2*s]
  * before and events[2*s+1] after stage s on `stream` (caller-created events,
  * 2*SLA_NUM_STAGES of them), so the caller can time each stage with hipEventElapsedTime
  * after synchronising. NULL events: identical to the plain call. Any other flags value
- * (including both bits together) returns SLA_ERR_UNSUPPORTED. */
+ * (including two bits together) returns SLA_ERR_UNSUPPORTED. */
 sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void* k,
                                 const void* v, const float* proj_q, const float* proj_k,
                                 const float* alpha, void* o, int32_t* block_idx,
@@ -155,12 +181,20 @@ typedef enum {
   SLA_WS_EV = 5,        /* int32 block exponents of V  [B*H][ceil(n_kv/64)]          */
   SLA_WS_SCORES = 6,    /* float64 block scores [B*H][ceil(n_q/64)][ceil(n_kv/64)]   */
   SLA_WS_SC = 7,        /* bf16 S_c^T per query block [B*H][ceil(n_q/64)][d][d]      */
-  SLA_WS_ZC = 8         /* fp32 z_c per query block [B*H][ceil(n_q/64)][d]           */
+  SLA_WS_ZC = 8,        /* fp32 z_c per query block [B*H][ceil(n_q/64)][d]           */
+  /* piecewise forward (SLA_VARIANT_PISA); npad = ceil(n_kv/64) rounded up to a multiple of
+     64; entries past ceil(n_kv/64) are not written                                   */
+  SLA_WS_HBAR = 9,      /* bf16 H_bar^T [B*H][d(value channel)][d(key channel)]      */
+  SLA_WS_CENT_HI = 10,  /* bf16 centroids, rounded  [B*H][npad][d]                   */
+  SLA_WS_CENT_LO = 11,  /* bf16 centroid minus its rounded value [B*H][npad][d]      */
+  SLA_WS_VSUM = 12      /* f16 value sums of the key blocks, [B*H][d][npad]         */
 } sla_ws_region;
 
-/* Byte offset and size of a workspace region for problem p (fp8 selects the sla_forward_fp8
- * layout). Returns SLA_ERR_SHAPE / SLA_ERR_NULL on invalid arguments. Host only. */
-sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,
+/* Byte offset and size of a workspace region for problem p in the layout of `variant`
+ * (fp8 regions need SLA_VARIANT_FP8, piecewise ones SLA_VARIANT_PISA; SC and ZC do not exist
+ * in the piecewise layout). Returns SLA_ERR_SHAPE / SLA_ERR_NULL on invalid arguments. Host
+ * only. */
+sla_status sla_workspace_region(const sla_problem* p, int variant, int region, size_t* offset,
                                 size_t* bytes);
 
 /* ---------------------------------------------------------------- key/value summary cache

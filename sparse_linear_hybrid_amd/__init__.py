@@ -7,10 +7,12 @@ from .sla import (SlaError, Problem, make_problem, workspace_size, sla_route, sl
                   sla_forward_fp8, sla_forward_profiled, library, LIB_PATH, EXPORTS,
                   STAGES, workspace_region, WS_REGIONS, kv_cache_size, sla_kv_cache_update,
                   cached_workspace_size, sla_forward_cached, sla_route_taylor,
-                  sla_forward_taylor)
+                  sla_forward_taylor, sla_forward_pisa, VARIANT_FORWARD, VARIANT_FP8,
+                  VARIANT_PISA)
 
 __all__ = ["SlaError", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
            "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES",
            "workspace_region", "WS_REGIONS", "kv_cache_size", "sla_kv_cache_update",
            "cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
-           "sla_forward_taylor"]
+           "sla_forward_taylor", "sla_forward_pisa", "VARIANT_FORWARD", "VARIANT_FP8",
+           "VARIANT_PISA"]

@@ -155,7 +155,16 @@ struct Plan {
   size_t v16, sblk, zblk, spart, zpart, stot, ztot, sc, zc;   // linear branch
   size_t q8, k8, v8, sq8, sk8, sv8;             // fp8 sparse branch
   size_t total_route, total_fwd, total_fp8;
+  // piecewise (exact-or-approximate) forward: its own layout after the router's buffers
+  int npad;                                     // key blocks rounded up to whole 64-tiles
+  size_t p_spart, p_zpart, p_stot, p_ztot;      // chunk partials and totals of H
+  size_t cent_hi, cent_lo;                      // centroids, bf16 hi + lo [BH][npad][D]
+  size_t vsum;                                  // value sums, f16 [BH][D][npad]
+  size_t hbar;                                  // bf16 H_bar^T [BH][D(c)][D(r)]
+  size_t tail_m, tail_d, tail_a, tail_n;        // tail state per query row
+  size_t total_pisa;
 };
+
 
 constexpr int kSummaryChunk = 8;  // key blocks per partial-total chunk
 
@@ -195,6 +204,24 @@ inline Plan make_plan(const sla_problem& p) {
   s.sk8 = take(BH * nbk * 4);
   s.sv8 = take(BH * nbk * 4);
   s.total_fp8 = off;
+  // piecewise forward: router buffers, f16 V, then its own regions
+  s.npad = (s.nbk + kBlock - 1) / kBlock * kBlock;
+  const size_t npad = s.npad, nqpad = nbq * kBlock;
+  off = s.v16;
+  take(BH * nbk * kBlock * D * 2);               // v16, same offset as the forward's
+  s.p_spart = take(BH * (size_t)s.nchunk * D * D * 4);
+  s.p_zpart = take(BH * (size_t)s.nchunk * D * 4);
+  s.p_stot = take(BH * D * D * 4);
+  s.p_ztot = take(BH * D * 4);
+  s.cent_hi = take(BH * npad * D * 2);
+  s.cent_lo = take(BH * npad * D * 2);
+  s.vsum = take(BH * D * npad * 2);
+  s.hbar = take(BH * D * D * 2);
+  s.tail_m = take(BH * nqpad * 4);
+  s.tail_d = take(BH * nqpad * 4);
+  s.tail_a = take(BH * nqpad * 4);
+  s.tail_n = take(BH * nqpad * D * 4);
+  s.total_pisa = off;
   return s;
 }
 

@@ -48,4 +48,20 @@ hipError_t launch_decode(const Plan& s, const void* q, const void* k, const void
                          const int32_t* idx, const float* alpha, const char* cache, void* o,
                          char* ws, hipStream_t st);
 
+// Piecewise forward (PISA page, core algorithm), part 1: the learnable router's k~, the f16
+// copy of V, per key block its centroid (bf16 hi + lo) and value-sum column, and
+// H_bar^T = (1/nbk) sum_j H_j^T in bf16.
+hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const float* pk,
+                             char* ws, hipStream_t st);
+
+// Piecewise forward, part 2: per query row the zero-order tail over the unrouted blocks'
+// centroids (running max, weighted and plain row sums, numerator).
+hipError_t launch_pisa_tail(const Plan& s, const void* q, const int32_t* idx, char* ws,
+                            hipStream_t st);
+
+// Piecewise forward, part 3: the exact branch, merged with the tail and the first-order
+// correction inside one normalisation.
+hipError_t launch_sparse_pisa(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                              void* o, char* ws, hipStream_t st);
+
 }  // namespace sla

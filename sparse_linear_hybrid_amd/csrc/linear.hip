@@ -41,12 +41,20 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // BLOCKS: also store each block's S_j^T, z_j and its f16 copy of V (the full forward; then
 // jbase = t0 = 0). Without BLOCKS this is the key/value summary cache update. Pk = nullptr
 // (the training-free router) skips k~.
-template <typename T, int D, bool BLOCKS, int CHUNK>
+// PISA (piecewise forward, PISA page, core algorithm; needs BLOCKS): the MFMA product uses
+// the keys centred on their block mean instead of phi(K), so the partial totals add up
+// H_j = sum_n (k_n - k_bar_j)^T v_n; no S_j or z_j is stored; instead each block's centroid
+// (bf16 hi + lo, [BH][npad][D]) and its column of the transposed value-sum table
+// ([BH][D][npad] f16) are written.
+template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
 __global__ __launch_bounds__(256) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
-    float* __restrict__ zpart, int nkv, int nbk, int jbase, int t0) {
+    float* __restrict__ zpart, int nkv, int nbk, int jbase, int t0,
+    uint16_t* __restrict__ cent_hi, uint16_t* __restrict__ cent_lo, uint16_t* __restrict__ vsum,
+    int npad) {
+  static_assert(!PISA || BLOCKS, "the piecewise pass is a full-forward pass");
   constexpr int LS = D + 8;                  // padded LDS row (elements)
   constexpr int TPR = D / 8, RPP = 256 / TPR;
   constexpr int CPT = 64 * TPR / 256;        // 16-byte chunks per thread per tensor
@@ -57,6 +65,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LS];
   __shared__ double pool_lds[RPP * D];
   __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
+  __shared__ double vpool_lds[PISA ? RPP * D : 1];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
@@ -91,9 +100,9 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
   for (int j = j0; j < j1; ++j) {
     const int row0 = j * kBlock;
     const int nrows = min(kBlock, nkv - row0);
-    double pacc[8];
+    double pacc[8], vacc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pacc[e] = 0.0;
+    for (int e = 0; e < 8; ++e) pacc[e] = vacc[e] = 0.0;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = t + 256 * u;
@@ -119,6 +128,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
         pacc[e] += ok ? (double)kf[e] : 0.0;
         kf[e] = ok_sum ? kf[e] : 0.f;
         vf[e] = ok_sum ? vf[e] : 0.f;
+        if constexpr (PISA) vacc[e] += (double)vf[e];
       }
       u32x4 kw, vw;
 #pragma unroll
@@ -139,6 +149,10 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
       const int cg = t % TPR, r = t / TPR;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pool_lds[r * D + cg * 8 + e] = pacc[e];
+      if constexpr (PISA) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vpool_lds[r * D + cg * 8 + e] = vacc[e];
+      }
     }
     if (j + 1 < j1) load_block(j + 1);   // in flight during this block's compute
     __syncthreads();
@@ -146,19 +160,38 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
       double sm = 0.0;
       for (int rr = 0; rr < RPP; ++rr) sm += pool_lds[rr * D + t];
       means[(j - j0) % kSummaryChunk][t] = sm / (double)nrows;
+      if constexpr (PISA) {
+        const double mean = sm / (double)nrows;
+        const float hi = bf16_lo(pack_bf16((float)mean, 0.f));
+        const size_t ci = ((size_t)bh * npad + j) * D + t;
+        cent_hi[ci] = (uint16_t)(pack_bf16(hi, 0.f) & 0xffffu);
+        cent_lo[ci] = (uint16_t)(pack_bf16((float)(mean - (double)hi), 0.f) & 0xffffu);
+        double vs = 0.0;
+        for (int rr = 0; rr < RPP; ++rr) vs += vpool_lds[rr * D + t];
+        vsum[((size_t)bh * D + t) * npad + j] = (uint16_t)(f16_sat_pack((float)vs, 0.f) & 0xffffu);
+      }
     }
+    if constexpr (PISA) __syncthreads();   // block means are read by every wave below
     // S_j[r][c] = sum_m relu(K[m][r]) V[m][c]: M = r, N = c, reduction over the 64 keys;
-    // z_j[r] = sum_m relu(K[m][r]) from the same A fragments.
+    // z_j[r] = sum_m relu(K[m][r]) from the same A fragments. (PISA: K[m][r] - mean_r
+    // instead of relu(K[m][r]); padded keys have V = 0 and contribute nothing.)
     u32x4 af[4];
     float zl = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      af[s4] = relu_bf16x8(frag_tr(Ks, LS, 32 * mt, 16 * s4));
+      if constexpr (PISA) {
+        const float mr = (float)means[(j - j0) % kSummaryChunk][32 * mt + l32];
+        const u32x4 raw = frag_tr(Ks, LS, 32 * mt, 16 * s4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zl += bf16_lo(af[s4][e]) + bf16_hi(af[s4][e]);
+        for (int e = 0; e < 4; ++e) af[s4][e] = pack_bf16(bf16_lo(raw[e]) - mr, bf16_hi(raw[e]) - mr);
+      } else {
+        af[s4] = relu_bf16x8(frag_tr(Ks, LS, 32 * mt, 16 * s4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zl += bf16_lo(af[s4][e]) + bf16_hi(af[s4][e]);
+      }
     }
     zl += swap_halves(zl);
-    if (BLOCKS && ((NT == 4) || (w & 1) == 0) && h == 0) {
+    if (BLOCKS && !PISA && ((NT == 4) || (w & 1) == 0) && h == 0) {
       zblk[((size_t)bh * nbk + j) * D + 32 * mt + l32] = zl;
     }
     zp += zl;
@@ -169,7 +202,7 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) acc = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), acc);
       part[u] += acc;
-      if constexpr (BLOCKS) {
+      if constexpr (BLOCKS && !PISA) {
         // store S_j^T[c][r] (bf16): lane column c = 32 nt + l32, rows r in runs of 4
         const int c = 32 * nt + l32;
         uint16_t* dst = sblk + (((size_t)bh * nbk + j) * D + c) * D;
@@ -217,9 +250,12 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
                                                             const float* __restrict__ zpart,
                                                             float* __restrict__ stot,
                                                             float* __restrict__ ztot, int nchunk,
-                                                            int accumulate) {
+                                                            int accumulate,
+                                                            uint16_t* __restrict__ scaled_bf16,
+                                                            float scale) {
   // chunk partials are added in chunk order (deterministic), onto the previous totals when
-  // accumulating (summary cache update); loads go out 8 at a time
+  // accumulating (summary cache update); loads go out 8 at a time. scaled_bf16 (optional):
+  // also store bf16(scale * total) (the piecewise forward's H_bar^T = H_sum^T / nbk).
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const float* src = spart + (size_t)bh * nchunk * D * D + e;
@@ -234,6 +270,8 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
   }
   for (; c < nchunk; ++c) s += src[(size_t)c * D * D];
   stot[(size_t)bh * D * D + e] = s;
+  if (scaled_bf16 != nullptr)
+    scaled_bf16[(size_t)bh * D * D + e] = (uint16_t)(pack_bf16(s * scale, 0.f) & 0xffffu);
   if (blockIdx.x == 0 && threadIdx.x < D) {
     float z = accumulate ? ztot[(size_t)bh * D + threadIdx.x] : 0.f;
     for (int cc = 0; cc < nchunk; ++cc) z += zpart[((size_t)bh * nchunk + cc) * D + threadIdx.x];
@@ -521,14 +559,41 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   if (s.in_bf16)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
-                       spart, zpart, s.nkv, s.nbk, 0, 0);
+                       spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
   else
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
-                       zpart, s.nkv, s.nbk, 0, 0);
+                       zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
-                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0);
+                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* v, const float* pk,
+                                      char* ws, hipStream_t st) {
+  double* kt = reinterpret_cast<double*>(ws + s.kt);
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + s.v16);
+  float* spart = reinterpret_cast<float*>(ws + s.p_spart);
+  float* zpart = reinterpret_cast<float*>(ws + s.p_zpart);
+  uint16_t* chi = reinterpret_cast<uint16_t*>(ws + s.cent_hi);
+  uint16_t* clo = reinterpret_cast<uint16_t*>(ws + s.cent_lo);
+  uint16_t* vsum = reinterpret_cast<uint16_t*>(ws + s.vsum);
+  const dim3 grid(s.nchunk, s.BH);
+  const size_t kbh = (size_t)s.nbk * D, kj = D;
+  if (s.in_bf16)
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, true>), grid, dim3(256),
+                       0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16,
+                       nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad);
+  else
+    hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk, true>), grid, dim3(256), 0,
+                       st, (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, nullptr,
+                       nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad);
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
+                     zpart, reinterpret_cast<float*>(ws + s.p_stot),
+                     reinterpret_cast<float*>(ws + s.p_ztot), s.nchunk, 0,
+                     reinterpret_cast<uint16_t*>(ws + s.hbar), 1.f / (float)s.nbk);
   return hipGetLastError();
 }
 
@@ -546,10 +611,11 @@ static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const v
   hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false, kCacheChunk>), grid, dim3(256), 0, st,
                      (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
                      (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
-                     jbase, n_done);
+                     jbase, n_done, nullptr, nullptr, nullptr, 0);
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(cache + c.stot),
-                     reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0);
+                     reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
+                     nullptr, 0.f);
   return hipGetLastError();
 }
 
@@ -564,6 +630,12 @@ hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const 
                              char* ws, hipStream_t st) {
   if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st);
   return launch_kv_summary_T<64>(s, k, v, pk, ws, st);
+}
+
+hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const float* pk,
+                             char* ws, hipStream_t st) {
+  if (s.D == 128) return launch_pisa_stats_T<128>(s, k, v, pk, ws, st);
+  return launch_pisa_stats_T<64>(s, k, v, pk, ws, st);
 }
 
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st) {

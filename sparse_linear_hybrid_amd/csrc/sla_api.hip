@@ -34,49 +34,68 @@ sla_status check_ptrs(std::initializer_list<const void*> ps) {
   return SLA_OK;
 }
 
-// taylor: the training-free router (proj_q / proj_k unused and may be NULL)
+// The forward variants: SLA2 (learnable router), its fp8 sparse branch, SLA2 with the
+// training-free router (proj_q / proj_k unused and may be NULL), and the piecewise forward
+// (learnable router; exact routed blocks plus the Taylor tail; alpha unused and may be NULL).
+enum class Fwd { kSla, kFp8, kTaylor, kPisa };
+
 sla_status forward_impl(const sla_problem* p, const void* q, const void* k, const void* v,
                         const float* proj_q, const float* proj_k, const float* alpha, void* o,
                         int32_t* block_idx, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream, bool fp8, hipEvent_t* ev, bool taylor = false) {
+                        hipStream_t stream, Fwd mode, hipEvent_t* ev) {
   sla_status st = check_problem(p);
   if (st != SLA_OK) return st;
-  if (fp8 && p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
-  st = taylor ? check_ptrs({q, k, v, alpha, o}) : check_ptrs({q, k, v, proj_q, proj_k, alpha, o});
+  if (mode == Fwd::kFp8 && p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  switch (mode) {
+    case Fwd::kTaylor: st = check_ptrs({q, k, v, alpha, o}); break;
+    case Fwd::kPisa: st = check_ptrs({q, k, v, proj_q, proj_k, o}); break;
+    default: st = check_ptrs({q, k, v, proj_q, proj_k, alpha, o}); break;
+  }
   if (st != SLA_OK) return st;
   if (block_idx && !aligned16(block_idx)) return SLA_ERR_ALIGN;
   const Plan s = make_plan(*p);
-  const size_t need = fp8 ? s.total_fp8 : s.total_fwd;
+  const size_t need = mode == Fwd::kFp8 ? s.total_fp8 : (mode == Fwd::kPisa ? s.total_pisa
+                                                                            : s.total_fwd);
   if (!workspace || workspace_bytes < need) return SLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SLA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
-  if (mark(2 * SLA_STAGE_KV_SUMMARY) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_kv_summary(s, k, v, taylor ? nullptr : proj_k, ws, stream) != hipSuccess)
-    return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_KV_SUMMARY + 1) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_ROUTE) != hipSuccess) return SLA_ERR_HIP;
-  if (taylor) {
-    if (launch_route_taylor(s, q, k, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
-  } else if (launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream) !=
-             hipSuccess) {
+  auto ok = [](hipError_t e) { return e == hipSuccess; };
+  if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY))) return SLA_ERR_HIP;
+  if (mode == Fwd::kPisa) {
+    if (!ok(launch_pisa_stats(s, k, v, proj_k, ws, stream))) return SLA_ERR_HIP;
+  } else if (!ok(launch_kv_summary(s, k, v, mode == Fwd::kTaylor ? nullptr : proj_k, ws,
+                                   stream))) {
     return SLA_ERR_HIP;
   }
-  if (mark(2 * SLA_STAGE_ROUTE + 1) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_COMPLEMENT) != hipSuccess) return SLA_ERR_HIP;
-  if (launch_complement(s, idx, ws, stream) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_COMPLEMENT + 1) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_QUANT) != hipSuccess) return SLA_ERR_HIP;
-  if (fp8 && launch_quant(s, q, k, v, ws, stream) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_QUANT + 1) != hipSuccess) return SLA_ERR_HIP;
-  if (mark(2 * SLA_STAGE_SPARSE) != hipSuccess) return SLA_ERR_HIP;
-  if (fp8) {
-    if (launch_sparse_fp8(s, q, idx, alpha, o, ws, stream) != hipSuccess) return SLA_ERR_HIP;
-  } else if (launch_sparse(s, q, k, idx, alpha, o, ws, stream) != hipSuccess) {
+  if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY + 1))) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_ROUTE))) return SLA_ERR_HIP;
+  if (mode == Fwd::kTaylor) {
+    if (!ok(launch_route_taylor(s, q, k, idx, ws, stream))) return SLA_ERR_HIP;
+  } else if (!ok(launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream))) {
     return SLA_ERR_HIP;
   }
-  if (mark(2 * SLA_STAGE_SPARSE + 1) != hipSuccess) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_ROUTE + 1))) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_COMPLEMENT))) return SLA_ERR_HIP;
+  if (mode == Fwd::kPisa) {
+    if (!ok(launch_pisa_tail(s, q, idx, ws, stream))) return SLA_ERR_HIP;
+  } else if (!ok(launch_complement(s, idx, ws, stream))) {
+    return SLA_ERR_HIP;
+  }
+  if (!ok(mark(2 * SLA_STAGE_COMPLEMENT + 1))) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_QUANT))) return SLA_ERR_HIP;
+  if (mode == Fwd::kFp8 && !ok(launch_quant(s, q, k, v, ws, stream))) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_QUANT + 1))) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_SPARSE))) return SLA_ERR_HIP;
+  hipError_t e;
+  switch (mode) {
+    case Fwd::kFp8: e = launch_sparse_fp8(s, q, idx, alpha, o, ws, stream); break;
+    case Fwd::kPisa: e = launch_sparse_pisa(s, q, k, idx, o, ws, stream); break;
+    default: e = launch_sparse(s, q, k, idx, alpha, o, ws, stream); break;
+  }
+  if (!ok(e)) return SLA_ERR_HIP;
+  if (!ok(mark(2 * SLA_STAGE_SPARSE + 1))) return SLA_ERR_HIP;
   return SLA_OK;
 }
 
@@ -84,10 +103,15 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
 
 extern "C" {
 
-size_t sla_workspace_size(const sla_problem* p, int fp8) {
+size_t sla_workspace_size(const sla_problem* p, int variant) {
   if (check_problem(p) != SLA_OK) return 0;
   const Plan s = make_plan(*p);
-  return fp8 ? s.total_fp8 : s.total_fwd;
+  switch (variant) {
+    case SLA_VARIANT_FORWARD: return s.total_fwd;
+    case SLA_VARIANT_FP8: return s.total_fp8;
+    case SLA_VARIANT_PISA: return s.total_pisa;
+    default: return 0;
+  }
 }
 
 sla_status sla_route(const sla_problem* p, const void* q, const void* k, const float* proj_q,
@@ -111,7 +135,7 @@ sla_status sla_forward(const sla_problem* p, const void* q, const void* k, const
                        int32_t* block_idx, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
-                      workspace_bytes, stream, false, nullptr);
+                      workspace_bytes, stream, Fwd::kSla, nullptr);
 }
 
 sla_status sla_forward_fp8(const sla_problem* p, const void* q, const void* k, const void* v,
@@ -119,7 +143,7 @@ sla_status sla_forward_fp8(const sla_problem* p, const void* q, const void* k, c
                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
-                      workspace_bytes, stream, true, nullptr);
+                      workspace_bytes, stream, Fwd::kFp8, nullptr);
 }
 
 sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void* k,
@@ -127,11 +151,16 @@ sla_status sla_forward_profiled(const sla_problem* p, const void* q, const void*
                                 const float* alpha, void* o, int32_t* block_idx,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
                                 int flags, hipEvent_t* events) {
-  if (flags != 0 && flags != SLA_PROFILE_FP8 && flags != SLA_PROFILE_TAYLOR)
-    return SLA_ERR_UNSUPPORTED;
+  Fwd mode;
+  switch (flags) {
+    case 0: mode = Fwd::kSla; break;
+    case SLA_PROFILE_FP8: mode = Fwd::kFp8; break;
+    case SLA_PROFILE_TAYLOR: mode = Fwd::kTaylor; break;
+    case SLA_PROFILE_PISA: mode = Fwd::kPisa; break;
+    default: return SLA_ERR_UNSUPPORTED;
+  }
   return forward_impl(p, q, k, v, proj_q, proj_k, alpha, o, block_idx, workspace,
-                      workspace_bytes, stream, flags == SLA_PROFILE_FP8, events,
-                      flags == SLA_PROFILE_TAYLOR);
+                      workspace_bytes, stream, mode, events);
 }
 
 sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,
@@ -153,10 +182,18 @@ sla_status sla_forward_taylor(const sla_problem* p, const void* q, const void* k
                               const float* alpha, void* o, int32_t* block_idx, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
   return forward_impl(p, q, k, v, nullptr, nullptr, alpha, o, block_idx, workspace,
-                      workspace_bytes, stream, false, nullptr, /*taylor=*/true);
+                      workspace_bytes, stream, Fwd::kTaylor, nullptr);
 }
 
-sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_t* offset,
+sla_status sla_forward_pisa(const sla_problem* p, const void* q, const void* k, const void* v,
+                            const float* proj_q, const float* proj_k, void* o,
+                            int32_t* block_idx, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return forward_impl(p, q, k, v, proj_q, proj_k, nullptr, o, block_idx, workspace,
+                      workspace_bytes, stream, Fwd::kPisa, nullptr);
+}
+
+sla_status sla_workspace_region(const sla_problem* p, int variant, int region, size_t* offset,
                                 size_t* bytes) {
   const sla_status st = check_problem(p);
   if (st != SLA_OK) return st;
@@ -173,9 +210,20 @@ sla_status sla_workspace_region(const sla_problem* p, int fp8, int region, size_
     case SLA_WS_SCORES: *offset = s.scores; *bytes = BH * nbq * nbk * 8; break;
     case SLA_WS_SC: *offset = s.sc; *bytes = BH * nbq * D * D * 2; break;
     case SLA_WS_ZC: *offset = s.zc; *bytes = BH * nbq * D * 4; break;
+    case SLA_WS_HBAR: *offset = s.hbar; *bytes = BH * D * D * 2; break;
+    case SLA_WS_CENT_HI: *offset = s.cent_hi; *bytes = BH * (size_t)s.npad * D * 2; break;
+    case SLA_WS_CENT_LO: *offset = s.cent_lo; *bytes = BH * (size_t)s.npad * D * 2; break;
+    case SLA_WS_VSUM: *offset = s.vsum; *bytes = BH * D * (size_t)s.npad * 2; break;
     default: return SLA_ERR_SHAPE;
   }
-  if (region <= SLA_WS_EV && !fp8) return SLA_ERR_SHAPE;
+  const bool fp8_region = region <= SLA_WS_EV;
+  const bool pisa_region = region >= SLA_WS_HBAR;
+  const bool linear_region = region == SLA_WS_SC || region == SLA_WS_ZC;
+  if (variant != SLA_VARIANT_FORWARD && variant != SLA_VARIANT_FP8 && variant != SLA_VARIANT_PISA)
+    return SLA_ERR_SHAPE;
+  if (fp8_region && variant != SLA_VARIANT_FP8) return SLA_ERR_SHAPE;
+  if (pisa_region && variant != SLA_VARIANT_PISA) return SLA_ERR_SHAPE;
+  if (linear_region && variant == SLA_VARIANT_PISA) return SLA_ERR_SHAPE;
   return SLA_OK;
 }
 

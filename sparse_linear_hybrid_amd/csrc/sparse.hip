@@ -164,6 +164,12 @@ struct SparseArgs {
   const int32_t* eq;       // block exponents [BH][nbq]
   const int32_t* ek;       // [BH][nbk]
   const int32_t* ev;       // [BH][nbk]
+  // piecewise epilogue only
+  const uint16_t* hbar;    // bf16 H_bar^T [BH][D(c)][D(r)]
+  const float* tail_m;     // [BH][nbq * 64]: the tail's running max (base-2 scaled units)
+  const float* tail_d;     // its token-count-weighted row sum
+  const float* tail_a;     // its plain row sum
+  const float* tail_n;     // [BH][nbq * 64][D]: its numerator
 };
 
 template <typename T>
@@ -192,7 +198,7 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
   }
 }
 
-template <typename T, int D, int QB, bool OUT_BF16>
+template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false>
 __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
   constexpr bool DMA = !SPLIT;             // bf16 inputs: K/V tiles go global -> LDS directly
@@ -463,6 +469,52 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
 
   // ---------------------------------------------------------------- epilogue
   l += swap_halves(l);
+  if constexpr (PISA) {
+    // Piecewise merge (PISA page, core algorithm): the exact part (o, l in the frame 2^m) and
+    // the tail (N_U, D_U, A_U in the frame 2^m_U) share one normalisation; the first-order
+    // term tau (q H_bar) A_U joins the tail's numerator.
+    const int q = qrow0 + l32;
+    const size_t row = (size_t)bh * a.nbq * kBlock + (q < a.nq ? q : qrow0);
+    const float tm = a.tail_m[row], td = a.tail_d[row], ta = a.tail_a[row];
+    const float mm = fmaxf(m, tm);
+    const float cs = __builtin_amdgcn_exp2f(m - mm), cu = __builtin_amdgcn_exp2f(tm - mm);
+    const float den = l * cs + td * cu;
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float first = ta * cu * (1.f / sqrtf((float)D));
+    const uint16_t* hb = a.hbar + (size_t)bh * D * D;
+    const float* tn = a.tail_n + row * D;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      f32x16 lin = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 af =
+            *reinterpret_cast<const u32x4*>(hb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
+        lin = mfma_bf16(af, qf[s], lin);
+      }
+      if (q < a.nq) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = 32 * c + 8 * g + 4 * h;
+          const f32x4 nu = *reinterpret_cast<const f32x4*>(tn + ch);
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int ix = 4 * g + e;
+            r[e] = (o[c][ix] * cs + nu[e] * cu + lin[ix] * first) * inv;
+          }
+          if constexpr (OUT_BF16) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
+          } else {
+            float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
+            *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
+          }
+        }
+      }
+    }
+    return;
+  }
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
   const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
@@ -754,7 +806,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(Spars
   }
 }
 
-template <typename T, int D, int QB, bool FP8>
+template <typename T, int D, int QB, bool FP8, bool PISA = false>
 hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
   SparseArgs a;
@@ -775,7 +827,17 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
   a.eq = reinterpret_cast<const int32_t*>(ws + s.sq8);
   a.ek = reinterpret_cast<const int32_t*>(ws + s.sk8);
   a.ev = reinterpret_cast<const int32_t*>(ws + s.sv8);
-  if constexpr (FP8) {
+  a.hbar = reinterpret_cast<const uint16_t*>(ws + s.hbar);
+  a.tail_m = reinterpret_cast<const float*>(ws + s.tail_m);
+  a.tail_d = reinterpret_cast<const float*>(ws + s.tail_d);
+  a.tail_a = reinterpret_cast<const float*>(ws + s.tail_a);
+  a.tail_n = reinterpret_cast<const float*>(ws + s.tail_n);
+  if constexpr (PISA) {
+    if (s.out_bf16)
+      hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, true, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
+    else
+      hipLaunchKernelGGL((sparse_attn_kernel<T, D, QB, false, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
+  } else if constexpr (FP8) {
     if (s.out_bf16)
       hipLaunchKernelGGL((sparse_attn_fp8_kernel<D, QB, true>), dim3(a.total), dim3(128 * QB), 0, st, a);
     else
@@ -789,13 +851,13 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
   return hipGetLastError();
 }
 
-template <typename T, int D, bool FP8 = false>
+template <typename T, int D, bool FP8 = false, bool PISA = false>
 hipError_t launch_sparse_D(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
   // Pair neighbouring query blocks when there are enough of them to fill the GPU.
   if (s.nbq >= 2 && (long long)s.BH * s.nbq >= 1024)
-    return launch_sparse_T<T, D, 2, FP8>(s, q, k, idx, alpha, o, ws, st);
-  return launch_sparse_T<T, D, 1, FP8>(s, q, k, idx, alpha, o, ws, st);
+    return launch_sparse_T<T, D, 2, FP8, PISA>(s, q, k, idx, alpha, o, ws, st);
+  return launch_sparse_T<T, D, 1, FP8, PISA>(s, q, k, idx, alpha, o, ws, st);
 }
 
 }  // namespace
@@ -808,6 +870,16 @@ hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int3
   }
   if (s.D == 128) return launch_sparse_D<float, 128>(s, q, k, idx, alpha, o, ws, st);
   return launch_sparse_D<float, 64>(s, q, k, idx, alpha, o, ws, st);
+}
+
+hipError_t launch_sparse_pisa(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                              void* o, char* ws, hipStream_t st) {
+  if (s.in_bf16) {
+    if (s.D == 128) return launch_sparse_D<uint16_t, 128, false, true>(s, q, k, idx, nullptr, o, ws, st);
+    return launch_sparse_D<uint16_t, 64, false, true>(s, q, k, idx, nullptr, o, ws, st);
+  }
+  if (s.D == 128) return launch_sparse_D<float, 128, false, true>(s, q, k, idx, nullptr, o, ws, st);
+  return launch_sparse_D<float, 64, false, true>(s, q, k, idx, nullptr, o, ws, st);
 }
 
 hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,

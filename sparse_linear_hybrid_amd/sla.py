@@ -25,12 +25,16 @@ EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_profiled", "sla_workspace_region", "sla_status_string",
            "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
            "sla_cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
-           "sla_forward_taylor")
-WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8}
+           "sla_forward_taylor", "sla_forward_pisa")
+WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8,
+              "hbar": 9, "cent_hi": 10, "cent_lo": 11, "vsum": 12}
+# workspace layouts (sla_workspace_size / sla_workspace_region)
+VARIANT_FORWARD, VARIANT_FP8, VARIANT_PISA = 0, 1, 2
 STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
 # flags of sla_forward_profiled
 PROFILE_FP8 = 1
 PROFILE_TAYLOR = 2
+PROFILE_PISA = 4
 
 
 class SlaError(RuntimeError):
@@ -58,6 +62,8 @@ def _load() -> ctypes.CDLL:
     lib.sla_workspace_size.restype = sz
     lib.sla_route.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sla_route.restype = ctypes.c_int
+    lib.sla_forward_pisa.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_forward_pisa.restype = ctypes.c_int
     for name in ("sla_forward", "sla_forward_fp8"):
         f = getattr(lib, name)
         f.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -118,8 +124,10 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, top_k: int, block: int = 64,
                    _dtype_code(out_dtype))
 
 
-def workspace_size(p: Problem, fp8: bool = False) -> int:
-    return int(library().sla_workspace_size(ctypes.byref(p), int(fp8)))
+def workspace_size(p: Problem, variant=VARIANT_FORWARD) -> int:
+    """Workspace bytes for a layout: VARIANT_FORWARD (False), VARIANT_FP8 (True) or
+    VARIANT_PISA."""
+    return int(library().sla_workspace_size(ctypes.byref(p), int(variant)))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -134,8 +142,8 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _workspace(p: Problem, fp8: bool, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
-    need = workspace_size(p, fp8)
+def _workspace(p: Problem, variant, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    need = workspace_size(p, variant)
     if need == 0:
         raise SlaError(2, "sla_workspace_size")
     if workspace is None or workspace.numel() < need:
@@ -195,33 +203,36 @@ def sla_forward_fp8(q, k, v, proj_q, proj_k, alpha, top_k: int, block: int = 64,
 def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8: bool = False,
                          block: int = 64, out_dtype: torch.dtype = torch.float32,
                          workspace: Optional[torch.Tensor] = None,
-                         out: Optional[torch.Tensor] = None, taylor: bool = False):
+                         out: Optional[torch.Tensor] = None, taylor: bool = False,
+                         pisa: bool = False):
     """sla_forward / sla_forward_fp8 / sla_forward_taylor (``taylor=True``: proj_q and proj_k
-    are ignored) that also records ``events`` (2 per stage, in the order of STAGES: before,
-    after) on the current stream. ``events``: ctypes array of hipEvent_t handles created by
-    the caller. Returns O."""
-    if fp8 and taylor:
-        raise ValueError("the fp8 and Taylor-router variants are separate paths")
+    are ignored) / sla_forward_pisa (``pisa=True``: alpha is ignored) that also records
+    ``events`` (2 per stage, in the order of STAGES: before, after) on the current stream.
+    ``events``: ctypes array of hipEvent_t handles created by the caller. Returns O."""
+    if int(fp8) + int(taylor) + int(pisa) > 1:
+        raise ValueError("fp8, taylor and pisa select different forward paths")
     p = make_problem(q, k, top_k, block, out_dtype)
-    ws = _workspace(p, fp8, q.device, workspace)
+    variant = VARIANT_FP8 if fp8 else (VARIANT_PISA if pisa else VARIANT_FORWARD)
+    ws = _workspace(p, variant, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    flags = PROFILE_FP8 if fp8 else (PROFILE_TAYLOR if taylor else 0)
+    flags = PROFILE_FP8 if fp8 else (PROFILE_TAYLOR if taylor else (PROFILE_PISA if pisa else 0))
     pq = None if taylor else _ptr(proj_q)
     pk = None if taylor else _ptr(proj_k)
-    st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), pq, pk,
-                                        _ptr(alpha), _ptr(out), None, _ptr(ws),
-                                        ctypes.c_size_t(ws.numel()), _stream(q.device), flags,
-                                        events)
+    al = None if pisa else _ptr(alpha)
+    st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), pq, pk, al,
+                                        _ptr(out), None, _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                        _stream(q.device), flags, events)
     if st != 0:
         raise SlaError(st, "sla_forward_profiled")
     return out
 
 
-def workspace_region(p: Problem, name: str, fp8: bool = False) -> Tuple[int, int]:
-    """(byte offset, byte size) of a named workspace region (see WS_REGIONS)."""
+def workspace_region(p: Problem, name: str, variant=VARIANT_FORWARD) -> Tuple[int, int]:
+    """(byte offset, byte size) of a named workspace region (see WS_REGIONS) in the layout
+    of ``variant`` (False / True select the forward / fp8 layouts)."""
     off, size = ctypes.c_size_t(), ctypes.c_size_t()
-    st = library().sla_workspace_region(ctypes.byref(p), int(fp8), WS_REGIONS[name],
+    st = library().sla_workspace_region(ctypes.byref(p), int(variant), WS_REGIONS[name],
                                         ctypes.byref(off), ctypes.byref(size))
     if st != 0:
         raise SlaError(st, "sla_workspace_region")
@@ -318,4 +329,26 @@ def sla_forward_taylor(q, k, v, alpha, top_k: int, block: int = 64,
                                       _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_forward_taylor")
+    return out, idx
+
+
+def sla_forward_pisa(q, k, v, proj_q, proj_k, top_k: int, block: int = 64,
+                     out_dtype: torch.dtype = torch.float32, return_idx: bool = True,
+                     workspace: Optional[torch.Tensor] = None,
+                     out: Optional[torch.Tensor] = None):
+    """Piecewise exact-or-approximate forward (learnable router; exact routed blocks, Taylor
+    tail for the rest, one normalisation). Returns (O, block_idx or None)."""
+    p = make_problem(q, k, top_k, block, out_dtype)
+    ws = _workspace(p, VARIANT_PISA, q.device, workspace)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    idx = None
+    if return_idx:
+        idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
+                          device=q.device)
+    st = library().sla_forward_pisa(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
+                                    _ptr(proj_k), _ptr(out), _ptr(idx), _ptr(ws),
+                                    ctypes.c_size_t(ws.numel()), _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_forward_pisa")
     return out, idx

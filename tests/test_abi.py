@@ -204,7 +204,7 @@ def test_taylor_entry_points_validation(lib):
     assert fwd(prob_=prob(head_dim=96)) == 7
 
 
-@pytest.mark.parametrize("flags", [3, 4, -1])
+@pytest.mark.parametrize("flags", [3, 5, 6, 8, -1])
 def test_profiled_rejects_unknown_flags(lib, flags):
     vp = ctypes.c_void_p
     p = prob()
@@ -212,3 +212,58 @@ def test_profiled_rejects_unknown_flags(lib, flags):
     r = lib.sla_forward_profiled(ctypes.byref(p), *[vp(FAKE)] * 7, vp(None), vp(FAKE),
                                  ctypes.c_size_t(need), vp(0), flags, vp(None))
     assert r == 7
+
+
+def test_workspace_variants(lib):
+    """Variants 0, 1, 2 have their own sizes; anything else is invalid (size 0)."""
+    p = prob()
+    sizes = [lib.sla_workspace_size(ctypes.byref(p), v) for v in (0, 1, 2)]
+    assert all(s > 0 for s in sizes)
+    assert lib.sla_workspace_size(ctypes.byref(p), 3) == 0
+    assert lib.sla_workspace_size(ctypes.byref(p), -1) == 0
+    text = open(HEADER).read()
+    vals = {m.group(1): int(m.group(2))
+            for m in re.finditer(r"SLA_VARIANT_(\w+)\s*=\s*(\d+)", text)}
+    assert vals == {"FORWARD": sla.VARIANT_FORWARD, "FP8": sla.VARIANT_FP8,
+                    "PISA": sla.VARIANT_PISA}
+
+
+def test_workspace_regions_by_variant(lib):
+    """fp8 regions exist only in the fp8 layout, piecewise regions only in the piecewise one,
+    and the complement regions not in the piecewise one."""
+    p = prob()
+    off, size = ctypes.c_size_t(), ctypes.c_size_t()
+
+    def region(variant, name):
+        return lib.sla_workspace_region(ctypes.byref(p), variant, sla.WS_REGIONS[name],
+                                        ctypes.byref(off), ctypes.byref(size))
+    assert region(1, "q8") == 0 and region(0, "q8") == 2 and region(2, "q8") == 2
+    assert region(2, "hbar") == 0 and region(0, "hbar") == 2 and region(1, "hbar") == 2
+    assert region(0, "sc") == 0 and region(2, "sc") == 2
+    assert region(2, "scores") == 0 and region(5, "scores") == 2
+    total = lib.sla_workspace_size(ctypes.byref(p), 2)
+    for name in ("hbar", "cent_hi", "cent_lo", "vsum"):
+        assert region(2, name) == 0
+        assert off.value % 256 == 0 and off.value + size.value <= total
+    d, BH = p.head_dim, p.batch * p.heads
+    npad = -(-(-(-p.n_kv // 64)) // 64) * 64
+    region(2, "vsum")
+    assert size.value == BH * d * npad * 2
+    region(2, "hbar")
+    assert size.value == BH * d * d * 2
+
+
+def test_pisa_validation(lib):
+    vp = ctypes.c_void_p
+    p = prob()
+    need = lib.sla_workspace_size(ctypes.byref(p), 2)
+
+    def fwd(prob_=p, q=FAKE, pq=FAKE, o=FAKE, ws=FAKE, ws_bytes=need, idx=None):
+        return lib.sla_forward_pisa(ctypes.byref(prob_), vp(q), vp(FAKE), vp(FAKE), vp(pq),
+                                    vp(FAKE), vp(o), vp(idx), vp(ws), ctypes.c_size_t(ws_bytes),
+                                    vp(0))
+    assert fwd(q=0) == 1 and fwd(pq=0) == 1 and fwd(o=0) == 1
+    assert fwd(ws_bytes=need - 1) == 6
+    assert fwd(ws=MISALIGNED) == 5 and fwd(idx=MISALIGNED) == 5
+    assert fwd(prob_=prob(head_dim=96)) == 7
+    assert fwd(prob_=prob(top_k=12)) == 4

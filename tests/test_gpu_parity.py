@@ -284,7 +284,7 @@ def test_fp8_quantiser_bit_exact(sla, nq, nkv, d):
     wsh = ws.cpu().numpy()
 
     def region(name, dtype):
-        off, size = sla.workspace_region(prob, name, fp8=True)
+        off, size = sla.workspace_region(prob, name, sla.VARIANT_FP8)
         return wsh[off:off + size].view(dtype)
 
     nbq, nbk = prob.n_q // 64 + (prob.n_q % 64 > 0), -(-nkv // 64)
