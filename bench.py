@@ -254,7 +254,8 @@ def bench_cached(args, sla, x, q, k, v, pq, pk, al, out):
         "config": {"workload": p.name, "path": "sla_forward_cached", "batch": p.batch,
                    "heads": p.heads, "n_q": p.n_q, "n_kv": p.n_kv, "head_dim": d,
                    "block": p.block, "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
-                   "router": args.router, "parallelism": "single GPU"},
+                   "router": args.router, "path": "sla_forward_pisa" if pisa else None,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
                      "kernel": "sla_forward_cached (whole call: route, decode, combine)",
@@ -284,6 +285,9 @@ def main():
                          "(the decode path); the cache build is timed separately")
     ap.add_argument("--router", choices=("learnable", "taylor"), default="learnable",
                     help="taylor: time sla_forward_taylor (training-free second-order router)")
+    ap.add_argument("--pisa", action="store_true",
+                    help="time sla_forward_pisa (exact routed blocks + Taylor tail, one "
+                         "normalisation) instead of sla_forward")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     args = ap.parse_args()
@@ -324,14 +328,18 @@ def main():
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     if args.cached:
         return bench_cached(args, sla, x, q, k, v, pq, pk, al, out)
-    ws = torch.empty(sla.workspace_size(prob, fp8), dtype=torch.uint8, device=dev)
     taylor = args.router == "taylor"
-    if taylor and fp8:
-        print("the Taylor router is timed on the bf16 forward only", file=sys.stderr)
+    pisa = args.pisa
+    if int(taylor) + int(pisa) + int(fp8) > 1:
+        print("--router taylor, --pisa and the fp8 workload are separate paths", file=sys.stderr)
         return 2
+    variant = sla.VARIANT_FP8 if fp8 else (sla.VARIANT_PISA if pisa else sla.VARIANT_FORWARD)
+    ws = torch.empty(sla.workspace_size(prob, variant), dtype=torch.uint8, device=dev)
 
     def fwd():
-        if taylor:
+        if pisa:
+            sla.sla_forward_pisa(q, k, v, pq, pk, p.top_k, return_idx=False, workspace=ws, out=out)
+        elif taylor:
             sla.sla_forward_taylor(q, k, v, al, p.top_k, return_idx=False, workspace=ws, out=out)
         elif fp8:
             sla.sla_forward_fp8(q, k, v, pq, pk, al, p.top_k, return_idx=False, workspace=ws,
@@ -366,7 +374,7 @@ def main():
     t0 = time.perf_counter()
     for s in range(K):
         sla.sla_forward_profiled(q, k, v, pq, pk, al, p.top_k, handles[s], fp8=fp8,
-                                 workspace=ws, out=out, taylor=taylor)
+                                 workspace=ws, out=out, taylor=taylor, pisa=pisa)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / K
@@ -390,6 +398,11 @@ def main():
     }
     if fp8:
         kernels["quant_GBps"] = w["quant_bytes"] / (stage_ms["quant"] * 1e-3) / 1e9
+    if pisa:
+        # tail kernel (timed as the complement stage): Q K_bar^T and P Vsum over the
+        # unrouted centroids, 4 d FLOP per (query row, centroid)
+        tail_flops = p.batch * p.heads * p.n_q * (p.nbk - p.top_k) * 4 * p.head_dim
+        kernels["tail_TFLOPs"] = tail_flops / (stage_ms["complement"] * 1e-3) / 1e12
 
     # ---------------------------------------------------------------- dense baselines
     dense = None
@@ -445,7 +458,8 @@ def main():
                    "n_kv": p.n_kv, "head_dim": p.head_dim, "block": p.block,
                    "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
                    "grid": "x".join(map(str, p.grid)) if p.grid else None,
-                   "router": args.router, "parallelism": "single GPU"},
+                   "router": args.router, "path": "sla_forward_pisa" if pisa else None,
+                   "parallelism": "single GPU"},
         "effective_tflops": w["dense_flops"] / (ms * 1e-3) / 1e12,
         "roofline": roofline,
         "cpu_baseline": cpu,
