@@ -114,12 +114,12 @@ struct UnionWalk {
   // on all outstanding loads, happens once per 64 steps.
   int uvec = -1, upos = 64;
   __device__ __forceinline__ void fill() {
+    uvec = -1;
 #pragma unroll 1
     for (int i = 0; i < 64; ++i) {
       int j, f;
-      const bool ok = next_direct(j, f);
-      const int e = ok ? (j | (f << 24)) : -1;
-      uvec = (int)(threadIdx.x & 63) == i ? e : uvec;
+      if (!next_direct(j, f)) break;     // lanes past the end of the walk stay -1
+      uvec = (int)(threadIdx.x & 63) == i ? (j | (f << 24)) : uvec;
     }
     upos = 0;
   }
@@ -224,9 +224,6 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   const T* kb = reinterpret_cast<const T*>(a.k) + (size_t)bh * a.nkv * D;
   const uint16_t* vb = a.v16 + (size_t)bh * a.nbk * kBlock * D;
 
-  UnionWalk<QB> walk;
-  walk.init(a.idx, bh, a.nbq, grp, a.topk);
-
   // Q^T fragments (B operand): lane column q = qrow0 + l32, channels 16 s + 8 h .. +7
   u32x4 qf[KS];
   u32x4 ql[SPLIT ? KS : 1];
@@ -246,6 +243,10 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       if (!ok) qf[s] = u32x4{0, 0, 0, 0};
     }
   }
+
+  // the selection lists load after Q, so that both round trips overlap
+  UnionWalk<QB> walk;
+  walk.init(a.idx, bh, a.nbq, grp, a.topk);
 
   f32x16 o[CT];
 #pragma unroll
@@ -465,6 +466,38 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
       step(std::integral_constant<int, 1>{});
     }
   }
+  // Linear-branch inputs of the epilogue (bf16 path, SLA2 mix): S_c^T of both query blocks,
+  // their z_c and this head's alpha are staged into the idle tile ring with one round of
+  // loads into LDS, so that no wave waits on several dependent global round trips. S_c^T of
+  // query block qb takes two swizzled 64-row tiles at 2 qb TILE; z_c takes the 1 KB at 4 TILE
+  // (each load into LDS writes 1 KB, lanes past the data write zeros), alpha the next 1 KB.
+  constexpr bool STAGE_EPI = DMA && !PISA;
+  if constexpr (STAGE_EPI) {
+    __syncthreads();   // every wave has drained its ring loads (wait_vmem above)
+    constexpr int SCP = D * D * 2 / 1024;           // 1-KB pieces of one S_c^T
+    const int iqs = grp * QB + (wvs >> 1);            // iq, wave-uniform for the descriptor
+    const int iqc = iqs < a.nbq ? iqs : a.nbq - 1;
+    const auto rs = make_rsrc(a.sc + ((size_t)bh * a.nbq + iqc) * D * D, (uint32_t)(D * D * 2));
+    const uint32_t sbase = lds_addr(smem + (wvs >> 1) * 2 * TILE);
+#pragma unroll
+    for (int u = 0; u < SCP / 2; ++u) {
+      const int pc = (wvs & 1) * (SCP / 2) + u;        // piece of this wave
+      const int e = pc * 512 + lane * 8;
+      const int r = e / D, pch = (e % D) / 8;
+      load_lds16(rs, sbase + pc * 1024, (uint32_t)(r * D * 2 + ((pch ^ r) & (CH - 1)) * 16));
+    }
+    if (wvs == 0) {
+      const int iq0 = grp * QB;
+      const auto rz = make_rsrc(a.zc + ((size_t)bh * a.nbq + iq0) * D,
+                                (uint32_t)(min(QB, a.nbq - iq0) * D * 4));
+      load_lds16(rz, lds_addr(smem + 4 * TILE), (uint32_t)(lane * 16));
+    } else if (wvs == 1) {
+      const auto ra = make_rsrc(a.alpha + (size_t)(bh % a.H) * D, (uint32_t)(D * 4));
+      load_lds16(ra, lds_addr(smem + 4 * TILE + 512), (uint32_t)(lane * 16));
+    }
+    wait_vmem();
+    __syncthreads();
+  }
   if (!active) return;   // no barrier follows
 
   // ---------------------------------------------------------------- epilogue
@@ -517,7 +550,15 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   }
   const float inv_l = l > 0.f ? 1.f / l : 0.f;
   const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
-  const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
+  const float* zcb = STAGE_EPI ? reinterpret_cast<const float*>(smem + 4 * TILE) + qb * D
+                               : a.zc + ((size_t)bh * a.nbq + iq) * D;
+  // A fragment of S_c^T (rows 32 c + lane % 32, columns 16 s + 8 h .. +7)
+  auto sc_frag = [&](int c, int s_) __attribute__((always_inline)) {
+    if constexpr (STAGE_EPI)
+      return *reinterpret_cast<const u32x4*>(&smem[qb * 2 * TILE + swz<D>(32 * c + l32, 16 * s_ + 8 * h)]);
+    else
+      return *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s_ + 8 * h);
+  };
   // phi(Q) . z_c for this lane's query: this lane holds channels 16 s + 8 h .. +7
   float d = 0.f;
 #pragma unroll
@@ -532,17 +573,14 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
   }
   d += swap_halves(d);
   const float inv_den = 1.f / (d + kEps);
-  const float* al = a.alpha + (size_t)(bh % a.H) * D;
+  const float* al = STAGE_EPI ? reinterpret_cast<const float*>(smem + 4 * TILE + 512)
+                              : a.alpha + (size_t)(bh % a.H) * D;
   const int q = qrow0 + l32;
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     f32x16 lin = f32x16{};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 af =
-          *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
-      lin = mfma_bf16(af, relu_bf16x8(qf[s]), lin);
-    }
+    for (int s = 0; s < KS; ++s) lin = mfma_bf16(sc_frag(c, s), relu_bf16x8(qf[s]), lin);
     if (q < a.nq) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
