@@ -416,12 +416,15 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
     // loads get two steps to land and V loads one.
     uint16_t* const kring = smem;
     uint16_t* const vring = smem + 3 * TILE;
+    // The first two union entries come straight from the lists, so that their tiles are in
+    // flight while the rest of the walk is buffered.
     int j0, f0, j1, f1;
-    bool have0 = walk.next(j0, f0);
-    bool have1 = walk.next(j1, f1);
+    bool have0 = walk.next_direct(j0, f0);
+    bool have1 = walk.next_direct(j1, f1);
     stage_k(have0 ? j0 : -1, kring);
     stage_k(have1 ? j1 : -1, kring + TILE);
     stage_v(have0 ? j0 : -1, vring);
+    walk.fill();
     barrier_vmem_n<0>();
     int ks = 0, vs = 0;
     while (have0) {
