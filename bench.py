@@ -254,7 +254,6 @@ def bench_cached(args, sla, x, q, k, v, pq, pk, al, out):
         "config": {"workload": p.name, "path": "sla_forward_cached", "batch": p.batch,
                    "heads": p.heads, "n_q": p.n_q, "n_kv": p.n_kv, "head_dim": d,
                    "block": p.block, "top_k": p.top_k, "sparsity": round(p.sparsity, 4),
-                   "router": args.router, "path": "sla_forward_pisa" if pisa else None,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,

@@ -47,7 +47,7 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // (bf16 hi + lo, [BH][npad][D]) and its column of the transposed value-sum table
 // ([BH][D][npad] f16) are written.
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
-__global__ __launch_bounds__(256) void kv_summary_kernel(
+__global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
@@ -218,12 +218,25 @@ __global__ __launch_bounds__(256) void kv_summary_kernel(
     // projected pooled K of each finished group of kSummaryChunk blocks: k~ = mean @ P_k
     // (float64; means are visible after the barrier above)
     if (Pk != nullptr && ((j - j0) % kSummaryChunk == kSummaryChunk - 1 || j + 1 == j1)) {
+      // thread (c, b0) projects blocks b0, b0 + 256 / D, ... of the group for output channel
+      // c, reading each P_k entry once for all of them (rows of a partial group are computed
+      // and not stored)
+      constexpr int NBT = kSummaryChunk * D / 256;
       const int g0 = j - (j - j0) % kSummaryChunk;
-      for (int b = t / D; b <= j - g0; b += 256 / D) {
-        const int c = t % D;
-        double acc = 0.0;
-        for (int r = 0; r < D; ++r) acc = fma(means[b][r], (double)Pk[r * D + c], acc);
-        kt[(size_t)bh * kbh + (size_t)(g0 + b) * kj + c] = acc;
+      const int c = t % D, b0 = t / D;
+      double acc[NBT];
+#pragma unroll
+      for (int u = 0; u < NBT; ++u) acc[u] = 0.0;
+#pragma unroll 4
+      for (int r = 0; r < D; ++r) {
+        const double pv = (double)Pk[r * D + c];
+#pragma unroll
+        for (int u = 0; u < NBT; ++u) acc[u] = fma(means[b0 + u * (256 / D)][r], pv, acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NBT; ++u) {
+        const int b = b0 + u * (256 / D);
+        if (b <= j - g0) kt[(size_t)bh * kbh + (size_t)(g0 + b) * kj + c] = acc[u];
       }
       __syncthreads();   // means are rewritten by the next group
     }
@@ -253,29 +266,44 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
                                                             int accumulate,
                                                             uint16_t* __restrict__ scaled_bf16,
                                                             float scale) {
-  // chunk partials are added in chunk order (deterministic), onto the previous totals when
-  // accumulating (summary cache update); loads go out 8 at a time. scaled_bf16 (optional):
-  // also store bf16(scale * total) (the piecewise forward's H_bar^T = H_sum^T / nbk).
+  // A workgroup owns 32 consecutive entries e of the d x d total (and, for the first D / 32
+  // workgroups, 32 entries of z). Thread group g (8 of 32 threads) adds the chunk partials
+  // c = g, g + 8, ... with all its loads in flight at once; the 8 group sums are then added
+  // in group order, onto the previous totals when accumulating (summary cache update), so
+  // the result does not depend on timing. scaled_bf16 (optional): also store
+  // bf16(scale * total) (the piecewise forward's H_bar^T = H_sum^T / nbk).
+  constexpr int G = 8;
+  __shared__ float part[2][G][32];
   const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const float* src = spart + (size_t)bh * nchunk * D * D + e;
-  float s = accumulate ? stot[(size_t)bh * D * D + e] : 0.f;
-  int c = 0;
-  for (; c + 8 <= nchunk; c += 8) {
-    float v[8];
+  const int t = threadIdx.x, lane = t & 31, g = t >> 5;
+  const int e = blockIdx.x * 32 + lane;
+  const bool do_z = blockIdx.x * 32 < D;
+  auto group_sum = [&](const float* src, size_t stride) {
+    float acc = 0.f;
+    int c = g;
+    for (; c + 3 * G < nchunk; c += 4 * G) {
+      const float v0 = src[(size_t)c * stride], v1 = src[(size_t)(c + G) * stride];
+      const float v2 = src[(size_t)(c + 2 * G) * stride], v3 = src[(size_t)(c + 3 * G) * stride];
+      acc += v0; acc += v1; acc += v2; acc += v3;
+    }
+    for (; c < nchunk; c += G) acc += src[(size_t)c * stride];
+    return acc;
+  };
+  part[0][g][lane] = group_sum(spart + (size_t)bh * nchunk * D * D + e, (size_t)D * D);
+  if (do_z) part[1][g][lane] = group_sum(zpart + (size_t)bh * nchunk * D + e, (size_t)D);
+  __syncthreads();
+  if (g == 0) {
+    float s = accumulate ? stot[(size_t)bh * D * D + e] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(c + u) * D * D];
+    for (int i = 0; i < G; ++i) s += part[0][i][lane];
+    stot[(size_t)bh * D * D + e] = s;
+    if (scaled_bf16 != nullptr)
+      scaled_bf16[(size_t)bh * D * D + e] = (uint16_t)(pack_bf16(s * scale, 0.f) & 0xffffu);
+  } else if (g == 1 && do_z) {
+    float z = accumulate ? ztot[(size_t)bh * D + e] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += v[u];
-  }
-  for (; c < nchunk; ++c) s += src[(size_t)c * D * D];
-  stot[(size_t)bh * D * D + e] = s;
-  if (scaled_bf16 != nullptr)
-    scaled_bf16[(size_t)bh * D * D + e] = (uint16_t)(pack_bf16(s * scale, 0.f) & 0xffffu);
-  if (blockIdx.x == 0 && threadIdx.x < D) {
-    float z = accumulate ? ztot[(size_t)bh * D + threadIdx.x] : 0.f;
-    for (int cc = 0; cc < nchunk; ++cc) z += zpart[((size_t)bh * nchunk + cc) * D + threadIdx.x];
-    ztot[(size_t)bh * D + threadIdx.x] = z;
+    for (int i = 0; i < G; ++i) z += part[1][i][lane];
+    ztot[(size_t)bh * D + e] = z;
   }
 }
 
@@ -564,7 +592,7 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
                        zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
-  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
                      reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f);
   return hipGetLastError();
@@ -590,7 +618,7 @@ static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* 
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk, true>), grid, dim3(256), 0,
                        st, (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, nullptr,
                        nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad);
-  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.p_stot),
                      reinterpret_cast<float*>(ws + s.p_ztot), s.nchunk, 0,
                      reinterpret_cast<uint16_t*>(ws + s.hbar), 1.f / (float)s.nbk);
@@ -612,7 +640,7 @@ static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const v
                      (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
                      (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
                      jbase, n_done, nullptr, nullptr, nullptr, 0);
-  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 256, s.BH), dim3(256), 0, st, spart,
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(cache + c.stot),
                      reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
                      nullptr, 0.f);

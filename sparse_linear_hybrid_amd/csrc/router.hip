@@ -126,15 +126,18 @@ __global__ __launch_bounds__(256) void pool_project_kernel(const T* __restrict__
   }
 }
 
-// Block means and (optionally) per-channel population variances of G = 4 consecutive blocks
-// of one (batch, head), float64, two passes over the register-held tokens (the training-free
-// router's block statistics, SPLA page, section 2.1). Only valid tokens count.
+// Block means and (optionally) per-channel population variances of kStatsBlocks<D>
+// consecutive blocks of one (batch, head), float64, two passes over the register-held tokens
+// (the training-free router's block statistics, SPLA page, section 2.1). Only valid tokens
+// count. Two blocks per workgroup keep the tokens of two waves per SIMD in registers.
+template <int D>
+constexpr int kStatsBlocks = 2;
 template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_stats_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void pool_stats_kernel(const T* __restrict__ x,
                                                          double* __restrict__ mean_out,
                                                          double* __restrict__ var_out, int n,
                                                          int nb) {
-  constexpr int TPR = D / 8, RPP = 256 / TPR, LPB = kBlock / RPP, G = 4;
+  constexpr int TPR = D / 8, RPP = 256 / TPR, LPB = kBlock / RPP, G = kStatsBlocks<D>;
   __shared__ double part[4][G][D];
   __shared__ double mean[G][D];
   const int j0 = blockIdx.x * G, bh = blockIdx.y;
@@ -546,7 +549,8 @@ static hipError_t launch_route_taylor_T(const Plan& s, const void* q, const void
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   double* kv = reinterpret_cast<double*>(ws + s.kvar);
   double* sc = reinterpret_cast<double*>(ws + s.scores);
-  const dim3 gq((s.nbq + 3) / 4, s.BH), gk((s.nbk + 3) / 4, s.BH);
+  constexpr int G = kStatsBlocks<D>;
+  const dim3 gq((s.nbq + G - 1) / G, s.BH), gk((s.nbk + G - 1) / G, s.BH);
   if (s.in_bf16) {
     hipLaunchKernelGGL((pool_stats_kernel<uint16_t, D>), gq, dim3(256), 0, st, (const uint16_t*)q,
                        qt, nullptr, s.nq, s.nbq);

@@ -199,7 +199,7 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
 }
 
 template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false>
-__global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArgs a) {
+__global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
   constexpr bool DMA = !SPLIT;             // bf16 inputs: K/V tiles go global -> LDS directly
   constexpr int NT = 128 * QB;             // threads
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_kernel(SparseArg
 // holds 32 of the 64 reduction elements; the two 32-element scale blocks take their E8M0
 // scale from lanes x and x+32, which here always carry the same value.
 template <int D, int QB, bool OUT_BF16>
-__global__ __launch_bounds__(128 * QB, 4 / QB) void sparse_attn_fp8_kernel(SparseArgs a) {
+__global__ __launch_bounds__(128 * QB, 2) void sparse_attn_fp8_kernel(SparseArgs a) {
   constexpr int NT = 128 * QB;
   constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
   constexpr int CT = D / 32;
