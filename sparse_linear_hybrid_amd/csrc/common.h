@@ -153,6 +153,8 @@ struct Plan {
   // byte offsets into the workspace
   size_t qt, kt, scores, idx, kvar;              // router (kvar: training-free router)
   size_t v16, sblk, zblk, spart, zpart, stot, ztot, sc, zc;   // linear branch
+  int nwords;                                   // 32-bit words of a key-block bitmap row
+  size_t selbits;                               // routed-block bitmap [BH][nbq][nwords]
   size_t q8, k8, v8, sq8, sk8, sv8;             // fp8 sparse branch
   size_t total_route, total_fwd, total_fp8;
   // piecewise (exact-or-approximate) forward: its own layout after the router's buffers
@@ -196,6 +198,8 @@ inline Plan make_plan(const sla_problem& p) {
   s.ztot = take(BH * D * 4);
   s.sc = take(BH * nbq * D * D * 2);
   s.zc = take(BH * nbq * D * 4);
+  s.nwords = (s.nbk + 31) / 32;
+  s.selbits = take(BH * nbq * (size_t)s.nwords * 4);
   s.total_fwd = off;
   s.q8 = take(BH * nbq * kBlock * D * 2);   // E4M3 values held as bf16
   s.k8 = take(BH * nbk * kBlock * D * 2);

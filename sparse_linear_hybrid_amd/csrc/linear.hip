@@ -310,15 +310,35 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // Complement, summary part: for a tile of CQ query blocks and CN columns n of the d x d
 // summary, C[n][i] = sum_j M[i][j] S_j[n] with M the 0/1 selection matrix, computed as an
 // MFMA product over steps of CK key blocks (M is exact in bf16), then S_c = S_tot - C.
-// Each thread first turns one query block's ascending selection list into an LDS bitmap
-// row (one 32-bit word per step of a window of up to 32 * MAXW key blocks), and steps that
-// no query block of the tile selects are skipped. The summary slices of a step (CK rows of
+// Each thread first copies one query block's row of the routed-block bitmap (built once per
+// query block by selection_bits_kernel; one 32-bit word per step of a window of up to
+// 32 * MAXW key blocks) into LDS, and steps that no query block of the tile selects are
+// skipped. The summary slices of a step (CK rows of
 // CN bf16) are loaded straight into a CBUF-deep LDS ring, two steps ahead of their use.
 // Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
 // reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
 // builds 4 B fragments (its bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a
 // column slice are consecutive workgroups (same XCD), so each S_j slice comes from HBM
 // about once and from L2 ceil(n_blocks / CQ) times.
+// Routed-block bitmap of every query block (bit j of row i: key block j is routed to query
+// block i), built once from the selection lists for the complement's workgroups.
+__global__ __launch_bounds__(64) void selection_bits_kernel(const int32_t* __restrict__ idx,
+                                                            uint32_t* __restrict__ bits, int nbq,
+                                                            int k, int nwords) {
+  __shared__ uint32_t w[kMaxKeyBlocks / 32];
+  const size_t row = (size_t)blockIdx.y * nbq + blockIdx.x;
+  const int t = threadIdx.x;
+  for (int i = t; i < nwords; i += 64) w[i] = 0u;
+  __syncthreads();
+  const int32_t* sel = idx + row * k;
+  for (int i = t; i < k; i += 64) {
+    const int j = sel[i];
+    atomicOr(&w[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  for (int i = t; i < nwords; i += 64) bits[row * nwords + i] = w[i];
+}
+
 constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
 constexpr int CN = 128;    // summary columns per workgroup
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
@@ -365,7 +385,7 @@ __device__ __forceinline__ u32x4 bits_to_bf16x8(uint32_t m8) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void complement_kernel(
-    const int32_t* __restrict__ idx, const uint16_t* __restrict__ sblk,
+    const uint32_t* __restrict__ selbits, int nwords, const uint16_t* __restrict__ sblk,
     const float* __restrict__ stot, uint16_t* __restrict__ sc, int nbq, int nbk, int k,
     int nqt, int total, int ww) {
   constexpr int NCS = D * D / CN;      // column slices per (batch, head)
@@ -393,11 +413,9 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     }
     return;
   }
-  // this thread's query block and its selection list
+  // this thread's query block and its row of the routed-block bitmap
   const int qi = qt * CQ + t;
-  const int32_t* my_sel = idx + ((size_t)bh * nbq + min(qi, nbq - 1)) * k;
-  const int my_n = qi < nbq ? k : 0;
-  int my_p = 0;
+  const uint32_t* my_bits = selbits + ((size_t)bh * nbq + min(qi, nbq - 1)) * nwords;
 
   // ring loads: wave w moves pieces LPW w .. LPW w + LPW - 1 (1 KB = 4 rows of 256 bytes);
   // lane l lands at row 4 piece + l / 16, physical chunk l % 16, and fetches the logical
@@ -428,39 +446,18 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   for (int win0 = 0; win0 < nbk; win0 += win) {
     const int nstep = min(ww, (nbk - win0 + CK - 1) / CK);
     barrier_vmem_n<0>();   // the previous window's ring and bitmap are no longer in use
-    // bitmap row of this thread's query block (the list is ascending: one pass per window;
-    // entries are fetched 16 at a time so that their loads overlap)
+    // this window's words of the thread's bitmap row (loads in flight together)
     uint64_t my_occ = 0;
     {
-      int word_i = 0;
-      uint32_t word = 0;
-      bool more = my_p < my_n;
-      while (more) {
-        int e16[16];
+      const int w0 = win0 / CK;
+      const int nw = qi < nbq ? min(ww, nwords - w0) : 0;
+      uint32_t wv_[MAXW];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) e16[u] = my_p + u < my_n ? my_sel[my_p + u] : 0x7fffffff;
+      for (int wi = 0; wi < MAXW; ++wi) wv_[wi] = wi < nw ? my_bits[w0 + wi] : 0u;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int j = e16[u] - win0;          // e16 = INT_MAX past the end: j >= win
-          if (more && j < win) {
-            ++my_p;
-            while (word_i < (j >> 5)) {
-              bits[t * WW + word_i] = word;
-              my_occ |= (uint64_t)(word != 0) << word_i;
-              word = 0;
-              ++word_i;
-            }
-            word |= 1u << (j & 31);
-          } else {
-            more = false;
-          }
-        }
-        more = more && my_p < my_n;
-      }
-      for (; word_i < ww; ++word_i) {
-        bits[t * WW + word_i] = word;
-        my_occ |= (uint64_t)(word != 0) << word_i;
-        word = 0;
+      for (int wi = 0; wi < MAXW; ++wi) {
+        if (wi < ww) bits[t * WW + wi] = wv_[wi];
+        my_occ |= (uint64_t)(wv_[wi] != 0) << wi;
       }
     }
     // union of the occupancy masks over the workgroup
@@ -672,8 +669,12 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
   const int total = s.BH * ncs * nqt;
   const int ww = min(MAXW, (s.nbk + CK - 1) / CK);
   const size_t lds = complement_lds_bytes(ww);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + s.selbits);
+  if (s.k < s.nbk)   // (k = 0: all-zero rows)
+    hipLaunchKernelGGL(selection_bits_kernel, dim3(s.nbq, s.BH), dim3(64), 0, st, idx, bits,
+                       s.nbq, s.k, s.nwords);
   auto go = [&](auto kern, auto zkern) {
-    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, idx,
+    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, s.nwords,
                        reinterpret_cast<const uint16_t*>(ws + s.sblk),
                        reinterpret_cast<const float*>(ws + s.stot),
                        reinterpret_cast<uint16_t*>(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww);
