@@ -349,9 +349,13 @@ constexpr int RING_BYTES = CBUF * CK * CN * 2;
 // Dynamic LDS of complement_kernel for a window of `ww` words: ring, bitmap (ww + 1 words
 // per query block: the odd row length keeps the per-lane word accesses on distinct banks)
 // and four 64-bit step-occupancy masks.
-inline size_t complement_lds_bytes(int ww) {
-  return (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
+// S_tot slice staged at kernel start: 1 KB (one load into LDS per wave instruction) at or
+// after 32 KB, the size of the epilogue's store staging area.
+__host__ __device__ inline size_t complement_tot_offset(int ww) {
+  const size_t end = (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
+  return end > 32768 ? end : 32768;
 }
+inline size_t complement_lds_bytes(int ww) { return complement_tot_offset(ww) + 1024; }
 
 // Swizzle of a ring row (CN bf16 = 16 chunks of 16 bytes): chunk c of row r sits at
 // c ^ f(r % 4), which keeps the transposing fragment reads (4 rows x 2 or 4 adjacent chunks
@@ -441,6 +445,11 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = f32x16{};
+  // this slice of S_tot for the epilogue, staged now (the first window barrier waits for it)
+  const float* tot_lds = reinterpret_cast<const float*>(dyn + complement_tot_offset(ww));
+  if (ws == 0)
+    load_lds16(make_rsrc(stot + (size_t)bh * D * D + col0, (uint32_t)(CN * 4)),
+               lds_addr(tot_lds), (uint32_t)(lane * 16));
 
   const int win = ww * CK;
   for (int win0 = 0; win0 < nbk; win0 += win) {
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   // stages its 32 query blocks x CN columns; 16-byte chunk c of staged row q sits at
   // c ^ (q % 16).
   __syncthreads();
-  const float* tot = stot + (size_t)bh * D * D + col0;
+  const float* tot = tot_lds;
   uint16_t* stg = reinterpret_cast<uint16_t*>(dyn) + w * 32 * CN;
 #pragma unroll
   for (int tq = 0; tq < 2; ++tq) {
