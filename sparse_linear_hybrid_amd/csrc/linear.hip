@@ -55,6 +55,9 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     uint16_t* __restrict__ cent_hi, uint16_t* __restrict__ cent_lo, uint16_t* __restrict__ vsum,
     int npad) {
   static_assert(!PISA || BLOCKS, "the piecewise pass is a full-forward pass");
+  // The SLA2 forward's complement sums the unselected S_j itself, so its pass keeps no d x d
+  // chunk totals (only the z partials); the cache update and the piecewise pass do.
+  constexpr bool TOTALS = !BLOCKS || PISA;
   constexpr int LS = D + 8;                  // padded LDS row (elements)
   constexpr int TPR = D / 8, RPP = 256 / TPR;
   constexpr int CPT = 64 * TPR / 256;        // 16-byte chunks per thread per tensor
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       f32x16 acc = {};
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) acc = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), acc);
-      part[u] += acc;
+      if constexpr (TOTALS) part[u] += acc;
       if constexpr (BLOCKS && !PISA) {
         // store S_j^T[c][r] (bf16): lane column c = 32 nt + l32, rows r in runs of 4
         const int c = 32 * nt + l32;
@@ -243,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
   }
   // chunk partial totals (fp32, layout [c][r])
 #pragma unroll
-  for (int u = 0; u < TILES_PER_WAVE; ++u) {
+  for (int u = 0; u < (TOTALS ? TILES_PER_WAVE : 0); ++u) {
     const int nt = (NT == 4) ? u : (w & 1);
     const int c = 32 * nt + l32;
     float* dst = spart + (((size_t)bh * gridDim.x + chunk) * D + c) * D;
@@ -265,13 +268,14 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
                                                             float* __restrict__ ztot, int nchunk,
                                                             int accumulate,
                                                             uint16_t* __restrict__ scaled_bf16,
-                                                            float scale) {
+                                                            float scale, int z_only) {
   // A workgroup owns 32 consecutive entries e of the d x d total (and, for the first D / 32
   // workgroups, 32 entries of z). Thread group g (8 of 32 threads) adds the chunk partials
   // c = g, g + 8, ... with all its loads in flight at once; the 8 group sums are then added
   // in group order, onto the previous totals when accumulating (summary cache update), so
   // the result does not depend on timing. scaled_bf16 (optional): also store
-  // bf16(scale * total) (the piecewise forward's H_bar^T = H_sum^T / nbk).
+  // bf16(scale * total) (the piecewise forward's H_bar^T = H_sum^T / nbk). z_only: only the
+  // z partials exist (grid of D / 32 workgroups per head).
   constexpr int G = 8;
   __shared__ float part[2][G][32];
   const int bh = blockIdx.y;
@@ -289,10 +293,10 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
     for (; c < nchunk; c += G) acc += src[(size_t)c * stride];
     return acc;
   };
-  part[0][g][lane] = group_sum(spart + (size_t)bh * nchunk * D * D + e, (size_t)D * D);
+  if (!z_only) part[0][g][lane] = group_sum(spart + (size_t)bh * nchunk * D * D + e, (size_t)D * D);
   if (do_z) part[1][g][lane] = group_sum(zpart + (size_t)bh * nchunk * D + e, (size_t)D);
   __syncthreads();
-  if (g == 0) {
+  if (g == 0 && !z_only) {
     float s = accumulate ? stot[(size_t)bh * D * D + e] : 0.f;
 #pragma unroll
     for (int i = 0; i < G; ++i) s += part[0][i][lane];
@@ -308,12 +312,13 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 }
 
 // Complement, summary part: for a tile of CQ query blocks and CN columns n of the d x d
-// summary, C[n][i] = sum_j M[i][j] S_j[n] with M the 0/1 selection matrix, computed as an
-// MFMA product over steps of CK key blocks (M is exact in bf16), then S_c = S_tot - C.
+// summary, S_c[n][i] = sum_j (1 - M[i][j]) S_j[n] with M the 0/1 selection matrix (SPLA
+// page, section 2.2: the linear term covers the blocks the sparse part did not select),
+// computed as an MFMA product over steps of CK key blocks (the 0/1 matrix is exact in bf16).
 // Each thread first copies one query block's row of the routed-block bitmap (built once per
 // query block by selection_bits_kernel; one 32-bit word per step of a window of up to
-// 32 * MAXW key blocks) into LDS, and steps that no query block of the tile selects are
-// skipped. The summary slices of a step (CK rows of
+// 32 * MAXW key blocks) into LDS, inverted over the valid key blocks, and steps in which
+// every query block of the tile selected every block are skipped. The summary slices of a step (CK rows of
 // CN bf16) are loaded straight into a CBUF-deep LDS ring, two steps ahead of their use.
 // Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
 // reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
@@ -349,13 +354,11 @@ constexpr int RING_BYTES = CBUF * CK * CN * 2;
 // Dynamic LDS of complement_kernel for a window of `ww` words: ring, bitmap (ww + 1 words
 // per query block: the odd row length keeps the per-lane word accesses on distinct banks)
 // and four 64-bit step-occupancy masks.
-// S_tot slice staged at kernel start: 1 KB (one load into LDS per wave instruction) at or
-// after 32 KB, the size of the epilogue's store staging area.
-__host__ __device__ inline size_t complement_tot_offset(int ww) {
-  const size_t end = (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
-  return end > 32768 ? end : 32768;
+// (at least 32 KB: the epilogue stages its stores there)
+inline size_t complement_lds_bytes(int ww) {
+  const size_t b = (size_t)RING_BYTES + (size_t)CQ * (ww + 1) * 4 + 4 * 8;
+  return b > 32768 ? b : 32768;
 }
-inline size_t complement_lds_bytes(int ww) { return complement_tot_offset(ww) + 1024; }
 
 // Swizzle of a ring row (CN bf16 = 16 chunks of 16 bytes): chunk c of row r sits at
 // c ^ f(r % 4), which keeps the transposing fragment reads (4 rows x 2 or 4 adjacent chunks
@@ -445,11 +448,6 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = f32x16{};
-  // this slice of S_tot for the epilogue, staged now (the first window barrier waits for it)
-  const float* tot_lds = reinterpret_cast<const float*>(dyn + complement_tot_offset(ww));
-  if (ws == 0)
-    load_lds16(make_rsrc(stot + (size_t)bh * D * D + col0, (uint32_t)(CN * 4)),
-               lds_addr(tot_lds), (uint32_t)(lane * 16));
 
   const int win = ww * CK;
   for (int win0 = 0; win0 < nbk; win0 += win) {
@@ -462,7 +460,12 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       const int nw = qi < nbq ? min(ww, nwords - w0) : 0;
       uint32_t wv_[MAXW];
 #pragma unroll
-      for (int wi = 0; wi < MAXW; ++wi) wv_[wi] = wi < nw ? my_bits[w0 + wi] : 0u;
+      for (int wi = 0; wi < MAXW; ++wi) {
+        // unselected valid key blocks of this word (bits past nbk stay clear)
+        const int jb = (w0 + wi) * CK;
+        const uint32_t valid = nbk - jb >= CK ? 0xffffffffu : (nbk > jb ? (1u << (nbk - jb)) - 1u : 0u);
+        wv_[wi] = wi < nw ? ~my_bits[w0 + wi] & valid : 0u;
+      }
 #pragma unroll
       for (int wi = 0; wi < MAXW; ++wi) {
         if (wi < ww) bits[t * WW + wi] = wv_[wi];
@@ -517,12 +520,11 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     }
   }
   wait_vmem();   // no load into LDS outlives the workgroup
-  // S_c = S_tot - C, staged through LDS (the ring and bitmap are free now) so that every
+  // S_c, staged through LDS (the ring and bitmap are free now) so that every
   // query block's CN columns go out as contiguous 16-byte stores. Per half tq, wave w
   // stages its 32 query blocks x CN columns; 16-byte chunk c of staged row q sits at
   // c ^ (q % 16).
   __syncthreads();
-  const float* tot = tot_lds;
   uint16_t* stg = reinterpret_cast<uint16_t*>(dyn) + w * 32 * CN;
 #pragma unroll
   for (int tq = 0; tq < 2; ++tq) {
@@ -531,11 +533,10 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = 32 * nt + 8 * g + 4 * h;
-        const f32x4 tv = *reinterpret_cast<const f32x4*>(tot + n);
         const int off = l32 * CN + ((((n >> 3) ^ l32) & 15) << 3) + (n & 7);
         *reinterpret_cast<u32x2*>(stg + off) =
-            u32x2{pack_bf16(tv[0] - acc[tq][nt][4 * g], tv[1] - acc[tq][nt][4 * g + 1]),
-                  pack_bf16(tv[2] - acc[tq][nt][4 * g + 2], tv[3] - acc[tq][nt][4 * g + 3])};
+            u32x2{pack_bf16(acc[tq][nt][4 * g], acc[tq][nt][4 * g + 1]),
+                  pack_bf16(acc[tq][nt][4 * g + 2], acc[tq][nt][4 * g + 3])};
       }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -598,9 +599,10 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
                        zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
-  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
+  // only z_tot: the complement sums the unselected S_j itself
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
-                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f);
+                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f, 1);
   return hipGetLastError();
 }
 
@@ -627,7 +629,7 @@ static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* 
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.p_stot),
                      reinterpret_cast<float*>(ws + s.p_ztot), s.nchunk, 0,
-                     reinterpret_cast<uint16_t*>(ws + s.hbar), 1.f / (float)s.nbk);
+                     reinterpret_cast<uint16_t*>(ws + s.hbar), 1.f / (float)s.nbk, 0);
   return hipGetLastError();
 }
 
@@ -649,7 +651,7 @@ static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const v
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(cache + c.stot),
                      reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
-                     nullptr, 0.f);
+                     nullptr, 0.f, 0);
   return hipGetLastError();
 }
 
