@@ -47,7 +47,7 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // (bf16 hi + lo, [BH][npad][D]) and its column of the transposed value-sum table
 // ([BH][D][npad] f16) are written.
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
-__global__ __launch_bounds__(256, 2) void kv_summary_kernel(
+__global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
   constexpr int EPC = sizeof(T) == 2 ? 1 : 2;   // 16-byte loads per 8-element chunk
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LS];
-  __shared__ double pool_lds[RPP * D];
+  __shared__ double pool_lds[4 * D];          // per-wave block sums (rows folded by shuffles)
   __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
-  __shared__ double vpool_lds[PISA ? RPP * D : 1];
+  __shared__ double vpool_lds[PISA ? 4 * D : 1];
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
@@ -149,19 +149,30 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       }
     }
     {
-      const int cg = t % TPR, r = t / TPR;
+      // lanes lane ^ TPR, lane ^ 2 TPR, ... of a wave hold the same channels: fold them, then
+      // one partial per wave goes to LDS
+      const int cg = t % TPR;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pool_lds[r * D + cg * 8 + e] = pacc[e];
-      if constexpr (PISA) {
+      for (int o = TPR; o < 64; o <<= 1)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vpool_lds[r * D + cg * 8 + e] = vacc[e];
+        for (int e = 0; e < 8; ++e) {
+          pacc[e] += __shfl_xor(pacc[e], o, 64);
+          if constexpr (PISA) vacc[e] += __shfl_xor(vacc[e], o, 64);
+        }
+      if (lane < TPR) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pool_lds[w * D + cg * 8 + e] = pacc[e];
+        if constexpr (PISA) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vpool_lds[w * D + cg * 8 + e] = vacc[e];
+        }
       }
     }
     if (j + 1 < j1) load_block(j + 1);   // in flight during this block's compute
     __syncthreads();
     if (t < D) {
       double sm = 0.0;
-      for (int rr = 0; rr < RPP; ++rr) sm += pool_lds[rr * D + t];
+      for (int ww_ = 0; ww_ < 4; ++ww_) sm += pool_lds[ww_ * D + t];
       means[(j - j0) % kSummaryChunk][t] = sm / (double)nrows;
       if constexpr (PISA) {
         const double mean = sm / (double)nrows;
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         cent_hi[ci] = (uint16_t)(pack_bf16(hi, 0.f) & 0xffffu);
         cent_lo[ci] = (uint16_t)(pack_bf16((float)(mean - (double)hi), 0.f) & 0xffffu);
         double vs = 0.0;
-        for (int rr = 0; rr < RPP; ++rr) vs += vpool_lds[rr * D + t];
+        for (int ww_ = 0; ww_ < 4; ++ww_) vs += vpool_lds[ww_ * D + t];
         vsum[((size_t)bh * D + t) * npad + j] = (uint16_t)(f16_sat_pack((float)vs, 0.f) & 0xffffu);
       }
     }
