@@ -330,7 +330,7 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // query block by selection_bits_kernel; one 32-bit word per step of a window of up to
 // 32 * MAXW key blocks) into LDS, inverted over the valid key blocks, and steps in which
 // every query block of the tile selected every block are skipped. The summary slices of a step (CK rows of
-// CN bf16) are loaded straight into a CBUF-deep LDS ring, two steps ahead of their use.
+// CN bf16) are loaded straight into a CBUF-deep LDS ring, a pair of steps ahead of their use.
 // Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
 // reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
 // builds 4 B fragments (its bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64) void selection_bits_kernel(const int32_t* __res
 constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
 constexpr int CN = 128;    // summary columns per workgroup
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
-constexpr int CBUF = 3;    // steps in the LDS ring
+constexpr int CBUF = 4;    // steps in the LDS ring (two pairs)
 constexpr int MAXW = 30;   // bitmap words per query block and window (window <= 960 blocks)
 constexpr int RING_BYTES = CBUF * CK * CN * 2;
 
@@ -498,21 +498,13 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       const uint64_t rest = st >= 63 ? 0ull : occ & ~((2ull << st) - 1ull);
       return rest ? __builtin_ctzll(rest) : -1;
     };
-    int s_cur = occ ? __builtin_ctzll(occ) : -1;
-    int s_ld = s_cur;
-    stage(s_ld < 0 ? -1 : win0 + s_ld * CK, 0);
-    s_ld = s_ld < 0 ? -1 : next_after(s_ld);
-    stage(s_ld < 0 ? -1 : win0 + s_ld * CK, 1);
-    s_ld = s_ld < 0 ? -1 : next_after(s_ld);
-    barrier_vmem_n<0>();
-    int slot = 0;
-    while (s_cur >= 0) {
-      stage(s_ld < 0 ? -1 : win0 + s_ld * CK, slot == 0 ? 2 : slot - 1);
-      s_ld = s_ld < 0 ? -1 : next_after(s_ld);
-      const uint16_t* M = ring + slot * CK * CN;
+    // Occupied steps are taken in pairs, one barrier per pair: the pair after the current one
+    // loads into the other half of the 4-slot ring while the current pair is multiplied.
+    auto compute_step = [&](int sl, int st) __attribute__((always_inline)) {
+      const uint16_t* M = ring + sl * CK * CN;
       uint32_t word[2];
 #pragma unroll
-      for (int tq = 0; tq < 2; ++tq) word[tq] = bits[(64 * w + 32 * tq + l32) * WW + s_cur];
+      for (int tq = 0; tq < 2; ++tq) word[tq] = bits[(64 * w + 32 * tq + l32) * WW + st];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         u32x4 a[4];
@@ -525,9 +517,26 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
           for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = mfma_bf16(a[nt], b, acc[tq][nt]);
         }
       }
-      barrier_vmem_n<LPW>();   // the next step's slices have landed; its slot is free
-      s_cur = next_after(s_cur);
-      slot = slot == 2 ? 0 : slot + 1;
+    };
+    int s_cur = occ ? __builtin_ctzll(occ) : -1;
+    int s_cur2 = s_cur < 0 ? -1 : next_after(s_cur);
+    int s_ld = s_cur2 < 0 ? -1 : next_after(s_cur2);
+    int s_ld2 = s_ld < 0 ? -1 : next_after(s_ld);
+    stage(s_cur < 0 ? -1 : win0 + s_cur * CK, 0);
+    stage(s_cur2 < 0 ? -1 : win0 + s_cur2 * CK, 1);
+    barrier_vmem_n<0>();
+    int slot = 0;
+    while (s_cur >= 0) {
+      stage(s_ld < 0 ? -1 : win0 + s_ld * CK, slot ^ 2);
+      stage(s_ld2 < 0 ? -1 : win0 + s_ld2 * CK, (slot ^ 2) + 1);
+      compute_step(slot, s_cur);
+      if (s_cur2 >= 0) compute_step(slot + 1, s_cur2);
+      barrier_vmem_n<0>();   // the next pair has landed; this pair's slots are free
+      s_cur = s_ld;
+      s_cur2 = s_ld2;
+      s_ld = s_cur2 < 0 ? -1 : next_after(s_cur2);
+      s_ld2 = s_ld < 0 ? -1 : next_after(s_ld);
+      slot ^= 2;
     }
   }
   wait_vmem();   // no load into LDS outlives the workgroup
