@@ -254,19 +254,18 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   float m = kNegBig, l = 0.f;
   const float qk_scale = kLog2e / sqrtf((float)D);
 
-  // LDS DMA: piece u of wave w is 1 KB of the swizzled tile (elements 512 (KPW w + u) ..);
-  // lane l lands at element +8 l, i.e. row r, physical chunk p, so it fetches the logical
-  // chunk that the swizzle puts there.
-  uint32_t koff[DMA ? KPW : 1], voff[DMA ? KPW : 1];
+  // LDS DMA: wave w moves the 1-KB pieces p = KPW w .. KPW w + KPW - 1 of the swizzled tile
+  // (elements 512 p ..), each lane the logical chunk that the swizzle puts where it lands.
+  // Lane l lands at element 512 p + 8 l of piece p: row 512 p / D + l / CH, physical chunk
+  // l % CH. Its source offset is p KB plus a lane part (V), or p KB plus a lane part XORed
+  // with a constant of the piece (K at d = 128, whose chunk swizzle sees the low bits of the
+  // piece's first row), so two lane registers serve every piece.
+  uint32_t klane = 0, vlane = 0;
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
   if constexpr (DMA) {
-#pragma unroll
-    for (int u = 0; u < KPW; ++u) {
-      const int e = (wv * KPW + u) * 512 + lane * 8;
-      const int r = e / D, pch = (e % D) / 8;
-      koff[u] = (uint32_t)(r * D * 2 + ((pch ^ r) & (CH - 1)) * 16);
-      voff[u] = (uint32_t)(r * D * 2 + ((pch ^ swzv_f<D>(r)) & (CH - 1)) * 16);
-    }
+    const int lr = lane / CH, pc = lane % CH;
+    klane = (uint32_t)(lr * D * 2 + ((pc ^ lr) & (CH - 1)) * 16);
+    vlane = (uint32_t)(lr * D * 2 + ((pc ^ swzv_f<D>(lr)) & (CH - 1)) * 16);
   }
   // j < 0: an absent tile; the loads then cover an empty range (no memory access) so that
   // every step issues the same number of loads, which the vmcnt waits below rely on.
@@ -275,13 +274,20 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
     const uint32_t bytes = j < 0 ? 0u : (uint32_t)(min(kBlock, a.nkv - row0) * D * 2);
     const auto r = make_rsrc(kb + (size_t)row0 * D, bytes);
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) load_lds16(r, lds_addr(slot) + (wvs * KPW + u) * 1024, koff[u]);
+    for (int u = 0; u < KPW; ++u) {
+      const int pp = wvs * KPW + u;
+      const uint32_t xo = D == 128 ? (uint32_t)((pp & 3) << 6) : 0u;
+      load_lds16(r, lds_addr(slot) + pp * 1024, (uint32_t)(pp * 1024) + (klane ^ xo));
+    }
   };
   auto stage_v = [&](int j, uint16_t* slot) __attribute__((always_inline)) {
     const int row0 = j < 0 ? 0 : j * kBlock;
     const auto r = make_rsrc(vb + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D * 2));
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) load_lds16(r, lds_addr(slot) + (wvs * KPW + u) * 1024, voff[u]);
+    for (int u = 0; u < KPW; ++u) {
+      const int pp = wvs * KPW + u;
+      load_lds16(r, lds_addr(slot) + pp * 1024, (uint32_t)(pp * 1024) + vlane);
+    }
   };
 
   // Register path (fp32 inputs): rows beyond n_kv read row n_kv-1; their logits are masked

@@ -176,6 +176,14 @@ def _sampled_check(sla, x, blocks_per_head=3, heads=None, seed=0):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_grouped_launch_ragged_group(sla, d):
+    """Enough query blocks that neighbouring blocks share a workgroup (133 blocks per head:
+    the last group holds one active block), checked on sampled blocks incl. the last."""
+    x = make_custom(1, 12, 64 * 132 + 30, 1500, d, 5, dtype="bf16", kind="smooth", seed=40 + d)
+    _sampled_check(sla, x, blocks_per_head=3, heads=[(0, 0), (0, 11)])
+
+
 def test_tiny_workload(sla):
     x = make_inputs("tiny")
     out, idx = run_forward(sla, x)

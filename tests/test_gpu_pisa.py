@@ -62,6 +62,25 @@ def test_pisa_small(sla, B, H, nq, nkv, d, top_k, dtype, kind):
     assert err <= TOL
 
 
+def test_pisa_grouped_launch(sla):
+    """133 query blocks per head, so neighbouring blocks share a workgroup and the last
+    group holds one active block; checked on sampled blocks incl. the last."""
+    x = make_custom(1, 12, 64 * 132 + 30, 1500, 128, 5, dtype="bf16", kind="smooth", seed=93)
+    p = x.problem
+    out, idx = run(sla, x)
+    check_masks(idx, so.route_full(x), p.top_k)
+    blocks = [0, 67, p.nbq - 1]
+    rws = np.concatenate([np.arange(i * 64, min(i * 64 + 64, p.n_q)) for i in blocks])
+    refs, gots = [], []
+    for hh in (0, 11):
+        ref, _ = oracle_pisa(x, heads=[(0, hh)], rows=rws)
+        refs.append(ref[0, hh, rws])
+        gots.append(out[0, hh, rws])
+    err, _ = max_err_over_rms(np.concatenate(gots), np.concatenate(refs))
+    print(f"pisa grouped: max-abs/rms {err:.3e}")
+    assert err <= TOL
+
+
 @pytest.mark.parametrize("top_k", [0, 11])
 def test_pisa_degenerate_counts(sla, top_k):
     """top_k = 0 (every block through the tail) and top_k = all 11 blocks (dense attention,
