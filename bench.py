@@ -78,10 +78,10 @@ def work(p, fp8=False):
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(x, n_heads_sample=4):
-    """The oracle, as it stands, on a bounded sample: n complete heads of the workload;
-    scaled to the whole workload (all heads) in ms."""
-    import numpy as np
+def cpu_baseline(x, min_seconds=10.0):
+    """The oracle, as it stands, on a bounded sample: complete (batch, head) pairs in turn
+    until at least ``min_seconds`` of CPU work (or the whole workload) is done; scaled to
+    all pairs, in ms."""
     from oracle import sla_oracle as so
     try:
         import threadpoolctl
@@ -89,15 +89,18 @@ def cpu_baseline(x, n_heads_sample=4):
     except Exception:   # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
     p = x.problem
-    pairs = [(b, h) for b in range(p.batch) for h in range(p.heads)][:n_heads_sample]
+    pairs = [(b, h) for b in range(p.batch) for h in range(p.heads)]
+    done = 0
     t0 = time.perf_counter()
-    so.forward(x, heads=pairs)
+    while done < len(pairs) and (done == 0 or time.perf_counter() - t0 < min_seconds):
+        so.forward(x, heads=[pairs[done]])
+        done += 1
     dt = time.perf_counter() - t0
-    total = p.batch * p.heads
-    return {"value": dt * 1e3 * total / len(pairs), "unit": "ms", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(pairs)} of {total} (batch, head) pairs computed in full "
-                      f"({dt:.1f} s), scaled to all pairs"}
+    total = len(pairs)
+    what = ("the whole workload" if done == total else
+            f"{done} of {total} (batch, head) pairs computed in full, scaled to all pairs")
+    return {"value": dt * 1e3 * total / done, "unit": "ms", "cores": int(threads),
+            "kind": "oracle", "sample": f"{what} ({dt:.1f} s)"}
 
 
 # --------------------------------------------------------------------------- traffic summary
@@ -110,6 +113,11 @@ def read_traffic(workload):
     if rec.get("source_sha256") != sources_sha(SPARSE_SOURCES):
         return None          # the kernel changed since the counters were taken
     return rec.get("traffic_bytes_per_launch")
+
+
+def short_name(name):
+    """Kernel name without the return type, anonymous namespace and parameter list."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
 
 
 def summarize_pmc(fetch_dir, write_dir, workload):
@@ -153,8 +161,8 @@ def summarize_pmc(fetch_dir, write_dir, workload):
         "fetch_scale": sf, "write_scale": sw,
         "traffic_bytes_per_launch": (sp_f * 1024 / sf + sp_w * 1024 / sw)
         if (sp_f and sp_w and sf and sw) else None,
-        "per_kernel_fetch_kib": {k.split("(")[0][-60:]: sum(v) / len(v) for k, v in f.items()},
-        "per_kernel_write_kib": {k.split("(")[0][-60:]: sum(v) / len(v) for k, v in w.items()},
+        "per_kernel_fetch_kib": {short_name(k): sum(v) / len(v) for k, v in f.items()},
+        "per_kernel_write_kib": {short_name(k): sum(v) / len(v) for k, v in w.items()},
     }
     path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
     with open(path, "w") as fh:
@@ -172,7 +180,7 @@ def summarize_trace(d, out, command):
              f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'total_%':>8s}"]
     for r in rows:
         name = r.get("Name", "")
-        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")[:70]
+        short = short_name(name)[:70]
         lines.append(f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['Percentage']):8.2f}")
     with open(out, "w") as f:

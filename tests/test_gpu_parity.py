@@ -184,6 +184,14 @@ def test_grouped_launch_ragged_group(sla, d):
     _sampled_check(sla, x, blocks_per_head=3, heads=[(0, 0), (0, 11)])
 
 
+def test_single_block_groups_many_workgroups(sla):
+    """640 query blocks in all (below the grouping threshold, so one query block per
+    workgroup): more workgroups than the GPU holds at once, bf16 and fp32 inputs."""
+    for dtype in ("bf16", "f32"):
+        x = make_custom(1, 8, 64 * 80 - 20, 512, 128, 3, dtype=dtype, kind="smooth", seed=47)
+        _sampled_check(sla, x, blocks_per_head=3, heads=[(0, 1), (0, 7)])
+
+
 def test_tiny_workload(sla):
     x = make_inputs("tiny")
     out, idx = run_forward(sla, x)
