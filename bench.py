@@ -8,7 +8,10 @@ the fused linear apply and mix) over the workload's synthetic inputs, which are 
 HBM before timing starts. Prints ONE JSON line with the latency, the roofline of the
 dominant kernel (the sparse-attention kernel, timed with HIP events that the library
 records around it on the same stream), the dense-attention baseline on the same GPU and
-the CPU oracle baseline.
+the CPU oracle baseline. Outside the timed region it also reports the per-step spread
+(p10 / median / p90) of the timed forwards and of K more forwards each preceded by a 512 MB
+write that evicts L2 and the MALL (cold caches), and what the GPU reaches on a 1 GiB copy
+and an 8192^3 bf16 GEMM (achievable peaks next to the published ones).
 
 Other modes:
     --profile            only warm-up + K plain forward calls and a 1 GiB copy (short runs
@@ -41,6 +44,7 @@ PEAK_HBM = 8.0e12
 SPARSE_SOURCES = ["sparse_linear_hybrid_amd/csrc/sparse.hip", "sparse_linear_hybrid_amd/csrc/common.h"]
 TRAFFIC_FILE = "profiles/sparse_attn_{workload}_traffic.json"
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 512 << 20      # written before each cold-cache step: more than L2 + MALL
 
 
 def sources_sha(paths) -> str:
@@ -75,6 +79,43 @@ def work(p, fp8=False):
     return {"pairs": pairs, "sparse_flops": sparse_flops, "kv_summary_bytes": kv_bytes,
             "dense_flops": dense_flops, "sparse_peak": sparse_flops / floor_s,
             "quant_bytes": quant_bytes}
+
+
+# --------------------------------------------------------------------------- measured peaks
+def spread(vals):
+    """p10 / median / p90 of a list of per-step times (ms)."""
+    import numpy as np
+    v = np.asarray(vals, dtype=np.float64)
+    return {"p10": float(np.percentile(v, 10)), "median": float(np.median(v)),
+            "p90": float(np.percentile(v, 90))}
+
+
+def achievable_peaks(torch, dev):
+    """What this GPU reaches in practice: a 1 GiB device-to-device copy (bytes read plus
+    written per second) and an 8192^3 bf16 GEMM through torch (dense MFMA work)."""
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 5)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    t_mm = timed(lambda: torch.mm(a, b), 5)
+    del a, b
+    return {"copy_GBps": 2 * COPY_BYTES / t_copy / 1e9,
+            "bf16_gemm_TFLOPs": 2 * n ** 3 / t_mm / 1e12,
+            "how": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.mm"}
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -287,6 +328,10 @@ def main():
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache pass (512 MB written before each forward)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy and GEMM peaks")
     ap.add_argument("--cached", action="store_true",
                     help="time sla_forward_cached against a prebuilt key/value summary cache "
                          "(the decode path); the cache build is timed separately")
@@ -388,6 +433,25 @@ def main():
     stage_ms = {name: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
                                      for s in range(K)]))
                 for i, name in enumerate(sla.STAGES)}
+    # per-step GPU time of the timed forwards: first stage's start to last stage's end
+    warm_steps = [evs[s][0].elapsed_time(evs[s][2 * nst - 1]) for s in range(K)]
+
+    # Cold caches (outside the timed region): before each of K forwards, 512 MB are written,
+    # which evicts L2 and the 256 MB MALL, so the inputs come from HBM.
+    cold_steps = None
+    if not args.no_cold:
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(K)]
+        for s in range(K):
+            flush.fill_(float(s))
+            marks[s][0].record()
+            fwd()
+            marks[s][1].record()
+        torch.cuda.synchronize()
+        cold_steps = [a.elapsed_time(b) for a, b in marks]
+        del flush
+    peaks = None if args.no_peaks else achievable_peaks(torch, dev)
 
     w = work(p, fp8)
     sparse_s = stage_ms["sparse"] * 1e-3
@@ -398,11 +462,19 @@ def main():
                 "kernel": "sparse_attn_fp8_kernel" if fp8 else "sparse_attn_kernel",
                 "flops_per_launch": w["sparse_flops"],
                 "avg_launch_ms": stage_ms["sparse"]}
+    if peaks and not fp8:
+        roofline["achievable_peak"] = peaks["bf16_gemm_TFLOPs"]
+        roofline["frac_of_achievable"] = achieved / 1e12 / peaks["bf16_gemm_TFLOPs"]
     kernels = {
         "stage_ms": stage_ms,
         "kv_summary_GBps": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / 1e9,
         "kv_summary_hbm_frac": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM,
+        "step_ms_warm": spread(warm_steps),
+        "step_ms_cold": spread(cold_steps) if cold_steps else None,
+        "achievable": peaks,
     }
+    if peaks:
+        kernels["kv_summary_frac_of_copy"] = kernels["kv_summary_GBps"] / peaks["copy_GBps"]
     if fp8:
         kernels["quant_GBps"] = w["quant_bytes"] / (stage_ms["quant"] * 1e-3) / 1e9
     if pisa:

@@ -3,7 +3,8 @@
 Checked: graph capture of each forward replays bit-identically to the eager call (several
 replays, with eager library work and synchronisations between them; the library records
 no memset nodes); forwards on two caller streams at once give the results each gives
-alone; the profiled entry point writes exactly what the plain one writes, for every variant.
+alone; the profiled entry point writes exactly what the plain one writes, for every variant;
+junk in one head does not reach another head's output (ragged last blocks).
 """
 import ctypes
 
@@ -132,3 +133,27 @@ def test_profiled_matches_plain(sla, variant):
     assert torch.equal(prof, plain)
     times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(sla.STAGES))]
     assert all(np.isfinite(times)) and min(times) >= 0.0
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_heads_are_isolated_with_ragged_blocks(sla, variant):
+    """Ragged last blocks (n_q = 200, n_kv = 130): in memory, the rows after a head's last
+    token are the next head's. Replacing one head's Q, K and V by large finite junk must leave
+    the other head's output unchanged bit for bit (each head in turn)."""
+    dev = torch.device("cuda")
+    x = make_custom(1, 2, 200, 130, 128, 2, dtype="bf16", kind="normal", seed=61)
+    t = to_device(x)
+    call, out = runner(sla, variant, dev, 2)(t)
+    call()
+    torch.cuda.synchronize()
+    base = out.clone()
+    gen = torch.Generator().manual_seed(7)
+    for h_junk, h_keep in ((1, 0), (0, 1)):
+        q, k, v = (a.clone() for a in t[:3])
+        for a in (q, k, v):
+            junk = torch.randn(a[0, h_junk].shape, generator=gen) * 300.0
+            a[0, h_junk] = junk.to(dtype=a.dtype, device=dev)
+        call2, out2 = runner(sla, variant, dev, 2)((q, k, v) + tuple(t[3:]))
+        call2()
+        torch.cuda.synchronize()
+        assert torch.equal(out2[0, h_keep], base[0, h_keep]), (variant, h_keep)

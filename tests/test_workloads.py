@@ -17,6 +17,28 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(bf16_bits_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
 
 
+def test_bf16_rounding_exhaustive():
+    """Every finite bf16 value converts back to itself; the exact midpoint between two
+    neighbours rounds to the one with an even last bit, and one float32 ulp either side of it
+    rounds to the nearer neighbour (round to nearest, ties to even)."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    exp_all_ones = (bits & 0x7F80) == 0x7F80
+    finite = bits[~exp_all_ones]
+    f = (finite << 16).view(np.float32)
+    assert np.array_equal(bf16_round_bits(f), finite.astype(np.uint16))
+    # midpoints between finite neighbours of the same sign (the successor of the largest
+    # finite value is infinity, which is not a neighbour here)
+    lo = finite[((finite + 1) & 0x7F80) != 0x7F80]
+    lo = lo[(lo & 0x7FFF) != 0x7FFF]
+    mid = ((lo << 16) + 0x8000).view(np.float32)
+    even = np.where(lo & 1, lo + 1, lo).astype(np.uint16)
+    assert np.array_equal(bf16_round_bits(mid), even)
+    below = ((lo << 16) + 0x7FFF).view(np.float32)
+    above = ((lo << 16) + 0x8001).view(np.float32)
+    assert np.array_equal(bf16_round_bits(below), lo.astype(np.uint16))
+    assert np.array_equal(bf16_round_bits(above), (lo + 1).astype(np.uint16))
+
+
 def test_tiny_is_deterministic_and_shaped():
     a = make_inputs("tiny")
     b = make_inputs("tiny")
