@@ -330,7 +330,8 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // query block by selection_bits_kernel; one 32-bit word per step of a window of up to
 // 32 * MAXW key blocks) into LDS, inverted over the valid key blocks, and steps in which
 // every query block of the tile selected every block are skipped. The summary slices of a step (CK rows of
-// CN bf16) are loaded straight into a CBUF-deep LDS ring, a pair of steps ahead of their use.
+// CN bf16) are loaded straight into a CBUF-deep LDS ring, two pairs of steps ahead of their
+// use.
 // Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
 // reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
 // builds 4 B fragments (its bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a
@@ -358,7 +359,7 @@ __global__ __launch_bounds__(64) void selection_bits_kernel(const int32_t* __res
 constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
 constexpr int CN = 128;    // summary columns per workgroup
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
-constexpr int CBUF = 4;    // steps in the LDS ring (two pairs)
+constexpr int CBUF = 6;    // steps in the LDS ring (three pairs)
 constexpr int MAXW = 30;   // bitmap words per query block and window (window <= 960 blocks)
 constexpr int RING_BYTES = CBUF * CK * CN * 2;
 
@@ -498,8 +499,9 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       const uint64_t rest = st >= 63 ? 0ull : occ & ~((2ull << st) - 1ull);
       return rest ? __builtin_ctzll(rest) : -1;
     };
-    // Occupied steps are taken in pairs, one barrier per pair: the pair after the current one
-    // loads into the other half of the 4-slot ring while the current pair is multiplied.
+    // Occupied steps are taken in pairs, one barrier per pair: while a pair is multiplied, the
+    // pair two ahead loads into the slots of the pair before it (6-slot ring), so every load
+    // has two pairs' time to land.
     auto compute_step = [&](int sl, int st) __attribute__((always_inline)) {
       const uint16_t* M = ring + sl * CK * CN;
       uint32_t word[2];
@@ -518,25 +520,27 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
         }
       }
     };
-    int s_cur = occ ? __builtin_ctzll(occ) : -1;
-    int s_cur2 = s_cur < 0 ? -1 : next_after(s_cur);
-    int s_ld = s_cur2 < 0 ? -1 : next_after(s_cur2);
-    int s_ld2 = s_ld < 0 ? -1 : next_after(s_ld);
-    stage(s_cur < 0 ? -1 : win0 + s_cur * CK, 0);
-    stage(s_cur2 < 0 ? -1 : win0 + s_cur2 * CK, 1);
-    barrier_vmem_n<0>();
+    // the next six occupied steps (-1: none); st[0], st[1] is the pair being multiplied
+    int st[6];
+    st[0] = occ ? __builtin_ctzll(occ) : -1;
+#pragma unroll
+    for (int u = 1; u < 6; ++u) st[u] = st[u - 1] < 0 ? -1 : next_after(st[u - 1]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) stage(st[u] < 0 ? -1 : win0 + st[u] * CK, u);
+    barrier_vmem_n<2 * LPW>();   // the first pair has landed (the second may be in flight)
     int slot = 0;
-    while (s_cur >= 0) {
-      stage(s_ld < 0 ? -1 : win0 + s_ld * CK, slot ^ 2);
-      stage(s_ld2 < 0 ? -1 : win0 + s_ld2 * CK, (slot ^ 2) + 1);
-      compute_step(slot, s_cur);
-      if (s_cur2 >= 0) compute_step(slot + 1, s_cur2);
-      barrier_vmem_n<0>();   // the next pair has landed; this pair's slots are free
-      s_cur = s_ld;
-      s_cur2 = s_ld2;
-      s_ld = s_cur2 < 0 ? -1 : next_after(s_cur2);
-      s_ld2 = s_ld < 0 ? -1 : next_after(s_ld);
-      slot ^= 2;
+    while (st[0] >= 0) {
+      const int ls = slot == 0 ? 4 : slot - 2;   // the slots of the previous pair
+      stage(st[4] < 0 ? -1 : win0 + st[4] * CK, ls);
+      stage(st[5] < 0 ? -1 : win0 + st[5] * CK, ls + 1);
+      compute_step(slot, st[0]);
+      if (st[1] >= 0) compute_step(slot + 1, st[1]);
+      barrier_vmem_n<2 * LPW>();   // the next pair has landed; this pair's slots are free
+#pragma unroll
+      for (int u = 0; u < 4; ++u) st[u] = st[u + 2];
+      st[4] = st[3] < 0 ? -1 : next_after(st[3]);
+      st[5] = st[4] < 0 ? -1 : next_after(st[4]);
+      slot = slot == 4 ? 0 : slot + 2;
     }
   }
   wait_vmem();   // no load into LDS outlives the workgroup
@@ -704,7 +708,14 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
   if (s.k < s.nbk)   // (k = 0: all-zero rows)
     hipLaunchKernelGGL(selection_bits_kernel, dim3(s.nbq, s.BH), dim3(64), 0, st, idx, bits,
                        s.nbq, s.k, s.nwords);
+  hipError_t err = hipSuccess;
   auto go = [&](auto kern, auto zkern) {
+    // more than 64 KB of dynamic LDS (wide windows) has to be allowed per kernel
+    if (lds > 65536) {
+      err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return;
+    }
     hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, s.nwords,
                        reinterpret_cast<const uint16_t*>(ws + s.sblk),
                        reinterpret_cast<const float*>(ws + s.stot),
@@ -716,7 +727,7 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
   };
   if (s.D == 128) go(complement_kernel<128>, complement_z_kernel<128>);
   else go(complement_kernel<64>, complement_z_kernel<64>);
-  return hipGetLastError();
+  return err != hipSuccess ? err : hipGetLastError();
 }
 
 }  // namespace sla
