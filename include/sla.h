@@ -22,6 +22,9 @@
  *     Q is [batch, heads, n_q, head_dim]; K and V are [batch, heads, n_kv, head_dim];
  *     O is [batch, heads, n_q, head_dim]; the channel index is the fastest.
  *   - Q, K, V have element type in_dtype (bf16 or f32); O has out_dtype.
+ *   - Range: the exact (sparse) branch multiplies the softmax weights, held in f16 in
+ *     [0, 256], with an f16 copy of V, so entries of V beyond +-65504 saturate there; the
+ *     piecewise forward's per-block value sums (64 tokens each) are f16 as well.
  *   - proj_q, proj_k: f32 [head_dim (in), head_dim (out)], shared by all batches and heads;
  *     the pooled row vector x is mapped to x @ proj.
  *   - alpha: f32 [heads, head_dim], values expected in [0, 1].
