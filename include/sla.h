@@ -190,7 +190,7 @@ typedef enum {
   SLA_WS_HBAR = 9,      /* bf16 H_bar^T [B*H][d(value channel)][d(key channel)]      */
   SLA_WS_CENT_HI = 10,  /* bf16 centroids, rounded  [B*H][npad][d]                   */
   SLA_WS_CENT_LO = 11,  /* bf16 centroid minus its rounded value [B*H][npad][d]      */
-  SLA_WS_VSUM = 12      /* f16 value sums of the key blocks, [B*H][d][npad]         */
+  SLA_WS_VSUM = 12      /* f16 value sums of the key blocks, [B*H][npad][d]         */
 } sla_ws_region;
 
 /* Byte offset and size of a workspace region for problem p in the layout of `variant`

@@ -122,6 +122,47 @@ __device__ __forceinline__ void barrier_vmem_n() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// ----------------------------------------------------------------------------- tile layout
+// 64-row tiles of D 16-bit columns in LDS (attention K and V tiles, centroid and value-sum
+// tiles), shared by the exact branch and the piecewise tail.
+// Element offset of (row, col) in a swizzled LDS tile with D 16-bit columns per row: the
+// 16-byte chunk index is XORed with the row (mod chunks per row).
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int CH = D / 8;
+  return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
+}
+
+// Swizzle of the V tile. A transposing V^T read has each group of 16 lanes touch 4
+// consecutive key rows x 2 adjacent chunks (and each 32 lanes 4 rows x 4 chunks); XORing
+// the chunk index with f(row % 4) spreads those accesses over distinct banks whether the LDS
+// serves 128 or 256 bytes per clock. Rows are bijective, so the row-wise tile writes stay
+// conflict-free as well.
+template <int D>
+__device__ __forceinline__ int swzv_f(int row) {
+  const int r = row & 3;
+  return D == 128 ? (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) : 2 * r;
+}
+template <int D>
+__device__ __forceinline__ int swzv(int row, int col) {
+  constexpr int CH = D / 8;
+  return row * D + ((((col >> 3) ^ swzv_f<D>(row)) & (CH - 1)) << 3) + (col & 7);
+}
+
+// P^T-matched V^T fragment from a swizzled row-major [key][channel] tile: lane row (channel)
+// x0 + lane%32; reduction slot e holds key k0 + 4h + e (e < 4) or k0 + 8 + 4h + (e - 4)
+// (e >= 4), h = lane / 32.
+template <int D>
+__device__ __forceinline__ u32x4 vt_frag(const uint16_t* M, int x0, int k0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 4 * (g >> 1) + (L >> 2);
+  const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
+  const u32x2 lo = lds_read_tr16(M + swzv<D>(row, col));
+  const u32x2 hi = lds_read_tr16(M + swzv<D>(row + 8, col));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Exchange with lane l ^ 32: returns the value held by the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) {
   uint32_t u = __float_as_uint(x);
@@ -161,7 +202,7 @@ struct Plan {
   int npad;                                     // key blocks rounded up to whole 64-tiles
   size_t p_spart, p_zpart, p_stot, p_ztot;      // chunk partials and totals of H
   size_t cent_hi, cent_lo;                      // centroids, bf16 hi + lo [BH][npad][D]
-  size_t vsum;                                  // value sums, f16 [BH][D][npad]
+  size_t vsum;                                  // value sums, f16 [BH][npad][D]
   size_t hbar;                                  // bf16 H_bar^T [BH][D(c)][D(r)]
   size_t tail_m, tail_d, tail_a, tail_n;        // tail state per query row
   size_t total_pisa;

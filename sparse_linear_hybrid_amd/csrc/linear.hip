@@ -44,8 +44,8 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // PISA (piecewise forward, PISA page, core algorithm; needs BLOCKS): the MFMA product uses
 // the keys centred on their block mean instead of phi(K), so the partial totals add up
 // H_j = sum_n (k_n - k_bar_j)^T v_n; no S_j or z_j is stored; instead each block's centroid
-// (bf16 hi + lo, [BH][npad][D]) and its column of the transposed value-sum table
-// ([BH][D][npad] f16) are written.
+// (bf16 hi + lo, [BH][npad][D]) and its row of the value-sum table ([BH][npad][D] f16) are
+// written.
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
 __global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_ker
         cent_lo[ci] = (uint16_t)(pack_bf16((float)(mean - (double)hi), 0.f) & 0xffffu);
         double vs = 0.0;
         for (int ww_ = 0; ww_ < 4; ++ww_) vs += vpool_lds[ww_ * D + t];
-        vsum[((size_t)bh * D + t) * npad + j] = (uint16_t)(f16_sat_pack((float)vs, 0.f) & 0xffffu);
+        vsum[((size_t)bh * npad + j) * D + t] = (uint16_t)(f16_sat_pack((float)vs, 0.f) & 0xffffu);
       }
     }
     if constexpr (PISA) __syncthreads();   // block means are read by every wave below

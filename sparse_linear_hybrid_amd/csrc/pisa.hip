@@ -7,14 +7,18 @@
 // The exact branch adds its routed blocks and the global first-order term tau (q H_bar) A_U
 // and normalises the sum once (sparse.hip, piecewise epilogue).
 //
-// A workgroup of 4 waves covers 2 query blocks (wave w: rows 32 (w % 2) .. +31 of query
-// block w / 2). The centroids are walked in tiles of 64 staged through LDS, computed
-// transposed like the exact branch, one 32-centroid half at a time (the running max is
-// updated per half):
+// A workgroup of 8 waves covers 4 query blocks (wave w: rows 32 (w % 2) .. +31 of query
+// block w / 2). The centroid tiles (64 centroids each) are walked in order through LDS rings
+// filled by loads straight into LDS, pipelined like the exact branch: step s multiplies tile
+// s while the value sums of tile s + 1 and the centroids of tile s + 2 load, and one barrier
+// per step releases the slots (centroid ring: 3 slots of hi + lo tiles; value-sum ring: 2).
+// Each tile is computed transposed, in two 32-centroid halves whose MFMA chains interleave
+// with the other half's softmax:
 //   S^T (32 centroids x 32 queries) = K_bar Q^T    bf16 MFMA 32x32x16, K_bar as hi + lo
 //   O^T (D x 32 queries)          += Vsum^T P^T    f16 MFMA 32x32x16
-// D_U and A_U are register sums of the f16-rounded weights that enter the product (n_j = 64
-// except for a partial last block).
+// The running max may lag the true one while the weights stay below 2^8 (f16). D_U and A_U
+// are register sums of the f16-rounded weights that enter the product (n_j = 64 except for a
+// partial last block). A wave skips a tile whose every centroid is routed to its query block.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,20 +34,13 @@ struct TailArgs {
   const int32_t* idx;            // [BH][nbq][topk], ascending
   const uint16_t* cent_hi;       // bf16 [BH][npad][D]
   const uint16_t* cent_lo;
-  const uint16_t* vsum;          // f16 [BH][D][npad]
+  const uint16_t* vsum;          // f16 [BH][npad][D]
   float* tail_m;                 // [BH][nbq * 64]
   float* tail_d;
   float* tail_a;
   float* tail_n;                 // [BH][nbq * 64][D]
   int nq, nbq, nbk, npad, topk, ngroups, nlast;   // nlast: valid tokens of the last key block
 };
-
-// Swizzled offset of (row, col) in a 64 x D bf16 centroid tile: 16-byte chunk index XOR row.
-template <int D>
-__device__ __forceinline__ int cswz(int row, int col) {
-  constexpr int CH = D / 8;
-  return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
-}
 
 template <typename T>
 __device__ __forceinline__ void load_q8(const T* p, u32x4& hi, u32x4& lo) {
@@ -63,42 +60,48 @@ __device__ __forceinline__ void load_q8(const T* p, u32x4& hi, u32x4& lo) {
   }
 }
 
+constexpr int kTailGroup = 4;                  // query blocks per workgroup
+constexpr float kTailSlack = 8.0f;             // keep a stale max while the weights <= 2^8
+
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void pisa_tail_kernel(TailArgs a) {
+__global__ __launch_bounds__(128 * kTailGroup, 2) void pisa_tail_kernel(TailArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 queries: hi + lo bf16 parts
+  constexpr int QG = kTailGroup;
+  constexpr int NW = 2 * QG;               // waves
   constexpr int KS = D / 16;
   constexpr int CT = D / 32;
   constexpr int CH = D / 8;
-  constexpr int VR = 64 + 4;               // Vsum^T LDS row: 136 bytes (8-byte reads spread)
-  constexpr int KCPT = 64 * CH / 256;      // 16-byte centroid chunks per thread per array
-  constexpr int VCPT = D * 8 / 256;        // 16-byte value-sum chunks per thread
-  static_assert(64 * CH % 256 == 0 && D * 8 % 256 == 0, "tile staging split");
-  __shared__ __attribute__((aligned(16))) uint16_t khi[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t klo[64 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vx[D * VR];
-  __shared__ uint32_t bits[2][kMaxKeyBlocks / 32];
+  constexpr int TILE = 64 * D;             // elements of one 64-row tile
+  constexpr int TP = TILE * 2 / 1024;      // 1-KB pieces of a tile
+  constexpr int KPW = TP / NW;             // pieces of each tile array per wave
+  static_assert(KPW * NW == TP, "tile pieces split evenly over the waves");
+  // centroid ring: slot s holds hi at 2 s TILE and lo at (2 s + 1) TILE; value sums after it
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(3 * 2 + 2) * TILE];
+  __shared__ uint32_t bits[QG][kMaxKeyBlocks / 32];
 
   const int bh = blockIdx.x / a.ngroups, grp = blockIdx.x % a.ngroups;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
   const int qb = wv >> 1;
-  const int iq = grp * 2 + qb;
+  const int iq = grp * QG + qb;
   const bool active = iq < a.nbq;
   const int qrow0 = iq * kBlock + 32 * (wv & 1);
   const int nwords = a.npad / 32;
 
   // routed-block bitmap of each query block; centroid slots past nbk are marked as well
-  for (int i = t; i < 2 * nwords; i += 256) bits[i / nwords][i % nwords] = 0u;
+  for (int i = t; i < QG * nwords; i += NW * 64) bits[i / nwords][i % nwords] = 0u;
   __syncthreads();
-  for (int b = 0; b < 2; ++b) {
-    const int ib = grp * 2 + b;
+  for (int b = 0; b < QG; ++b) {
+    const int ib = grp * QG + b;
     if (ib >= a.nbq) continue;
     const int32_t* sel = a.idx + ((size_t)bh * a.nbq + ib) * a.topk;
-    for (int i = t; i < a.topk; i += 256) {
+    for (int i = t; i < a.topk; i += NW * 64) {
       const int j = sel[i];
       atomicOr(&bits[b][j >> 5], 1u << (j & 31));
     }
-    for (int j = a.nbk + t; j < a.npad; j += 256) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
+    for (int j = a.nbk + t; j < a.npad; j += NW * 64) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
   }
+  __syncthreads();   // the bitmap is complete (its LDS atomics have finished)
 
   // Q^T fragments (B operand): lane column q = qrow0 + l32, channels 16 s + 8 h .. +7
   u32x4 qf[KS], ql[SPLIT ? KS : 1];
@@ -115,53 +118,45 @@ __global__ __launch_bounds__(256, 2) void pisa_tail_kernel(TailArgs a) {
     }
   }
 
-  // tile staging: global -> registers -> LDS; centroid rows and value columns past nbk are
-  // zeroed (their memory is allocated but never written)
+  // Loads into LDS: piece p (1 KB, elements 512 p ..) of a tile; wave w moves pieces
+  // KPW w .. KPW w + KPW - 1 of each array. Lane l lands at row 512 p / D + l / CH, physical
+  // chunk l % CH, and fetches the logical chunk the swizzle puts there; the offset is p KB
+  // plus a lane part (value sums), or p KB plus a lane part XORed with a constant of the
+  // piece (centroids at d = 128, whose chunk swizzle sees the low bits of the first row).
+  // Rows past nbk read as zero (the buffer bound); j < 0: an empty range, so that every step
+  // issues the same number of loads.
+  uint32_t klane, vlane;
+  {
+    const int lr = lane / CH, pc = lane % CH;
+    klane = (uint32_t)(lr * D * 2 + ((pc ^ lr) & (CH - 1)) * 16);
+    vlane = (uint32_t)(lr * D * 2 + ((pc ^ swzv_f<D>(lr)) & (CH - 1)) * 16);
+  }
   const uint16_t* chb = a.cent_hi + (size_t)bh * a.npad * D;
   const uint16_t* clb = a.cent_lo + (size_t)bh * a.npad * D;
-  const uint16_t* vxb = a.vsum + (size_t)bh * D * a.npad;
-  u32x4 rh[KCPT], rl[KCPT], rv[VCPT];
-  auto load_tile = [&](int j0) __attribute__((always_inline)) {
+  const uint16_t* vxb = a.vsum + (size_t)bh * a.npad * D;
+  auto tile_bytes = [&](int j) -> uint32_t {
+    return j < 0 ? 0u : (uint32_t)(min(kBlock, a.nbk - j * kBlock) * D * 2);
+  };
+  auto stage_k = [&](int j, int slot) __attribute__((always_inline)) {
+    const size_t row0 = (size_t)(j < 0 ? 0 : j) * kBlock * D;
+    const auto rh = make_rsrc(chb + row0, tile_bytes(j));
+    const auto rl = make_rsrc(clb + row0, tile_bytes(j));
+    const uint32_t dh = lds_addr(smem + 2 * slot * TILE), dl = lds_addr(smem + (2 * slot + 1) * TILE);
 #pragma unroll
-    for (int u = 0; u < KCPT; ++u) {
-      const int id = t + 256 * u;
-      const int r = id / CH, c = id % CH;
-      const bool ok = j0 + r < a.nbk;
-      const size_t off = (size_t)(ok ? j0 + r : 0) * D + c * 8;
-      rh[u] = ok ? *reinterpret_cast<const u32x4*>(chb + off) : u32x4{0, 0, 0, 0};
-      rl[u] = ok ? *reinterpret_cast<const u32x4*>(clb + off) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < VCPT; ++u) {
-      const int id = t + 256 * u;
-      const int r = id / 8, g = id % 8;
-      const int j = j0 + 8 * g;
-      u32x4 w = j < a.nbk ? *reinterpret_cast<const u32x4*>(vxb + (size_t)r * a.npad + j)
-                          : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t keep_lo = j + 2 * e < a.nbk ? 0xffffu : 0u;
-        const uint32_t keep_hi = j + 2 * e + 1 < a.nbk ? 0xffff0000u : 0u;
-        w[e] &= keep_lo | keep_hi;
-      }
-      rv[u] = w;
+    for (int u = 0; u < KPW; ++u) {
+      const int pp = wvs * KPW + u;
+      const uint32_t off = (uint32_t)(pp * 1024) + (klane ^ (D == 128 ? (uint32_t)((pp & 3) << 6) : 0u));
+      load_lds16(rh, dh + pp * 1024, off);
+      load_lds16(rl, dl + pp * 1024, off);
     }
   };
-  auto store_tile = [&]() __attribute__((always_inline)) {
+  auto stage_v = [&](int j, int slot) __attribute__((always_inline)) {
+    const auto rv = make_rsrc(vxb + (size_t)(j < 0 ? 0 : j) * kBlock * D, tile_bytes(j));
+    const uint32_t dv = lds_addr(smem + (6 + slot) * TILE);
 #pragma unroll
-    for (int u = 0; u < KCPT; ++u) {
-      const int id = t + 256 * u;
-      const int r = id / CH, c = id % CH;
-      *reinterpret_cast<u32x4*>(&khi[cswz<D>(r, c * 8)]) = rh[u];
-      *reinterpret_cast<u32x4*>(&klo[cswz<D>(r, c * 8)]) = rl[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VCPT; ++u) {
-      const int id = t + 256 * u;
-      const int r = id / 8, g = id % 8;
-      uint16_t* dst = &vx[r * VR + 8 * g];     // 8-byte aligned rows
-      *reinterpret_cast<u32x2*>(dst) = u32x2{rv[u][0], rv[u][1]};
-      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{rv[u][2], rv[u][3]};
+    for (int u = 0; u < KPW; ++u) {
+      const int pp = wvs * KPW + u;
+      load_lds16(rv, dv + pp * 1024, (uint32_t)(pp * 1024) + vlane);
     }
   };
 
@@ -172,86 +167,111 @@ __global__ __launch_bounds__(256, 2) void pisa_tail_kernel(TailArgs a) {
   const float qk_scale = kLog2eT / sqrtf((float)D);
   const int ntiles = a.npad / kBlock;
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
 
-  load_tile(0);
-  store_tile();
-  __syncthreads();   // bitmap and tile 0 visible
-  for (int tt = 0; tt < ntiles; ++tt) {
-    if (tt + 1 < ntiles) load_tile((tt + 1) * kBlock);
-    if (active) {
-      const uint64_t mask = ((uint64_t)bits[qb][2 * tt + 1] << 32) | bits[qb][2 * tt];
-#pragma unroll 1
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x16 sh = f32x16{};
+  // One tile for this wave in two 32-centroid halves: Q K_bar^T of half 0, its mask and
+  // rescale check; Q K_bar^T of half 1 alongside the weights of half 0; the check of half 1;
+  // the value-sum product of half 0 alongside the weights of half 1; then that of half 1.
+  u32x4 pf[4];
+  auto qk_half = [&](const uint16_t* Kh, const uint16_t* Kl, int mt, f32x16& sh)
+                     __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = cswz<D>(32 * mt + l32, 16 * ks + 8 * h);
-          const u32x4 ah = *reinterpret_cast<const u32x4*>(&khi[off]);
-          const u32x4 al = *reinterpret_cast<const u32x4*>(&klo[off]);
-          sh = mfma_bf16(ah, qf[ks], sh);
-          sh = mfma_bf16(al, qf[ks], sh);
-          if constexpr (SPLIT) sh = mfma_bf16(ah, ql[ks], sh);
-        }
-        // routed blocks and padding -> -inf; max of this lane's query over the half
-        float r = kNegBigT;
+    for (int ks = 0; ks < KS; ++ks) {
+      const int off = swz<D>(32 * mt + l32, 16 * ks + 8 * h);
+      const u32x4 ah = *reinterpret_cast<const u32x4*>(&Kh[off]);
+      const u32x4 al = *reinterpret_cast<const u32x4*>(&Kl[off]);
+      sh = mfma_bf16(ah, qf[ks], sh);
+      sh = mfma_bf16(al, qf[ks], sh);
+      if constexpr (SPLIT) sh = mfma_bf16(ah, ql[ks], sh);
+    }
+  };
+  // routed centroids and padding -> -inf; rescale when the half's max passes m + slack
+  auto check_half = [&](f32x16& sh, int mt, uint64_t mask) __attribute__((always_inline)) {
+    float r = kNegBigT;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int jl = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          sh[e] = ((mask >> jl) & 1u) ? -INFINITY : sh[e];
-          r = fmaxf(r, sh[e]);
-        }
-        r = fmaxf(r, swap_halves(r)) * qk_scale;
-        if (__ballot(r > m)) {
-          const float mn = fmaxf(m, r);
-          const float corr = __builtin_amdgcn_exp2f(m - mn);
+    for (int e = 0; e < 16; ++e) {
+      const int jl = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+      sh[e] = ((mask >> jl) & 1u) ? -INFINITY : sh[e];
+      r = fmaxf(r, sh[e]);
+    }
+    r = fmaxf(r, swap_halves(r)) * qk_scale;
+    if (__ballot(r > m + kTailSlack)) {
+      const float mn = fmaxf(m, r);
+      const float corr = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-          for (int c = 0; c < CT; ++c) o[c] *= corr;
-          dsum *= corr;
-          asum *= corr;
-          m = mn;
-        }
-        // P^T fragments: fragment hh holds centroids 32 mt + 16 hh + 8 (i / 4) + 4 h + i % 4;
-        // the row sums add the f16-rounded weights
-        u32x4 pf[2];
-        float ps = 0.f, pl = 0.f;   // plain sum, and the part that belongs to the last block
+      for (int c = 0; c < CT; ++c) o[c] *= corr;
+      dsum *= corr;
+      asum *= corr;
+      if (mt == 1) {   // the weights of half 0 are formed but not yet multiplied
+        const _Float16 ch = (_Float16)corr;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int e = 8 * hh + 2 * e2;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e], qk_scale, -m));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e + 1], qk_scale, -m));
-            const uint32_t pk = pack_f16(p0, p1);
-            pf[hh][e2] = pk;
-            ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, ps, false);
-            const int j = tt * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-            const f16x2 pv = __builtin_bit_cast(f16x2, pk);
-            pl += (j == a.nbk - 1 ? (float)pv[0] : 0.f) + (j + 1 == a.nbk - 1 ? (float)pv[1] : 0.f);
-          }
-        asum += ps;
-        dsum += (float)kBlock * ps - (float)(kBlock - a.nlast) * pl;
-        // O^T += Vsum^T P^T; the A operand row c, reduction slot 8 h + i takes centroid
-        // 16 kk + 8 (i / 4) + 4 h + i % 4, matching the P^T fragment
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int kk = 2 * mt + hh;
-#pragma unroll
-          for (int c = 0; c < CT; ++c) {
-            const uint16_t* row = &vx[(32 * c + l32) * VR + 16 * kk + 4 * h];
-            const u32x2 v0 = *reinterpret_cast<const u32x2*>(row);
-            const u32x2 v1 = *reinterpret_cast<const u32x2*>(row + 8);
-            o[c] = mfma_f16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pf[hh], o[c]);
-          }
-        }
+        for (int kk = 0; kk < 2; ++kk)
+          pf[kk] = __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, pf[kk]) * ch);
       }
+      m = mn;
     }
-    if (tt + 1 < ntiles) {
-      __syncthreads();   // every wave is done with tile tt
-      store_tile();
-      __syncthreads();   // tile tt + 1 visible
+  };
+  // weights of one half (P^T fragments pf[2 mt], pf[2 mt + 1]) and their sums: fragment hh
+  // holds centroids 32 mt + 16 hh + 8 (i / 4) + 4 h + i % 4
+  auto exp_half = [&](const f32x16& sh, int mt, int tt) __attribute__((always_inline)) {
+    float ps = 0.f, pl = 0.f;   // plain sum, and the part that belongs to the last block
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int e = 8 * hh + 2 * e2;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e], qk_scale, -m));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[e + 1], qk_scale, -m));
+        const uint32_t pk = pack_f16(p0, p1);
+        pf[2 * mt + hh][e2] = pk;
+        ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, ps, false);
+        const int j = tt * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+        const f16x2 pv = __builtin_bit_cast(f16x2, pk);
+        pl += (j == a.nbk - 1 ? (float)pv[0] : 0.f) + (j + 1 == a.nbk - 1 ? (float)pv[1] : 0.f);
+      }
+    asum += ps;
+    dsum += (float)kBlock * ps - (float)(kBlock - a.nlast) * pl;
+  };
+  // O^T += Vsum^T P^T over the 32 centroids of one half
+  auto pv_half = [&](const uint16_t* Vt, int mt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 2 * mt; kk < 2 * mt + 2; ++kk) {
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] = mfma_f16(vt_frag<D>(Vt, 32 * c, 16 * kk), pf[kk], o[c]);
     }
+  };
+  auto compute_tile = [&](int kslot, int vslot, int tt, uint64_t mask)
+                          __attribute__((always_inline)) {
+    const uint16_t* Kh = smem + 2 * kslot * TILE;
+    const uint16_t* Kl = Kh + TILE;
+    const uint16_t* Vt = smem + (6 + vslot) * TILE;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    qk_half(Kh, Kl, 0, s0);
+    check_half(s0, 0, mask);
+    qk_half(Kh, Kl, 1, s1);
+    exp_half(s0, 0, tt);
+    check_half(s1, 1, mask);
+    pv_half(Vt, 0);
+    exp_half(s1, 1, tt);
+    pv_half(Vt, 1);
+  };
+
+  stage_k(0, 0);
+  stage_k(ntiles > 1 ? 1 : -1, 1);
+  stage_v(0, 0);
+  barrier_vmem_n<0>();
+  int ks = 0, vs = 0;
+  for (int tt = 0; tt < ntiles; ++tt) {
+    stage_v(tt + 1 < ntiles ? tt + 1 : -1, vs ^ 1);
+    stage_k(tt + 2 < ntiles ? tt + 2 : -1, ks == 0 ? 2 : ks - 1);
+    const uint64_t mask = ((uint64_t)bits[qb][2 * tt + 1] << 32) | bits[qb][2 * tt];
+    if (active && mask != ~0ull) compute_tile(ks, vs, tt, mask);
+    barrier_vmem_n<2 * KPW>();   // V(tt + 1) and K(tt + 1) landed; this step's slots are free
+    ks = ks == 2 ? 0 : ks + 1;
+    vs ^= 1;
   }
+  wait_vmem();   // no load into LDS outlives the workgroup
   if (!active) return;
 
   // O^T layout: lane column q, rows 32 c + 8 g + 4 h + e in element 4 g + e
@@ -289,8 +309,9 @@ hipError_t launch_tail_T(const Plan& s, const void* q, const int32_t* idx, char*
   a.tail_n = reinterpret_cast<float*>(ws + s.tail_n);
   a.nq = s.nq; a.nbq = s.nbq; a.nbk = s.nbk; a.npad = s.npad; a.topk = s.k;
   a.nlast = s.nkv - (s.nbk - 1) * kBlock;
-  a.ngroups = (s.nbq + 1) / 2;
-  hipLaunchKernelGGL((pisa_tail_kernel<T, D>), dim3(s.BH * a.ngroups), dim3(256), 0, st, a);
+  a.ngroups = (s.nbq + kTailGroup - 1) / kTailGroup;
+  hipLaunchKernelGGL((pisa_tail_kernel<T, D>), dim3(s.BH * a.ngroups), dim3(128 * kTailGroup), 0,
+                     st, a);
   return hipGetLastError();
 }
 

@@ -37,30 +37,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;      // finite "minus infinity" for running maxima
 constexpr float kRescaleSlack = 8.0f;    // keep a stale max while p <= 2^8
 
-// Element offset of (row, col) in a swizzled LDS tile with D 16-bit columns per row: the
-// 16-byte chunk index is XORed with the row (mod chunks per row).
-template <int D>
-__device__ __forceinline__ int swz(int row, int col) {
-  constexpr int CH = D / 8;
-  return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
-}
-
-// Swizzle of the V tile. A transposing V^T read has each group of 16 lanes touch 4
-// consecutive key rows x 2 adjacent chunks (and each 32 lanes 4 rows x 4 chunks); XORing
-// the chunk index with f(row % 4) spreads those accesses over distinct banks whether the LDS
-// serves 128 or 256 bytes per clock. Rows are bijective, so the row-wise tile writes stay
-// conflict-free as well.
-template <int D>
-__device__ __forceinline__ int swzv_f(int row) {
-  const int r = row & 3;
-  return D == 128 ? (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) : 2 * r;
-}
-template <int D>
-__device__ __forceinline__ int swzv(int row, int col) {
-  constexpr int CH = D / 8;
-  return row * D + ((((col >> 3) ^ swzv_f<D>(row)) & (CH - 1)) << 3) + (col & 7);
-}
-
 // Ascending walk over the union of QB ascending selection lists. Each list is held 64
 // entries at a time in a VGPR (lane l: entry base + l) and read with readlane, so the walk
 // costs no memory round trip per step.
@@ -132,20 +108,6 @@ struct UnionWalk {
     return e >= 0;
   }
 };
-
-// P^T-matched V^T fragment from a swizzled row-major [key][channel] tile: lane row (channel)
-// x0 + lane%32; reduction slot e holds key k0 + 4h + e (e < 4) or k0 + 8 + 4h + (e - 4)
-// (e >= 4), h = lane / 32.
-template <int D>
-__device__ __forceinline__ u32x4 vt_frag(const uint16_t* M, int x0, int k0) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, L = lane & 15;
-  const int row = k0 + 4 * (g >> 1) + (L >> 2);
-  const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const u32x2 lo = lds_read_tr16(M + swzv<D>(row, col));
-  const u32x2 hi = lds_read_tr16(M + swzv<D>(row + 8, col));
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
 
 struct SparseArgs {
   const void* q;

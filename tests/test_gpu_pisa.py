@@ -134,13 +134,13 @@ def test_block_statistics(sla):
     chi = region("cent_hi", np.uint16).astype(np.uint32) << 16
     clo = region("cent_lo", np.uint16).astype(np.uint32) << 16
     cent = (chi.view(np.float32).astype(np.float64) + clo.view(np.float32)).reshape(2, npad, d)
-    vsum = region("vsum", np.float16).astype(np.float64).reshape(2, d, npad)
+    vsum = region("vsum", np.float16).astype(np.float64).reshape(2, npad, d)
     for h in range(2):
         kk, vv = x.as_f64("k")[0, h], x.as_f64("v")[0, h]
         k_bar, vs, counts, H = op.block_stats(kk, vv, 64)
         hb = H.mean(axis=0)
         assert np.abs(cent[h, :nb] - k_bar).max() <= 1e-5 * np.abs(k_bar).max()
-        assert np.all(np.abs(vsum[h, :, :nb].T - vs) <= 1e-3 * np.abs(vs) + 1e-3)
+        assert np.all(np.abs(vsum[h, :nb] - vs) <= 1e-3 * np.abs(vs) + 1e-3)
         assert np.abs(hbar[h].T - hb).max() <= 1e-2 * np.abs(hb).max()
 
 
