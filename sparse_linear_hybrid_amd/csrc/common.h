@@ -23,6 +23,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 64;          // query block = key block = 64 tokens
 constexpr float kEps = 1e-6f;       // linear-branch denominator epsilon
 constexpr int kMaxKeyBlocks = 8064;   // top-k keeps a row of 64-bit keys in 64 KB of LDS
+// Online softmax in base 2: logits are scaled by log2(e)/sqrt(d); running maxima start at a
+// finite "minus infinity"; a max may lag the true one while the weights stay below 2^8,
+// which f16 weights hold exactly enough and which saves most rescales.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+constexpr float kRescaleSlack = 8.0f;
 
 // ----------------------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

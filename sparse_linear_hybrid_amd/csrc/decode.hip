@@ -27,26 +27,6 @@ namespace sla {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;
-constexpr float kRescaleSlack = 8.0f;
-
-template <int D>
-__device__ __forceinline__ int dswz(int row, int col) {       // K tile: chunk ^ row
-  constexpr int CH = D / 8;
-  return row * D + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7);
-}
-template <int D>
-__device__ __forceinline__ int dswzv_f(int row) {              // V tile: chunk ^ f(row % 4)
-  const int r = row & 3;
-  return D == 128 ? (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) : 2 * r;
-}
-template <int D>
-__device__ __forceinline__ int dswzv(int row, int col) {
-  constexpr int CH = D / 8;
-  return row * D + ((((col >> 3) ^ dswzv_f<D>(row)) & (CH - 1)) << 3) + (col & 7);
-}
-
 // Transposing fragment read from a [key][channel] tile: lane owns channel x0 + lane%32 and
 // the 8 keys k0 + 8*(lane/32) .. +7 (A or B operand with the keys as reduction index).
 template <int D, bool VTILE>
@@ -55,22 +35,10 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* M, int x0, int k0) {
   const int g = lane >> 4, L = lane & 15;
   const int row = k0 + 8 * (g >> 1) + (L >> 2);
   const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const int o0 = VTILE ? dswzv<D>(row, col) : dswz<D>(row, col);
-  const int o1 = VTILE ? dswzv<D>(row + 4, col) : dswz<D>(row + 4, col);
+  const int o0 = VTILE ? swzv<D>(row, col) : swz<D>(row, col);
+  const int o1 = VTILE ? swzv<D>(row + 4, col) : swz<D>(row + 4, col);
   const u32x2 lo = lds_read_tr16(M + o0);
   const u32x2 hi = lds_read_tr16(M + o1);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
-// P^T-matched V^T fragment (same key order as the S^T accumulator; see sparse.hip)
-template <int D>
-__device__ __forceinline__ u32x4 vt_frag_d(const uint16_t* M, int x0, int k0) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, L = lane & 15;
-  const int row = k0 + 4 * (g >> 1) + (L >> 2);
-  const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
-  const u32x2 lo = lds_read_tr16(M + dswzv<D>(row, col));
-  const u32x2 hi = lds_read_tr16(M + dswzv<D>(row + 8, col));
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -126,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeArgs a) {
     const int e = (wv * KPW + u) * 512 + lane * 8;
     const int r = e / D, pch = (e % D) / 8;
     koff[u] = (uint32_t)(r * D * 2 + ((pch ^ r) & (CH - 1)) * 16);
-    voff[u] = (uint32_t)(r * D * 2 + ((pch ^ dswzv_f<D>(r)) & (CH - 1)) * 16);
+    voff[u] = (uint32_t)(r * D * 2 + ((pch ^ swzv_f<D>(r)) & (CH - 1)) * 16);
   }
   const int wvs = __builtin_amdgcn_readfirstlane(wv);
   auto stage = [&](int j, int buf) __attribute__((always_inline)) {   // j < 0: nothing
@@ -175,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeArgs a) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[dswz<D>(32 * mt + l32, 16 * ks + 8 * h)]);
+        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(32 * mt + l32, 16 * ks + 8 * h)]);
         s2[mt] = mfma_bf16(af, qf[ks], s2[mt]);
       }
     if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
@@ -222,7 +190,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeArgs a) {
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int c = 0; c < CT; ++c) {
-        const u32x4 vf = vt_frag_d<D>(Vt, 32 * c, 16 * kk);
+        const u32x4 vf = vt_frag<D>(Vt, 32 * c, 16 * kk);
         o[c] = mfma_bf16(vf, phi[kk], o[c]);
         o[c] = mfma_bf16(vf, plo[kk], o[c]);
       }

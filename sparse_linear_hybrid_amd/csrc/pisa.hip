@@ -26,8 +26,6 @@ namespace sla {
 
 namespace {
 
-constexpr float kLog2eT = 1.4426950408889634f;
-constexpr float kNegBigT = -1.0e30f;   // finite "minus infinity" for the running max
 
 struct TailArgs {
   const void* q;                 // [BH][nq][D] (bf16 or fp32)
@@ -61,7 +59,6 @@ __device__ __forceinline__ void load_q8(const T* p, u32x4& hi, u32x4& lo) {
 }
 
 constexpr int kTailGroup = 4;                  // query blocks per workgroup
-constexpr float kTailSlack = 8.0f;             // keep a stale max while the weights <= 2^8
 
 template <typename T, int D>
 __global__ __launch_bounds__(128 * kTailGroup, 2) void pisa_tail_kernel(TailArgs a) {
@@ -163,8 +160,8 @@ __global__ __launch_bounds__(128 * kTailGroup, 2) void pisa_tail_kernel(TailArgs
   f32x16 o[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) o[c] = f32x16{};
-  float m = kNegBigT, dsum = 0.f, asum = 0.f;
-  const float qk_scale = kLog2eT / sqrtf((float)D);
+  float m = kNegBig, dsum = 0.f, asum = 0.f;
+  const float qk_scale = kLog2e / sqrtf((float)D);
   const int ntiles = a.npad / kBlock;
   typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -188,7 +185,7 @@ __global__ __launch_bounds__(128 * kTailGroup, 2) void pisa_tail_kernel(TailArgs
   };
   // routed centroids and padding -> -inf; rescale when the half's max passes m + slack
   auto check_half = [&](f32x16& sh, int mt, uint64_t mask) __attribute__((always_inline)) {
-    float r = kNegBigT;
+    float r = kNegBig;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int jl = 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(128 * kTailGroup, 2) void pisa_tail_kernel(TailArgs
       r = fmaxf(r, sh[e]);
     }
     r = fmaxf(r, swap_halves(r)) * qk_scale;
-    if (__ballot(r > m + kTailSlack)) {
+    if (__ballot(r > m + kRescaleSlack)) {
       const float mn = fmaxf(m, r);
       const float corr = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll

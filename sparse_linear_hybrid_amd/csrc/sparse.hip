@@ -33,9 +33,6 @@ namespace sla {
 
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;      // finite "minus infinity" for running maxima
-constexpr float kRescaleSlack = 8.0f;    // keep a stale max while p <= 2^8
 
 // Ascending walk over the union of QB ascending selection lists. Each list is held 64
 // entries at a time in a VGPR (lane l: entry base + l) and read with readlane, so the walk
