@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void pool_stats_kernel(const T* __restrict_
 
 // ----------------------------------------------------------------------------- scores
 // scores[bh][i][j] = sum_c qt[bh][i][c] * kt[bh][j][c]; float64, 64x64 output tile per
-// 256-thread workgroup, 4x4 outputs per thread, channel chunks of 32 staged in LDS.
+// 256-thread workgroup on float64 MFMA (16x16x4), channel chunks of 32 staged in LDS.
 // k~ of key block j of (batch, head) bh is at kt + bh * kbh + j * kj.
 // TAYLOR (training-free router, SPLA page, section 2.1): qt holds the block means of Q, kt
 // those of K and kv the variances of K (same strides); the score is
@@ -256,17 +256,22 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
   const double* kb = kt + (size_t)bh * kbh;
   const double* vb = TAYLOR ? kv + (size_t)bh * kbh : nullptr;
   const int t = threadIdx.x;
-  const int ty = t / 16, tx = t % 16;
-  double acc[4][4], acc2[TAYLOR ? 4 : 1][TAYLOR ? 4 : 1];
+  // wave w: the 32 x 32 sub-tile (rows 32 (w / 2), columns 32 (w % 2)) as 2 x 2 float64
+  // MFMA 16x16x4 tiles. Operand lane l holds row (A) or column (B) l % 16 at reduction
+  // index l / 16; result element e of lane l is row l / 16 + 4 e, column l % 16.
+  const int w = t >> 6, lane = t & 63, lr = lane & 15, lk = lane >> 4;
+  const int wi = (w >> 1) * 32, wj = (w & 1) * 32;
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  f64x4 acc[2][2], acc2[TAYLOR ? 2 : 1][TAYLOR ? 2 : 1];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   if constexpr (TAYLOR) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc2[a][b] = 0.0;
+      for (int b = 0; b < 2; ++b) acc2[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   }
   // 64 rows x 32 channels per operand and chunk = 2048 values, 8 per thread; the next
   // chunk is fetched into registers while the current one is multiplied
@@ -293,43 +298,49 @@ __global__ __launch_bounds__(256) void score_kernel(const double* __restrict__ q
     }
     __syncthreads();
     if (c0 + C < D) fetch(c0 + C);
-#pragma unroll 4
-    for (int cc = 0; cc < C; ++cc) {
-      double a[4], b[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = As[cc][ty + 16 * u];
-        b[u] = Bs[cc][tx + 16 * u];
+    for (int st = 0; st < C / 4; ++st) {
+      const int cc = 4 * st + lk;
+      double a[2], b[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        a[x] = As[cc][wi + 16 * x + lr];
+        b[x] = Bs[cc][wj + 16 * x + lr];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fma(a[u], b[w], acc[u][w]);
+        for (int y = 0; y < 2; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[x], b[y], acc[x][y], 0, 0, 0);
       if constexpr (TAYLOR) {
-        double vv[4];
+        double vv[2];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) vv[w] = Vs[cc][tx + 16 * w];
+        for (int y = 0; y < 2; ++y) vv[y] = Vs[cc][wj + 16 * y + lr];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) acc2[u][w] = fma(a[u] * a[u], vv[w], acc2[u][w]);
+          for (int y = 0; y < 2; ++y)
+            acc2[x][y] =
+                __builtin_amdgcn_mfma_f64_16x16x4f64(a[x] * a[x], vv[y], acc2[x][y], 0, 0, 0);
       }
     }
     __syncthreads();
   }
   const double tau = 1.0 / sqrt((double)D);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int gi = i0 + ty + 16 * u;
-    if (gi >= nbq) continue;
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int gj = j0 + tx + 16 * w;
-      double sc = acc[u][w];
-      if constexpr (TAYLOR) sc = tau * acc[u][w] + log1p(0.5 * tau * tau * acc2[u][w]);
-      if (gj < nbk) scores[((size_t)bh * nbq + gi) * nbk + gj] = sc;
+    for (int e = 0; e < 4; ++e) {
+      const int gi = i0 + wi + 16 * x + lk + 4 * e;
+      if (gi >= nbq) continue;
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int gj = j0 + wj + 16 * y + lr;
+        double sc = acc[x][y][e];
+        if constexpr (TAYLOR) sc = tau * acc[x][y][e] + log1p(0.5 * tau * tau * acc2[x][y][e]);
+        if (gj < nbk) scores[((size_t)bh * nbq + gi) * nbk + gj] = sc;
+      }
     }
-  }
 }
 
 // Scores for few query blocks (nbq <= kFewRows): one workgroup per 64 key blocks of a head;
