@@ -4,9 +4,11 @@
 
 namespace sla {
 
-// Router: pool + project Q (and K if pool_k), score, top-k -> idx.
+// Router: pool + project Q (and K if pool_k), score, top-k -> idx; bits != nullptr: also the
+// routed-block bitmap [BH][nbq][nwords] that the complement reads.
 hipError_t launch_route(const Plan& s, const void* q, const void* k, const float* pq,
-                        const float* pk, int32_t* idx, char* ws, bool pool_k, hipStream_t st);
+                        const float* pk, int32_t* idx, uint32_t* bits, char* ws, bool pool_k,
+                        hipStream_t st);
 
 // Linear branch, part 1 (independent of routing): per key block phi(K)^T V, sum phi(K),
 // the projected pooled K (for the router), an f16 copy of V, and the per-head totals.
@@ -32,7 +34,7 @@ hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
 // Training-free router (SPLA page, section 2.1): block means of Q and K, variances of K,
 // second-order Taylor scores, top-k -> idx.
 hipError_t launch_route_taylor(const Plan& s, const void* q, const void* k, int32_t* idx,
-                               char* ws, hipStream_t st);
+                               uint32_t* bits, char* ws, hipStream_t st);
 
 // Summary cache: bring k~, S_tot, z_tot from the first n_done tokens to s.nkv tokens.
 hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,

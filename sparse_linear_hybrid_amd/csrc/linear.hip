@@ -326,36 +326,16 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // summary, S_c[n][i] = sum_j (1 - M[i][j]) S_j[n] with M the 0/1 selection matrix (SPLA
 // page, section 2.2: the linear term covers the blocks the sparse part did not select),
 // computed as an MFMA product over steps of CK key blocks (the 0/1 matrix is exact in bf16).
-// Each thread first copies one query block's row of the routed-block bitmap (built once per
-// query block by selection_bits_kernel; one 32-bit word per step of a window of up to
-// 32 * MAXW key blocks) into LDS, inverted over the valid key blocks, and steps in which
-// every query block of the tile selected every block are skipped. The summary slices of a step (CK rows of
-// CN bf16) are loaded straight into a CBUF-deep LDS ring, two pairs of steps ahead of their
-// use.
+// Each thread first copies one query block's row of the routed-block bitmap (written by the
+// router's top-k pass; one 32-bit word per step of a window of up to 32 * MAXW key blocks)
+// into LDS, inverted over the valid key blocks, and steps in which every query block of the
+// tile selected every block are skipped. The summary slices of a step (CK rows of CN bf16)
+// are loaded straight into a CBUF-deep LDS ring, two pairs of steps ahead of their use.
 // Wave w owns query blocks 64 w .. 64 w + 63 of the tile and all CN columns: per step it
 // reads 8 A fragments (summaries, transposing LDS reads, shared by the four waves) and
 // builds 4 B fragments (its bitmap bits -> bf16 0/1) for 16 MFMAs. Query tiles sharing a
 // column slice are consecutive workgroups (same XCD), so each S_j slice comes from HBM
 // about once and from L2 ceil(n_blocks / CQ) times.
-// Routed-block bitmap of every query block (bit j of row i: key block j is routed to query
-// block i), built once from the selection lists for the complement's workgroups.
-__global__ __launch_bounds__(64) void selection_bits_kernel(const int32_t* __restrict__ idx,
-                                                            uint32_t* __restrict__ bits, int nbq,
-                                                            int k, int nwords) {
-  __shared__ uint32_t w[kMaxKeyBlocks / 32];
-  const size_t row = (size_t)blockIdx.y * nbq + blockIdx.x;
-  const int t = threadIdx.x;
-  for (int i = t; i < nwords; i += 64) w[i] = 0u;
-  __syncthreads();
-  const int32_t* sel = idx + row * k;
-  for (int i = t; i < k; i += 64) {
-    const int j = sel[i];
-    atomicOr(&w[j >> 5], 1u << (j & 31));
-  }
-  __syncthreads();
-  for (int i = t; i < nwords; i += 64) bits[row * nwords + i] = w[i];
-}
-
 constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
 constexpr int CN = 128;    // summary columns per workgroup
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
@@ -704,10 +684,7 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
   const int total = s.BH * ncs * nqt;
   const int ww = min(MAXW, (s.nbk + CK - 1) / CK);
   const size_t lds = complement_lds_bytes(ww);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + s.selbits);
-  if (s.k < s.nbk)   // (k = 0: all-zero rows)
-    hipLaunchKernelGGL(selection_bits_kernel, dim3(s.nbq, s.BH), dim3(64), 0, st, idx, bits,
-                       s.nbq, s.k, s.nwords);
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(ws + s.selbits);   // from top-k
   hipError_t err = hipSuccess;
   auto go = [&](auto kern, auto zkern) {
     // more than 64 KB of dynamic LDS (wide windows) has to be allowed per kernel

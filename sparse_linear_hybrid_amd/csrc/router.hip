@@ -407,10 +407,12 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 // One wave per (bh, query block) row. Radix-select (8 passes of 8 bits, most significant
 // first) finds the k-th largest key T exactly; then one ascending sweep over j keeps every
 // key > T and the lowest-index keys == T until k are kept. The output is therefore
-// ascending and ties go to the lowest index.
+// ascending and ties go to the lowest index. bits != nullptr: the row of the routed-block
+// bitmap (bit j of word j / 32: key block j kept; nwords words) is written as well.
 __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ scores,
-                                                  int32_t* __restrict__ idx, int rows, int nbk,
-                                                  int k) {
+                                                  int32_t* __restrict__ idx,
+                                                  uint32_t* __restrict__ bits, int rows, int nbk,
+                                                  int k, int nwords) {
   extern __shared__ uint64_t smem[];
   uint64_t* keys = smem;                                   // nbk
   uint32_t* hist = reinterpret_cast<uint32_t*>(smem + nbk); // 256
@@ -418,9 +420,15 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ sco
   const int lane = threadIdx.x;
   const double* s = scores + (size_t)row * nbk;
   int32_t* out = idx + (size_t)row * k;
-  if (k <= 0) return;
-  if (k >= nbk) {
-    for (int j = lane; j < nbk; j += 64) out[j] = j;
+  uint32_t* brow = bits ? bits + (size_t)row * nwords : nullptr;
+  if (k <= 0 || k >= nbk) {
+    if (k > 0)
+      for (int j = lane; j < nbk; j += 64) out[j] = j;
+    if (brow)
+      for (int w = lane; w < nwords; w += 64) {
+        const int left = nbk - 32 * w;   // valid blocks from bit 0 of this word
+        brow[w] = k <= 0 ? 0u : (left >= 32 ? 0xffffffffu : (1u << left) - 1u);
+      }
     return;
   }
   for (int j = lane; j < nbk; j += 64) keys[j] = score_key(s[j]);
@@ -487,6 +495,8 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ sco
     const bool sel = gt || (eq && eq_rank < remaining);
     const unsigned long long sb = __ballot(sel);
     if (sel) out[written + __popcll(sb & lt_mask)] = j;
+    if (brow && lane < 2 && base / 32 + lane < nwords)
+      brow[base / 32 + lane] = (uint32_t)(sb >> (32 * lane));
     written += __popcll(sb);
     eq_seen += __popcll(eqb);
   }
@@ -508,7 +518,8 @@ static void launch_pool_q(const Plan& s, const void* q, const float* pq, double*
 // kv != nullptr: training-free (Taylor) scores with the key variances kv
 template <int D>
 static void launch_select(const Plan& s, const double* qt, const double* kt, const double* kv,
-                          size_t kbh, size_t kj, double* sc, int32_t* idx, hipStream_t st) {
+                          size_t kbh, size_t kj, double* sc, int32_t* idx, uint32_t* bits,
+                          hipStream_t st) {
   const int rq = s.BH * s.nbq;
   const dim3 gf((s.nbk + 63) / 64, s.BH), gt((s.nbk + 63) / 64, (s.nbq + 63) / 64, s.BH);
   if (s.nbq <= kFewRows) {
@@ -526,16 +537,17 @@ static void launch_select(const Plan& s, const double* qt, const double* kt, con
       hipLaunchKernelGGL((score_kernel<D, false>), gt, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
                          s.nbk, kbh, kj);
   }
-  if (s.k > 0) {
+  if (s.k > 0 || bits) {
     const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
-    hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, rq, s.nbk, s.k);
+    hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, bits, rq, s.nbk, s.k,
+                       s.nwords);
   }
 }
 
 template <int D>
 static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, const float* pq,
-                                 const float* pk, int32_t* idx, char* ws, bool pool_k,
-                                 hipStream_t st) {
+                                 const float* pk, int32_t* idx, uint32_t* bits, char* ws,
+                                 bool pool_k, hipStream_t st) {
   double* qt = reinterpret_cast<double*>(ws + s.qt);
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   double* sc = reinterpret_cast<double*>(ws + s.scores);
@@ -549,13 +561,13 @@ static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, co
       hipLaunchKernelGGL((pool_project_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k,
                          pk, kt, s.nkv, s.nbk);
   }
-  launch_select<D>(s, qt, kt, nullptr, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
+  launch_select<D>(s, qt, kt, nullptr, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, bits, st);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_route_taylor_T(const Plan& s, const void* q, const void* k,
-                                        int32_t* idx, char* ws, hipStream_t st) {
+                                        int32_t* idx, uint32_t* bits, char* ws, hipStream_t st) {
   double* qt = reinterpret_cast<double*>(ws + s.qt);
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   double* kv = reinterpret_cast<double*>(ws + s.kvar);
@@ -573,20 +585,21 @@ static hipError_t launch_route_taylor_T(const Plan& s, const void* q, const void
     hipLaunchKernelGGL((pool_stats_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k, kt,
                        kv, s.nkv, s.nbk);
   }
-  launch_select<D>(s, qt, kt, kv, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, st);
+  launch_select<D>(s, qt, kt, kv, (size_t)s.nbk * s.D, (size_t)s.D, sc, idx, bits, st);
   return hipGetLastError();
 }
 
 hipError_t launch_route_taylor(const Plan& s, const void* q, const void* k, int32_t* idx,
-                               char* ws, hipStream_t st) {
-  if (s.D == 128) return launch_route_taylor_T<128>(s, q, k, idx, ws, st);
-  return launch_route_taylor_T<64>(s, q, k, idx, ws, st);
+                               uint32_t* bits, char* ws, hipStream_t st) {
+  if (s.D == 128) return launch_route_taylor_T<128>(s, q, k, idx, bits, ws, st);
+  return launch_route_taylor_T<64>(s, q, k, idx, bits, ws, st);
 }
 
 hipError_t launch_route(const Plan& s, const void* q, const void* k, const float* pq,
-                        const float* pk, int32_t* idx, char* ws, bool pool_k, hipStream_t st) {
-  if (s.D == 128) return launch_route_T<128>(s, q, k, pq, pk, idx, ws, pool_k, st);
-  return launch_route_T<64>(s, q, k, pq, pk, idx, ws, pool_k, st);
+                        const float* pk, int32_t* idx, uint32_t* bits, char* ws, bool pool_k,
+                        hipStream_t st) {
+  if (s.D == 128) return launch_route_T<128>(s, q, k, pq, pk, idx, bits, ws, pool_k, st);
+  return launch_route_T<64>(s, q, k, pq, pk, idx, bits, ws, pool_k, st);
 }
 
 hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, const double* kt,
@@ -594,10 +607,10 @@ hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, co
                                hipStream_t st) {
   if (s.D == 128) {
     launch_pool_q<128>(s, q, pq, qt, st);
-    launch_select<128>(s, qt, kt, nullptr, kbh, kj, sc, idx, st);
+    launch_select<128>(s, qt, kt, nullptr, kbh, kj, sc, idx, nullptr, st);
   } else {
     launch_pool_q<64>(s, q, pq, qt, st);
-    launch_select<64>(s, qt, kt, nullptr, kbh, kj, sc, idx, st);
+    launch_select<64>(s, qt, kt, nullptr, kbh, kj, sc, idx, nullptr, st);
   }
   return hipGetLastError();
 }

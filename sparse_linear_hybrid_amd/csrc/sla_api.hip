@@ -71,9 +71,13 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   }
   if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY + 1))) return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_ROUTE))) return SLA_ERR_HIP;
+  // the complement's routed-block bitmap comes out of the top-k pass (the piecewise tail
+  // builds its own)
+  uint32_t* bits = mode == Fwd::kPisa ? nullptr : reinterpret_cast<uint32_t*>(ws + s.selbits);
   if (mode == Fwd::kTaylor) {
-    if (!ok(launch_route_taylor(s, q, k, idx, ws, stream))) return SLA_ERR_HIP;
-  } else if (!ok(launch_route(s, q, k, proj_q, proj_k, idx, ws, /*pool_k=*/false, stream))) {
+    if (!ok(launch_route_taylor(s, q, k, idx, bits, ws, stream))) return SLA_ERR_HIP;
+  } else if (!ok(launch_route(s, q, k, proj_q, proj_k, idx, bits, ws, /*pool_k=*/false,
+                              stream))) {
     return SLA_ERR_HIP;
   }
   if (!ok(mark(2 * SLA_STAGE_ROUTE + 1))) return SLA_ERR_HIP;
@@ -124,7 +128,7 @@ sla_status sla_route(const sla_problem* p, const void* q, const void* k, const f
   const Plan s = make_plan(*p);
   if (!workspace || workspace_bytes < s.total_route) return SLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SLA_ERR_ALIGN;
-  if (launch_route(s, q, k, proj_q, proj_k, block_idx, static_cast<char*>(workspace),
+  if (launch_route(s, q, k, proj_q, proj_k, block_idx, nullptr, static_cast<char*>(workspace),
                    /*pool_k=*/true, stream) != hipSuccess)
     return SLA_ERR_HIP;
   return SLA_OK;
@@ -173,7 +177,8 @@ sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,
   const Plan s = make_plan(*p);
   if (!workspace || workspace_bytes < s.total_route) return SLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SLA_ERR_ALIGN;
-  if (launch_route_taylor(s, q, k, block_idx, static_cast<char*>(workspace), stream) != hipSuccess)
+  if (launch_route_taylor(s, q, k, block_idx, nullptr, static_cast<char*>(workspace), stream) !=
+      hipSuccess)
     return SLA_ERR_HIP;
   return SLA_OK;
 }
