@@ -1,7 +1,9 @@
-"""GPU parity at the largest key-block count the library accepts (8064 blocks of 64 keys, the
-row of 64-bit keys that top-k holds in 64 KB of LDS), with a ragged last block.
+"""GPU parity at the size limits: the smallest shapes (one partial query block of 5 rows
+against one partial key block of 10 keys), and the largest key-block count the library
+accepts (8064 blocks of 64 keys, the row of 64-bit keys that top-k holds in 64 KB of LDS),
+with a ragged last block.
 
-At this size the complement walks its bitmap in several windows with more than 64 KB of
+At the largest size the complement walks its bitmap in several windows with more than 64 KB of
 LDS, the piecewise tail's bitmap is full, and the router scores 8064 blocks per row. Masks
 must equal the oracle's; outputs are compared on sampled rows (first and ragged last query
 block) within the bf16 / fp8 bars.
@@ -92,3 +94,22 @@ def test_maximum_key_blocks_d64(sla):
     err, _ = max_err_over_rms(np.concatenate(gots), np.concatenate(refs))
     print(f"maximum key blocks d=64: max-abs/rms {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("fn", ["sla", "fp8", "pisa"])
+@pytest.mark.parametrize("top_k", [0, 1])
+def test_single_partial_blocks(sla, fn, top_k):
+    """5 queries, 10 keys: one partial block each. top_k = 0 leaves everything to the linear
+    branch (or the tail); top_k = 1 routes the only block (empty complement / tail)."""
+    x = make_custom(1, 2, 5, 10, 64, top_k, dtype="bf16", kind="normal", seed=7 + top_k)
+    out, idx = gpu(sla, x, fn)
+    assert idx.shape == (1, 2, 1, top_k) and (top_k == 0 or np.all(idx == 0))
+    if fn == "pisa":
+        ref, _ = op.forward(x)
+    elif fn == "fp8":
+        ref, _ = oracle.forward_fp8(x)
+    else:
+        ref, _ = oracle.forward(x)
+    err, _ = max_err_over_rms(out, ref)
+    print(f"single partial blocks {fn} top_k={top_k}: max-abs/rms {err:.3e}")
+    assert err <= (TOL_FP8 if fn == "fp8" else TOL)
