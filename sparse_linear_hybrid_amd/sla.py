@@ -124,6 +124,44 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, top_k: int, block: int = 64,
                    _dtype_code(out_dtype))
 
 
+def _check(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
+           proj: Tuple[Optional[torch.Tensor], ...] = (), alpha: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+           buffers: Tuple[Optional[torch.Tensor], ...] = ()) -> None:
+    """Checks what the C ABI cannot see before anything is enqueued: every tensor is on the
+    GPU that holds q, K and V share q's dtype (V has K's shape), projections are fp32
+    [d, d], alpha is fp32 [heads, d], a caller's output has q's shape and out_dtype, and
+    workspace or cache buffers are device tensors. Raises ValueError / TypeError."""
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    dev = q.device
+    B, H, _, d = q.shape
+    named = [("k", k), ("v", v), ("alpha", alpha), ("out", out)]
+    named += [(f"proj[{i}]", t) for i, t in enumerate(proj)]
+    named += [(f"buffer[{i}]", t) for i, t in enumerate(buffers)]
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
+    if k.dtype != q.dtype:
+        raise TypeError(f"k has dtype {k.dtype}, q {q.dtype}")
+    if v is not None and (v.dtype != k.dtype or v.shape != k.shape):
+        raise ValueError(f"v must match k: v {v.dtype}{tuple(v.shape)}, "
+                         f"k {k.dtype}{tuple(k.shape)}")
+    for i, t in enumerate(proj):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (d, d)):
+            raise ValueError(f"proj[{i}] must be float32 [{d}, {d}], got {t.dtype}{tuple(t.shape)}")
+    if alpha is not None and (alpha.dtype != torch.float32 or tuple(alpha.shape) != (H, d)):
+        raise ValueError(f"alpha must be float32 [{H}, {d}], got {alpha.dtype}"
+                         f"{tuple(alpha.shape)}")
+    if out is not None and (out.shape != q.shape or out.dtype != out_dtype):
+        raise ValueError(f"out must be {out_dtype}{tuple(q.shape)}, got {out.dtype}"
+                         f"{tuple(out.shape)}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def workspace_size(p: Problem, variant=VARIANT_FORWARD) -> int:
     """Workspace bytes for a layout: VARIANT_FORWARD (False), VARIANT_FP8 (True) or
     VARIANT_PISA."""
@@ -143,10 +181,12 @@ def _stream(device: torch.device):
 
 
 def _workspace(p: Problem, variant, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    """The caller's workspace if it is large enough (any dtype; its bytes count), else a new
+    uint8 tensor of the size the library asks for."""
     need = workspace_size(p, variant)
     if need == 0:
         raise SlaError(2, "sla_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     return workspace
 
@@ -155,21 +195,24 @@ def sla_route(q, k, proj_q, proj_k, top_k: int, block: int = 64,
               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Router: int32 block indices [B, H, ceil(n_q/block), top_k], ascending per row."""
     p = make_problem(q, k, top_k, block)
-    ws = _workspace(p, False, q.device, workspace)
+    _check(q, k, proj=(proj_q, proj_k), buffers=(workspace,))
+    ws = _workspace(p, VARIANT_FORWARD, q.device, workspace)
     idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
                       device=q.device)
-    st = library().sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k), _ptr(idx),
-                        _ptr(ws), ctypes.c_size_t(ws.numel()), _stream(q.device))
+    st = library().sla_route(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(proj_q), _ptr(proj_k),
+                             _ptr(idx), _ptr(ws), ctypes.c_size_t(_nbytes(ws)), _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_route")
     return idx
 
 
 def _forward(name: str, q, k, v, proj_q, proj_k, alpha, top_k: int, block: int,
-             out_dtype: torch.dtype, return_idx: bool, workspace, out) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+             out_dtype: torch.dtype, return_idx: bool, workspace,
+             out) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     p = make_problem(q, k, top_k, block, out_dtype)
-    fp8 = name == "sla_forward_fp8"
-    ws = _workspace(p, fp8, q.device, workspace)
+    _check(q, k, v, (proj_q, proj_k), alpha, out, out_dtype, (workspace,))
+    variant = VARIANT_FP8 if name == "sla_forward_fp8" else VARIANT_FORWARD
+    ws = _workspace(p, variant, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     idx = None
@@ -178,7 +221,7 @@ def _forward(name: str, q, k, v, proj_q, proj_k, alpha, top_k: int, block: int,
                           device=q.device)
     st = getattr(library(), name)(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
                              _ptr(proj_k), _ptr(alpha), _ptr(out), _ptr(idx), _ptr(ws),
-                             ctypes.c_size_t(ws.numel()), _stream(q.device))
+                             ctypes.c_size_t(_nbytes(ws)), _stream(q.device))
     if st != 0:
         raise SlaError(st, name)
     return out, idx
@@ -212,6 +255,8 @@ def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8
     if int(fp8) + int(taylor) + int(pisa) > 1:
         raise ValueError("fp8, taylor and pisa select different forward paths")
     p = make_problem(q, k, top_k, block, out_dtype)
+    _check(q, k, v, () if taylor else (proj_q, proj_k), None if pisa else alpha, out,
+           out_dtype, (workspace,))
     variant = VARIANT_FP8 if fp8 else (VARIANT_PISA if pisa else VARIANT_FORWARD)
     ws = _workspace(p, variant, q.device, workspace)
     if out is None:
@@ -221,7 +266,7 @@ def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8
     pk = None if taylor else _ptr(proj_k)
     al = None if pisa else _ptr(alpha)
     st = library().sla_forward_profiled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), pq, pk, al,
-                                        _ptr(out), None, _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                        _ptr(out), None, _ptr(ws), ctypes.c_size_t(_nbytes(ws)),
                                         _stream(q.device), flags, events)
     if st != 0:
         raise SlaError(st, "sla_forward_profiled")
@@ -250,16 +295,17 @@ def sla_kv_cache_update(k, v, proj_k, cache: torch.Tensor, n_done: int = 0, bloc
     """Bring ``cache`` (uint8 device tensor of at least kv_cache_size bytes) from the first
     n_done tokens of k, v to all of them (n_done = 0 builds it). Returns ``cache``."""
     p = make_problem(k, k, 0, block)
-    if cache.numel() < kv_cache_size(p):
+    _check(k, k, v, (proj_k,), buffers=(cache, workspace))
+    if _nbytes(cache) < kv_cache_size(p):
         raise ValueError("cache tensor too small")
     need = int(library().sla_kv_cache_workspace_size(ctypes.byref(p), int(n_done)))
     if need == 0:
         raise SlaError(2, "sla_kv_cache_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     st = library().sla_kv_cache_update(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(proj_k),
                                        int(n_done), _ptr(cache), _ptr(workspace),
-                                       ctypes.c_size_t(workspace.numel()), _stream(k.device))
+                                       ctypes.c_size_t(_nbytes(workspace)), _stream(k.device))
     if st != 0:
         raise SlaError(st, "sla_kv_cache_update")
     return cache
@@ -276,10 +322,11 @@ def sla_forward_cached(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor, 
     """SLA2 forward against a summary cache covering all of k, v. Returns (O, block_idx or
     None)."""
     p = make_problem(q, k, top_k, block, out_dtype)
+    _check(q, k, v, (proj_q,), alpha, out, out_dtype, (cache, workspace))
     need = cached_workspace_size(p)
     if need == 0:
         raise SlaError(2, "sla_cached_workspace_size")
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -289,7 +336,7 @@ def sla_forward_cached(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor, 
                           device=q.device)
     st = library().sla_forward_cached(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
                                       _ptr(alpha), _ptr(cache), _ptr(out), _ptr(idx),
-                                      _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                      _ptr(workspace), ctypes.c_size_t(_nbytes(workspace)),
                                       _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_forward_cached")
@@ -301,11 +348,12 @@ def sla_route_taylor(q, k, top_k: int, block: int = 64,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Training-free router: int32 block indices [B, H, ceil(n_q/block), top_k]."""
     p = make_problem(q, k, top_k, block)
-    ws = _workspace(p, False, q.device, workspace)
+    _check(q, k, buffers=(workspace,))
+    ws = _workspace(p, VARIANT_FORWARD, q.device, workspace)
     idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
                       device=q.device)
     st = library().sla_route_taylor(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(idx), _ptr(ws),
-                                    ctypes.c_size_t(ws.numel()), _stream(q.device))
+                                    ctypes.c_size_t(_nbytes(ws)), _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_route_taylor")
     return idx
@@ -317,7 +365,8 @@ def sla_forward_taylor(q, k, v, alpha, top_k: int, block: int = 64,
                        out: Optional[torch.Tensor] = None):
     """SLA2 forward with the training-free router. Returns (O, block_idx or None)."""
     p = make_problem(q, k, top_k, block, out_dtype)
-    ws = _workspace(p, False, q.device, workspace)
+    _check(q, k, v, alpha=alpha, out=out, out_dtype=out_dtype, buffers=(workspace,))
+    ws = _workspace(p, VARIANT_FORWARD, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     idx = None
@@ -325,7 +374,7 @@ def sla_forward_taylor(q, k, v, alpha, top_k: int, block: int = 64,
         idx = torch.empty((p.batch, p.heads, -(-p.n_q // block), top_k), dtype=torch.int32,
                           device=q.device)
     st = library().sla_forward_taylor(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                      _ptr(out), _ptr(idx), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                      _ptr(out), _ptr(idx), _ptr(ws), ctypes.c_size_t(_nbytes(ws)),
                                       _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_forward_taylor")
@@ -339,6 +388,7 @@ def sla_forward_pisa(q, k, v, proj_q, proj_k, top_k: int, block: int = 64,
     """Piecewise exact-or-approximate forward (learnable router; exact routed blocks, Taylor
     tail for the rest, one normalisation). Returns (O, block_idx or None)."""
     p = make_problem(q, k, top_k, block, out_dtype)
+    _check(q, k, v, (proj_q, proj_k), out=out, out_dtype=out_dtype, buffers=(workspace,))
     ws = _workspace(p, VARIANT_PISA, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -348,7 +398,7 @@ def sla_forward_pisa(q, k, v, proj_q, proj_k, top_k: int, block: int = 64,
                           device=q.device)
     st = library().sla_forward_pisa(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(proj_q),
                                     _ptr(proj_k), _ptr(out), _ptr(idx), _ptr(ws),
-                                    ctypes.c_size_t(ws.numel()), _stream(q.device))
+                                    ctypes.c_size_t(_nbytes(ws)), _stream(q.device))
     if st != 0:
         raise SlaError(st, "sla_forward_pisa")
     return out, idx

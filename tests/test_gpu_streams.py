@@ -157,3 +157,25 @@ def test_heads_are_isolated_with_ragged_blocks(sla, variant):
         call2()
         torch.cuda.synchronize()
         assert torch.equal(out2[0, h_keep], base[0, h_keep]), (variant, h_keep)
+
+
+def test_binding_refuses_mismatched_tensors(sla):
+    """Checks that the C ABI cannot make: dtypes, shapes and devices of every tensor."""
+    x = make_custom(1, 2, 128, 256, 64, 2, dtype="bf16", kind="normal", seed=3)
+    q, k, v, pq, pk, al = to_device(x)
+    bad = [
+        ({"v": v.float()}, "v must match k"),
+        ({"v": v[:, :, :128].contiguous()}, "v must match k"),
+        ({"pq": pq.double()}, "proj"),
+        ({"pk": pk[:32].contiguous()}, "proj"),
+        ({"al": al[:1].contiguous()}, "alpha"),
+        ({"al": al.cpu()}, "alpha is on"),
+        ({"out": torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)}, "out must be"),
+    ]
+    for change, msg in bad:
+        a = {"v": v, "pq": pq, "pk": pk, "al": al, "out": None}
+        a.update(change)
+        with pytest.raises(ValueError, match=msg):
+            sla.sla_forward(q, k, a["v"], a["pq"], a["pk"], a["al"], 2, out=a["out"])
+    with pytest.raises(TypeError, match="k has dtype"):
+        sla.sla_forward(q, k.float(), v.float(), pq, pk, al, 2)
