@@ -47,7 +47,7 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // (bf16 hi + lo, [BH][npad][D]) and its row of the value-sum table ([BH][npad][D] f16) are
 // written.
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
-__global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_kernel(
+__global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
@@ -64,8 +64,11 @@ __global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_ker
   constexpr int NT = D / 32;                 // 32-wide tiles per dimension
   constexpr int TILES_PER_WAVE = NT * NT / 4;
   constexpr int EPC = sizeof(T) == 2 ? 1 : 2;   // 16-byte loads per 8-element chunk
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LS];
+  // K and V tiles, one array: the full forward stages each block's S_j^T over both
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[2 * 64 * LS];
+  uint16_t* const Ks = KVs;
+  uint16_t* const Vs = KVs + 64 * LS;
+  static_assert(D * LS <= 2 * 64 * LS, "S_j^T staging fits the K and V tiles");
   __shared__ double pool_lds[4 * D];          // per-wave block sums (rows folded by shuffles)
   __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
   __shared__ double vpool_lds[PISA ? 4 * D : 1];
@@ -209,23 +212,39 @@ __global__ __launch_bounds__(256, (BLOCKS && !PISA) ? 3 : 2) void kv_summary_ker
       zblk[((size_t)bh * nbk + j) * D + 32 * mt + l32] = zl;
     }
     zp += zl;
+    f32x16 accs[TILES_PER_WAVE];
 #pragma unroll
     for (int u = 0; u < TILES_PER_WAVE; ++u) {
       const int nt = (NT == 4) ? u : (w & 1);
-      f32x16 acc = {};
+      accs[u] = f32x16{};
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) acc = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), acc);
-      if constexpr (TOTALS) part[u] += acc;
-      if constexpr (BLOCKS && !PISA) {
-        // store S_j^T[c][r] (bf16): lane column c = 32 nt + l32, rows r in runs of 4
-        const int c = 32 * nt + l32;
-        uint16_t* dst = sblk + (((size_t)bh * nbk + j) * D + c) * D;
+      for (int s4 = 0; s4 < 4; ++s4)
+        accs[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), accs[u]);
+      if constexpr (TOTALS) part[u] += accs[u];
+    }
+    if constexpr (BLOCKS && !PISA) {
+      // S_j^T[c][r] (bf16) goes out in whole 2D-byte rows: staged over the K and V tiles
+      // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
+      // Lane column c = 32 nt + l32 holds rows r in runs of 4.
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < TILES_PER_WAVE; ++u) {
+        const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 32 * mt + 8 * q + 4 * h;
-          *reinterpret_cast<u32x2*>(dst + r) = u32x2{pack_bf16(acc[4 * q], acc[4 * q + 1]),
-                                                     pack_bf16(acc[4 * q + 2], acc[4 * q + 3])};
+          *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
+              u32x2{pack_bf16(accs[u][4 * q], accs[u][4 * q + 1]),
+                    pack_bf16(accs[u][4 * q + 2], accs[u][4 * q + 3])};
         }
+      }
+      __syncthreads();
+      uint16_t* dst = sblk + ((size_t)bh * nbk + j) * D * D;
+#pragma unroll
+      for (int e = t; e < D * D / 8; e += 256) {
+        const int c = e / (D / 8), ch = e % (D / 8);
+        *reinterpret_cast<u32x4*>(dst + c * D + ch * 8) =
+            *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
       }
     }
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
