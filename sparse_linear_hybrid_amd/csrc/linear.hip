@@ -46,6 +46,12 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // H_j = sum_n (k_n - k_bar_j)^T v_n; no S_j or z_j is stored; instead each block's centroid
 // (bf16 hi + lo, [BH][npad][D]) and its row of the value-sum table ([BH][npad][D] f16) are
 // written.
+// The per-block summaries S_j^T are stored slice-major: the flattened d x d matrix (row c,
+// column r at c d + r) is cut into slices of kSlice consecutive elements, and slice s of
+// every key block of a (batch, head) is contiguous: [BH][d d / kSlice][nbk][kSlice]. The
+// complement reads one slice of consecutive key blocks per step.
+constexpr int kSlice = 128;
+
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
 __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
@@ -200,7 +206,8 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         const float mr = (float)means[(j - j0) % kSummaryChunk][32 * mt + l32];
         const u32x4 raw = frag_tr(Ks, LS, 32 * mt, 16 * s4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) af[s4][e] = pack_bf16(bf16_lo(raw[e]) - mr, bf16_hi(raw[e]) - mr);
+        for (int e = 0; e < 4; ++e)
+          af[s4][e] = pack_bf16(bf16_lo(raw[e]) - mr, bf16_hi(raw[e]) - mr);
       } else {
         af[s4] = relu_bf16x8(frag_tr(Ks, LS, 32 * mt, 16 * s4));
 #pragma unroll
@@ -239,12 +246,13 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         }
       }
       __syncthreads();
-      uint16_t* dst = sblk + ((size_t)bh * nbk + j) * D * D;
 #pragma unroll
       for (int e = t; e < D * D / 8; e += 256) {
         const int c = e / (D / 8), ch = e % (D / 8);
-        *reinterpret_cast<u32x4*>(dst + c * D + ch * 8) =
-            *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
+        const int f = c * D + ch * 8;             // flattened index of the chunk
+        uint16_t* dst = sblk + (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
+                        f % kSlice;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
       }
     }
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(256) void reduce_totals_kernel(const float* __restr
 // column slice are consecutive workgroups (same XCD), so each S_j slice comes from HBM
 // about once and from L2 ceil(n_blocks / CQ) times.
 constexpr int CQ = 256;    // query blocks per workgroup (64 per wave)
-constexpr int CN = 128;    // summary columns per workgroup
+constexpr int CN = kSlice; // summary columns per workgroup: one slice
 constexpr int CK = 32;     // key blocks per step = bits per bitmap word
 constexpr int CBUF = 6;    // steps in the LDS ring (three pairs)
 constexpr int MAXW = 30;   // bitmap words per query block and window (window <= 960 blocks)
@@ -442,13 +450,13 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
 #pragma unroll
   for (int u = 0; u < LPW; ++u) {
     const int r = 4 * (LPW * w + u) + (lane >> 4), pch = lane & 15;
-    roff[u] = (uint32_t)((size_t)r * D * D * 2 + ((pch ^ ring_f(r)) & 15) * 16);
+    roff[u] = (uint32_t)(r * CN * 2 + ((pch ^ ring_f(r)) & 15) * 16);
   }
   const int ws = __builtin_amdgcn_readfirstlane(w);
-  const uint16_t* sbase = sblk + (size_t)bh * nbk * D * D + col0;
+  const uint16_t* sbase = sblk + ((size_t)bh * NCS + cs) * nbk * CN;   // this slice, block 0
   auto stage = [&](int j0, int slot) __attribute__((always_inline)) {   // j0 < 0: nothing
-    const uint32_t bytes = j0 < 0 ? 0u : (uint32_t)min(CK, nbk - j0) * D * D * 2;
-    const i32x4 r = make_rsrc(sbase + (size_t)(j0 < 0 ? 0 : j0) * D * D, bytes);
+    const uint32_t bytes = j0 < 0 ? 0u : (uint32_t)min(CK, nbk - j0) * CN * 2;
+    const i32x4 r = make_rsrc(sbase + (size_t)(j0 < 0 ? 0 : j0) * CN, bytes);
     const uint32_t dst = lds_addr(ring + slot * CK * CN) + ws * LPW * 1024;
 #pragma unroll
     for (int u = 0; u < LPW; ++u) load_lds16(r, dst + u * 1024, roff[u]);
@@ -474,7 +482,8 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       for (int wi = 0; wi < MAXW; ++wi) {
         // unselected valid key blocks of this word (bits past nbk stay clear)
         const int jb = (w0 + wi) * CK;
-        const uint32_t valid = nbk - jb >= CK ? 0xffffffffu : (nbk > jb ? (1u << (nbk - jb)) - 1u : 0u);
+        const uint32_t valid =
+            nbk - jb >= CK ? 0xffffffffu : (nbk > jb ? (1u << (nbk - jb)) - 1u : 0u);
         wv_[wi] = wi < nw ? ~my_bits[w0 + wi] & valid : 0u;
       }
 #pragma unroll
@@ -568,7 +577,8 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       const int q = 4 * u + (lane >> 4), c = lane & 15;
       const int i = qt * CQ + 64 * w + 32 * tq + q;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stg + q * CN + (((c ^ q) & 15) << 3));
-      if (i < nbq) *reinterpret_cast<u32x4*>(sc + ((size_t)bh * nbq + i) * D * D + col0 + c * 8) = v;
+      if (i < nbq)
+        *reinterpret_cast<u32x4*>(sc + ((size_t)bh * nbq + i) * D * D + col0 + c * 8) = v;
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -615,7 +625,8 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   const dim3 grid(s.nchunk, s.BH);
   const size_t kbh = (size_t)s.nbk * D, kj = D;
   if (s.in_bf16)
-    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0,
+                       st,
                        (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
                        spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
   else
