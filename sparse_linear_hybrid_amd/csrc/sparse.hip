@@ -228,22 +228,25 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   }
   // j < 0: an absent tile; the loads then cover an empty range (no memory access) so that
   // every step issues the same number of loads, which the vmcnt waits below rely on.
-  auto stage_k = [&](int j, uint16_t* slot) __attribute__((always_inline)) {
+  // (pieces u0 .. u1 - 1 of this wave's share)
+  auto stage_k = [&](int j, uint16_t* slot, int u0, int u1)
+                     __attribute__((always_inline)) {
     const int row0 = j < 0 ? 0 : j * kBlock;
     const uint32_t bytes = j < 0 ? 0u : (uint32_t)(min(kBlock, a.nkv - row0) * D * 2);
     const auto r = make_rsrc(kb + (size_t)row0 * D, bytes);
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int pp = wvs * KPW + u;
       const uint32_t xo = D == 128 ? (uint32_t)((pp & 3) << 6) : 0u;
       load_lds16(r, lds_addr(slot) + pp * 1024, (uint32_t)(pp * 1024) + (klane ^ xo));
     }
   };
-  auto stage_v = [&](int j, uint16_t* slot) __attribute__((always_inline)) {
+  auto stage_v = [&](int j, uint16_t* slot, int u0, int u1)
+                     __attribute__((always_inline)) {
     const int row0 = j < 0 ? 0 : j * kBlock;
     const auto r = make_rsrc(vb + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D * 2));
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int pp = wvs * KPW + u;
       load_lds16(r, lds_addr(slot) + pp * 1024, (uint32_t)(pp * 1024) + vlane);
     }
@@ -360,18 +363,25 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
       }
     }
   };
-  auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j)
-                          __attribute__((always_inline)) {
+  // ld(p), p = 0 .. 3: a quarter of this step's tile loads into LDS, issued between the
+  // phases so that the loads leave while the MFMAs of the phase before them run
+  auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j,
+                          auto&& ld) __attribute__((always_inline)) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};
+    ld(0);
     qk_half(Kt, Klo, 0, s0);
+    ld(1);
     check_half(s0, 0, j);
     qk_half(Kt, Klo, 1, s1);
+    ld(2);
     exp_half(s0, 0);
     check_half(s1, 1, j);
+    ld(3);
     pv_half(Vt, 0);
     exp_half(s1, 1);
     pv_half(Vt, 1);
   };
+  auto no_loads = [](int) __attribute__((always_inline)) {};
 
   if constexpr (DMA) {
     // Ring pipeline. Step s computes tile s while V(s+1) and K(s+2) load (issued in that
@@ -386,9 +396,9 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
     int j0, f0, j1, f1;
     bool have0 = walk.next_direct(j0, f0);
     bool have1 = walk.next_direct(j1, f1);
-    stage_k(have0 ? j0 : -1, kring);
-    stage_k(have1 ? j1 : -1, kring + TILE);
-    stage_v(have0 ? j0 : -1, vring);
+    stage_k(have0 ? j0 : -1, kring, 0, KPW);
+    stage_k(have1 ? j1 : -1, kring + TILE, 0, KPW);
+    stage_v(have0 ? j0 : -1, vring, 0, KPW);
     walk.fill();
     barrier_vmem_n<0>();
     int ks = 0, vs = 0;
@@ -396,9 +406,20 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
       int j2, f2;
       const bool have2 = walk.next(j2, f2);
       const int ks2 = ks == 0 ? 2 : ks - 1;          // (ks + 2) % 3
-      stage_v(have1 ? j1 : -1, vring + (vs ^ 1) * TILE);
-      stage_k(have2 ? j2 : -1, kring + ks2 * TILE);
-      if ((f0 >> qb) & 1) compute_tile(kring + ks * TILE, nullptr, vring + vs * TILE, j0);
+      // V(s + 1) pieces first, then K(s + 2): the wait below counts on that order
+      const int jv = have1 ? j1 : -1, jk = have2 ? j2 : -1;
+      uint16_t* const vdst = vring + (vs ^ 1) * TILE;
+      uint16_t* const kdst = kring + ks2 * TILE;
+      if ((f0 >> qb) & 1) {
+        compute_tile(kring + ks * TILE, nullptr, vring + vs * TILE, j0,
+                     [&](int p) __attribute__((always_inline)) {
+                       if (p < 2) stage_v(jv, vdst, p * KPW / 2, (p + 1) * KPW / 2);
+                       else stage_k(jk, kdst, (p - 2) * KPW / 2, (p - 1) * KPW / 2);
+                     });
+      } else {
+        stage_v(jv, vdst, 0, KPW);
+        stage_k(jk, kdst, 0, KPW);
+      }
       barrier_vmem_n<KPW>();
       j0 = j1; f0 = f1; have0 = have1;
       j1 = j2; f1 = f2; have1 = have2;
@@ -421,7 +442,8 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
       const bool have_nxt = walk.next(j_nxt, f_nxt);
       if (have_nxt) load_tile(j_nxt);
       if ((f_cur >> qb) & 1)
-        compute_tile(smem + B * TILE, smem + (4 + B) * TILE, smem + (2 + B) * TILE, j_cur);
+        compute_tile(smem + B * TILE, smem + (4 + B) * TILE, smem + (2 + B) * TILE, j_cur,
+                     no_loads);
       if (have_nxt) store_tile(B ^ 1);
       __syncthreads();
       j_cur = j_nxt;
