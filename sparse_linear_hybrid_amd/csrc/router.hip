@@ -502,6 +502,112 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ sco
   }
 }
 
+// Rows of at most 64 * KPL key blocks (0 < k < nbk): one wave per row with its keys in
+// registers (KPL per lane) and no histogram. The k-th largest key T is found one bit at a
+// time, most significant first: a candidate bit is kept when at least k keys are >= the
+// candidate, counted with one compare per key whose wave mask is popcounted. Keys above the
+// undecided range of T are carried as a count; once at most 64 keys remain inside that range
+// they are gathered one per lane (through LDS) and the remaining bits compare only those. The
+// search stops as soon as exactly k keys are >= the candidate (then those k are the
+// selection); otherwise it ends with T exact, and every key > T is kept plus the lowest-index
+// keys == T. Same selection, ascending output and bitmap rows as topk_kernel.
+// Four rows (one per wave) per workgroup; the waves never wait for each other.
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_reg_kernel(const double* __restrict__ scores,
+                                                       int32_t* __restrict__ idx,
+                                                       uint32_t* __restrict__ bits, int rows,
+                                                       int nbk, int k, int nwords) {
+  __shared__ uint64_t bucket_all[4][64];
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;   // whole waves only
+  uint64_t* bucket = bucket_all[threadIdx.x >> 6];
+  const double* s = scores + (size_t)row * nbk;
+  int32_t* out = idx + (size_t)row * k;
+  uint32_t* brow = bits ? bits + (size_t)row * nwords : nullptr;
+  uint64_t key[KPL];   // padding (j >= nbk) is 0: below every candidate, never counted
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int j = 64 * u + lane;
+    key[u] = j < nbk ? score_key(s[j]) : 0ull;
+  }
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  uint64_t T = 0;
+  bool exact = false;
+  // Undecided range of T after deciding bits 63 .. b: [T, T + 2^b). ge: keys >= T (valid
+  // keys only), above: keys >= T + 2^b.
+  int ge = nbk, above = 0, bit = 63;
+  for (; bit >= 0; --bit) {
+    const uint64_t c = T | (1ull << bit);
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) n += __popcll(__ballot(key[u] >= c));
+    if (n >= k) {
+      T = c;
+      ge = n;
+      if (n == k) {
+        exact = true;
+        break;
+      }
+    } else {
+      above = n;
+    }
+    if (ge - above <= 64) break;   // few keys left inside the range: gather them
+  }
+  if (!exact && bit > 0) {
+    // gather the keys in [T, T + 2^bit) (valid ones), then decide bits bit-1 .. 0 on them
+    const uint64_t hi = T + (1ull << bit);   // no overflow: bits below `bit` of T are 0
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const bool in = 64 * u + lane < nbk && key[u] >= T && (hi == 0 || key[u] < hi);
+      const unsigned long long m = __ballot(in);
+      if (in) bucket[base + __popcll(m & lt_mask)] = key[u];
+      base += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // this wave's writes, then reads
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint64_t bk = lane < base ? bucket[lane] : 0ull;
+    for (--bit; bit >= 0; --bit) {
+      const uint64_t c = T | (1ull << bit);
+      const int n = above + __popcll(__ballot(bk >= c));
+      if (n >= k) {
+        T = c;
+        if (n == k) {
+          exact = true;
+          break;
+        }
+      }
+    }
+  }
+  int remaining = 0;   // keys == T to keep, lowest index first
+  if (!exact) {
+    int n_gt = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) n_gt += __popcll(__ballot(key[u] > T));
+    remaining = k - n_gt;
+  }
+  int written = 0, eq_seen = 0;
+#pragma unroll
+  for (int u = 0; u < KPL; ++u) {
+    const int j = 64 * u + lane;
+    if (64 * u >= nbk) break;   // uniform
+    const bool valid = j < nbk;
+    const bool gt = valid && (exact ? key[u] >= T : key[u] > T);
+    const bool eq = !exact && valid && key[u] == T;
+    const unsigned long long eqb = __ballot(eq);
+    const int eq_rank = eq_seen + __popcll(eqb & lt_mask);
+    const bool sel = gt || (eq && eq_rank < remaining);
+    const unsigned long long sb = __ballot(sel);
+    if (sel) out[written + __popcll(sb & lt_mask)] = j;
+    if (brow && lane < 2 && 2 * u + lane < nwords)
+      brow[2 * u + lane] = (uint32_t)(sb >> (32 * lane));
+    written += __popcll(sb);
+    eq_seen += __popcll(eqb);
+  }
+}
+
 // ----------------------------------------------------------------------------- launchers
 template <int D>
 static void launch_pool_q(const Plan& s, const void* q, const float* pq, double* qt,
@@ -537,7 +643,18 @@ static void launch_select(const Plan& s, const double* qt, const double* kt, con
       hipLaunchKernelGGL((score_kernel<D, false>), gt, dim3(256), 0, st, qt, kt, kv, sc, s.nbq,
                          s.nbk, kbh, kj);
   }
-  if (s.k > 0 || bits) {
+  if (s.k > 0 && s.k < s.nbk && s.nbk <= 64 * 32) {   // keys fit in registers
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((rq + 3) / 4), dim3(256), 0, st, sc, idx, bits, rq, s.nbk,
+                         s.k, s.nwords);
+    };
+    if (s.nbk <= 64 * 8) go(topk_reg_kernel<8>);
+    else if (s.nbk <= 64 * 12) go(topk_reg_kernel<12>);
+    else if (s.nbk <= 64 * 16) go(topk_reg_kernel<16>);
+    else if (s.nbk <= 64 * 20) go(topk_reg_kernel<20>);
+    else if (s.nbk <= 64 * 24) go(topk_reg_kernel<24>);
+    else go(topk_reg_kernel<32>);
+  } else if (s.k > 0 || bits) {
     const size_t lds = (size_t)s.nbk * 8 + 256 * 4;
     hipLaunchKernelGGL(topk_kernel, dim3(rq), dim3(64), lds, st, sc, idx, bits, rq, s.nbk, s.k,
                        s.nwords);
