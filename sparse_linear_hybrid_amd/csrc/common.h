@@ -191,6 +191,60 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return slot < cnt ? start + slot : w;
 }
 
+// ----------------------------------------------------------------------------- E4M3 blocks
+// Block exponent for E4M3 (SLA2 page, section 2.C, quantised sparse branch): the smallest
+// integer e with 448 * 2^e >= absmax (0 for an all-zero block).
+__device__ __forceinline__ int e8m0_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int ex;
+  (void)frexpf(amax / 448.f, &ex);
+  int e = ex;
+  while (448.f * ldexpf(1.f, e - 1) >= amax) --e;    // exact: products with powers of two
+  while (448.f * ldexpf(1.f, e) < amax) ++e;
+  return e;
+}
+// position (0..63) of key k inside a V8 tile row (the P8 operand order of P.V)
+__device__ __forceinline__ int v8_slot_pos(int k) {
+  const int mt = k >> 5, rem = k & 31;
+  const int g = rem >> 3, hh = (rem >> 2) & 1, i = rem & 3;
+  return 32 * hh + 16 * mt + 4 * g + i;
+}
+// E4M3 byte -> the same value as bf16 (exact: E4M3 has at most 4 significant bits and its
+// exponent range lies inside bf16's).
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
+  const uint32_t sgn = (c & 0x80u) << 8;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  // subnormal: m * 2^-9, exact in fp32 and in its top 16 bits
+  if (e == 0) return sgn | (__float_as_uint((float)m * 0x1p-9f) >> 16);
+  return sgn | ((e - 7 + 127) << 7) | (m << 4);
+}
+// 8 values scaled by 2^-e (exact) and rounded once to E4M3 (hardware round-to-nearest-even):
+// bytes 0..3 in w0, 4..7 in w1
+__device__ __forceinline__ void e4m3x8(const float (&v)[8], int e, uint32_t& w0, uint32_t& w1) {
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[0], -e), ldexpf(v[1], -e), 0u, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[2], -e), ldexpf(v[3], -e), w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -e), ldexpf(v[5], -e), 0u, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -e), ldexpf(v[7], -e), w1, true);
+}
+// 8 E4M3 bytes (w0, w1) as 8 bf16 values
+__device__ __forceinline__ u32x4 e4m3x8_as_bf16(uint32_t w0, uint32_t w1) {
+  u32x4 o;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    o[b] = e4m3_to_bf16((w0 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w0 >> (16 * b + 8)) & 0xffu) << 16);
+    o[2 + b] = e4m3_to_bf16((w1 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w1 >> (16 * b + 8)) & 0xffu) << 16);
+  }
+  return o;
+}
+// Outputs of the E4M3 quantisation of K and V when the key/value pass does it (fp8 forward):
+// K8 [BH][nb*64][D] bf16-held, V8 tiles [BH][nb][D][64] bytes, block exponents [BH][nb].
+struct Fp8Out {
+  uint8_t* k8;
+  uint8_t* v8;
+  int32_t* ek;
+  int32_t* ev;
+};
+
 // ----------------------------------------------------------------------------- workspace
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

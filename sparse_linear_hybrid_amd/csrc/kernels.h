@@ -13,7 +13,7 @@ hipError_t launch_route(const Plan& s, const void* q, const void* k, const float
 // Linear branch, part 1 (independent of routing): per key block phi(K)^T V, sum phi(K),
 // the projected pooled K (for the router), an f16 copy of V, and the per-head totals.
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk, char* ws,
-                             hipStream_t st);
+                             hipStream_t st, bool fp8 = false);
 
 // Linear branch, part 2: complement = total - selected, per query block.
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);

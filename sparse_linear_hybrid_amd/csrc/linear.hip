@@ -52,15 +52,20 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 // complement reads one slice of consecutive key blocks per step.
 constexpr int kSlice = 128;
 
-template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false>
+// FP8 (fp8 forward, bf16 inputs; needs BLOCKS): the pass also quantises each block of K and V
+// to E4M3 exactly as the quantiser does (block absmax over the valid tokens, power-of-two
+// scale, one rounding), from the tiles it has staged in LDS, and writes K8, the V8 tiles and
+// the block exponents (Fp8Out).
+template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false>
 __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
     float* __restrict__ zpart, int nkv, int nbk, int jbase, int t0,
     uint16_t* __restrict__ cent_hi, uint16_t* __restrict__ cent_lo, uint16_t* __restrict__ vsum,
-    int npad) {
+    int npad, Fp8Out f8) {
   static_assert(!PISA || BLOCKS, "the piecewise pass is a full-forward pass");
+  static_assert(!FP8 || (BLOCKS && !PISA && sizeof(T) == 2), "fused E4M3: bf16 full forward");
   // The SLA2 forward's complement sums the unselected S_j itself, so its pass keeps no d x d
   // chunk totals (only the z partials); the cache update and the piecewise pass do.
   constexpr bool TOTALS = !BLOCKS || PISA;
@@ -78,6 +83,8 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
   __shared__ double pool_lds[4 * D];          // per-wave block sums (rows folded by shuffles)
   __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
   __shared__ double vpool_lds[PISA ? 4 * D : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t vt8[FP8 ? D * 64 : 16];   // V8 tile
+  __shared__ float amax_lds[8];                                             // per wave: K, V
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
@@ -115,6 +122,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     double pacc[8], vacc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pacc[e] = vacc[e] = 0.0;
+    float kmx = 0.f, vmx = 0.f;   // FP8: absmax of the valid tokens
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = t + 256 * u;
@@ -141,6 +149,10 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         kf[e] = ok_sum ? kf[e] : 0.f;
         vf[e] = ok_sum ? vf[e] : 0.f;
         if constexpr (PISA) vacc[e] += (double)vf[e];
+        if constexpr (FP8) {
+          kmx = fmaxf(kmx, fabsf(kf[e]));
+          vmx = fmaxf(vmx, fabsf(vf[e]));
+        }
       }
       u32x4 kw, vw;
 #pragma unroll
@@ -177,6 +189,17 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         }
       }
     }
+    if constexpr (FP8) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
+        vmx = fmaxf(vmx, __shfl_xor(vmx, o, 64));
+      }
+      if (lane == 0) {
+        amax_lds[2 * w] = kmx;
+        amax_lds[2 * w + 1] = vmx;
+      }
+    }
     if (j + 1 < j1) load_block(j + 1);   // in flight during this block's compute
     __syncthreads();
     if (t < D) {
@@ -192,6 +215,41 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         double vs = 0.0;
         for (int ww_ = 0; ww_ < 4; ++ww_) vs += vpool_lds[ww_ * D + t];
         vsum[((size_t)bh * npad + j) * D + t] = (uint16_t)(f16_sat_pack((float)vs, 0.f) & 0xffffu);
+      }
+    }
+    if constexpr (FP8) {
+      // E4M3 of this thread's chunks, read back from the staged (masked) tiles
+      const int ek = e8m0_exponent(fmaxf(fmaxf(amax_lds[0], amax_lds[2]),
+                                         fmaxf(amax_lds[4], amax_lds[6])));
+      const int ev = e8m0_exponent(fmaxf(fmaxf(amax_lds[1], amax_lds[3]),
+                                         fmaxf(amax_lds[5], amax_lds[7])));
+      if (t == 0) {
+        f8.ek[(size_t)bh * nbk + j] = ek;
+        f8.ev[(size_t)bh * nbk + j] = ev;
+      }
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int cidx = t + 256 * u;
+        const int r = cidx / TPR, c8 = cidx % TPR;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(&Ks[r * LS + c8 * 8]);
+        const u32x4 vw = *reinterpret_cast<const u32x4*>(&Vs[r * LS + c8 * 8]);
+        float kf[8], vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kf[2 * e] = bf16_lo(kw[e]); kf[2 * e + 1] = bf16_hi(kw[e]);
+          vf[2 * e] = bf16_lo(vw[e]); vf[2 * e + 1] = bf16_hi(vw[e]);
+        }
+        uint32_t w0, w1;
+        e4m3x8(kf, ek, w0, w1);
+        *reinterpret_cast<u32x4*>(f8.k8 + (((size_t)bh * nbk * kBlock + row0 + r) * D + c8 * 8) * 2) =
+            e4m3x8_as_bf16(w0, w1);
+        e4m3x8(vf, ev, w0, w1);
+        const int pos = v8_slot_pos(r);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          vt8[(c8 * 8 + b) * 64 + pos] = (uint8_t)(w0 >> (8 * b));
+          vt8[(c8 * 8 + 4 + b) * 64 + pos] = (uint8_t)(w1 >> (8 * b));
+        }
       }
     }
     if constexpr (PISA) __syncthreads();   // block means are read by every wave below
@@ -234,6 +292,11 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
       // Lane column c = 32 nt + l32 holds rows r in runs of 4.
       __syncthreads();
+      if constexpr (FP8) {   // the V8 tile (complete after the barrier) goes out
+        uint8_t* dst = f8.v8 + ((size_t)bh * nbk + j) * D * 64;
+        for (int id = t; id < D * 64 / 16; id += 256)
+          *reinterpret_cast<u32x4*>(dst + id * 16) = *reinterpret_cast<const u32x4*>(&vt8[id * 16]);
+      }
 #pragma unroll
       for (int u = 0; u < TILES_PER_WAVE; ++u) {
         const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
@@ -615,7 +678,7 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
 
 template <int D>
 static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* v, const float* pk,
-                                      char* ws, hipStream_t st) {
+                                      char* ws, hipStream_t st, bool fp8) {
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + s.v16);
   uint16_t* sblk = reinterpret_cast<uint16_t*>(ws + s.sblk);
@@ -624,15 +687,24 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   float* zpart = reinterpret_cast<float*>(ws + s.zpart);
   const dim3 grid(s.nchunk, s.BH);
   const size_t kbh = (size_t)s.nbk * D, kj = D;
-  if (s.in_bf16)
+  if (s.in_bf16 && fp8)
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, false, true>), grid,
+                       dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj,
+                       v16, sblk, zblk, spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr,
+                       nullptr, 0,
+                       Fp8Out{reinterpret_cast<uint8_t*>(ws + s.k8),
+                              reinterpret_cast<uint8_t*>(ws + s.v8),
+                              reinterpret_cast<int32_t*>(ws + s.sk8),
+                              reinterpret_cast<int32_t*>(ws + s.sv8)});
+  else if (s.in_bf16)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0,
                        st,
                        (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
-                       spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
+                       spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0, Fp8Out{});
   else
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
                        (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
-                       zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0);
+                       zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0, Fp8Out{});
   // only z_tot: the complement sums the unselected S_j itself
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
@@ -655,11 +727,11 @@ static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* 
   if (s.in_bf16)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, true>), grid, dim3(256),
                        0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16,
-                       nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad);
+                       nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad, Fp8Out{});
   else
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk, true>), grid, dim3(256), 0,
                        st, (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, nullptr,
-                       nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad);
+                       nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad, Fp8Out{});
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.p_stot),
                      reinterpret_cast<float*>(ws + s.p_ztot), s.nchunk, 0,
@@ -681,7 +753,7 @@ static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const v
   hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false, kCacheChunk>), grid, dim3(256), 0, st,
                      (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
                      (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
-                     jbase, n_done, nullptr, nullptr, nullptr, 0);
+                     jbase, n_done, nullptr, nullptr, nullptr, 0, Fp8Out{});
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(cache + c.stot),
                      reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
@@ -697,9 +769,9 @@ hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, c
 }
 
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk,
-                             char* ws, hipStream_t st) {
-  if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st);
-  return launch_kv_summary_T<64>(s, k, v, pk, ws, st);
+                             char* ws, hipStream_t st, bool fp8) {
+  if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st, fp8);
+  return launch_kv_summary_T<64>(s, k, v, pk, ws, st, fp8);
 }
 
 hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const float* pk,

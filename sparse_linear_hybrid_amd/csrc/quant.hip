@@ -23,33 +23,6 @@
 
 namespace sla {
 
-__device__ __forceinline__ int e8m0_exponent(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int ex;
-  (void)frexpf(amax / 448.f, &ex);
-  int e = ex;
-  while (448.f * ldexpf(1.f, e - 1) >= amax) --e;    // exact: products with powers of two
-  while (448.f * ldexpf(1.f, e) < amax) ++e;
-  return e;
-}
-
-// position (0..63) of key k inside a V8 tile row
-__device__ __forceinline__ int v8_slot_pos(int k) {
-  const int mt = k >> 5, rem = k & 31;
-  const int g = rem >> 3, hh = (rem >> 2) & 1, i = rem & 3;
-  return 32 * hh + 16 * mt + 4 * g + i;
-}
-
-// E4M3 byte -> the same value as bf16 (exact: E4M3 has at most 4 significant bits and its
-// exponent range lies inside bf16's).
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
-  const uint32_t sgn = (c & 0x80u) << 8;
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  // subnormal: m * 2^-9, exact in fp32 and in its top 16 bits
-  if (e == 0) return sgn | (__float_as_uint((float)m * 0x1p-9f) >> 16);
-  return sgn | ((e - 7 + 127) << 7) | (m << 4);
-}
-
 template <int D, bool VTILE>
 __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__ x,
                                                     uint8_t* __restrict__ x8,
@@ -86,19 +59,11 @@ __global__ __launch_bounds__(256) void quant_kernel(const uint16_t* __restrict__
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int id = t + 256 * u, r = id / CH, c = id % CH;
-    uint32_t w0 = 0, w1 = 0;
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[u][0], -e), ldexpf(v[u][1], -e), w0, false);
-    w0 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[u][2], -e), ldexpf(v[u][3], -e), w0, true);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[u][4], -e), ldexpf(v[u][5], -e), w1, false);
-    w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[u][6], -e), ldexpf(v[u][7], -e), w1, true);
+    uint32_t w0, w1;
+    e4m3x8(v[u], e, w0, w1);
     if constexpr (!VTILE) {
-      u32x4 o;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        o[b] = e4m3_to_bf16((w0 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w0 >> (16 * b + 8)) & 0xffu) << 16);
-        o[2 + b] = e4m3_to_bf16((w1 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w1 >> (16 * b + 8)) & 0xffu) << 16);
-      }
-      *reinterpret_cast<u32x4*>(x8 + (((size_t)bh * nb * kBlock + row0 + r) * D + c * 8) * 2) = o;
+      *reinterpret_cast<u32x4*>(x8 + (((size_t)bh * nb * kBlock + row0 + r) * D + c * 8) * 2) =
+          e4m3x8_as_bf16(w0, w1);
     } else {
       const int pos = v8_slot_pos(r);
 #pragma unroll
@@ -122,6 +87,7 @@ static hipError_t launch_quant_T(const Plan& s, const void* q, const void* k, co
   hipLaunchKernelGGL((quant_kernel<D, false>), dim3(s.nbq, s.BH), dim3(256), 0, st,
                      (const uint16_t*)q, reinterpret_cast<uint8_t*>(ws + s.q8),
                      reinterpret_cast<int32_t*>(ws + s.sq8), s.nq, s.nbq);
+  if (k == nullptr) return hipGetLastError();   // K and V quantised by the key/value pass
   hipLaunchKernelGGL((quant_kernel<D, false>), dim3(s.nbk, s.BH), dim3(256), 0, st,
                      (const uint16_t*)k, reinterpret_cast<uint8_t*>(ws + s.k8),
                      reinterpret_cast<int32_t*>(ws + s.sk8), s.nkv, s.nbk);

@@ -66,7 +66,7 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   if (mode == Fwd::kPisa) {
     if (!ok(launch_pisa_stats(s, k, v, proj_k, ws, stream))) return SLA_ERR_HIP;
   } else if (!ok(launch_kv_summary(s, k, v, mode == Fwd::kTaylor ? nullptr : proj_k, ws,
-                                   stream))) {
+                                   stream, /*fp8=*/mode == Fwd::kFp8))) {
     return SLA_ERR_HIP;
   }
   if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY + 1))) return SLA_ERR_HIP;
@@ -89,7 +89,10 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   }
   if (!ok(mark(2 * SLA_STAGE_COMPLEMENT + 1))) return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_QUANT))) return SLA_ERR_HIP;
-  if (mode == Fwd::kFp8 && !ok(launch_quant(s, q, k, v, ws, stream))) return SLA_ERR_HIP;
+  // fp8: Q is quantised here; K and V already were, by the key/value pass (bf16 inputs)
+  if (mode == Fwd::kFp8 && !ok(launch_quant(s, q, s.in_bf16 ? nullptr : k,
+                                            s.in_bf16 ? nullptr : v, ws, stream)))
+    return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_QUANT + 1))) return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_SPARSE))) return SLA_ERR_HIP;
   hipError_t e;
