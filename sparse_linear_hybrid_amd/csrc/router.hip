@@ -556,7 +556,7 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const double* __restrict_
   }
   if (!exact && bit > 0) {
     // gather the keys in [T, T + 2^bit) (valid ones), then decide bits bit-1 .. 0 on them
-    const uint64_t hi = T + (1ull << bit);   // no overflow: bits below `bit` of T are 0
+    const uint64_t hi = T + (1ull << bit);   // 0 (wrapped): the range reaches the top key
     int base = 0;
 #pragma unroll
     for (int u = 0; u < KPL; ++u) {
