@@ -57,7 +57,8 @@ def sources_sha(paths) -> str:
 
 # --------------------------------------------------------------------------- algorithmic work
 def work(p, fp8=False):
-    """Algorithmic FLOPs / bytes of each stage for problem p (see the design notes)."""
+    """Algorithmic FLOPs / bytes of each stage for problem p: FLOPs of the executed MFMA
+    work, bytes each stage must move at least (per-unit figures times the units)."""
     BH, d, b = p.batch * p.heads, p.head_dim, 64
     pairs = BH * p.nbq * p.top_k
     qk_flops = pairs * 2 * b * b * d
@@ -351,9 +352,9 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each (batch, head) is independent; sharding is described in the design "
-              "notes, not built). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (every "
+              "(batch, head) is independent, so heads would shard across GPUs without "
+              "communication). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import ctypes

@@ -20,7 +20,7 @@ What is computed (per batch b and head h, independently):
   the block score is the second-order Taylor estimate of the block's attention mass
   around its mean key with a diagonal covariance (``taylor_scores``).
 
-Readings taken where the pages are silent (each listed in the design notes):
+Readings taken where the pages are silent:
   block b for queries and keys; pool over valid tokens only; project after pooling with
   x @ P (P stored [d_in, d_out]); plain dot-product block score; ties broken toward the
   lowest key-block index; softmax scale 1/sqrt(d); phi = ReLU on raw Q and K; eps = 1e-6
