@@ -662,9 +662,17 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
   }
   const int32_t* sel = idx + ((size_t)bh * nbq + i) * k;
   const float* zb = zblk + (size_t)bh * nbk * D + r;
-  // selected blocks are added in list order (deterministic); loads go out 8 at a time
+  // selected blocks are added in list order (deterministic); loads go out 32 at a time, so a
+  // row of k selections waits for about k / 32 round trips
   float z = 0.f;
   int s = 0;
+  for (; s + 32 <= k; s += 32) {
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = zb[(size_t)sel[s + u] * D];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) z += v[u];
+  }
   for (; s + 8 <= k; s += 8) {
     float v[8];
 #pragma unroll
