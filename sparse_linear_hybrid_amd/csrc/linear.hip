@@ -673,14 +673,16 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
 #pragma unroll
     for (int u = 0; u < 32; ++u) z += v[u];
   }
-  for (; s + 8 <= k; s += 8) {
-    float v[8];
+  if (s < k) {   // the last (partial) batch, also in one round trip: absent slots add 0
+    float v[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = zb[(size_t)sel[s + u] * D];
+    for (int u = 0; u < 32; ++u) {
+      const int jj = sel[min(s + u, k - 1)];   // in bounds whichever slot is read
+      v[u] = s + u < k ? zb[(size_t)jj * D] : 0.f;
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) z += v[u];
+    for (int u = 0; u < 32; ++u) z += v[u];
   }
-  for (; s < k; ++s) z += zb[(size_t)sel[s] * D];
   out[r] = ztot[(size_t)bh * D + r] - z;
 }
 
