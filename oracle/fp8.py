@@ -25,6 +25,12 @@ absmax scales on Q K^T and a per-tile scale on P.V):
 This form does not depend on the order in which tiles are visited: an online softmax that
 keeps its running maximum on integers and rescales by exact powers of two gives the same
 value in exact arithmetic.
+
+A second, literal reading of the fp8 workload's wording is kept beside it for comparison
+(``forward_fp8_literal``): float32 absmax/448 block scales for Q, K and V, and one
+absmax/448 scale for P over each 64 x 64 (query block x key tile) tile of the online
+softmax, visited in ascending key-block order. The GPU path implements the first reading;
+the second only measures how far the choice of reading moves the output.
 """
 from __future__ import annotations
 
@@ -146,5 +152,86 @@ def forward_fp8(inputs, heads=None, rows=None):
             o_s = sparse_rows_fp8(q8[toks], sq[i], k8, sk, v8, sv, r.idx[i], p.block)
             o_l = linear_complement(q[toks], S, z, M[i])
             out[b, h, toks] = mix(al[h], o_s, o_l)
+        idx[b, h] = r.idx
+    return out, idx
+
+
+# ----------------------------------------------------------------------------- literal reading
+def quantise_blocks_absmax(x: np.ndarray, block: int):
+    """Per-block E4M3 quantisation with a float32 scale s = fp32(absmax / 448) (s = 1 for an
+    all-zero block) and x8 = E4M3(fp32(x / s)): the scale is not a power of two, so the
+    division is rounded to float32 before the E4M3 rounding. x: [N, d] float64 holding
+    float32-exact values. Returns (x8 [N, d] float64, s [Nb] float64)."""
+    n = x.shape[0]
+    nb = n_blocks(n, block)
+    x8 = np.empty_like(x)
+    s = np.empty(nb)
+    for j in range(nb):
+        sl = block_slice(j, n, block)
+        amax = float(np.abs(x[sl]).max())
+        sj = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+        x8[sl] = e4m3_round((x[sl].astype(np.float32) / sj).astype(np.float64))
+        s[j] = float(sj)
+    return x8, s
+
+
+def sparse_block_fp8_literal(q8_blk: np.ndarray, sq: float, k8: np.ndarray, sk: np.ndarray,
+                             v8: np.ndarray, sv: np.ndarray, sel: Sequence[int],
+                             block: int) -> np.ndarray:
+    """Quantised sparse attention of all rows of one query block, literal reading: online
+    softmax over the selected key tiles in ascending order with m the running row maximum
+    of the logits z = tau s_Q s_K (Q8 K8^T), p = exp(z - m_new), one scale
+    s_P = max(p over the query block x key tile) / 448 per tile, P8 = E4M3(p / s_P),
+    acc <- acc e^(m - m_new) + s_P s_V (P8 V8), l <- l e^(m - m_new) + sum p (unquantised)."""
+    n, d = k8.shape
+    rows = q8_blk.shape[0]
+    if len(sel) == 0:
+        return np.zeros((rows, d))
+    tau = 1.0 / math.sqrt(d)
+    m = np.full(rows, -np.inf)
+    acc = np.zeros((rows, d))
+    lsum = np.zeros(rows)
+    for j in sorted(sel):
+        sl = block_slice(j, n, block)
+        z = tau * sq * sk[j] * (q8_blk @ k8[sl].T)
+        m_new = np.maximum(m, z.max(axis=1))
+        corr = np.exp(m - m_new)
+        p = np.exp(z - m_new[:, None])
+        s_p = p.max() / E4M3_MAX
+        p8 = e4m3_round(p / s_p)
+        acc = acc * corr[:, None] + (s_p * sv[j]) * (p8 @ v8[sl])
+        lsum = lsum * corr + p.sum(axis=1)
+        m = m_new
+    return acc / lsum[:, None]
+
+
+def forward_fp8_literal(inputs, heads=None, rows=None):
+    """SLA2 forward with the quantised sparse branch in the literal reading (module
+    docstring); router, linear branch and mix as in ``forward_fp8``. Returns (out, idx)."""
+    p = inputs.problem
+    pq = inputs.proj_q.astype(np.float64)
+    pk = inputs.proj_k.astype(np.float64)
+    al = inputs.alpha.astype(np.float64)
+    out = np.full((p.batch, p.heads, p.n_q, p.head_dim), np.nan)
+    idx = np.full((p.batch, p.heads, p.nbq, p.top_k), -1, np.int32)
+    pairs = heads if heads is not None else [(b, h) for b in range(p.batch) for h in range(p.heads)]
+    for b, h in pairs:
+        q = _head(inputs, "q", b, h)
+        k = _head(inputs, "k", b, h)
+        v = _head(inputs, "v", b, h)
+        r = route_head(q, k, pq, pk, p.block, p.top_k)
+        M = selection_mask(r.idx, p.nbk)
+        S, z = block_summaries(k, v, p.block)
+        q8, sq = quantise_blocks_absmax(q, p.block)
+        k8, sk = quantise_blocks_absmax(k, p.block)
+        v8, sv = quantise_blocks_absmax(v, p.block)
+        want = np.arange(p.n_q) if rows is None else np.asarray(rows)
+        for i in np.unique(want // p.block):
+            blk = np.arange(p.n_q)[block_slice(i, p.n_q, p.block)]
+            o_blk = sparse_block_fp8_literal(q8[blk], sq[i], k8, sk, v8, sv, r.idx[i], p.block)
+            keep = np.isin(blk, want)
+            toks = blk[keep]
+            o_l = linear_complement(q[toks], S, z, M[i])
+            out[b, h, toks] = mix(al[h], o_blk[keep], o_l)
         idx[b, h] = r.idx
     return out, idx

@@ -99,6 +99,18 @@ def boundary_gaps(scores: np.ndarray, top_k: int) -> np.ndarray:
     return srt[:, top_k - 1] - srt[:, top_k]
 
 
+NEAR_TIE_REL = 1e-12
+
+
+def near_ties(scores: np.ndarray, gaps: np.ndarray) -> np.ndarray:
+    """Rows whose boundary gap is below 1e-12 of the row's largest |score|: there a rounding
+    difference of the score arithmetic (about 1e-16 relative in float64) could decide which
+    block is the k-th, so more than one selection may be reported as correct. An exact tie
+    (gap 0) is flagged too; a row with an infinite gap (k = 0 or all blocks) never is."""
+    scale = np.abs(scores).max(axis=1) if scores.size else np.zeros(scores.shape[0])
+    return gaps < NEAR_TIE_REL * scale
+
+
 @dataclass
 class Route:
     idx: np.ndarray        # int32 [Nbq, k], ascending
@@ -115,8 +127,7 @@ def route_head(q: np.ndarray, k: np.ndarray, proj_q: np.ndarray, proj_k: np.ndar
     s = block_scores(qt, kt)
     idx = select_topk(s, top_k)
     gaps = boundary_gaps(s, top_k)
-    scale = np.abs(s).max(axis=1) if s.size else np.zeros(s.shape[0])
-    return Route(idx, s, gaps, gaps < 1e-12 * scale)
+    return Route(idx, s, gaps, near_ties(s, gaps))
 
 
 # ----------------------------------------------------------------------------- Taylor router
@@ -150,8 +161,7 @@ def route_head_taylor(q: np.ndarray, k: np.ndarray, block: int, top_k: int) -> R
     s = taylor_scores(pool_blocks(q, block), pool_blocks(k, block), block_variances(k, block))
     idx = select_topk(s, top_k)
     gaps = boundary_gaps(s, top_k)
-    scale = np.abs(s).max(axis=1) if s.size else np.zeros(s.shape[0])
-    return Route(idx, s, gaps, gaps < 1e-12 * scale)
+    return Route(idx, s, gaps, near_ties(s, gaps))
 
 
 def selection_mask(idx: np.ndarray, nbk: int) -> np.ndarray:

@@ -151,6 +151,7 @@ def test_longctx_cached_full(sla):
     p = x.problem
     out, idx = run_cached(sla, x)
     rows, near = check_masks(idx, oracle.sla_oracle.route_full(x), p.top_k)
+    assert near == 0
     refs, gots = [], []
     for b, h in [(0, 0), (1, 7), (3, 31)]:
         ref, _ = oracle.forward(x, heads=[(b, h)])
