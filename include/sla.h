@@ -34,9 +34,10 @@
  *   - Work is enqueued on `stream`; calls return as soon as it is enqueued. A non-OK status
  *     other than SLA_ERR_HIP means nothing was enqueued; after SLA_ERR_HIP (a launch was
  *     refused) the outputs are undefined.
- *   - The library keeps no mutable global state: concurrent calls on different streams
- *     with separate workspaces are safe. Results are bit-reproducible for identical
- *     inputs (no floating-point atomics).
+ *   - Apart from the allocation-free entry point at the end of this header, which works in
+ *     one fixed device array per GPU, the library keeps no mutable global state: concurrent
+ *     calls on different streams with separate workspaces are safe. Results are
+ *     bit-reproducible for identical inputs (no floating-point atomics).
  */
 #ifndef SLA_H
 #define SLA_H
@@ -58,7 +59,9 @@ typedef enum {
   SLA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                       */
   SLA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than sla_workspace_size()    */
   SLA_ERR_UNSUPPORTED = 7, /* head_dim not in {64, 128}, block != 64, too many blocks */
-  SLA_ERR_HIP = 8          /* a kernel launch failed                                 */
+  SLA_ERR_HIP = 8,         /* a kernel launch failed                                 */
+  SLA_ERR_SCRATCH = 9      /* the problem needs more than the fixed scratch array of
+                              sla_forward_cached_noalloc (SLA_NOALLOC_SCRATCH_BYTES)      */
 } sla_status;
 
 typedef enum { SLA_F32 = 0, SLA_BF16 = 1 } sla_dtype;
@@ -242,6 +245,27 @@ sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k
                               const float* proj_q, const float* alpha, const void* cache,
                               void* o, int32_t* block_idx, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- allocation-free decode
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. sla_forward_cached without the workspace
+ * arguments: its workspace is a fixed device array inside the library,
+ * SLA_NOALLOC_SCRATCH_BYTES long, one per GPU, which each GPU the library runs on holds from
+ * the code object's load until the process ends. The call allocates and frees nothing; its
+ * kernels, outputs and conventions are those of sla_forward_cached, and the result is the
+ * same bit for bit. The array of the CURRENT device is used (`stream` must belong to it);
+ * its address is looked up on the first call on each device. Returns SLA_ERR_SCRATCH, with
+ * nothing enqueued, when sla_cached_workspace_size(p) exceeds the array (decode shapes up to
+ * e.g. 128 heads x 64 queries over 131072 keys with top_k 64 fit). Every call on one GPU
+ * shares that GPU's array and nothing in it must start cleared: calls ordered on one stream
+ * are safe, but calls that may overlap on one GPU (different streams or threads without
+ * ordering between them) race and give undefined results. */
+#define SLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+sla_status sla_forward_cached_noalloc(const sla_problem* p, const void* q, const void* k,
+                                      const void* v, const float* proj_q, const float* alpha,
+                                      const void* cache, void* o, int32_t* block_idx,
+                                      hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* sla_status_string(sla_status s);

@@ -307,6 +307,7 @@ const char* sla_status_string(sla_status s) {
     case SLA_ERR_WORKSPACE: return "workspace missing or too small";
     case SLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case SLA_ERR_HIP: return "kernel launch failed";
+    case SLA_ERR_SCRATCH: return "problem needs more than the allocation-free scratch array";
   }
   return "unknown status";
 }

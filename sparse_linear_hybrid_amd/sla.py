@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(_HERE, "libsla.so")
 SLA_F32, SLA_BF16 = 0, 1
 STATUS = {0: "SLA_OK", 1: "SLA_ERR_NULL", 2: "SLA_ERR_SHAPE", 3: "SLA_ERR_DTYPE",
           4: "SLA_ERR_TOPK", 5: "SLA_ERR_ALIGN", 6: "SLA_ERR_WORKSPACE",
-          7: "SLA_ERR_UNSUPPORTED", 8: "SLA_ERR_HIP"}
+          7: "SLA_ERR_UNSUPPORTED", 8: "SLA_ERR_HIP", 9: "SLA_ERR_SCRATCH"}
 EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_profiled", "sla_workspace_region", "sla_status_string",
            "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
            "sla_cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
-           "sla_forward_taylor", "sla_forward_pisa")
+           "sla_forward_taylor", "sla_forward_pisa", "sla_forward_cached_noalloc")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8,
               "hbar": 9, "cent_hi": 10, "cent_lo": 11, "vsum": 12}
 # workspace layouts (sla_workspace_size / sla_workspace_region)
@@ -86,6 +86,8 @@ def _load() -> ctypes.CDLL:
     lib.sla_cached_workspace_size.argtypes = [pp]
     lib.sla_cached_workspace_size.restype = sz
     lib.sla_forward_cached.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_forward_cached_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sla_forward_cached_noalloc.restype = ctypes.c_int
     lib.sla_forward_cached.restype = ctypes.c_int
     lib.sla_route_taylor.argtypes = [pp, vp, vp, vp, vp, sz, vp]
     lib.sla_route_taylor.restype = ctypes.c_int
@@ -341,6 +343,30 @@ def sla_forward_cached(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor, 
     if st != 0:
         raise SlaError(st, "sla_forward_cached")
     return out, idx
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def sla_forward_cached_noalloc(q, k, v, proj_q, alpha, top_k: int, cache: torch.Tensor,
+                               out: torch.Tensor, block_idx: Optional[torch.Tensor] = None,
+                               block: int = 64):
+    """sla_forward_cached with the library's fixed scratch array instead of a workspace: the
+    caller passes preallocated `out` (and optionally `block_idx`); nothing is allocated on
+    the device by this call. Returns (out, block_idx)."""
+    p = make_problem(q, k, top_k, block, out.dtype)
+    _check(q, k, v, (proj_q,), alpha, out, out.dtype, (cache,))
+    if block_idx is not None:
+        want = (p.batch, p.heads, -(-p.n_q // block), top_k)
+        if tuple(block_idx.shape) != want or block_idx.dtype != torch.int32 \
+                or block_idx.device != q.device or not block_idx.is_contiguous():
+            raise ValueError(f"block_idx must be a contiguous int32 {want} tensor on {q.device}")
+    st = library().sla_forward_cached_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(proj_q), _ptr(alpha), _ptr(cache), _ptr(out),
+                                              _ptr(block_idx), _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_forward_cached_noalloc")
+    return out, block_idx
 
 
 # ----------------------------------------------------------------------------- Taylor router

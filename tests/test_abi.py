@@ -110,7 +110,7 @@ def test_workspace_size_monotone(lib):
 
 
 def test_status_strings(lib):
-    for code in range(9):
+    for code in range(10):
         assert lib.sla_status_string(code).decode()
     assert lib.sla_status_string(99) == b"unknown status"
 
@@ -182,6 +182,28 @@ def test_forward_cached_validation(lib):
     assert fwd(idx=MISALIGNED) == 5
     need = lib.sla_cached_workspace_size(ctypes.byref(p))
     assert need > 0 and fwd(ws_bytes=need - 1) == 6
+
+
+def test_forward_cached_noalloc_validation(lib):
+    """The allocation-free entry point validates like sla_forward_cached and refuses, before
+    any device call, a problem whose decode workspace exceeds its fixed scratch array."""
+    vp = ctypes.c_void_p
+
+    def fwd(prob_, q=FAKE):
+        pp = ctypes.byref(prob_) if prob_ is not None else None
+        return lib.sla_forward_cached_noalloc(pp, vp(q), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                              vp(FAKE), vp(FAKE), vp(None), vp(0))
+    assert fwd(None) == 1
+    assert fwd(prob(top_k=12)) == 4
+    assert fwd(prob(head_dim=96)) == 7
+    big = prob(batch=4, heads=32, n_q=64 * 16, n_kv=131072, top_k=64)
+    assert lib.sla_cached_workspace_size(ctypes.byref(big)) > sla.NOALLOC_SCRATCH_BYTES
+    assert fwd(big) == 9
+    decode = prob(batch=4, heads=32, n_q=64, n_kv=131072, top_k=64)
+    assert 0 < lib.sla_cached_workspace_size(ctypes.byref(decode)) <= sla.NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "#define SLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in hdr
+    assert sla.NOALLOC_SCRATCH_BYTES == 128 << 20
 
 
 def test_taylor_entry_points_validation(lib):
