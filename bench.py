@@ -22,6 +22,9 @@ Other modes:
     --summarize-trace DIR OUT "COMMAND"
                          turn rocprofv3 --kernel-trace --stats CSV output into a short text
                          summary (per-kernel calls and average duration) with its command
+    --summarize-mfma DIR OUT "COMMAND"
+                         the same for one rocprofv3 --pmc pass over the matrix-core counters
+                         (executed MFMA FLOPs and MFMA-busy fraction per kernel)
 """
 from __future__ import annotations
 
@@ -75,9 +78,21 @@ def work(p, fp8=False):
     kv_bytes = (2 * BH * p.n_kv * d * elt                  # read K, V
                 + BH * p.nbk * d * d * 2                  # write S_j (bf16)
                 + BH * p.nbk * b * d * 2)                 # write f16 V
+    # HBM bytes each stage has to move, by what the method needs (SLA2 router, SPLA linear
+    # state): the key/value pass reads K and V once and writes S_j (bf16), z_j (fp32) and k~
+    # (fp64); its f16 copy of V is the exact branch's operand, reported apart. The router
+    # reads Q once, writes and reads its fp64 score rows once and writes the indices. The
+    # complement reads every S_j once and writes S_c (bf16) once per query block.
+    v16_bytes = BH * p.nbk * b * d * 2
+    hbm = {
+        "kv_summary": 2 * BH * p.n_kv * d * elt + BH * p.nbk * (d * d * 2 + d * 4 + d * 8),
+        "route": BH * p.n_q * d * elt + 2 * BH * p.nbq * p.nbk * 8 + BH * p.nbq * p.top_k * 4,
+        "complement": BH * p.nbk * d * d * 2 + BH * p.nbq * (d * d * 2 + d * 4),
+    }
     dense_flops = 4 * BH * p.n_q * p.n_kv * d
     quant_bytes = BH * (p.n_q + p.n_kv) * d * (2 + 2) + BH * p.n_kv * d * (2 + 1)
     return {"pairs": pairs, "sparse_flops": sparse_flops, "kv_summary_bytes": kv_bytes,
+            "hbm_bytes": hbm, "v16_bytes": v16_bytes,
             "dense_flops": dense_flops, "sparse_peak": sparse_flops / floor_s,
             "quant_bytes": quant_bytes}
 
@@ -212,19 +227,98 @@ def summarize_pmc(fetch_dir, write_dir, workload):
     print(json.dumps(rec))
 
 
-def summarize_trace(d, out, command):
-    """Short text summary of rocprofv3 --kernel-trace --stats CSV output."""
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4          # MI355X: 256 compute units with 4 SIMDs each
+XCDS = 8
+
+
+def summarize_mfma(d, out, command):
+    """Matrix-core utilisation per kernel from one rocprofv3 --pmc pass over MFMA_COUNTERS:
+    executed MFMA FLOPs (each MOPS unit is 512 FLOPs), the MFMA-busy fraction of the SIMD
+    cycles (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) and, where the dispatch
+    timestamps are present, the executed rate."""
+    rows = []
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for r in rows:
+        key = (r.get("Kernel_Name", ""), r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+        rec = per.setdefault(key, {})
+        rec[r["Counter_Name"]] = rec.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            rec["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    kern = {}
+    for (name, _), rec in per.items():
+        kern.setdefault(short_name(name), []).append(rec)
+    lines = ["# rocprofv3 matrix-core counters (one --pmc pass)", f"# command: {command}",
+             "# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) "
+             "(GRBM_GUI_ACTIVE comes summed over the 8 XCDs); clock_GHz = GRBM_GUI_ACTIVE / 8 / "
+             "duration; exec_TF = (MOPS_BF16 + MOPS_F16 + MOPS_F8) x 512 / duration", "#",
+             f"{'kernel':58s} {'calls':>5s} {'GFLOP_exec':>11s} {'mfma_busy':>9s} "
+             f"{'exec_TF':>8s} {'clock_GHz':>9s} {'mfma_insts':>11s} {'valu_insts':>11s}"]
+    for name, recs in sorted(kern.items(), key=lambda kv: -sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0)
+                                                                for r in kv[1])):
+        n = len(recs)
+        mean = lambda c: sum(r.get(c, 0.0) for r in recs) / n          # noqa: E731
+        flops = 512 * (mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") + mean("SQ_INSTS_VALU_MFMA_MOPS_F16")
+                       + mean("SQ_INSTS_VALU_MFMA_MOPS_F8"))
+        gui = mean("GRBM_GUI_ACTIVE") / XCDS
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (gui * SIMDS) if gui else float("nan")
+        ns = [r["_ns"] for r in recs if "_ns" in r]
+        tf = flops / (sum(ns) / len(ns)) / 1e3 if ns else float("nan")
+        ghz = gui / (sum(ns) / len(ns)) if ns else float("nan")
+        lines.append(f"{name[:58]:58s} {n:5d} {flops / 1e9:11.2f} {busy:9.3f} {tf:8.1f} "
+                     f"{ghz:9.2f} {mean('SQ_INSTS_MFMA'):11.0f} {mean('SQ_INSTS_VALU'):11.0f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_trace(d, out, command, timed=None, bench_log=None):
+    """Short text summary of rocprofv3 --kernel-trace --stats CSV output: per kernel the
+    calls and average duration. timed = "W,K": also the average over the dispatches W ..
+    W + K - 1 of each kernel, which for a profiled `bench.py --warmup W --steps K` run are the
+    calls of its timed region (bench.py's HIP-event average of the same run covers exactly
+    those); bench_log: the run's output, whose JSON line is quoted for comparison."""
     files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no kernel_stats.csv under {d}")
     rows = list(csv.DictReader(open(files[0])))
+    per = {}
+    tr = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if tr:
+        for r in csv.DictReader(open(tr[0])):
+            per.setdefault(short_name(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    w0, k0 = (int(x) for x in timed.split(",")) if timed else (0, 0)
     lines = [f"# rocprofv3 kernel statistics", f"# command: {command}", "#",
-             f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'total_%':>8s}"]
+             f"{'kernel':70s} {'calls':>6s} {'avg_us':>10s} {'total_%':>8s}"
+             + (f" {'timed_avg_us':>12s}" if timed else "")]
     for r in rows:
         name = r.get("Name", "")
         short = short_name(name)[:70]
-        lines.append(f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['Percentage']):8.2f}")
+        line = (f"{short:70s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                f"{float(r['Percentage']):8.2f}")
+        if timed:
+            ds = per.get(short_name(name), [])[w0:w0 + k0]
+            line += f" {sum(ds) / len(ds):12.2f}" if len(ds) == k0 else f" {'':12s}"
+        lines.append(line)
+    if timed:
+        lines.append(f"# timed_avg_us: mean duration of dispatches {w0} .. {w0 + k0 - 1} of each "
+                     "kernel (the timed steps of the profiled run)")
+    if bench_log and os.path.exists(bench_log):
+        for l in open(bench_log):
+            if l.startswith("{") and '"roofline"' in l:
+                rec = json.loads(l)
+                rf = rec["roofline"]
+                lines.append(f"# the run's own line: value {rec['value']:.4f} ms/step, "
+                             f"{rf['kernel']} avg_launch_ms {rf['avg_launch_ms']:.4f} "
+                             f"(HIP events), roofline frac {rf['frac']:.4f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -343,10 +437,18 @@ def main():
                          "normalisation) instead of sla_forward")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
+    ap.add_argument("--timed", default=None, metavar="W,K",
+                    help="with --summarize-trace: also average dispatches W .. W+K-1")
+    ap.add_argument("--bench-log", default=None,
+                    help="with --summarize-trace: the profiled run's output (its JSON line)")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace)
+        summarize_trace(*args.summarize_trace, timed=args.timed, bench_log=args.bench_log)
+        return 0
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
         return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
@@ -386,7 +488,8 @@ def main():
     if int(taylor) + int(pisa) + int(fp8) > 1:
         print("--router taylor, --pisa and the fp8 workload are separate paths", file=sys.stderr)
         return 2
-    variant = sla.VARIANT_FP8 if fp8 else (sla.VARIANT_PISA if pisa else sla.VARIANT_FORWARD)
+    variant = (sla.VARIANT_FP8 if fp8 else sla.VARIANT_PISA if pisa else
+               sla.VARIANT_TAYLOR if taylor else sla.VARIANT_FORWARD)
     ws = torch.empty(sla.workspace_size(prob, variant), dtype=torch.uint8, device=dev)
 
     def fwd():
@@ -466,8 +569,29 @@ def main():
     if peaks and not fp8:
         roofline["achievable_peak"] = peaks["bf16_gemm_TFLOPs"]
         roofline["frac_of_achievable"] = achieved / 1e12 / peaks["bf16_gemm_TFLOPs"]
+    # algorithmic HBM rate of the memory-bound stages (the key/value pass, the router, the
+    # complement), against the 8 TB/s peak; the f16 V copy is shown apart
+    hbm = {}
+    # sla_forward's cache path (bf16, at most 8 query blocks per head over at least 256 key
+    # blocks): the key/value stage is the cache build, which writes only k~ per key block,
+    # and there is no complement stage
+    cache_path = (p.dtype == "bf16" and p.nbq <= 8 and p.nbk >= 256
+                  and not (fp8 or taylor or pisa))
+    if cache_path:
+        BH, d = p.batch * p.heads, p.head_dim
+        w["hbm_bytes"] = {"kv_summary": 2 * BH * p.n_kv * d * 2 + BH * p.nbk * d * 8,
+                          "route": w["hbm_bytes"]["route"]}
+        w["v16_bytes"] = 0
+    for stg, nbytes in w["hbm_bytes"].items():
+        t_s = stage_ms[stg] * 1e-3
+        if t_s > 0 and not (pisa and stg == "complement"):
+            hbm[stg] = {"bytes": nbytes, "GBps": nbytes / t_s / 1e9, "frac": nbytes / t_s / PEAK_HBM}
+    if "kv_summary" in hbm:
+        hbm["kv_summary"]["with_v16_copy_frac"] = ((w["hbm_bytes"]["kv_summary"] + w["v16_bytes"])
+                                                   / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM)
     kernels = {
         "stage_ms": stage_ms,
+        "hbm": hbm,
         "kv_summary_GBps": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / 1e9,
         "kv_summary_hbm_frac": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM,
         "step_ms_warm": spread(warm_steps),

@@ -80,9 +80,10 @@ typedef struct {
 
 /* Workspace layouts (the `variant` of sla_workspace_size and sla_workspace_region). */
 enum {
-  SLA_VARIANT_FORWARD = 0,  /* sla_forward, sla_route, sla_route_taylor, sla_forward_taylor */
+  SLA_VARIANT_FORWARD = 0,  /* sla_forward, sla_route, sla_route_taylor                    */
   SLA_VARIANT_FP8 = 1,      /* sla_forward_fp8                                            */
-  SLA_VARIANT_PISA = 2      /* sla_forward_pisa                                           */
+  SLA_VARIANT_PISA = 2,     /* sla_forward_pisa                                           */
+  SLA_VARIANT_TAYLOR = 3    /* sla_forward_taylor                                         */
 };
 
 /* Bytes of device workspace a call of that variant needs. Returns 0 if the problem is
@@ -97,7 +98,14 @@ sla_status sla_route(const sla_problem* p, const void* q, const void* k,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Full forward with the bf16 sparse branch (SLA2 page, sections 2.A and 2.B).
- * block_idx is optional (NULL: the selection stays in the workspace). */
+ * block_idx is optional (NULL: the selection stays in the workspace).
+ * With bf16 inputs, at most 8 query blocks per head and at least 256 key blocks (a chunk of
+ * queries against a long key sequence) the call takes the cache path: one pass over K and V
+ * builds the key/value summary cache of sla_kv_cache_update in the workspace, and the rest
+ * is sla_forward_cached (same selection, same arithmetic), so no per-key-block summary is
+ * stored (SPLA page, section 2.2: the unselected blocks' linear term is the total minus the
+ * selected blocks' term). sla_workspace_size(p, SLA_VARIANT_FORWARD) accounts for it; the
+ * SCORES, SC and ZC workspace regions do not exist on that path. */
 sla_status sla_forward(const sla_problem* p, const void* q, const void* k, const void* v,
                        const float* proj_q, const float* proj_k, const float* alpha,
                        void* o, int32_t* block_idx,
@@ -124,7 +132,8 @@ sla_status sla_route_taylor(const sla_problem* p, const void* q, const void* k,
                             hipStream_t stream);
 
 /* sla_forward with the training-free router instead of the learnable one (no proj_q, proj_k).
- * Same workspace as sla_forward (fp8 = 0). */
+ * Workspace: SLA_VARIANT_TAYLOR (the per-key-block layout of sla_forward; the same size as
+ * SLA_VARIANT_FORWARD unless sla_forward takes its cache path). */
 sla_status sla_forward_taylor(const sla_problem* p, const void* q, const void* k, const void* v,
                               const float* alpha, void* o, int32_t* block_idx, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);

@@ -266,6 +266,12 @@ struct Plan {
   size_t hbar;                                  // bf16 H_bar^T [BH][D(c)][D(r)]
   size_t tail_m, tail_d, tail_a, tail_n;        // tail state per query row
   size_t total_pisa;
+  // Few query blocks over many key blocks (a decode chunk against a long key sequence): the
+  // learnable-router forward then builds the key/value summary cache in its workspace and
+  // runs the cached forward, instead of storing and re-reading every key block's summary.
+  bool few;
+  size_t few_cache, few_cws, few_dec;           // cache, its update workspace, decode workspace
+  size_t total_few;
 };
 
 
@@ -330,6 +336,11 @@ inline Plan make_plan(const sla_problem& p) {
   return s;
 }
 
+// When the forward takes the cache path (Plan::few): at most kFewQueryBlocks query blocks per
+// head and at least kFewMinKeyBlocks key blocks, bf16 inputs.
+constexpr int kFewQueryBlocks = 8;
+constexpr int kFewMinKeyBlocks = 256;
+
 // ----------------------------------------------------------------------------- summary cache
 // Key/value summary cache (caller-owned, see sla_kv_cache_update): S_tot^T [BH][D(c)][D(r)]
 // fp32, z_tot [BH][D] fp32, then k~ [nbk][BH][D] fp64. k~ is block-major so that the layout
@@ -388,6 +399,18 @@ inline DecodePlan make_decode_plan(const Plan& s) {
   d.pz = take(parts * D * 4);
   d.bytes = off;
   return d;
+}
+
+// Layout of the forward's workspace on the cache path: the key/value summary cache, the
+// update's partial totals, then the cached forward's workspace. Sets s.few and, when the
+// path is taken, its size s.total_few.
+inline void plan_few_path(Plan& s) {
+  s.few = s.in_bf16 && s.nbq <= kFewQueryBlocks && s.nbk >= kFewMinKeyBlocks;
+  if (!s.few) return;
+  s.few_cache = 0;
+  s.few_cws = align_up(make_cache_plan(s).bytes, 256);
+  s.few_dec = align_up(s.few_cws + cache_update_ws_bytes(s, 0), 256);
+  s.total_few = s.few_dec + make_decode_plan(s).bytes;
 }
 
 }  // namespace sla

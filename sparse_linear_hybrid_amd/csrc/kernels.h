@@ -40,6 +40,13 @@ hipError_t launch_route_taylor(const Plan& s, const void* q, const void* k, int3
 hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,
                                   int n_done, char* cache, char* ws, hipStream_t st);
 
+// Streaming cache pass (bf16): k~ of every key block from n_done / 64 on, and the chunk
+// partial totals of phi(K)^T V and phi(K) over the tokens from n_done on (into ws, laid out
+// as cache_update_ws_bytes describes).
+hipError_t launch_kv_totals(const Plan& s, const void* k, const void* v, const float* pk,
+                            int n_done, double* kt, size_t kbh, size_t kj, float* stot,
+                            float* ztot, char* ws, hipStream_t st);
+
 // Router against cached k~ (k~ of block j of head bh at kt + bh * kbh + j * kj).
 hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, const double* kt,
                                size_t kbh, size_t kj, int32_t* idx, double* qt, double* sc,

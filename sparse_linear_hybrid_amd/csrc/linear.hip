@@ -749,33 +749,31 @@ static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* 
   return hipGetLastError();
 }
 
-template <int D>
-static hipError_t launch_kv_cache_update_T(const Plan& s, const void* k, const void* v,
-                                           const float* pk, int n_done, const CachePlan& c,
-                                           char* cache, char* ws, hipStream_t st) {
-  const int jbase = n_done / kBlock;
-  const int nchunk = cache_update_chunks(s, n_done);
-  if (nchunk == 0) return hipSuccess;
-  double* kt = reinterpret_cast<double*>(cache + c.kt);
-  float* spart = reinterpret_cast<float*>(ws);
-  float* zpart = reinterpret_cast<float*>(ws + cache_update_zpart_offset(s, n_done));
-  const dim3 grid(nchunk, s.BH);
-  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, false, kCacheChunk>), grid, dim3(256), 0, st,
-                     (const uint16_t*)k, (const uint16_t*)v, pk, kt, (size_t)D,
-                     (size_t)s.BH * D, nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk,
-                     jbase, n_done, nullptr, nullptr, nullptr, 0, Fp8Out{});
-  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
-                     zpart, reinterpret_cast<float*>(cache + c.stot),
-                     reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
-                     nullptr, 0.f, 0);
-  return hipGetLastError();
-}
-
 hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, const float* pk,
                                   int n_done, char* cache, char* ws, hipStream_t st) {
   const CachePlan c = make_cache_plan(s);
-  if (s.D == 128) return launch_kv_cache_update_T<128>(s, k, v, pk, n_done, c, cache, ws, st);
-  return launch_kv_cache_update_T<64>(s, k, v, pk, n_done, c, cache, ws, st);
+  if (cache_update_chunks(s, n_done) == 0) return hipSuccess;
+  // the streaming totals pass (bf16 inputs, the only ones the cache takes), then the fixed-
+  // order reduction of its chunk partials onto the totals
+  hipError_t e = launch_kv_totals(s, k, v, pk, n_done, reinterpret_cast<double*>(cache + c.kt),
+                                  (size_t)s.D, (size_t)s.BH * s.D,
+                                  reinterpret_cast<float*>(cache + c.stot),
+                                  reinterpret_cast<float*>(cache + c.ztot), ws, st);
+  if (e != hipSuccess) return e;
+  float* spart = reinterpret_cast<float*>(ws);
+  float* zpart = reinterpret_cast<float*>(ws + cache_update_zpart_offset(s, n_done));
+  const int nchunk = cache_update_chunks(s, n_done);
+  if (s.D == 128)
+    hipLaunchKernelGGL((reduce_totals_kernel<128>), dim3(128 * 128 / 32, s.BH), dim3(256), 0, st,
+                       spart, zpart, reinterpret_cast<float*>(cache + c.stot),
+                       reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
+                       nullptr, 0.f, 0);
+  else
+    hipLaunchKernelGGL((reduce_totals_kernel<64>), dim3(64 * 64 / 32, s.BH), dim3(256), 0, st,
+                       spart, zpart, reinterpret_cast<float*>(cache + c.stot),
+                       reinterpret_cast<float*>(cache + c.ztot), nchunk, n_done > 0 ? 1 : 0,
+                       nullptr, 0.f, 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk,

@@ -1,5 +1,7 @@
 // C ABI entry points (include/sla.h): argument validation, workspace plan and the launch
 // sequence. Validation happens before anything is enqueued.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +36,13 @@ sla_status check_ptrs(std::initializer_list<const void*> ps) {
   return SLA_OK;
 }
 
+// Workspace plan of the forward entry points, with the cache path decided (Plan::few).
+Plan forward_plan(const sla_problem& p) {
+  Plan s = make_plan(p);
+  plan_few_path(s);
+  return s;
+}
+
 // The forward variants: SLA2 (learnable router), its fp8 sparse branch, SLA2 with the
 // training-free router (proj_q / proj_k unused and may be NULL), and the piecewise forward
 // (learnable router; exact routed blocks plus the Taylor tail; alpha unused and may be NULL).
@@ -53,15 +62,50 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
   }
   if (st != SLA_OK) return st;
   if (block_idx && !aligned16(block_idx)) return SLA_ERR_ALIGN;
-  const Plan s = make_plan(*p);
-  const size_t need = mode == Fwd::kFp8 ? s.total_fp8 : (mode == Fwd::kPisa ? s.total_pisa
-                                                                            : s.total_fwd);
+  const Plan s = forward_plan(*p);
+  // Only the learnable router's bf16 forward takes the cache path; the Taylor router's
+  // forward keeps the per-block layout (SLA_VARIANT_TAYLOR).
+  const bool few = s.few && mode == Fwd::kSla;
+  const size_t need = mode == Fwd::kFp8    ? s.total_fp8
+                      : mode == Fwd::kPisa ? s.total_pisa
+                      : few                ? s.total_few
+                                           : s.total_fwd;
   if (!workspace || workspace_bytes < need) return SLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return SLA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
-  int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   auto mark = [&](int e) { return ev ? hipEventRecord(ev[e], stream) : hipSuccess; };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
+  if (few && mode == Fwd::kSla) {
+    // Few query blocks over a long key sequence (SPLA page, section 2.2: the unselected blocks'
+    // linear term is the total minus the selected blocks' term, so no per-block summary is
+    // stored): build the summary cache (k~, S_tot, z_tot) in the workspace with one pass over
+    // K and V, route against it, and run the cached forward, whose exact branch forms the
+    // selected blocks' summaries from the tiles it reads. Stages: the cache build is the
+    // key/value stage, the complement and quantisation stages are empty.
+    char* cache = ws + s.few_cache;
+    char* dws = ws + s.few_dec;
+    const DecodePlan d = make_decode_plan(s);
+    const CachePlan c = make_cache_plan(s);
+    int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(dws + d.idx);
+    if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY))) return SLA_ERR_HIP;
+    if (!ok(launch_kv_cache_update(s, k, v, proj_k, 0, cache, ws + s.few_cws, stream)))
+      return SLA_ERR_HIP;
+    if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY + 1))) return SLA_ERR_HIP;
+    if (!ok(mark(2 * SLA_STAGE_ROUTE))) return SLA_ERR_HIP;
+    if (!ok(launch_route_cached(s, q, proj_q, reinterpret_cast<const double*>(cache + c.kt),
+                                (size_t)s.D, (size_t)s.BH * s.D, idx,
+                                reinterpret_cast<double*>(dws + d.qt),
+                                reinterpret_cast<double*>(dws + d.scores), stream)))
+      return SLA_ERR_HIP;
+    if (!ok(mark(2 * SLA_STAGE_ROUTE + 1))) return SLA_ERR_HIP;
+    for (int stg : {SLA_STAGE_COMPLEMENT, SLA_STAGE_QUANT})
+      if (!ok(mark(2 * stg)) || !ok(mark(2 * stg + 1))) return SLA_ERR_HIP;
+    if (!ok(mark(2 * SLA_STAGE_SPARSE))) return SLA_ERR_HIP;
+    if (!ok(launch_decode(s, q, k, v, idx, alpha, cache, o, dws, stream))) return SLA_ERR_HIP;
+    if (!ok(mark(2 * SLA_STAGE_SPARSE + 1))) return SLA_ERR_HIP;
+    return SLA_OK;
+  }
+  int32_t* idx = block_idx ? block_idx : reinterpret_cast<int32_t*>(ws + s.idx);
   if (!ok(mark(2 * SLA_STAGE_KV_SUMMARY))) return SLA_ERR_HIP;
   if (mode == Fwd::kPisa) {
     if (!ok(launch_pisa_stats(s, k, v, proj_k, ws, stream))) return SLA_ERR_HIP;
@@ -112,9 +156,11 @@ extern "C" {
 
 size_t sla_workspace_size(const sla_problem* p, int variant) {
   if (check_problem(p) != SLA_OK) return 0;
-  const Plan s = make_plan(*p);
+  const Plan s = forward_plan(*p);
   switch (variant) {
-    case SLA_VARIANT_FORWARD: return s.total_fwd;
+    case SLA_VARIANT_FORWARD:   // also the routers' layout (their buffers lead both layouts)
+      return s.few ? std::max(s.total_few, s.total_route) : s.total_fwd;
+    case SLA_VARIANT_TAYLOR: return s.total_fwd;
     case SLA_VARIANT_FP8: return s.total_fp8;
     case SLA_VARIANT_PISA: return s.total_pisa;
     default: return 0;
@@ -206,7 +252,7 @@ sla_status sla_workspace_region(const sla_problem* p, int variant, int region, s
   const sla_status st = check_problem(p);
   if (st != SLA_OK) return st;
   if (!offset || !bytes) return SLA_ERR_NULL;
-  const Plan s = make_plan(*p);
+  const Plan s = forward_plan(*p);
   const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk;
   switch (region) {
     case SLA_WS_Q8: *offset = s.q8; *bytes = BH * nbq * kBlock * D * 2; break;
@@ -227,11 +273,15 @@ sla_status sla_workspace_region(const sla_problem* p, int variant, int region, s
   const bool fp8_region = region <= SLA_WS_EV;
   const bool pisa_region = region >= SLA_WS_HBAR;
   const bool linear_region = region == SLA_WS_SC || region == SLA_WS_ZC;
-  if (variant != SLA_VARIANT_FORWARD && variant != SLA_VARIANT_FP8 && variant != SLA_VARIANT_PISA)
+  if (variant != SLA_VARIANT_FORWARD && variant != SLA_VARIANT_FP8 &&
+      variant != SLA_VARIANT_PISA && variant != SLA_VARIANT_TAYLOR)
     return SLA_ERR_SHAPE;
   if (fp8_region && variant != SLA_VARIANT_FP8) return SLA_ERR_SHAPE;
   if (pisa_region && variant != SLA_VARIANT_PISA) return SLA_ERR_SHAPE;
   if (linear_region && variant == SLA_VARIANT_PISA) return SLA_ERR_SHAPE;
+  // the cache path of sla_forward keeps no scores and no per-query-block complement
+  if (s.few && variant == SLA_VARIANT_FORWARD && (linear_region || region == SLA_WS_SCORES))
+    return SLA_ERR_UNSUPPORTED;
   return SLA_OK;
 }
 

@@ -29,7 +29,7 @@ EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8,
               "hbar": 9, "cent_hi": 10, "cent_lo": 11, "vsum": 12}
 # workspace layouts (sla_workspace_size / sla_workspace_region)
-VARIANT_FORWARD, VARIANT_FP8, VARIANT_PISA = 0, 1, 2
+VARIANT_FORWARD, VARIANT_FP8, VARIANT_PISA, VARIANT_TAYLOR = 0, 1, 2, 3
 STAGES = ("kv_summary", "route", "complement", "quant", "sparse")
 # flags of sla_forward_profiled
 PROFILE_FP8 = 1
@@ -165,8 +165,8 @@ def _nbytes(t: torch.Tensor) -> int:
 
 
 def workspace_size(p: Problem, variant=VARIANT_FORWARD) -> int:
-    """Workspace bytes for a layout: VARIANT_FORWARD (False), VARIANT_FP8 (True) or
-    VARIANT_PISA."""
+    """Workspace bytes for a layout: VARIANT_FORWARD (False), VARIANT_FP8 (True),
+    VARIANT_PISA or VARIANT_TAYLOR."""
     return int(library().sla_workspace_size(ctypes.byref(p), int(variant)))
 
 
@@ -259,7 +259,8 @@ def sla_forward_profiled(q, k, v, proj_q, proj_k, alpha, top_k: int, events, fp8
     p = make_problem(q, k, top_k, block, out_dtype)
     _check(q, k, v, () if taylor else (proj_q, proj_k), None if pisa else alpha, out,
            out_dtype, (workspace,))
-    variant = VARIANT_FP8 if fp8 else (VARIANT_PISA if pisa else VARIANT_FORWARD)
+    variant = (VARIANT_FP8 if fp8 else VARIANT_PISA if pisa else
+               VARIANT_TAYLOR if taylor else VARIANT_FORWARD)
     ws = _workspace(p, variant, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
@@ -392,7 +393,7 @@ def sla_forward_taylor(q, k, v, alpha, top_k: int, block: int = 64,
     """SLA2 forward with the training-free router. Returns (O, block_idx or None)."""
     p = make_problem(q, k, top_k, block, out_dtype)
     _check(q, k, v, alpha=alpha, out=out, out_dtype=out_dtype, buffers=(workspace,))
-    ws = _workspace(p, VARIANT_FORWARD, q.device, workspace)
+    ws = _workspace(p, VARIANT_TAYLOR, q.device, workspace)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     idx = None

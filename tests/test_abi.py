@@ -237,17 +237,18 @@ def test_profiled_rejects_unknown_flags(lib, flags):
 
 
 def test_workspace_variants(lib):
-    """Variants 0, 1, 2 have their own sizes; anything else is invalid (size 0)."""
+    """Variants 0 .. 3 have their own sizes; anything else is invalid (size 0)."""
     p = prob()
-    sizes = [lib.sla_workspace_size(ctypes.byref(p), v) for v in (0, 1, 2)]
+    sizes = [lib.sla_workspace_size(ctypes.byref(p), v) for v in (0, 1, 2, 3)]
     assert all(s > 0 for s in sizes)
-    assert lib.sla_workspace_size(ctypes.byref(p), 3) == 0
+    assert sizes[0] == sizes[3]           # no cache path here: Taylor shares the layout
+    assert lib.sla_workspace_size(ctypes.byref(p), 4) == 0
     assert lib.sla_workspace_size(ctypes.byref(p), -1) == 0
     text = open(HEADER).read()
     vals = {m.group(1): int(m.group(2))
             for m in re.finditer(r"SLA_VARIANT_(\w+)\s*=\s*(\d+)", text)}
     assert vals == {"FORWARD": sla.VARIANT_FORWARD, "FP8": sla.VARIANT_FP8,
-                    "PISA": sla.VARIANT_PISA}
+                    "PISA": sla.VARIANT_PISA, "TAYLOR": sla.VARIANT_TAYLOR}
 
 
 def test_workspace_regions_by_variant(lib):
@@ -273,6 +274,41 @@ def test_workspace_regions_by_variant(lib):
     assert size.value == BH * d * npad * 2
     region(2, "hbar")
     assert size.value == BH * d * d * 2
+
+
+def test_cache_path_workspace(lib):
+    """A chunk of at most 8 query blocks per head against at least 256 key blocks (bf16) takes
+    the cache path: its forward workspace is the summary cache, the update's partial totals
+    and the cached forward's workspace, far below the per-key-block layout that the Taylor
+    forward keeps; the scores and complement regions do not exist there."""
+    few = prob(batch=4, heads=32, n_q=64, n_kv=131072, top_k=64)
+    fwd = lib.sla_workspace_size(ctypes.byref(few), 0)
+    taylor = lib.sla_workspace_size(ctypes.byref(few), 3)
+    cache = lib.sla_kv_cache_size(ctypes.byref(few))
+    dec = lib.sla_cached_workspace_size(ctypes.byref(few))
+    upd = lib.sla_kv_cache_workspace_size(ctypes.byref(few), 0)
+    assert cache + dec + upd <= fwd <= cache + dec + upd + 3 * 256
+    # the routers share the forward variant: their buffers (pooled, projected Q and K,
+    # scores, indices, key variances) fit as well
+    small = prob(batch=1, heads=2, n_q=64 * 3, n_kv=64 * 512, top_k=1, head_dim=64)
+    BH, d, nbq, nbk = 2, 64, 3, 512
+    al = lambda x: -(-x // 256) * 256                     # noqa: E731
+    route = al(BH * nbq * d * 8) + al(BH * nbk * d * 8) + al(BH * nbq * nbk * 8) \
+        + al(BH * nbq * 1 * 4) + al(BH * nbk * d * 8)
+    assert lib.sla_workspace_size(ctypes.byref(small), 0) >= route
+    assert taylor > 10 * fwd
+    off, size = ctypes.c_size_t(), ctypes.c_size_t()
+    for name, want in (("sc", 7), ("zc", 7), ("scores", 7)):
+        assert lib.sla_workspace_region(ctypes.byref(few), 0, sla.WS_REGIONS[name],
+                                        ctypes.byref(off), ctypes.byref(size)) == want
+        assert lib.sla_workspace_region(ctypes.byref(few), 3, sla.WS_REGIONS[name],
+                                        ctypes.byref(off), ctypes.byref(size)) == 0
+    # fp32 inputs, more query blocks or fewer key blocks keep the per-block layout
+    for kw in (dict(in_dtype=0), dict(n_q=64 * 9), dict(n_kv=64 * 255)):
+        p = prob(batch=4, heads=32, n_q=kw.get("n_q", 64), n_kv=kw.get("n_kv", 131072),
+                 top_k=64, in_dtype=kw.get("in_dtype", 1))
+        assert lib.sla_workspace_size(ctypes.byref(p), 0) == lib.sla_workspace_size(
+            ctypes.byref(p), 3)
 
 
 def test_pisa_validation(lib):

@@ -160,3 +160,52 @@ def test_longctx_cached_full(sla):
     err, rms = max_err_over_rms(np.concatenate(gots), np.concatenate(refs))
     print(f"longctx cached: rows={rows} near_tie={near} max-abs/rms={err:.3e} rms={rms:.4f}")
     assert err <= TOL
+
+
+# ----------------------------------------------------------------------------- cache path
+# sla_forward with at most 8 query blocks per head over at least 256 key blocks builds the
+# summary cache in its workspace and runs the cached forward.
+FEW_CASES = [
+    (1, 4, 100, 64 * 300, 128, 10, "smooth"),     # two query blocks, ragged
+    (2, 2, 64 * 8, 64 * 256 + 40, 64, 7, "normal"),  # 8 query blocks, partial last key block
+    (1, 2, 64, 64 * 300, 128, 0, "smooth"),       # nothing routed: the linear branch alone
+    (1, 1, 30, 64 * 260, 128, 260, "normal"),     # everything routed: the complement is empty
+]
+
+
+@pytest.mark.parametrize("B,H,nq,nkv,d,top_k,kind", FEW_CASES)
+def test_forward_cache_path(sla, B, H, nq, nkv, d, top_k, kind):
+    x = make_custom(B, H, nq, nkv, d, top_k, dtype="bf16", kind=kind, seed=nq + nkv + top_k)
+    print(f"cache path B={B} H={H} nq={nq} nkv={nkv} d={d} k={top_k} {kind}", flush=True)
+    q, k, v, pq, pk, al = to_device(x)
+    out, idx = sla.sla_forward(q, k, v, pq, pk, al, top_k)
+    torch.cuda.synchronize()
+    out, idx = out.cpu().numpy(), idx.cpu().numpy()
+    check_masks(idx, oracle.sla_oracle.route_full(x), top_k)
+    ref, _ = oracle.forward(x)
+    err, _ = max_err_over_rms(out, ref)
+    print(f"  max-abs/rms {err:.3e}")
+    assert err <= TOL, f"max-abs/rms {err:.3e}"
+    # same selection and the same arithmetic as building the cache and calling the cached
+    # forward
+    out_c, idx_c = run_cached(sla, x)
+    assert np.array_equal(idx, idx_c) and np.array_equal(out, out_c)
+
+
+def test_forward_cache_path_bf16_output_and_profiled(sla):
+    x = make_custom(1, 3, 64 * 2, 64 * 270, 128, 9, dtype="bf16", kind="smooth", seed=77)
+    q, k, v, pq, pk, al = to_device(x)
+    o32, _ = sla.sla_forward(q, k, v, pq, pk, al, 9)
+    o16, _ = sla.sla_forward(q, k, v, pq, pk, al, 9, out_dtype=torch.bfloat16)
+    import ctypes
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(sla.STAGES))]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    op = sla.sla_forward_profiled(q, k, v, pq, pk, al, 9, handles)
+    torch.cuda.synchronize()
+    assert torch.equal(op, o32)
+    assert torch.equal(o16, o32.bfloat16())
+    times = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(sla.STAGES))]
+    assert all(t >= 0 for t in times)
