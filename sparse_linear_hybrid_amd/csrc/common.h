@@ -127,6 +127,14 @@ __device__ __forceinline__ void barrier_vmem_n() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+// The same for loops that also write LDS with ordinary stores that other waves read after
+// the barrier: those stores must have completed (lgkmcnt(0)) before the barrier, which
+// s_barrier alone does not ensure.
+template <int N>
+__device__ __forceinline__ void barrier_vmem_lds_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // ----------------------------------------------------------------------------- tile layout
 // 64-row tiles of D 16-bit columns in LDS (attention K and V tiles, centroid and value-sum
@@ -334,6 +342,31 @@ inline Plan make_plan(const sla_problem& p) {
   s.tail_n = take(BH * nqpad * D * 4);
   s.total_pisa = off;
   return s;
+}
+
+// Workspace of the backward (sla_backward): the forward's per-block layout (key/value pass,
+// complement, bitmap), then the backward's own regions.
+struct BwdPlan {
+  int nwq;                                      // 32-bit words of a query-block bitmap row
+  size_t bitsT, lse, dr, dos, dsc, dzc, gt, gz, dapart, bytes;
+};
+inline BwdPlan make_bwd_plan(const Plan& s) {
+  BwdPlan b{};
+  const size_t BH = s.BH, D = s.D, nbq = s.nbq, nbk = s.nbk, nq64 = nbq * kBlock;
+  b.nwq = (s.nbq + 31) / 32;
+  size_t off = s.total_fwd;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  b.bitsT = take(BH * nbk * (size_t)b.nwq * 4);
+  b.lse = take(BH * nq64 * 4);
+  b.dr = take(BH * nq64 * 4);
+  b.dos = take(BH * nq64 * D * 2);
+  b.dsc = take(BH * nbq * D * D * 2);
+  b.dzc = take(BH * nbq * D * 4);
+  b.gt = take(BH * nbk * D * D * 2);
+  b.gz = take(BH * nbk * D * 4);
+  b.dapart = take(BH * nbq * D * 4);
+  b.bytes = off;
+  return b;
 }
 
 // When the forward takes the cache path (Plan::few): at most kFewQueryBlocks query blocks per

@@ -47,6 +47,11 @@ hipError_t launch_kv_totals(const Plan& s, const void* k, const void* v, const f
                             int n_done, double* kt, size_t kbh, size_t kj, float* stot,
                             float* ztot, char* ws, hipStream_t st);
 
+// Projected block means (float64) of a bf16 tensor [BH][n][D] through a streaming ring:
+// out[bh][j][:] = mean of block j's valid tokens @ P.
+hipError_t launch_pool_stream(const Plan& s, const void* x, const float* P, double* out, int n,
+                              int nb, hipStream_t st);
+
 // Router against cached k~ (k~ of block j of head bh at kt + bh * kbh + j * kj).
 hipError_t launch_route_cached(const Plan& s, const void* q, const float* pq, const double* kt,
                                size_t kbh, size_t kj, int32_t* idx, double* qt, double* sc,
@@ -72,5 +77,17 @@ hipError_t launch_pisa_tail(const Plan& s, const void* q, const int32_t* idx, ch
 // correction inside one normalisation.
 hipError_t launch_sparse_pisa(const Plan& s, const void* q, const void* k, const int32_t* idx,
                               void* o, char* ws, hipStream_t st);
+
+// Linear branch, transposed complement for the backward: per key block j,
+// out[j] = sum over the query blocks i that did not route j of stacked[i] (stacked in the
+// per-block summary layout over query blocks; bitsT [BH][nbk][nwq]: the routed query blocks).
+hipError_t launch_complement_transposed(const Plan& s, const uint32_t* bitsT, int nwq,
+                                        const uint16_t* stacked, uint16_t* out, hipStream_t st);
+
+// Backward at the given selection (bf16 inputs): dq, dk, dv (fp32, like Q, K, V) and dalpha
+// [H][D] (fp32) from dout (out dtype); workspace as make_bwd_plan.
+hipError_t launch_backward(const Plan& s, const void* q, const void* k, const void* v,
+                           const float* alpha, const void* dout, const int32_t* idx, float* dq,
+                           float* dk, float* dv, float* dalpha, char* ws, hipStream_t st);
 
 }  // namespace sla

@@ -614,8 +614,7 @@ static void launch_pool_q(const Plan& s, const void* q, const float* pq, double*
                           hipStream_t st) {
   const dim3 gq((s.nbq + PB - 1) / PB, s.BH);
   if (s.in_bf16)
-    hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gq, dim3(256), 0, st,
-                       (const uint16_t*)q, pq, qt, s.nq, s.nbq);
+    launch_pool_stream(s, q, pq, qt, s.nq, s.nbq, st);
   else
     hipLaunchKernelGGL((pool_project_kernel<float, D>), gq, dim3(256), 0, st, (const float*)q,
                        pq, qt, s.nq, s.nbq);
@@ -672,8 +671,7 @@ static hipError_t launch_route_T(const Plan& s, const void* q, const void* k, co
   if (pool_k) {
     const dim3 gk((s.nbk + PB - 1) / PB, s.BH);
     if (s.in_bf16)
-      hipLaunchKernelGGL((pool_project_kernel<uint16_t, D>), gk, dim3(256), 0, st,
-                         (const uint16_t*)k, pk, kt, s.nkv, s.nbk);
+      launch_pool_stream(s, k, pk, kt, s.nkv, s.nbk, st);
     else
       hipLaunchKernelGGL((pool_project_kernel<float, D>), gk, dim3(256), 0, st, (const float*)k,
                          pk, kt, s.nkv, s.nbk);

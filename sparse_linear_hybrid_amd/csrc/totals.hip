@@ -17,6 +17,8 @@
 //   * k~ partial over the strip: sum_{r in strip} mean_r P_k[r][c] for every output channel c,
 //     with the strip's rows of P_k held in registers as float64; the four strip partials are
 //     added in a fixed order one iteration later (after the next barrier) and stored.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,27 +35,32 @@ struct TotalsArgs {
   float* spart;        // [BH][nchunk][D(c)][D(r)]
   float* zpart;        // [BH][nchunk][D]
   int nkv, nbk, jbase, t0, nchunk;
+  int chunk;           // key blocks per workgroup
 };
 
-template <int D>
+template <int D, bool POOL>
 struct TotalsCfg {
   static constexpr int NS = 4;                         // ring depth (blocks)
   static constexpr int TILE = 64 * D;                  // elements of a K or V tile
   static constexpr int KPW = TILE * 2 / 1024 / 4;      // 1-KB pieces per wave and tensor
   static constexpr int NT = D / 32;                    // 32-column tiles of the value side
   static constexpr int TPW = D == 128 ? NT : 1;        // value tiles per wave
-  static constexpr int OCC = D == 128 ? 1 : 2;         // workgroups per CU
+  static constexpr int OCC = (D == 128 && !POOL) ? 1 : 2;   // workgroups per CU
   static constexpr int CPL = D / 64;                   // output channels of k~ per lane
   static constexpr int STRIPS = D / 32;                // 32-channel strips of phi(K)^T
 };
 
-template <int D>
-__global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(TotalsArgs a) {
-  using C = TotalsCfg<D>;
+// POOL: only the projected block means of one tensor (the router's pooling of Q, or of K
+// when it routes on its own): the V tiles, the MFMA product and the partial totals drop out.
+template <int D, bool POOL>
+__global__ __launch_bounds__(256, (TotalsCfg<D, POOL>::OCC)) void kv_totals_kernel(TotalsArgs a) {
+  using C = TotalsCfg<D, POOL>;
   constexpr int NS = C::NS, TILE = C::TILE, KPW = C::KPW, TPW = C::TPW, CPL = C::CPL;
   constexpr int STRIPS = C::STRIPS;
   constexpr int CH = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t ring[NS * 2 * TILE];   // [slot][K, V]
+  constexpr int TPS = POOL ? 1 : 2;                     // tiles per ring slot
+  constexpr int LPS = TPS * KPW;                         // loads per wave and slot
+  __shared__ __attribute__((aligned(16))) uint16_t ring[NS * TPS * TILE];   // [slot][K, V]
   __shared__ double kpart[2][STRIPS][D];   // per strip: partial k~ of the last two blocks
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
@@ -62,8 +69,8 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
   const int mt = D == 128 ? w : (w >> 1);             // 32-channel strip of phi(K)^T
   const int nt0 = D == 128 ? 0 : (w & 1);             // first value tile of this wave
   const bool proj_wave = D == 128 || (w & 1) == 0;    // computes the strip's k~ partial
-  const int j0 = a.jbase + chunk * kCacheChunk;
-  const int j1 = min(j0 + kCacheChunk, a.nbk);
+  const int j0 = a.jbase + chunk * a.chunk;
+  const int j1 = min(j0 + a.chunk, a.nbk);
   const uint16_t* kb = a.k + (size_t)bh * a.nkv * D;
   const uint16_t* vb = a.v + (size_t)bh * a.nkv * D;
 
@@ -95,12 +102,14 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
     const uint32_t bytes = live ? (uint32_t)(min(kBlock, a.nkv - row0) * D * 2) : 0u;
     const i32x4 rk = make_rsrc(kb + (size_t)row0 * D, bytes);
     const i32x4 rv = make_rsrc(vb + (size_t)row0 * D, bytes);
-    const uint32_t kd = lds_addr(ring + slot * 2 * TILE) + wvs * KPW * 1024;
-    const uint32_t vd = lds_addr(ring + (slot * 2 + 1) * TILE) + wvs * KPW * 1024;
+    const uint32_t kd = lds_addr(ring + slot * TPS * TILE) + wvs * KPW * 1024;
 #pragma unroll
     for (int u = 0; u < KPW; ++u) load_lds16(rk, kd + u * 1024, koff[u]);
+    if constexpr (!POOL) {
+      const uint32_t vd = lds_addr(ring + (slot * 2 + 1) * TILE) + wvs * KPW * 1024;
 #pragma unroll
-    for (int u = 0; u < KPW; ++u) load_lds16(rv, vd + u * 1024, voff[u]);
+      for (int u = 0; u < KPW; ++u) load_lds16(rv, vd + u * 1024, voff[u]);
+    }
   };
 
   // transposing fragment reads (lane: index x0 + lane % 32, 8 tokens k0 + 8 h ..)
@@ -136,12 +145,13 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
   for (int j = j0; j < j1; ++j) {
     const int it = j - j0;
     const int slot = it % NS;
-    // tile j has landed for every wave (at most the NS - 2 later tiles are in flight), and
-    // every wave is done with the slot refilled below and with kpart[(j - 1) & 1]
-    barrier_vmem_n<(NS - 2) * 2 * KPW>();
+    // tile j has landed for every wave (at most the NS - 2 later tiles are in flight), every
+    // wave is done with the slot refilled below, and its kpart stores of block j - 1 are
+    // complete (ordinary LDS stores: the barrier waits for them explicitly)
+    barrier_vmem_lds_n<(NS - 2) * LPS>();
     stage(j + NS - 1, (it + NS - 1) % NS);
     if (j > j0) finish_kt(j - 1);
-    const uint16_t* Kt = ring + slot * 2 * TILE;
+    const uint16_t* Kt = ring + slot * TPS * TILE;
     const uint16_t* Vt = Kt + TILE;
     const int row0 = j * kBlock;
     const int nrows = min(kBlock, a.nkv - row0);
@@ -169,11 +179,13 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
       for (int e = 0; e < 4; ++e) zl += bf16_lo(af[s4][e]) + bf16_hi(af[s4][e]);
     }
     zsum += zl;
+    if constexpr (!POOL) {
 #pragma unroll
-    for (int u = 0; u < TPW; ++u)
+      for (int u = 0; u < TPW; ++u)
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        acc[u] = mfma_bf16(af[s4], frag(Vt, 32 * (nt0 + u), 16 * s4, true), acc[u]);
+        for (int s4 = 0; s4 < 4; ++s4)
+          acc[u] = mfma_bf16(af[s4], frag(Vt, 32 * (nt0 + u), 16 * s4, true), acc[u]);
+    }
     if (proj_wave) {
       // column sums over the 64 tokens (lane halves hold 32 each), then the strip's k~ part
       const double mean = (csum + __shfl_xor(csum, 32, 64)) / (double)nrows;
@@ -196,6 +208,7 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
   wait_vmem();          // no load into LDS outlives the workgroup
   __syncthreads();
   if (j1 > j0) finish_kt(j1 - 1);
+  if constexpr (POOL) return;
 
   // chunk partial totals, layout [c][r]; z over the strip (both lane halves hold it)
   const int cidx = chunk;
@@ -217,10 +230,12 @@ __global__ __launch_bounds__(256, TotalsCfg<D>::OCC) void kv_totals_kernel(Total
 }  // namespace
 
 // The cache update from n_done tokens (bf16 inputs): the streaming pass above, then the
-// fixed-order reduction of the chunk partials onto (or, from zero tokens, into) the totals.
+// fixed-order reduction of its chunk partials onto (or, from zero tokens, into) the totals.
 hipError_t launch_kv_totals(const Plan& s, const void* k, const void* v, const float* pk,
                             int n_done, double* kt, size_t kbh, size_t kj, float* stot,
                             float* ztot, char* ws, hipStream_t st) {
+  (void)stot;
+  (void)ztot;
   TotalsArgs a;
   a.k = reinterpret_cast<const uint16_t*>(k);
   a.v = reinterpret_cast<const uint16_t*>(v);
@@ -235,12 +250,37 @@ hipError_t launch_kv_totals(const Plan& s, const void* k, const void* v, const f
   a.jbase = n_done / kBlock;
   a.t0 = n_done;
   a.nchunk = cache_update_chunks(s, n_done);
+  a.chunk = kCacheChunk;
   if (a.nchunk == 0) return hipSuccess;
   const dim3 grid(a.nchunk, s.BH);
   if (s.D == 128)
-    hipLaunchKernelGGL(kv_totals_kernel<128>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kv_totals_kernel<128, false>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(kv_totals_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((kv_totals_kernel<64, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Projected block means x~ = mean(x_j) P (float64) of a bf16 tensor x [BH][n][D], written to
+// out[bh][j][D], streamed through the same ring.
+hipError_t launch_pool_stream(const Plan& s, const void* x, const float* P, double* out, int n,
+                              int nb, hipStream_t st) {
+  TotalsArgs a{};
+  a.k = reinterpret_cast<const uint16_t*>(x);
+  a.pk = P;
+  a.kt = out;
+  a.kbh = (size_t)nb * s.D;
+  a.kj = (size_t)s.D;
+  a.nkv = n;
+  a.nbk = nb;
+  // about three workgroups per CU over the whole tensor, at least four blocks each
+  const long long total = (long long)s.BH * nb;
+  a.chunk = (int)std::max(4LL, (total + 767) / 768);
+  a.nchunk = (nb + a.chunk - 1) / a.chunk;
+  const dim3 grid(a.nchunk, s.BH);
+  if (s.D == 128)
+    hipLaunchKernelGGL((kv_totals_kernel<128, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((kv_totals_kernel<64, true>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
