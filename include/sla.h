@@ -255,6 +255,30 @@ sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k
                               void* o, int32_t* block_idx, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of sla_forward at a given selection (SLA2 page, section 2.B: training replaces
+ * the hard top-k by a SoftTop-k the page does not define, so the selection is held fixed here
+ * and proj_q, proj_k receive no gradient through it; section 2.C: the backward runs at
+ * higher precision than a quantised forward). For the forward output O and the upstream
+ * gradient dO of the same shape:
+ *   dalpha = sum over batch and rows of dO (.) (O_s - O_l);
+ *   the exact branch: softmax-attention gradients over each query block's routed tokens with
+ *     dO_s = alpha (.) dO;
+ *   the linear branch: gradients of O_l = phi(q) S_c / (phi(q) . z_c + 1e-6) with
+ *     dO_l = (1 - alpha) (.) dO, flowing into every key token of the blocks a query block did
+ *     not route (phi = ReLU, derivative 0 at 0).
+ * Inputs as sla_forward (in_dtype must be SLA_BF16); dout has out_dtype and O's shape;
+ * block_idx (required unless top_k is 0) is the forward's selection [B, H, ceil(n_q/64),
+ * top_k], ascending.
+ * Outputs, fp32: dq like Q, dk and dv like K and V, dalpha [heads, head_dim]. Products run on
+ * bf16 / f16 MFMA with fp32 accumulation; results are bit-reproducible. */
+size_t sla_backward_workspace_size(const sla_problem* p);
+
+sla_status sla_backward(const sla_problem* p, const void* q, const void* k, const void* v,
+                        const float* alpha, const void* dout, const int32_t* block_idx,
+                        float* dq, float* dk, float* dv, float* dalpha, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- allocation-free decode
  * For callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc. sla_forward_cached without the workspace
@@ -275,6 +299,16 @@ sla_status sla_forward_cached_noalloc(const sla_problem* p, const void* q, const
                                       const void* v, const float* proj_q, const float* alpha,
                                       const void* cache, void* o, int32_t* block_idx,
                                       hipStream_t stream);
+
+/* ---------------------------------------------------------------- diagnostics
+ * Not part of the method: one 32 x 32 x 64 product C = A B of E4M3 codes (a: 32 x 64 row-major,
+ * b: 64 x 32 row-major, device bytes; no NaN codes) computed twice on the GPU, with the scaled
+ * fp8 matrix instruction (unit scales) into c_fp8 and with the bf16 matrix instruction on the
+ * same values (exact operands and products) into c_bf16, both fp32 32 x 32 row-major. It
+ * measures how the fp8 instruction accumulates products of different magnitude, which decides
+ * the quantised forward's choice of instruction for Q K^T (see sla_forward_fp8). */
+sla_status sla_diag_fp8_mfma(const uint8_t* a, const uint8_t* b, float* c_fp8, float* c_bf16,
+                             hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* sla_status_string(sla_status s);

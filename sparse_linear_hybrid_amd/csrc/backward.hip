@@ -1,0 +1,775 @@
+// Backward of the SLA2 forward at a given block selection (SLA2 page, section 2.B: the hard
+// top-k selection is held fixed, so proj_q and proj_k receive no gradient through it; section
+// 2.C: the backward runs in higher precision than a quantised forward — here bf16 / f16 MFMA
+// with fp32 accumulation on the unquantised branches). Given dO, per (batch, head):
+//   mix:     dalpha = sum_n dO (.) (O_s - O_l), dO_s = alpha dO, dO_l = (1 - alpha) dO;
+//   sparse:  FlashAttention-style, P recomputed from the row log-sum-exp:
+//            dV += P^T dO_s, dS = P (.) (dO_s V^T - D_n), dQ += tau dS K, dK += tau dS^T Q,
+//            D_n = dO_s[n] . O_s[n];
+//   linear:  g_n = dO_l[n] / den_n, h_n = -(dO_l[n] . O_l[n]) / den_n,
+//            dQ += (g S_c^T + h z_c) (.) 1[q > 0], dS_c(i) = phi(Q_i)^T g, dz_c(i) = phi(Q_i)^T h,
+//            and per key block j with G_j = sum_{i: j not in sel(i)} dS_c(i) (the transposed
+//            complement, computed by the complement kernel with the roles of query and key
+//            blocks swapped) and gz_j likewise: dV += phi(K_j) G_j,
+//            dK += (V_j G_j^T + gz_j) (.) 1[k > 0].
+// Kernels, in launch order:
+//   bwd_bits_kernel     routed-block bitmaps of both orientations from the index lists;
+//   (key/value pass)    S_j as bf16 high and low parts, z_j, z_tot and the f16 copy of V;
+//   (complement, fp32)  S_c(i) = sum of the unselected S_j, high and low parts summed in fp32;
+//                       z_c(i);
+//   bwd_query_kernel    per query block: the exact branch again (online softmax, so O_s and
+//                       the log-sum-exp), O_l, D, dO_s (f16), dalpha partials, the linear
+//                       part of dQ, dS_c(i) (bf16 high and low parts, summary layout), dz_c(i);
+//   (complement, fp32)  G_j from the dS_c(i), roles of query and key blocks swapped;
+//   bwd_gz_kernel       gz_j;
+//   bwd_key_kernel      per key block: dK, dV over the query blocks that selected it, plus
+//                       the linear parts;
+//   bwd_dq_kernel       per query block: the exact branch's dQ, added to the linear part;
+//   bwd_dalpha_kernel   dalpha from the per-query-block partials (fixed order).
+// The linear gradients are differences of nearly equal terms (g S_c^T against h z_c, and
+// V G^T against gz: both are covariances of the value with the feature map over the
+// complement), so S_c, g, dS_c and G are carried as bf16 high + low parts into the MFMAs.
+// Layout conventions follow the forward (transposed products so that an accumulator feeds
+// the next MFMA as an operand; transposing LDS reads supply the other operand in the same
+// permuted order). Everything is deterministic: no atomics, fixed reduction orders.
+#include "common.h"
+#include "kernels.h"
+
+namespace sla {
+
+namespace {
+
+struct BwdArgs {
+  const uint16_t* q;        // bf16 [BH][nq][D]
+  const uint16_t* k;        // bf16 [BH][nkv][D]
+  const uint16_t* v;        // bf16 [BH][nkv][D]
+  const uint16_t* v16;      // f16 copy of V [BH][nbk*64][D], padded rows zero
+  const void* dout;         // [BH][nq][D], f32 or bf16
+  int dout_bf16;
+  const float* alpha;       // [H][D]
+  const int32_t* idx;       // [BH][nbq][topk], ascending
+  const uint32_t* bitsT;    // [BH][nbk][nwq]: bit i of key block j's row: j in sel(i)
+  const float* sc;          // S_c^T [BH][nbq][D(c)][D(r)] fp32
+  const float* zc;          // [BH][nbq][D]
+  float* lse;               // [BH][nbq*64] (base-2 units; 1e30 where a row has no exact part)
+  float* dr;                // [BH][nbq*64]: D_n
+  uint16_t* dos;            // f16 [BH][nbq*64][D]: dO_s
+  uint16_t* dsc;            // bf16 [BH][D*D/128][nbq][128]: dS_c(i)^T flattened [c][r]
+  uint16_t* dsclo;          // dS_c(i)^T - bf16(dS_c(i)^T) rounded to bf16, same layout
+  float* dzc;               // [BH][nbq][D]
+  const float* gt;          // G_j^T [BH][nbk][D(c)][D(r)] fp32
+  float* gz;                // [BH][nbk][D]
+  float* dapart;            // [BH][nbq][D]
+  float* dq;                // [BH][nq][D]
+  float* dk;                // [BH][nkv][D]
+  float* dv;                // [BH][nkv][D]
+  int nq, nkv, nbq, nbk, topk, H, nwq;
+};
+
+constexpr float kNoRow = 1.0e30f;   // log-sum-exp of a row with no exact part: P = 0
+
+// Transposing fragment read in natural order from a swz-swizzled [row][col] tile of 16-bit
+// elements: lane owns column x0 + lane % 32 and the 8 rows k0 + 8 (lane / 32) .. + 7.
+template <int D>
+__device__ __forceinline__ u32x4 tr_nat(const uint16_t* M, int x0, int k0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, L = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (L >> 2);
+  const int col = x0 + 16 * (g & 1) + 4 * (L & 3);
+  const u32x2 lo = lds_read_tr16(M + swz<D>(row, col));
+  const u32x2 hi = lds_read_tr16(M + swz<D>(row + 4, col));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 64-row tile copy global -> LDS through registers (rows >= nvalid are zero). SWZV: the V
+// swizzle (tiles read with vt_frag), else the row swizzle swz.
+template <int D, bool SWZV>
+__device__ __forceinline__ void copy_tile(uint16_t* dst, const uint16_t* src, int nvalid) {
+  constexpr int CH = D / 8;
+  for (int id = threadIdx.x; id < 64 * CH; id += blockDim.x) {
+    const int r = id / CH, c = id % CH;
+    const u32x4 w = r < nvalid ? *reinterpret_cast<const u32x4*>(src + (size_t)r * D + c * 8)
+                               : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(dst + (SWZV ? swzv<D>(r, c * 8) : swz<D>(r, c * 8))) = w;
+  }
+}
+
+// 8 consecutive fp32 values as two bf16 fragments: the rounded values and the remainders
+__device__ __forceinline__ void split8(const float* p, u32x4& hi, u32x4& lo) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 y = *reinterpret_cast<const f32x4*>(p + 4);
+  const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = pack_bf16(v[2 * e], v[2 * e + 1]);
+    lo[e] = pack_bf16(v[2 * e] - bf16_lo(hi[e]), v[2 * e + 1] - bf16_hi(hi[e]));
+  }
+}
+
+// 8 consecutive elements of row `row` at column col (a multiple of 8) of a swizzled tile
+template <int D, bool SWZV>
+__device__ __forceinline__ u32x4 row_frag(const uint16_t* M, int row, int col) {
+  return *reinterpret_cast<const u32x4*>(M + (SWZV ? swzv<D>(row, col) : swz<D>(row, col)));
+}
+
+// ----------------------------------------------------------------------------- bitmaps
+// Row i of selbits: bit j set iff key block j is routed to query block i; row j of bitsT:
+// bit i set iff j is routed to i. One workgroup per (batch*head, row).
+__global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ idx,
+                                                       uint32_t* __restrict__ selbits,
+                                                       uint32_t* __restrict__ bitsT, int nbq,
+                                                       int nbk, int topk, int nwk, int nwq) {
+  extern __shared__ uint32_t wbits[];
+  const int bh = blockIdx.y, row = blockIdx.x, t = threadIdx.x;
+  if (row < nbq) {   // forward orientation
+    for (int w = t; w < nwk; w += 256) wbits[w] = 0u;
+    __syncthreads();
+    const int32_t* sel = idx + ((size_t)bh * nbq + row) * topk;
+    for (int e = t; e < topk; e += 256) {
+      const int j = sel[e];
+      atomicOr(&wbits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    for (int w = t; w < nwk; w += 256) selbits[((size_t)bh * nbq + row) * nwk + w] = wbits[w];
+  } else {           // transposed: key block j = row - nbq; binary search in each list
+    const int j = row - nbq;
+    for (int w = t; w < nwq; w += 256) {
+      uint32_t word = 0u;
+      for (int b = 0; b < 32; ++b) {
+        const int i = 32 * w + b;
+        if (i >= nbq) break;
+        const int32_t* sel = idx + ((size_t)bh * nbq + i) * topk;
+        int lo = 0, hi = topk;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (sel[mid] < j) lo = mid + 1; else hi = mid;
+        }
+        if (lo < topk && sel[lo] == j) word |= 1u << b;
+      }
+      bitsT[((size_t)bh * nbk + j) * nwq + w] = word;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- per query block
+// Two waves, wave w owns query rows 32 w .. 32 w + 31 of query block iq; the O^T accumulator
+// layout (lane: query row, elements: channels 32 c + 8 g + 4 h + e) is kept throughout.
+template <int D>
+__global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
+  constexpr int KS = D / 16, CT = D / 32, CH = D / 8, TILE = 64 * D;
+  constexpr int NCS = D * D / 128;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * D * D + 3 * TILE];
+  __shared__ float hh_s[64];
+  const int bh = blockIdx.x / a.nbq, iq = blockIdx.x % a.nbq;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int row = 32 * wv + l32;              // row within the query block
+  const int n = iq * kBlock + row;            // query token
+  const bool valid = n < a.nq;
+  const int hd = bh % a.H;
+  const float qk_scale = kLog2e / sqrtf((float)D);
+  const float tau = 1.f / sqrtf((float)D);
+  const uint16_t* qrow = a.q + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
+
+  u32x4 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    qf[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+
+  // ---------------------------------------------------------------- exact branch again
+  f32x16 o[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) o[c] = f32x16{};
+  float m = kNegBig, l = 0.f;
+  uint16_t* Kt = smem;
+  uint16_t* Vt = smem + TILE;
+  const int32_t* sel = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
+  for (int e = 0; e < a.topk; ++e) {
+    const int j = sel[e];
+    const int nval = min(kBlock, a.nkv - j * kBlock);
+    __syncthreads();
+    copy_tile<D, false>(Kt, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D, nval);
+    copy_tile<D, true>(Vt, a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
+    __syncthreads();
+    f32x16 sh[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sh[mt] = mfma_bf16(row_frag<D, false>(Kt, 32 * mt + l32, 16 * ks + 8 * h), qf[ks], sh[mt]);
+    float r = kNegBig;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int el = 0; el < 16; ++el) {
+        const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
+        sh[mt][el] = key < nval ? sh[mt][el] : -INFINITY;
+        r = fmaxf(r, sh[mt][el]);
+      }
+    r = fmaxf(r, swap_halves(r)) * qk_scale;
+    if (r > m) {
+      const float corr = __builtin_amdgcn_exp2f(m - r);
+      l *= corr;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] *= corr;
+      m = r;
+    }
+    u32x4 pf[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int el = 8 * hh + 2 * e2;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[mt][el], qk_scale, -m));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[mt][el + 1], qk_scale, -m));
+          const uint32_t pk = pack_f16(p0, p1);
+          pf[2 * mt + hh][e2] = pk;
+          rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, rs, false);
+        }
+    l += rs;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] = mfma_f16(vt_frag<D>(Vt, 32 * c, 16 * kk), pf[kk], o[c]);
+  }
+  l += swap_halves(l);
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
+  const float lse = (l > 0.f && valid) ? m + log2f(l) : kNoRow;
+
+  // ---------------------------------------------------------------- linear branch again
+  const bool empty_c = a.topk >= a.nbk;
+  const float* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
+  const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
+  f32x16 lin[CT];
+  float den = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const u32x4 rq = relu_bf16x8(qf[s]);
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2)
+      den += bf16_lo(rq[e2]) * zcb[16 * s + 8 * h + 2 * e2] +
+             bf16_hi(rq[e2]) * zcb[16 * s + 8 * h + 2 * e2 + 1];
+  }
+  den += swap_halves(den);
+  den += kEps;
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    lin[c] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 ah, alo;
+      split8(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h, ah, alo);
+      const u32x4 qb = relu_bf16x8(qf[s]);
+      lin[c] = mfma_bf16(ah, qb, lin[c]);
+      lin[c] = mfma_bf16(alo, qb, lin[c]);
+    }
+  }
+  const float inv_den = empty_c ? 0.f : 1.f / den;
+
+  // ---------------------------------------------------------------- upstream gradient
+  __syncthreads();   // the tile buffers are free: X (dalpha terms) goes to smem as fp32
+  float* xs = reinterpret_cast<float*>(smem);     // [64][D]
+  const float* al = a.alpha + (size_t)hd * D;
+  float dsum = 0.f, hsum = 0.f;
+  f32x16 gv[CT];                                  // g = dO_l / den, O^T layout
+  uint16_t* dosr = a.dos + ((size_t)bh * a.nbq * kBlock + iq * kBlock + row) * D;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = 32 * c + 8 * g4 + 4 * h;
+      float dov[4] = {0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        if (a.dout_bf16) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(
+              reinterpret_cast<const uint16_t*>(a.dout) + ((size_t)bh * a.nq + n) * D + ch);
+          dov[0] = bf16_lo(w[0]); dov[1] = bf16_hi(w[0]); dov[2] = bf16_lo(w[1]); dov[3] = bf16_hi(w[1]);
+        } else {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(
+              reinterpret_cast<const float*>(a.dout) + ((size_t)bh * a.nq + n) * D + ch);
+          dov[0] = w[0]; dov[1] = w[1]; dov[2] = w[2]; dov[3] = w[3];
+        }
+      }
+      const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
+      float dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ix = 4 * g4 + e;
+        const float os = o[c][ix] * inv_l;
+        const float ol = lin[c][ix] * inv_den;
+        dsv[e] = alv[e] * dov[e];
+        const float dl = (1.f - alv[e]) * dov[e];
+        dsum += dsv[e] * os;
+        hsum += dl * ol;
+        gv[c][ix] = dl * inv_den;
+        xs[row * D + ch + e] = dov[e] * (os - ol);
+      }
+      *reinterpret_cast<u32x2*>(dosr + ch) = u32x2{pack_f16(dsv[0], dsv[1]), pack_f16(dsv[2], dsv[3])};
+    }
+  dsum += swap_halves(dsum);
+  hsum += swap_halves(hsum);
+  const float hn = empty_c ? 0.f : -hsum * inv_den;
+  if (h == 0) {
+    a.lse[(size_t)bh * a.nbq * kBlock + iq * kBlock + row] = lse;
+    a.dr[(size_t)bh * a.nbq * kBlock + iq * kBlock + row] = valid ? dsum : 0.f;
+    hh_s[row] = valid ? hn : 0.f;
+  }
+  __syncthreads();
+  for (int c = t; c < D; c += 128) {   // dalpha partial: the block's rows in order
+    float s = 0.f;
+    for (int r2 = 0; r2 < kBlock; ++r2) s += xs[r2 * D + c];
+    a.dapart[((size_t)bh * a.nbq + iq) * D + c] = s;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- linear part of dQ
+  // smem: S_c^T [D][D] as bf16 high and low parts (V swizzle, read with vt_frag), then the
+  // Q tile and the g tiles (row swizzle, read with tr_nat)
+  uint16_t* Sct = smem;
+  uint16_t* Scl = smem + D * D;
+  uint16_t* Qt = smem + 2 * D * D;
+  uint16_t* Gt = Qt + TILE;     // g rounded to bf16
+  uint16_t* Gl = Gt + TILE;     // and its remainder, also bf16
+  for (int id = t; id < D * CH; id += 128) {
+    const int rr = id / CH, cc = id % CH;
+    u32x4 hi, lo;
+    split8(scb + (size_t)rr * D + cc * 8, hi, lo);
+    *reinterpret_cast<u32x4*>(Sct + swzv<D>(rr, cc * 8)) = hi;
+    *reinterpret_cast<u32x4*>(Scl + swzv<D>(rr, cc * 8)) = lo;
+  }
+  copy_tile<D, false>(Qt, a.q + ((size_t)bh * a.nq + (size_t)iq * kBlock) * D,
+                      min(kBlock, a.nq - iq * kBlock));
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = 32 * c + 8 * g4 + 4 * h;
+      const uint32_t h0 = pack_bf16(gv[c][4 * g4], gv[c][4 * g4 + 1]);
+      const uint32_t h1 = pack_bf16(gv[c][4 * g4 + 2], gv[c][4 * g4 + 3]);
+      *reinterpret_cast<u32x2*>(Gt + swz<D>(row, ch)) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(Gl + swz<D>(row, ch)) =
+          u32x2{pack_bf16(gv[c][4 * g4] - bf16_lo(h0), gv[c][4 * g4 + 1] - bf16_hi(h0)),
+                pack_bf16(gv[c][4 * g4 + 2] - bf16_lo(h1), gv[c][4 * g4 + 3] - bf16_hi(h1))};
+    }
+  __syncthreads();
+  // da^T = S_c g^T: M = r, N = this wave's rows, K = c (g's elements in vt_frag's order).
+  // S_c and g enter as bf16 high and low parts (the low x low product is below fp32's
+  // rounding): g S_c^T and h z_c nearly cancel (their difference is the covariance of phi(k)
+  // and v over the complement), so one bf16 rounding of either would show in dQ.
+  f32x16 da[CT];
+#pragma unroll
+  for (int rt = 0; rt < CT; ++rt) da[rt] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int c = s >> 1, e0 = 8 * (s & 1);
+    u32x4 gb, gl;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const float x0 = gv[c][e0 + 2 * e2], x1 = gv[c][e0 + 2 * e2 + 1];
+      gb[e2] = pack_bf16(x0, x1);
+      gl[e2] = pack_bf16(x0 - bf16_lo(gb[e2]), x1 - bf16_hi(gb[e2]));
+    }
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
+      const u32x4 sa = vt_frag<D>(Sct, 32 * rt, 16 * s);
+      da[rt] = mfma_bf16(sa, gb, da[rt]);
+      da[rt] = mfma_bf16(sa, gl, da[rt]);
+      da[rt] = mfma_bf16(vt_frag<D>(Scl, 32 * rt, 16 * s), gb, da[rt]);
+    }
+  }
+  if (valid) {
+    float* dqr = a.dq + ((size_t)bh * a.nq + n) * D;
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = 32 * rt + 8 * g4 + 4 * h;
+        const f32x4 z = *reinterpret_cast<const f32x4*>(zcb + r0);
+        const u32x2 qw = *reinterpret_cast<const u32x2*>(qrow + r0);
+        const float qv[4] = {bf16_lo(qw[0]), bf16_hi(qw[0]), bf16_lo(qw[1]), bf16_hi(qw[1])};
+        f32x4 outv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dav = da[rt][4 * g4 + e] + hn * z[e];
+          outv[e] = qv[e] > 0.f ? dav : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(dqr + r0) = outv;
+      }
+  }
+  // dS_c(i)^T[c][r] = sum_n g[n][c] relu(q[n][r]): M = c, N = r, K = the block's 64 rows.
+  // Wave w takes the c tiles w, w + 2, ...
+  for (int ct = wv; ct < CT; ct += 2) {
+#pragma unroll
+    for (int rt = 0; rt < CT; ++rt) {
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 qb = relu_bf16x8(tr_nat<D>(Qt, 32 * rt, 16 * kk));
+        acc = mfma_bf16(tr_nat<D>(Gt, 32 * ct, 16 * kk), qb, acc);
+        acc = mfma_bf16(tr_nat<D>(Gl, 32 * ct, 16 * kk), qb, acc);
+      }
+      // element el: c = 32 ct + 8 (el / 4) + 4 h + el % 4, r = 32 rt + l32
+      const int r = 32 * rt + l32;
+#pragma unroll
+      for (int el = 0; el < 16; ++el) {
+        const int c = 32 * ct + 8 * (el >> 2) + 4 * h + (el & 3);
+        const int f = c * D + r;
+        const size_t o = (((size_t)bh * NCS + f / 128) * a.nbq + iq) * 128 + f % 128;
+        const uint32_t hi = pack_bf16(acc[el], 0.f);
+        a.dsc[o] = (uint16_t)(hi & 0xffffu);
+        a.dsclo[o] = (uint16_t)(pack_bf16(acc[el] - bf16_lo(hi), 0.f) & 0xffffu);
+      }
+    }
+  }
+  // dz_c(i)[r] = sum_n relu(q[n][r]) h_n
+  for (int r = t; r < D; r += 128) {
+    float s = 0.f;
+    for (int r2 = 0; r2 < kBlock; ++r2)
+      s += fmaxf(bf16_bits_to_f32(Qt[swz<D>(r2, r)]), 0.f) * hh_s[r2];
+    a.dzc[((size_t)bh * a.nbq + iq) * D + r] = s;
+  }
+}
+
+// gz_j = sum over the query blocks i that did not select j of dz_c(i), in order of i
+template <int D>
+__global__ __launch_bounds__(64) void bwd_gz_kernel(BwdArgs a) {
+  const int bh = blockIdx.x / a.nbk, j = blockIdx.x % a.nbk, lane = threadIdx.x;
+  const uint32_t* row = a.bitsT + ((size_t)bh * a.nbk + j) * a.nwq;
+  float acc[D / 64];
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
+  for (int w = 0; w < a.nwq; ++w) {
+    const uint32_t word = row[w];
+    for (int b = 0; b < 32; ++b) {
+      const int i = 32 * w + b;
+      if (i >= a.nbq) break;
+      if ((word >> b) & 1u) continue;
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) acc[u] += a.dzc[((size_t)bh * a.nbq + i) * D + lane + 64 * u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u)
+    a.gz[((size_t)bh * a.nbk + j) * D + lane + 64 * u] = acc[u];
+}
+
+// ----------------------------------------------------------------------------- per key block
+// Two waves, wave w owns keys 32 w .. 32 w + 31 of key block j. Products are oriented so that
+// the score accumulator (rows: queries, lane: key) feeds the dV^T and dK^T products directly.
+template <int D>
+__global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
+  constexpr int KS = D / 16, CT = D / 32, TILE = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE > 2 * D * D ? 2 * TILE : 2 * D * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[64], dr_s[64];
+  const int bh = blockIdx.x / a.nbk, j = blockIdx.x % a.nbk;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int key = j * kBlock + 32 * wv + l32;
+  const bool kvalid = key < a.nkv;
+  const float qk_scale = kLog2e / sqrtf((float)D);
+  const float tau = 1.f / sqrtf((float)D);
+  const uint16_t* krow = a.k + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
+  const uint16_t* v16row = a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock + 32 * wv + l32) * D;
+  u32x4 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(krow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    vf[s] = *reinterpret_cast<const u32x4*>(v16row + 16 * s + 8 * h);
+  }
+  f32x16 dvt[CT], dkt[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) dvt[c] = dkt[c] = f32x16{};
+  uint16_t* Qs = smem;            // V swizzle: row reads and vt_frag reads
+  uint16_t* Os = smem + TILE;     // dO_s tile, f16, V swizzle
+  const uint32_t* brow = a.bitsT + ((size_t)bh * a.nbk + j) * a.nwq;
+  for (int w = 0; w < a.nwq; ++w) {
+    uint32_t word = brow[w];
+    while (word) {
+      const int i = 32 * w + __builtin_ctz(word);
+      word &= word - 1u;
+      __syncthreads();
+      copy_tile<D, true>(Qs, a.q + ((size_t)bh * a.nq + (size_t)i * kBlock) * D,
+                         min(kBlock, a.nq - i * kBlock));
+      copy_tile<D, true>(Os, a.dos + ((size_t)bh * a.nbq * kBlock + (size_t)i * kBlock) * D, kBlock);
+      if (t < 64) {
+        lse_s[t] = a.lse[(size_t)bh * a.nbq * kBlock + i * kBlock + t];
+        dr_s[t] = a.dr[(size_t)bh * a.nbq * kBlock + i * kBlock + t];
+      }
+      __syncthreads();
+      // S = Q K^T and dP = dO_s V^T: rows n (two 32-row tiles), lane: key
+      f32x16 sv[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          sv[mt] = mfma_bf16(row_frag<D, true>(Qs, 32 * mt + l32, 16 * s + 8 * h), kf[s], sv[mt]);
+          dp[mt] = mfma_f16(row_frag<D, true>(Os, 32 * mt + l32, 16 * s + 8 * h), vf[s], dp[mt]);
+        }
+      u32x4 pf[4], df[4], dl[4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int nb0 = 32 * mt + 16 * hh + 4 * h;   // rows of elements 8 hh .. 8 hh + 3
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[nb0]);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[nb0 + 8]);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dr_s[nb0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dr_s[nb0 + 8]);
+          float pv[8], dsv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int el = 8 * hh + e;
+            const float lv = e < 4 ? l0[e] : l1[e - 4];
+            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+            const float p = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[mt][el], qk_scale, -lv)) : 0.f;
+            pv[e] = p;
+            dsv[e] = p * (dp[mt][el] - dv_) * tau;
+          }
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            pf[2 * mt + hh][e2] = pack_f16(pv[2 * e2], pv[2 * e2 + 1]);
+            const uint32_t hi = pack_bf16(dsv[2 * e2], dsv[2 * e2 + 1]);
+            df[2 * mt + hh][e2] = hi;
+            dl[2 * mt + hh][e2] = pack_bf16(dsv[2 * e2] - bf16_lo(hi), dsv[2 * e2 + 1] - bf16_hi(hi));
+          }
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          dvt[c] = mfma_f16(vt_frag<D>(Os, 32 * c, 16 * kk), pf[kk], dvt[c]);
+          const u32x4 qa = vt_frag<D>(Qs, 32 * c, 16 * kk);
+          dkt[c] = mfma_bf16(qa, df[kk], dkt[c]);
+          dkt[c] = mfma_bf16(qa, dl[kk], dkt[c]);
+        }
+    }
+  }
+  // linear parts: dV^T += G_j^T relu(K)^T (M = c, K = r), dK_lin^T = G_j V^T (M = r, K = c),
+  // with G_j as bf16 high and low parts (V G^T + gz nearly cancels, like the query side)
+  __syncthreads();
+  const float* gtb = a.gt + ((size_t)bh * a.nbk + j) * D * D;
+  uint16_t* Gs = smem;           // G_j^T [c][r], row swizzle (tr_nat gives G[r][c] fragments)
+  uint16_t* Gl = smem + D * D;   // its low parts
+  for (int id = t; id < D * (D / 8); id += 128) {
+    const int rr = id / (D / 8), cc = id % (D / 8);
+    u32x4 hi, lo;
+    split8(gtb + (size_t)rr * D + cc * 8, hi, lo);
+    *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
+    *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
+  }
+  __syncthreads();
+  const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
+  f32x16 lk[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    lk[c] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 gh, glo;
+      split8(gtb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h, gh, glo);
+      const u32x4 kb = relu_bf16x8(kf[s]);
+      dvt[c] = mfma_bf16(gh, kb, dvt[c]);
+      dvt[c] = mfma_bf16(glo, kb, dvt[c]);
+      const u32x4 vb = kvalid ? *reinterpret_cast<const u32x4*>(vrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+      lk[c] = mfma_bf16(tr_nat<D>(Gs, 32 * c, 16 * s), vb, lk[c]);
+      lk[c] = mfma_bf16(tr_nat<D>(Gl, 32 * c, 16 * s), vb, lk[c]);
+    }
+  }
+  if (!kvalid) return;
+  const float* gzb = a.gz + ((size_t)bh * a.nbk + j) * D;
+  float* dkr = a.dk + ((size_t)bh * a.nkv + key) * D;
+  float* dvr = a.dv + ((size_t)bh * a.nkv + key) * D;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 32 * c + 8 * g4 + 4 * h;
+      const f32x4 z = *reinterpret_cast<const f32x4*>(gzb + r0);
+      const u32x2 kw = *reinterpret_cast<const u32x2*>(krow + r0);
+      const float kv[4] = {bf16_lo(kw[0]), bf16_hi(kw[0]), bf16_lo(kw[1]), bf16_hi(kw[1])};
+      f32x4 ko, vo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ix = 4 * g4 + e;
+        ko[e] = dkt[c][ix] + (kv[e] > 0.f ? lk[c][ix] + z[e] : 0.f);
+        vo[e] = dvt[c][ix];
+      }
+      *reinterpret_cast<f32x4*>(dkr + r0) = ko;
+      *reinterpret_cast<f32x4*>(dvr + r0) = vo;
+    }
+}
+
+// ----------------------------------------------------------------------------- dQ of the exact branch
+template <int D>
+__global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int KS = D / 16, CT = D / 32, TILE = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
+  const int bh = blockIdx.x / a.nbq, iq = blockIdx.x % a.nbq;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int row = 32 * wv + l32;
+  const int n = iq * kBlock + row;
+  const bool valid = n < a.nq;
+  const float qk_scale = kLog2e / sqrtf((float)D);
+  const float tau = 1.f / sqrtf((float)D);
+  const uint16_t* qrow = a.q + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
+  const uint16_t* drow = a.dos + ((size_t)bh * a.nbq * kBlock + iq * kBlock + row) * D;
+  u32x4 qf[KS], of[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    qf[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    of[s] = *reinterpret_cast<const u32x4*>(drow + 16 * s + 8 * h);
+  }
+  const float lse = a.lse[(size_t)bh * a.nbq * kBlock + iq * kBlock + row];
+  const float dn = a.dr[(size_t)bh * a.nbq * kBlock + iq * kBlock + row];
+  f32x16 dqt[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) dqt[c] = f32x16{};
+  uint16_t* Ks = smem;          // V swizzle: row reads and vt_frag reads
+  uint16_t* Vs = smem + TILE;   // f16 V, row swizzle
+  const int32_t* sel = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
+  for (int e = 0; e < a.topk; ++e) {
+    const int j = sel[e];
+    const int nval = min(kBlock, a.nkv - j * kBlock);
+    __syncthreads();
+    copy_tile<D, true>(Ks, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D, nval);
+    copy_tile<D, false>(Vs, a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
+    __syncthreads();
+    f32x16 st[2] = {f32x16{}, f32x16{}}, dpt[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        st[mt] = mfma_bf16(row_frag<D, true>(Ks, 32 * mt + l32, 16 * s + 8 * h), qf[s], st[mt]);
+        dpt[mt] = mfma_f16(row_frag<D, false>(Vs, 32 * mt + l32, 16 * s + 8 * h), of[s], dpt[mt]);
+      }
+    u32x4 df[4], dl[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float dsv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int el = 8 * hh + 2 * e2 + u;
+            const int kk = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
+            const float p = kk < nval ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[mt][el], qk_scale, -lse)) : 0.f;
+            dsv[u] = p * (dpt[mt][el] - dn) * tau;
+          }
+          const uint32_t hi = pack_bf16(dsv[0], dsv[1]);
+          df[2 * mt + hh][e2] = hi;
+          dl[2 * mt + hh][e2] = pack_bf16(dsv[0] - bf16_lo(hi), dsv[1] - bf16_hi(hi));
+        }
+    // dS enters as bf16 high and low parts: its rows sum to zero, so dQ is a small difference
+    // of large terms and one bf16 rounding of dS would show in it
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const u32x4 ka = vt_frag<D>(Ks, 32 * c, 16 * kk);
+        dqt[c] = mfma_bf16(ka, df[kk], dqt[c]);
+        dqt[c] = mfma_bf16(ka, dl[kk], dqt[c]);
+      }
+  }
+  if (!valid) return;
+  float* dqr = a.dq + ((size_t)bh * a.nq + n) * D;
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int r0 = 32 * c + 8 * g4 + 4 * h;
+      f32x4 cur = *reinterpret_cast<const f32x4*>(dqr + r0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cur[e] += dqt[c][4 * g4 + e];
+      *reinterpret_cast<f32x4*>(dqr + r0) = cur;
+    }
+}
+
+// dalpha[h][c] = sum over batches and query blocks of the partials, in order
+template <int D>
+__global__ __launch_bounds__(D) void bwd_dalpha_kernel(const float* __restrict__ part,
+                                                       float* __restrict__ dalpha, int B, int H,
+                                                       int nbq) {
+  const int hd = blockIdx.x, c = threadIdx.x;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int i = 0; i < nbq; ++i) s += part[(((size_t)b * H + hd) * nbq + i) * D + c];
+  dalpha[(size_t)hd * D + c] = s;
+}
+
+template <int D>
+hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* ws,
+                             hipStream_t st) {
+  const int nwk = s.nwords;
+  hipLaunchKernelGGL(bwd_bits_kernel, dim3(s.nbq + s.nbk, s.BH), dim3(256),
+                     (size_t)nwk * 4, st, a.idx,
+                     reinterpret_cast<uint32_t*>(ws + s.selbits),
+                     reinterpret_cast<uint32_t*>(ws + bp.bitsT), s.nbq, s.nbk, s.k, nwk, a.nwq);
+  uint16_t* sblo = reinterpret_cast<uint16_t*>(ws + bp.sblo);
+  hipError_t e = launch_kv_summary(s, a.k, a.v, nullptr, ws, st, false, sblo);
+  if (e != hipSuccess) return e;
+  e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + s.selbits), nwk, s.nbq,
+                            s.nbk, s.k, reinterpret_cast<const uint16_t*>(ws + s.sblk), sblo,
+                            const_cast<float*>(a.sc), st);
+  if (e != hipSuccess) return e;
+  e = launch_complement_z(s, a.idx, ws, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_query_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
+  e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + bp.bitsT), a.nwq, s.nbk,
+                            s.nbq, 0, a.dsc, a.dsclo, const_cast<float*>(a.gt), st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_gz_kernel<D>, dim3(s.BH * s.nbk), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Plan& s, const void* q, const void* k, const void* v,
+                           const float* alpha, const void* dout, const int32_t* idx, float* dq,
+                           float* dk, float* dv, float* dalpha, char* ws, hipStream_t st) {
+  const BwdPlan bp = make_bwd_plan(s);
+  BwdArgs a;
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.v16 = reinterpret_cast<const uint16_t*>(ws + s.v16);
+  a.dout = dout;
+  a.dout_bf16 = s.out_bf16 ? 1 : 0;
+  a.alpha = alpha;
+  a.idx = idx;
+  a.bitsT = reinterpret_cast<const uint32_t*>(ws + bp.bitsT);
+  a.sc = reinterpret_cast<const float*>(ws + bp.scf);
+  a.zc = reinterpret_cast<const float*>(ws + s.zc);
+  a.lse = reinterpret_cast<float*>(ws + bp.lse);
+  a.dr = reinterpret_cast<float*>(ws + bp.dr);
+  a.dos = reinterpret_cast<uint16_t*>(ws + bp.dos);
+  a.dsc = reinterpret_cast<uint16_t*>(ws + bp.dsc);
+  a.dsclo = reinterpret_cast<uint16_t*>(ws + bp.dsclo);
+  a.dzc = reinterpret_cast<float*>(ws + bp.dzc);
+  a.gt = reinterpret_cast<const float*>(ws + bp.gt);
+  a.gz = reinterpret_cast<float*>(ws + bp.gz);
+  a.dapart = reinterpret_cast<float*>(ws + bp.dapart);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.nq = s.nq; a.nkv = s.nkv; a.nbq = s.nbq; a.nbk = s.nbk; a.topk = s.k; a.H = s.H;
+  a.nwq = bp.nwq;
+  hipError_t e = s.D == 128 ? launch_backward_T<128>(s, bp, a, ws, st)
+                            : launch_backward_T<64>(s, bp, a, ws, st);
+  if (e != hipSuccess) return e;
+  if (s.D == 128)
+    hipLaunchKernelGGL(bwd_dalpha_kernel<128>, dim3(s.H), dim3(128), 0, st, a.dapart, dalpha,
+                       s.B, s.H, s.nbq);
+  else
+    hipLaunchKernelGGL(bwd_dalpha_kernel<64>, dim3(s.H), dim3(64), 0, st, a.dapart, dalpha,
+                       s.B, s.H, s.nbq);
+  return hipGetLastError();
+}
+
+}  // namespace sla

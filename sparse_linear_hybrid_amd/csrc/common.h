@@ -348,7 +348,7 @@ inline Plan make_plan(const sla_problem& p) {
 // complement, bitmap), then the backward's own regions.
 struct BwdPlan {
   int nwq;                                      // 32-bit words of a query-block bitmap row
-  size_t bitsT, lse, dr, dos, dsc, dzc, gt, gz, dapart, bytes;
+  size_t bitsT, sblo, scf, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, bytes;
 };
 inline BwdPlan make_bwd_plan(const Plan& s) {
   BwdPlan b{};
@@ -357,12 +357,15 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   size_t off = s.total_fwd;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   b.bitsT = take(BH * nbk * (size_t)b.nwq * 4);
+  b.sblo = take(BH * nbk * D * D * 2);          // S_j - bf16(S_j), bf16, summary layout
+  b.scf = take(BH * nbq * D * D * 4);           // S_c^T fp32
   b.lse = take(BH * nq64 * 4);
   b.dr = take(BH * nq64 * 4);
   b.dos = take(BH * nq64 * D * 2);
-  b.dsc = take(BH * nbq * D * D * 2);
+  b.dsc = take(BH * nbq * D * D * 2);           // dS_c(i)^T, bf16 high part, summary layout
+  b.dsclo = take(BH * nbq * D * D * 2);         // and its low part
   b.dzc = take(BH * nbq * D * 4);
-  b.gt = take(BH * nbk * D * D * 2);
+  b.gt = take(BH * nbk * D * D * 4);            // G_j^T fp32
   b.gz = take(BH * nbk * D * 4);
   b.dapart = take(BH * nbq * D * 4);
   b.bytes = off;

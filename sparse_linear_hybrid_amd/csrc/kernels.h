@@ -12,8 +12,9 @@ hipError_t launch_route(const Plan& s, const void* q, const void* k, const float
 
 // Linear branch, part 1 (independent of routing): per key block phi(K)^T V, sum phi(K),
 // the projected pooled K (for the router), an f16 copy of V, and the per-head totals.
+// sblk_lo (bf16 inputs, not fp8): also S_j - bf16(S_j), rounded to bf16, in the layout of S_j.
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk, char* ws,
-                             hipStream_t st, bool fp8 = false);
+                             hipStream_t st, bool fp8 = false, uint16_t* sblk_lo = nullptr);
 
 // Linear branch, part 2: complement = total - selected, per query block.
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);
@@ -78,11 +79,17 @@ hipError_t launch_pisa_tail(const Plan& s, const void* q, const int32_t* idx, ch
 hipError_t launch_sparse_pisa(const Plan& s, const void* q, const void* k, const int32_t* idx,
                               void* o, char* ws, hipStream_t st);
 
-// Linear branch, transposed complement for the backward: per key block j,
-// out[j] = sum over the query blocks i that did not route j of stacked[i] (stacked in the
-// per-block summary layout over query blocks; bitsT [BH][nbk][nwq]: the routed query blocks).
-hipError_t launch_complement_transposed(const Plan& s, const uint32_t* bitsT, int nwq,
-                                        const uint16_t* stacked, uint16_t* out, hipStream_t st);
+// Complement sums in fp32 for the backward: per row r (rows of [BH][rows][D*D] out),
+// out[r] = sum over the columns c < cols whose bit is clear in row r of bits ([BH][rows]
+// [nwords]) of hi[c] + lo[c] (hi, lo: bf16 in the per-block summary layout over cols). k >= cols
+// gives exactly zero. Forward orientation: rows = query blocks, cols = key blocks, bits the
+// selection; transposed: rows = key blocks, cols = query blocks, bits the routed query blocks.
+hipError_t launch_complement_f32(const Plan& s, const uint32_t* bits, int nwords, int rows,
+                                 int cols, int k, const uint16_t* hi, const uint16_t* lo,
+                                 float* out, hipStream_t st);
+
+// z_c(i) = z_tot - sum_{j in sel(i)} z_j alone (fp32), into the workspace's zc.
+hipError_t launch_complement_z(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);
 
 // Backward at the given selection (bf16 inputs): dq, dk, dv (fp32, like Q, K, V) and dalpha
 // [H][D] (fp32) from dout (out dtype); workspace as make_bwd_plan.

@@ -56,16 +56,18 @@ constexpr int kSlice = 128;
 // to E4M3 exactly as the quantiser does (block absmax over the valid tokens, power-of-two
 // scale, one rounding), from the tiles it has staged in LDS, and writes K8, the V8 tiles and
 // the block exponents (Fp8Out).
-template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false>
+template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false,
+          bool LO = false>
 __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
-    uint16_t* __restrict__ sblk, float* __restrict__ zblk, float* __restrict__ spart,
+    uint16_t* __restrict__ sblk, uint16_t* __restrict__ sblk_lo, float* __restrict__ zblk, float* __restrict__ spart,
     float* __restrict__ zpart, int nkv, int nbk, int jbase, int t0,
     uint16_t* __restrict__ cent_hi, uint16_t* __restrict__ cent_lo, uint16_t* __restrict__ vsum,
     int npad, Fp8Out f8) {
   static_assert(!PISA || BLOCKS, "the piecewise pass is a full-forward pass");
   static_assert(!FP8 || (BLOCKS && !PISA && sizeof(T) == 2), "fused E4M3: bf16 full forward");
+  static_assert(!LO || (BLOCKS && !PISA && !FP8), "low parts of S_j: plain full pass");
   // The SLA2 forward's complement sums the unselected S_j itself, so its pass keeps no d x d
   // chunk totals (only the z partials); the cache update and the piecewise pass do.
   constexpr bool TOTALS = !BLOCKS || PISA;
@@ -317,6 +319,33 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
                         f % kSlice;
         *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
       }
+      if constexpr (LO) {   // S_j - bf16(S_j), rounded to bf16, in the same layout
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < TILES_PER_WAVE; ++u) {
+          const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * mt + 8 * q + 4 * h;
+            float lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              lo[e] = accs[u][4 * q + e] - bf16_lo(pack_bf16(accs[u][4 * q + e], 0.f));
+            *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
+                u32x2{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = t; e < D * D / 8; e += 256) {
+          const int c = e / (D / 8), ch = e % (D / 8);
+          const int f = c * D + ch * 8;
+          uint16_t* dst = sblk_lo +
+                          (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
+                          f % kSlice;
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
+        }
+      }
     }
     __syncthreads();   // LDS tiles and pool_lds are rewritten by the next block
     // projected pooled K of each finished group of kSummaryChunk blocks: k~ = mean @ P_k
@@ -472,11 +501,15 @@ __device__ __forceinline__ u32x4 bits_to_bf16x8(uint32_t m8) {
   return b;
 }
 
-template <int D>
+// F32: the sums go out as fp32 (stored, or added to what `sc` holds when accum != 0) instead
+// of bf16; the backward sums the high and low bf16 parts of its summaries that way.
+template <int D, bool F32 = false>
 __global__ __launch_bounds__(256, 2) void complement_kernel(
     const uint32_t* __restrict__ selbits, int nwords, const uint16_t* __restrict__ sblk,
-    const float* __restrict__ stot, uint16_t* __restrict__ sc, int nbq, int nbk, int k,
-    int nqt, int total, int ww) {
+    const float* __restrict__ stot, void* __restrict__ out, int nbq, int nbk, int k,
+    int nqt, int total, int ww, int accum) {
+  uint16_t* sc = reinterpret_cast<uint16_t*>(out);
+  float* scf = reinterpret_cast<float*>(out);
   constexpr int NCS = D * D / CN;      // column slices per (batch, head)
   constexpr int LPW = CK * CN * 2 / 1024 / 4;   // 1-KB ring loads per wave per step
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
@@ -493,6 +526,17 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   const size_t col0 = (size_t)cs * CN;
 
   if (k >= nbk) {   // every block selected: the complement is empty, exactly zero
+    if constexpr (F32) {
+      if (accum) return;
+      for (int e = t; e < CQ * CN / 4; e += 256) {
+        const int il = e / (CN / 4), c4 = e % (CN / 4);
+        const int i = qt * CQ + il;
+        if (i < nbq)
+          *reinterpret_cast<f32x4*>(scf + ((size_t)bh * nbq + i) * D * D + col0 + c4 * 4) =
+              f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      return;
+    }
     for (int e = t; e < CQ * CN / 8; e += 256) {
       const int il = e / (CN / 8), c8 = e % (CN / 8);
       const int i = qt * CQ + il;
@@ -615,6 +659,27 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     }
   }
   wait_vmem();   // no load into LDS outlives the workgroup
+  if constexpr (F32) {
+    // lane: query block 64 w + 32 tq + l32 of the group; elements 4 g .. 4 g + 3: the four
+    // consecutive columns 32 nt + 8 g + 4 h ..
+#pragma unroll
+    for (int tq = 0; tq < 2; ++tq) {
+      const int i = qt * CQ + 64 * w + 32 * tq + l32;
+      if (i >= nbq) continue;
+      float* row = scf + ((size_t)bh * nbq + i) * D * D + col0;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4* p = reinterpret_cast<f32x4*>(row + 32 * nt + 8 * g + 4 * h);
+          f32x4 v{acc[tq][nt][4 * g], acc[tq][nt][4 * g + 1], acc[tq][nt][4 * g + 2],
+                  acc[tq][nt][4 * g + 3]};
+          if (accum) v += *p;
+          *p = v;
+        }
+    }
+    return;
+  }
   // S_c, staged through LDS (the ring and bitmap are free now) so that every
   // query block's CN columns go out as contiguous 16-byte stores. Per half tq, wave w
   // stages its 32 query blocks x CN columns; 16-byte chunk c of staged row q sits at
@@ -688,7 +753,7 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
 
 template <int D>
 static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* v, const float* pk,
-                                      char* ws, hipStream_t st, bool fp8) {
+                                      char* ws, hipStream_t st, bool fp8, uint16_t* sblk_lo) {
   double* kt = reinterpret_cast<double*>(ws + s.kt);
   uint16_t* v16 = reinterpret_cast<uint16_t*>(ws + s.v16);
   uint16_t* sblk = reinterpret_cast<uint16_t*>(ws + s.sblk);
@@ -700,21 +765,27 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   if (s.in_bf16 && fp8)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, false, true>), grid,
                        dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj,
-                       v16, sblk, zblk, spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr,
-                       nullptr, 0,
+                       v16, sblk, nullptr, zblk, spart, zpart, s.nkv, s.nbk, 0, 0, nullptr,
+                       nullptr, nullptr, 0,
                        Fp8Out{reinterpret_cast<uint8_t*>(ws + s.k8),
                               reinterpret_cast<uint8_t*>(ws + s.v8),
                               reinterpret_cast<int32_t*>(ws + s.sk8),
                               reinterpret_cast<int32_t*>(ws + s.sv8)});
+  else if (s.in_bf16 && sblk_lo)
+    hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, false, false, true>),
+                       grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh,
+                       kj, v16, sblk, sblk_lo, zblk, spart, zpart, s.nkv, s.nbk, 0, 0, nullptr,
+                       nullptr, nullptr, 0, Fp8Out{});
   else if (s.in_bf16)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk>), grid, dim3(256), 0,
                        st,
-                       (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, zblk,
-                       spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0, Fp8Out{});
+                       (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16, sblk, nullptr,
+                       zblk, spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0,
+                       Fp8Out{});
   else
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk>), grid, dim3(256), 0, st,
-                       (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, zblk, spart,
-                       zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0, Fp8Out{});
+                       (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, sblk, nullptr, zblk,
+                       spart, zpart, s.nkv, s.nbk, 0, 0, nullptr, nullptr, nullptr, 0, Fp8Out{});
   // only z_tot: the complement sums the unselected S_j itself
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
@@ -737,11 +808,13 @@ static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* 
   if (s.in_bf16)
     hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, true>), grid, dim3(256),
                        0, st, (const uint16_t*)k, (const uint16_t*)v, pk, kt, kbh, kj, v16,
-                       nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad, Fp8Out{});
+                       nullptr, nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum,
+                       s.npad, Fp8Out{});
   else
     hipLaunchKernelGGL((kv_summary_kernel<float, D, true, kSummaryChunk, true>), grid, dim3(256), 0,
                        st, (const float*)k, (const float*)v, pk, kt, kbh, kj, v16, nullptr,
-                       nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad, Fp8Out{});
+                       nullptr, nullptr, spart, zpart, s.nkv, s.nbk, 0, 0, chi, clo, vsum, s.npad,
+                       Fp8Out{});
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.p_stot),
                      reinterpret_cast<float*>(ws + s.p_ztot), s.nchunk, 0,
@@ -777,15 +850,55 @@ hipError_t launch_kv_cache_update(const Plan& s, const void* k, const void* v, c
 }
 
 hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const float* pk,
-                             char* ws, hipStream_t st, bool fp8) {
-  if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st, fp8);
-  return launch_kv_summary_T<64>(s, k, v, pk, ws, st, fp8);
+                             char* ws, hipStream_t st, bool fp8, uint16_t* sblk_lo) {
+  if (sblk_lo && (fp8 || !s.in_bf16)) return hipErrorInvalidValue;
+  if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st, fp8, sblk_lo);
+  return launch_kv_summary_T<64>(s, k, v, pk, ws, st, fp8, sblk_lo);
 }
 
 hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const float* pk,
                              char* ws, hipStream_t st) {
   if (s.D == 128) return launch_pisa_stats_T<128>(s, k, v, pk, ws, st);
   return launch_pisa_stats_T<64>(s, k, v, pk, ws, st);
+}
+
+hipError_t launch_complement_f32(const Plan& s, const uint32_t* bits, int nwords, int rows,
+                                 int cols, int k, const uint16_t* hi, const uint16_t* lo,
+                                 float* out, hipStream_t st) {
+  // out[row] = sum over the columns whose bit is clear of (hi + lo)[col], in fp32: the
+  // complement kernel on the high parts (stored), then on the low parts (added)
+  const int nqt = (rows + CQ - 1) / CQ;
+  const int ncs = s.D * s.D / CN;
+  const int total = s.BH * ncs * nqt;
+  const int ww = min(MAXW, (cols + CK - 1) / CK);
+  const size_t lds = complement_lds_bytes(ww);
+  hipError_t err = hipSuccess;
+  auto go = [&](auto kern) {
+    if (lds > 65536) {
+      err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return;
+    }
+    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, nwords, hi, nullptr,
+                       (void*)out, rows, cols, k, nqt, total, ww, 0);
+    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, nwords, lo, nullptr,
+                       (void*)out, rows, cols, k, nqt, total, ww, 1);
+  };
+  if (s.D == 128) go(complement_kernel<128, true>);
+  else go(complement_kernel<64, true>);
+  return err != hipSuccess ? err : hipGetLastError();
+}
+
+hipError_t launch_complement_z(const Plan& s, const int32_t* idx, char* ws, hipStream_t st) {
+  auto go = [&](auto zkern) {
+    hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
+                       reinterpret_cast<const float*>(ws + s.zblk),
+                       reinterpret_cast<const float*>(ws + s.ztot),
+                       reinterpret_cast<float*>(ws + s.zc), s.nbq, s.nbk, s.k);
+  };
+  if (s.D == 128) go(complement_z_kernel<128>);
+  else go(complement_z_kernel<64>);
+  return hipGetLastError();
 }
 
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st) {
@@ -806,7 +919,7 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
     hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, s.nwords,
                        reinterpret_cast<const uint16_t*>(ws + s.sblk),
                        reinterpret_cast<const float*>(ws + s.stot),
-                       reinterpret_cast<uint16_t*>(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww);
+                       (void*)(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww, 0);
     hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
                        reinterpret_cast<const float*>(ws + s.zblk),
                        reinterpret_cast<const float*>(ws + s.ztot),

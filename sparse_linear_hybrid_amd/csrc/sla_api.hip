@@ -346,6 +346,33 @@ sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k
   return SLA_OK;
 }
 
+size_t sla_backward_workspace_size(const sla_problem* p) {
+  if (check_problem(p) != SLA_OK) return 0;
+  return make_bwd_plan(make_plan(*p)).bytes;
+}
+
+sla_status sla_backward(const sla_problem* p, const void* q, const void* k, const void* v,
+                        const float* alpha, const void* dout, const int32_t* block_idx,
+                        float* dq, float* dk, float* dv, float* dalpha, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  sla_status st = check_problem(p);
+  if (st != SLA_OK) return st;
+  if (p->in_dtype != SLA_BF16) return SLA_ERR_DTYPE;
+  st = check_ptrs({q, k, v, alpha, dout, dq, dk, dv, dalpha});
+  if (st != SLA_OK) return st;
+  if (p->top_k > 0) {   // with no routed block the index list is empty and may be NULL
+    st = check_ptrs({block_idx});
+    if (st != SLA_OK) return st;
+  }
+  const Plan s = make_plan(*p);
+  if (!workspace || workspace_bytes < make_bwd_plan(s).bytes) return SLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return SLA_ERR_ALIGN;
+  if (launch_backward(s, q, k, v, alpha, dout, block_idx, dq, dk, dv, dalpha,
+                      static_cast<char*>(workspace), stream) != hipSuccess)
+    return SLA_ERR_HIP;
+  return SLA_OK;
+}
+
 const char* sla_status_string(sla_status s) {
   switch (s) {
     case SLA_OK: return "ok";

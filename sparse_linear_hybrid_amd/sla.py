@@ -25,7 +25,8 @@ EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_forward_profiled", "sla_workspace_region", "sla_status_string",
            "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
            "sla_cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
-           "sla_forward_taylor", "sla_forward_pisa", "sla_forward_cached_noalloc")
+           "sla_forward_taylor", "sla_forward_pisa", "sla_forward_cached_noalloc",
+           "sla_backward_workspace_size", "sla_backward", "sla_diag_fp8_mfma")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8,
               "hbar": 9, "cent_hi": 10, "cent_lo": 11, "vsum": 12}
 # workspace layouts (sla_workspace_size / sla_workspace_region)
@@ -86,6 +87,12 @@ def _load() -> ctypes.CDLL:
     lib.sla_cached_workspace_size.argtypes = [pp]
     lib.sla_cached_workspace_size.restype = sz
     lib.sla_forward_cached.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_diag_fp8_mfma.argtypes = [vp, vp, vp, vp, vp]
+    lib.sla_diag_fp8_mfma.restype = ctypes.c_int
+    lib.sla_backward_workspace_size.argtypes = [pp]
+    lib.sla_backward_workspace_size.restype = sz
+    lib.sla_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sla_backward.restype = ctypes.c_int
     lib.sla_forward_cached_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sla_forward_cached_noalloc.restype = ctypes.c_int
     lib.sla_forward_cached.restype = ctypes.c_int
@@ -366,8 +373,61 @@ def sla_forward_cached_noalloc(q, k, v, proj_q, alpha, top_k: int, cache: torch.
                                               _ptr(proj_q), _ptr(alpha), _ptr(cache), _ptr(out),
                                               _ptr(block_idx), _stream(q.device))
     if st != 0:
-        raise SlaError(st, "sla_forward_cached_noalloc")
+        raise SlaError(st, "sla_forward_cached_noalloc",
+           "sla_backward_workspace_size", "sla_backward", "sla_diag_fp8_mfma")
     return out, block_idx
+
+
+# ----------------------------------------------------------------------------- backward
+def sla_backward_workspace_size(p: Problem) -> int:
+    """Bytes of device workspace sla_backward needs for problem p (p.top_k = the selection's
+    width, p.out_dtype = dout's dtype code)."""
+    need = int(library().sla_backward_workspace_size(ctypes.byref(p)))
+    if need == 0:
+        raise SlaError(2, "sla_backward_workspace_size")
+    return need
+
+
+def sla_backward(q, k, v, alpha, dout, block_idx, block: int = 64,
+                 workspace: Optional[torch.Tensor] = None):
+    """Gradients of sla_forward at the selection block_idx for the upstream gradient dout
+    (O's shape, fp32 or bf16). Returns (dq, dk, dv, dalpha), fp32."""
+    top_k = int(block_idx.shape[-1])
+    p = make_problem(q, k, top_k, block, dout.dtype)
+    _check(q, k, v, (), alpha, dout, dout.dtype, (workspace, block_idx))
+    want = (p.batch, p.heads, -(-p.n_q // block), top_k)
+    if tuple(block_idx.shape) != want or block_idx.dtype != torch.int32 \
+            or not block_idx.is_contiguous():
+        raise ValueError(f"block_idx must be a contiguous int32 {want} tensor")
+    need = sla_backward_workspace_size(p)
+    if workspace is None or _nbytes(workspace) < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    dal = torch.empty((p.heads, p.head_dim), dtype=torch.float32, device=q.device)
+    st = library().sla_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                _ptr(dout), _ptr(block_idx), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(dal), _ptr(workspace), ctypes.c_size_t(_nbytes(workspace)),
+                                _stream(q.device))
+    if st != 0:
+        raise SlaError(st, "sla_backward")
+    return dq, dk, dv, dal
+
+
+def sla_diag_fp8_mfma(a: torch.Tensor, b: torch.Tensor):
+    """Diagnostic: (C on the fp8 instruction, C on the bf16 instruction) for E4M3 code tensors
+    a [32, 64] and b [64, 32] (uint8, on the GPU). Both fp32 [32, 32]."""
+    if a.shape != (32, 64) or b.shape != (64, 32) or a.dtype != torch.uint8 \
+            or b.dtype != torch.uint8 or not (a.is_cuda and b.is_cuda):
+        raise ValueError("a: uint8 [32, 64], b: uint8 [64, 32], GPU tensors")
+    a, b = a.contiguous(), b.contiguous()
+    c8 = torch.empty((32, 32), dtype=torch.float32, device=a.device)
+    c16 = torch.empty_like(c8)
+    st = library().sla_diag_fp8_mfma(_ptr(a), _ptr(b), _ptr(c8), _ptr(c16), _stream(a.device))
+    if st != 0:
+        raise SlaError(st, "sla_diag_fp8_mfma")
+    return c8, c16
 
 
 # ----------------------------------------------------------------------------- Taylor router

@@ -206,6 +206,26 @@ def test_forward_cached_noalloc_validation(lib):
     assert sla.NOALLOC_SCRATCH_BYTES == 128 << 20
 
 
+def test_backward_validation(lib):
+    vp = ctypes.c_void_p
+
+    def bwd(prob_, q=FAKE, idx=FAKE, ws=FAKE, ws_bytes=1 << 40):
+        pp = ctypes.byref(prob_) if prob_ is not None else None
+        return lib.sla_backward(pp, vp(q), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(idx),
+                                vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(ws),
+                                ctypes.c_size_t(ws_bytes), vp(0))
+    p = prob()
+    assert bwd(None) == 1
+    assert bwd(prob(in_dtype=0)) == 3
+    assert bwd(prob(top_k=12)) == 4
+    assert bwd(p, q=0) == 1 and bwd(p, idx=0) == 1
+    assert bwd(p, idx=MISALIGNED) == 5
+    need = lib.sla_backward_workspace_size(ctypes.byref(p))
+    assert need > lib.sla_workspace_size(ctypes.byref(p), 0)
+    assert bwd(p, ws_bytes=need - 1) == 6 and bwd(p, ws=0) == 6
+    assert lib.sla_backward_workspace_size(ctypes.byref(prob(head_dim=96))) == 0
+
+
 def test_taylor_entry_points_validation(lib):
     vp = ctypes.c_void_p
     p = prob()
