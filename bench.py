@@ -414,6 +414,61 @@ def bench_cached(args, sla, x, q, k, v, pq, pk, al, out):
 
 
 # --------------------------------------------------------------------------- main
+def bench_backward(args, sla, torch, p, q, k, v, pq, pk, al, ws, out, skip_dense=False):
+    """Outside the timed forward region: sla_backward at the forward's selection for a
+    random upstream gradient (fp32), K timed calls after the warm-up ones, and torch's SDPA
+    backward (bf16) on the same shapes for comparison. Sparse-branch FLOPs follow the
+    FlashAttention convention (2.5 x the forward's 4 b^2 d per routed pair: recomputed
+    scores, dP, dV, dK, dQ)."""
+    _, idx = sla.sla_forward(q, k, v, pq, pk, al, p.top_k, workspace=ws, out=out)
+    gen = torch.Generator(device=q.device).manual_seed(11)
+    dout = torch.randn(q.shape, device=q.device, dtype=torch.float32, generator=gen)
+    need = sla.sla_backward_workspace_size(sla.make_problem(q, k, p.top_k))
+    bws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    for _ in range(max(1, args.warmup)):
+        sla.sla_backward(q, k, v, al, dout, idx, workspace=bws)
+    torch.cuda.synchronize()
+    K = args.steps
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(K):
+        sla.sla_backward(q, k, v, al, dout, idx, workspace=bws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / K
+    pairs = p.batch * p.heads * p.nbq * p.top_k
+    flops = 2.5 * 4 * p.block * p.block * p.head_dim * pairs
+    res = {"ms": ms, "workspace_bytes": need, "sparse_flops": flops,
+           "sparse_TFLOPs_effective": flops / (ms * 1e-3) / 1e12}
+    del bws
+    if not skip_dense:
+        try:
+            f = torch.nn.functional.scaled_dot_product_attention
+            qd, kd, vd = (t.detach().clone().requires_grad_(True) for t in (q, k, v))
+            g16 = dout.to(torch.bfloat16)
+            for _ in range(2):
+                f(qd, kd, vd).backward(g16)
+            torch.cuda.synchronize()
+            n = 3
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            for _ in range(n):
+                f(qd, kd, vd)
+            e[1].record()
+            for _ in range(n):
+                f(qd, kd, vd).backward(g16)
+            e[2].record()
+            torch.cuda.synchronize()
+            fwd_ms = e[0].elapsed_time(e[1]) / n
+            res["sdpa_bf16_fwd_bwd_ms"] = e[1].elapsed_time(e[2]) / n
+            res["sdpa_bf16_bwd_ms"] = res["sdpa_bf16_fwd_bwd_ms"] - fwd_ms
+            res["speedup_vs_sdpa_bwd"] = res["sdpa_bf16_bwd_ms"] / ms
+            del qd, kd, vd
+        except Exception as ex:  # noqa: BLE001
+            res["sdpa_error"] = str(ex)[:200]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,6 +490,11 @@ def main():
     ap.add_argument("--pisa", action="store_true",
                     help="time sla_forward_pisa (exact routed blocks + Taylor tail, one "
                          "normalisation) instead of sla_forward")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (sla_backward at the forward's selection)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the backward leg (one forward for the selection, then "
+                         "W + K sla_backward calls); prints its own JSON line")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "OUT", "COMMAND"))
     ap.add_argument("--timed", default=None, metavar="W,K",
@@ -491,6 +551,15 @@ def main():
     variant = (sla.VARIANT_FP8 if fp8 else sla.VARIANT_PISA if pisa else
                sla.VARIANT_TAYLOR if taylor else sla.VARIANT_FORWARD)
     ws = torch.empty(sla.workspace_size(prob, variant), dtype=torch.uint8, device=dev)
+    if args.backward_only:
+        if fp8 or taylor or pisa or p.dtype != "bf16":
+            print("the backward takes the bf16 forward's selection", file=sys.stderr)
+            return 2
+        res = bench_backward(args, sla, torch, p, q, k, v, pq, pk, al, ws, out,
+                             skip_dense=args.no_dense)
+        print(json.dumps({"backward": res, "workload": p.name, "steps": args.steps,
+                          "warmup": args.warmup}))
+        return 0
 
     def fwd():
         if pisa:
@@ -651,6 +720,11 @@ def main():
         dense["best_dense_ms"] = best
         dense["speedup_vs_best_dense"] = best / ms
 
+    backward = None
+    if not (args.no_backward or fp8 or taylor or pisa or p.dtype != "bf16"):
+        backward = bench_backward(args, sla, torch, p, q, k, v, pq, pk, al, ws, out,
+                                  skip_dense=args.no_dense)
+
     cpu = None if args.no_cpu else cpu_baseline(x)
 
     line = {
@@ -669,6 +743,7 @@ def main():
         "cpu_baseline": cpu,
         "dense": dense,
         "kernels": kernels,
+        "backward": backward,
         "inputs_sha256": sha256_of(x.q, x.k, x.v, x.proj_q, x.proj_k, x.alpha),
         "gpu": torch.cuda.get_device_name(0),
     }
