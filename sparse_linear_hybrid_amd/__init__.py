@@ -3,7 +3,7 @@
 The computation lives in libsla.so (HIP kernels behind the C ABI of include/sla.h);
 ``sla`` is its ctypes binding. The library is loaded on first use; every entry point raises if it is not built.
 """
-from .sla import (SlaError, Problem, make_problem, workspace_size, sla_route, sla_forward,
+from .sla import (SlaError, STATUS, Problem, make_problem, workspace_size, sla_route, sla_forward,
                   sla_forward_fp8, sla_forward_profiled, library, LIB_PATH, EXPORTS,
                   STAGES, workspace_region, WS_REGIONS, kv_cache_size, sla_kv_cache_update,
                   cached_workspace_size, sla_forward_cached, sla_route_taylor,
@@ -11,7 +11,7 @@ from .sla import (SlaError, Problem, make_problem, workspace_size, sla_route, sl
                   VARIANT_PISA, VARIANT_TAYLOR, sla_forward_cached_noalloc, NOALLOC_SCRATCH_BYTES,
                   sla_backward, sla_backward_workspace_size, sla_diag_fp8_mfma)
 
-__all__ = ["SlaError", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
+__all__ = ["SlaError", "STATUS", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
            "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES",
            "workspace_region", "WS_REGIONS", "kv_cache_size", "sla_kv_cache_update",
            "cached_workspace_size", "sla_forward_cached", "sla_route_taylor",

@@ -21,8 +21,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
          "-Wno-unused-command-line-argument",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-munsafe-fp-atomics"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _compile(src: str) -> str:

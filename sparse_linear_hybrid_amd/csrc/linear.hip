@@ -8,10 +8,14 @@
 //              copy of V for the sparse branch's P.V. The next block's loads are in flight
 //              while a block is processed. Per-chunk fp32 partial totals are written for a
 //              fixed-order reduction (no atomics).
-// reduce:      S_tot = sum of the partials, z_tot likewise.
-// complement:  per query block i, S_c(i) = S_tot - sum_{j in sel(i)} S_j (an MFMA product of
-//              the 0/1 selection matrix with the stacked S_j) and z_c(i) likewise; an
-//              all-blocks selection gives exactly 0.
+// reduce:      z_tot = sum of the chunk partials (fixed order); S_tot only where a pass keeps
+//              d x d chunk totals (the summary cache, the piecewise statistics).
+// complement:  per query block i, S_c(i) = sum of the S_j that i did not select: an MFMA
+//              product of the 0/1 complement bitmap with the stacked S_j, slice by slice.
+//              It equals S_tot - sum_{j in sel(i)} S_j exactly in real arithmetic, without that
+//              difference's cancellation when the selected blocks hold most of the mass; an
+//              all-blocks selection gives exactly 0. z_c(i) = z_tot - sum_{j in sel(i)} z_j
+//              (fp32, d values per block, in the order of the index list).
 #include "common.h"
 #include "kernels.h"
 

@@ -373,8 +373,7 @@ def sla_forward_cached_noalloc(q, k, v, proj_q, alpha, top_k: int, cache: torch.
                                               _ptr(proj_q), _ptr(alpha), _ptr(cache), _ptr(out),
                                               _ptr(block_idx), _stream(q.device))
     if st != 0:
-        raise SlaError(st, "sla_forward_cached_noalloc",
-           "sla_backward_workspace_size", "sla_backward", "sla_diag_fp8_mfma")
+        raise SlaError(st, "sla_forward_cached_noalloc")
     return out, block_idx
 
 

@@ -89,6 +89,22 @@ def test_topk0_alpha0_is_linear(sla):
     assert err <= TOL
 
 
+@pytest.mark.parametrize("alpha_value", [0.0, None])
+def test_one_block_left_out(sla, alpha_value):
+    """top_k = Nbk - 1: each query block's complement is a single key block, so z_c and S_c
+    are the smallest they can be without being empty (z_c = z_tot minus nearly all of it);
+    alpha = 0 leaves the linear branch alone in the output."""
+    x = make_custom(1, 2, 300, 640, 128, 9, dtype="bf16", kind="smooth", seed=17)
+    if alpha_value is not None:
+        x.alpha[:] = alpha_value
+    out, idx = run_forward(sla, x)
+    ref, _ = oracle.forward(x)
+    check_masks(idx, oracle.sla_oracle.route_full(x), 9)
+    err, _ = max_err_over_rms(out, ref)
+    print(f"top_k = Nbk - 1, alpha {alpha_value}: max-abs/rms {err:.3e}", flush=True)
+    assert err <= TOL
+
+
 def test_bf16_output_matches_fp32_output(sla):
     x = make_custom(1, 2, 256, 256, 128, 2, dtype="bf16", kind="smooth", seed=3)
     o32, i32 = run_forward(sla, x, torch.float32)

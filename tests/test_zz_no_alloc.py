@@ -63,3 +63,24 @@ def test_noalloc_without_index_output(sla):
     sla.sla_forward_cached_noalloc(q, k, v, pq, al, 5, cache, out)
     torch.cuda.synchronize()
     assert torch.equal(out, ref_out)
+
+
+def test_noalloc_rejects_a_problem_beyond_the_scratch_array(sla):
+    """A problem whose workspace would exceed the fixed array is refused before anything is
+    enqueued (SLA_ERR_SCRATCH), and the binding raises SlaError; out is left untouched."""
+    B, H, nq, nkv, d, top_k = 1, 16, 16384, 1024, 128, 4
+    q = torch.zeros((B, H, nq, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((B, H, nkv, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    p = sla.make_problem(q, k, top_k)
+    assert sla.cached_workspace_size(p) > sla.NOALLOC_SCRATCH_BYTES
+    pq = torch.eye(d, dtype=torch.float32, device="cuda")
+    al = torch.full((H, d), 0.5, dtype=torch.float32, device="cuda")
+    cache = torch.zeros(sla.kv_cache_size(sla.make_problem(k, k, 0)), dtype=torch.uint8,
+                        device="cuda")
+    out = torch.full((B, H, nq, d), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(sla.SlaError) as exc:
+        sla.sla_forward_cached_noalloc(q, k, v, pq, al, top_k, cache, out)
+    assert exc.value.status == 9
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
