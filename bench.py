@@ -5,17 +5,21 @@
 
 One step is one full forward (router, linear summaries, complement, sparse attention with
 the fused linear apply and mix) over the workload's synthetic inputs, which are resident in
-HBM before timing starts. Prints ONE JSON line with the latency, the roofline of the
-dominant kernel (the sparse-attention kernel, timed with HIP events that the library
-records around it on the same stream), the dense-attention baseline on the same GPU and
-the CPU oracle baseline. Outside the timed region it also reports the per-step spread
-(p10 / median / p90) of the timed forwards and of K more forwards each preceded by a 512 MB
-write that evicts L2 and the MALL (cold caches), and what the GPU reaches on a 1 GiB copy
-and an 8192^3 bf16 GEMM (achievable peaks next to the published ones).
+HBM before timing starts. Each timed step is preceded by a 512 MB write that evicts L2 and
+the 256 MB MALL (--no-cold: no flush); the library records HIP events around every stage on
+its stream, and `value` is the median step (first stage start to last stage end). Prints ONE
+JSON line with the latency, the roofline of the dominant kernel (the sparse-attention
+kernel, from the same events), the dense-attention baselines on the same GPU, the backward
+at the forward's selection (sla_backward) beside torch's SDPA backward, and the CPU oracle
+baseline. Outside the timed region it also reports the spread (p10 / median / p90) of K warm
+back-to-back forwards and what the GPU reaches on a 1 GiB copy and an 8192^3 bf16 GEMM
+(achievable peaks next to the published ones).
 
 Other modes:
     --profile            only warm-up + K plain forward calls and a 1 GiB copy (short runs
                          under rocprofv3; the copy calibrates the memory counters)
+    --backward-only      one forward for the selection, then W + K sla_backward calls
+    --cached             the decode path (sla_forward_cached against a prebuilt summary cache)
     --summarize-pmc FETCH_DIR WRITE_DIR
                          turn two rocprofv3 --pmc CSV outputs (FETCH_SIZE, WRITE_SIZE) into
                          profiles/sparse_attn_<workload>_traffic.json
@@ -140,11 +144,25 @@ def cpu_baseline(x, min_seconds=10.0):
     until at least ``min_seconds`` of CPU work (or the whole workload) is done; scaled to
     all pairs, in ms."""
     from oracle import sla_oracle as so
+    blas = None
     try:
         import threadpoolctl
-        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = "; ".join(f"{i.get('internal_api')} {i.get('version')} "
+                         f"({i.get('threading_layer', '')}, {i.get('architecture', '')})"
+                         for i in info if i.get("user_api") == "blas") or None
     except Exception:   # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     p = x.problem
     pairs = [(b, h) for b in range(p.batch) for h in range(p.heads)]
     done = 0
@@ -157,7 +175,8 @@ def cpu_baseline(x, min_seconds=10.0):
     what = ("the whole workload" if done == total else
             f"{done} of {total} (batch, head) pairs computed in full, scaled to all pairs")
     return {"value": dt * 1e3 * total / done, "unit": "ms", "cores": int(threads),
-            "kind": "oracle", "sample": f"{what} ({dt:.1f} s)"}
+            "kind": "oracle", "sample": f"{what} ({dt:.1f} s)", "cpu_model": cpu_model,
+            "host_cpus": len(os.sched_getaffinity(0)), "blas": blas}
 
 
 # --------------------------------------------------------------------------- traffic summary
@@ -472,8 +491,8 @@ def bench_backward(args, sla, torch, p, q, k, v, pq, pk, al, ws, out, skip_dense
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="video95")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -587,8 +606,14 @@ def main():
         return 0
 
     # ---------------------------------------------------------------- timed region
+    # K forwards, each preceded by a 512 MB write that evicts L2 and the 256 MB MALL (so the
+    # inputs come from HBM); every stage of every forward is bracketed by HIP events on the
+    # library's stream, and a step's time runs from its first stage's start to its last
+    # stage's end (the flush is outside it). value = the median step.
     K = args.steps
     nst = len(sla.STAGES)
+    flush = None if args.no_cold else torch.empty(FLUSH_BYTES // 4, dtype=torch.float32,
+                                                   device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nst)] for _ in range(K)]
     for row in evs:
         for e in row:
@@ -598,32 +623,30 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
+        if flush is not None:
+            flush.fill_(float(s))
         sla.sla_forward_profiled(q, k, v, pq, pk, al, p.top_k, handles[s], fp8=fp8,
                                  workspace=ws, out=out, taylor=taylor, pisa=pisa)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / K
+    wall_ms = (t1 - t0) * 1e3 / K
     stage_ms = {name: float(np.mean([evs[s][2 * i].elapsed_time(evs[s][2 * i + 1])
                                      for s in range(K)]))
                 for i, name in enumerate(sla.STAGES)}
-    # per-step GPU time of the timed forwards: first stage's start to last stage's end
-    warm_steps = [evs[s][0].elapsed_time(evs[s][2 * nst - 1]) for s in range(K)]
+    steps = [evs[s][0].elapsed_time(evs[s][2 * nst - 1]) for s in range(K)]
+    ms = float(np.median(steps))
+    cold_steps = steps if flush is not None else None
 
-    # Cold caches (outside the timed region): before each of K forwards, 512 MB are written,
-    # which evicts L2 and the 256 MB MALL, so the inputs come from HBM.
-    cold_steps = None
-    if not args.no_cold:
-        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-        marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(K)]
-        for s in range(K):
-            flush.fill_(float(s))
-            marks[s][0].record()
-            fwd()
-            marks[s][1].record()
-        torch.cuda.synchronize()
-        cold_steps = [a.elapsed_time(b) for a, b in marks]
-        del flush
+    # Warm caches (outside the timed region): K back-to-back forwards, no flush.
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(K)]
+    for s in range(K):
+        marks[s][0].record()
+        fwd()
+        marks[s][1].record()
+    torch.cuda.synchronize()
+    warm_steps = [a.elapsed_time(b) for a, b in marks]
+    del flush
     peaks = None if args.no_peaks else achievable_peaks(torch, dev)
 
     w = work(p, fp8)
@@ -665,6 +688,11 @@ def main():
         "kv_summary_hbm_frac": w["kv_summary_bytes"] / (stage_ms["kv_summary"] * 1e-3) / PEAK_HBM,
         "step_ms_warm": spread(warm_steps),
         "step_ms_cold": spread(cold_steps) if cold_steps else None,
+        "wall_ms_per_step": wall_ms,
+        "timing": ("value = median over the timed steps of the HIP-event time from the first "
+                   "stage's start to the last stage's end"
+                   + (", each step after a 512 MB cache-flush write" if cold_steps else
+                      ", warm caches (--no-cold)")),
         "achievable": peaks,
     }
     if peaks:
@@ -719,6 +747,9 @@ def main():
         best = min([v_ for k_, v_ in dense.items() if k_.endswith("_ms")] or [float("nan")])
         dense["best_dense_ms"] = best
         dense["speedup_vs_best_dense"] = best / ms
+        # the dense baselines run back to back (warm caches): the same against the warm
+        # forwards
+        dense["speedup_vs_best_dense_warm"] = best / float(np.median(warm_steps))
 
     backward = None
     if not (args.no_backward or fp8 or taylor or pisa or p.dtype != "bf16"):

@@ -368,18 +368,61 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   auto compute_tile = [&](const uint16_t* Kt, const uint16_t* Klo, const uint16_t* Vt, int j,
                           auto&& ld) __attribute__((always_inline)) {
     f32x16 s0 = f32x16{}, s1 = f32x16{};
-    ld(0);
-    qk_half(Kt, Klo, 0, s0);
-    ld(1);
-    check_half(s0, 0, j);
-    qk_half(Kt, Klo, 1, s1);
-    ld(2);
-    exp_half(s0, 0);
-    check_half(s1, 1, j);
-    ld(3);
-    pv_half(Vt, 0);
-    exp_half(s1, 1);
-    pv_half(Vt, 1);
+    if constexpr (SPLIT) {
+      ld(0);
+      qk_half(Kt, Klo, 0, s0);
+      ld(1);
+      check_half(s0, 0, j);
+      qk_half(Kt, Klo, 1, s1);
+      ld(2);
+      exp_half(s0, 0);
+      check_half(s1, 1, j);
+      ld(3);
+      pv_half(Vt, 0);
+      exp_half(s1, 1);
+      pv_half(Vt, 1);
+    } else {
+      // every K fragment of the tile is read from LDS before the first product, and the
+      // V fragments of a half before its softmax, so that the reads are in flight while
+      // the matrix cores and the softmax work
+      u32x4 ka[KS], kb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[ks] = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(l32, 16 * ks + 8 * h)]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(32 + l32, 16 * ks + 8 * h)]);
+      ld(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_bf16(ka[ks], qf[ks], s0);
+      ld(1);
+      check_half(s0, 0, j);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s1 = mfma_bf16(kb[ks], qf[ks], s1);
+      u32x4 va[2 * CT];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) va[kk * CT + c] = vt_frag<D>(Vt, 32 * c, 16 * kk);
+      ld(2);
+      exp_half(s0, 0);
+      check_half(s1, 1, j);
+      ld(3);
+      u32x4 vb[2 * CT];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) vb[kk * CT + c] = vt_frag<D>(Vt, 32 * c, 16 * (kk + 2));
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) o[c] = mfma_f16(va[kk * CT + c], pf[kk], o[c]);
+      exp_half(s1, 1);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) o[c] = mfma_f16(vb[kk * CT + c], pf[2 + kk], o[c]);
+    }
   };
   auto no_loads = [](int) __attribute__((always_inline)) {};
 
