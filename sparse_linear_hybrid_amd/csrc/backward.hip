@@ -17,8 +17,9 @@
 //   (key/value pass)    S_j as bf16 high and low parts, z_j, z_tot and the f16 copy of V;
 //   (complement, fp32)  S_c(i) = sum of the unselected S_j, high and low parts summed in fp32;
 //                       z_c(i);
-//   bwd_query_kernel    per query block: the exact branch again (online softmax, so O_s and
-//                       the log-sum-exp), O_l, D, dO_s (f16), dalpha partials, the linear
+//   (sparse kernel)     the exact branch of the forward again, saving O_s (fp32) and each
+//                       row's log-sum-exp instead of mixing;
+//   bwd_query_kernel    per query block: O_l, D, dO_s (f16), dalpha partials, the linear
 //                       part of dQ, dS_c(i) (bf16 high and low parts, summary layout), dz_c(i);
 //   (complement, fp32)  G_j from the dS_c(i), roles of query and key blocks swapped;
 //   bwd_gz_kernel       gz_j;
@@ -51,7 +52,8 @@ struct BwdArgs {
   const uint32_t* bitsT;    // [BH][nbk][nwq]: bit i of key block j's row: j in sel(i)
   const float* sc;          // S_c^T [BH][nbq][D(c)][D(r)] fp32
   const float* zc;          // [BH][nbq][D]
-  float* lse;               // [BH][nbq*64] (base-2 units; 1e30 where a row has no exact part)
+  const float* os;          // O_s fp32 [BH][nq][D] (the forward's exact branch, saved)
+  const float* lse;         // [BH][nbq*64] (base-2 units; kNoRowLse where a row has no exact part)
   float* dr;                // [BH][nbq*64]: D_n
   uint16_t* dos;            // f16 [BH][nbq*64][D]: dO_s
   uint16_t* dsc;            // bf16 [BH][D*D/128][nbq][128]: dS_c(i)^T flattened [c][r]
@@ -66,7 +68,6 @@ struct BwdArgs {
   int nq, nkv, nbq, nbk, topk, H, nwq;
 };
 
-constexpr float kNoRow = 1.0e30f;   // log-sum-exp of a row with no exact part: P = 0
 
 // Transposing fragment read in natural order from a swz-swizzled [row][col] tile of 16-bit
 // elements: lane owns column x0 + lane % 32 and the 8 rows k0 + 8 (lane / 32) .. + 7.
@@ -81,16 +82,32 @@ __device__ __forceinline__ u32x4 tr_nat(const uint16_t* M, int x0, int k0) {
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// 64-row tile copy global -> LDS through registers (rows >= nvalid are zero). SWZV: the V
-// swizzle (tiles read with vt_frag), else the row swizzle swz.
-template <int D, bool SWZV>
-__device__ __forceinline__ void copy_tile(uint16_t* dst, const uint16_t* src, int nvalid) {
-  constexpr int CH = D / 8;
-  for (int id = threadIdx.x; id < 64 * CH; id += blockDim.x) {
-    const int r = id / CH, c = id % CH;
-    const u32x4 w = r < nvalid ? *reinterpret_cast<const u32x4*>(src + (size_t)r * D + c * 8)
-                               : u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4*>(dst + (SWZV ? swzv<D>(r, c * 8) : swz<D>(r, c * 8))) = w;
+// 64-row tile of 16-bit elements, global rows src[0 .. nvalid) -> swizzled LDS tile, as loads
+// straight into LDS shared by the NW waves of the workgroup (1-KB pieces: lane l of a piece
+// lands at element 8 l of it and fetches the logical chunk that the swizzle puts there);
+// rows >= nvalid read as zero. The caller waits (wait_vmem / barrier_vmem*) before reading.
+template <int D, bool SWZV, int NW>
+__device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* src, int nvalid) {
+  constexpr int CH = D / 8, RPP = 512 / D, PPW = (D / 8) / NW;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the descriptor and the LDS address live in scalar registers: every argument is uniform
+  // over the workgroup, made explicit for the compiler
+  const uint64_t b = reinterpret_cast<uint64_t>(src);
+  // (readfirstlane returns int: each half goes through uint32_t, so that a low word with bit
+  // 31 set is not sign-extended into the high word)
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t bu = ((uint64_t)bhi << 32) | (uint64_t)blo;
+  const int nv = __builtin_amdgcn_readfirstlane(nvalid > 0 ? nvalid : 0);
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+  const i32x4 r = make_rsrc(reinterpret_cast<const void*>(bu), (uint32_t)nv * D * 2);
+#pragma unroll
+  for (int u = 0; u < PPW; ++u) {
+    const int pp = w * PPW + u;
+    const int row = pp * RPP + lane / CH, pc = lane % CH;
+    const int lc = (pc ^ (SWZV ? swzv_f<D>(row) : row)) & (CH - 1);
+    load_lds16(r, l0 + pp * 1024, (uint32_t)(row * D * 2 + lc * 16));
   }
 }
 
@@ -166,83 +183,38 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   const int n = iq * kBlock + row;            // query token
   const bool valid = n < a.nq;
   const int hd = bh % a.H;
-  const float qk_scale = kLog2e / sqrtf((float)D);
-  const float tau = 1.f / sqrtf((float)D);
   const uint16_t* qrow = a.q + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
+
+  // smem: S_c^T [D][D] as bf16 high and low parts (V swizzle: row reads and vt_frag), the
+  // Q tile (row swizzle, read with tr_nat), then two tiles that first hold the dalpha terms
+  // (fp32 [64][D]) and then g as bf16 high and low parts (row swizzle)
+  uint16_t* Sct = smem;
+  uint16_t* Scl = smem + D * D;
+  uint16_t* Qt = smem + 2 * D * D;
+  uint16_t* Gt = Qt + TILE;     // g rounded to bf16
+  uint16_t* Gl = Gt + TILE;     // and its remainder, also bf16
+  float* xs = reinterpret_cast<float*>(Gt);
+  const float* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
+  dma_tile<D, false, 2>(Qt, a.q + ((size_t)bh * a.nq + (size_t)iq * kBlock) * D,
+                        min(kBlock, a.nq - iq * kBlock));
+  for (int id = t; id < D * CH; id += 128) {
+    const int rr = id / CH, cc = id % CH;
+    u32x4 hi, lo;
+    split8(scb + (size_t)rr * D + cc * 8, hi, lo);
+    *reinterpret_cast<u32x4*>(Sct + swzv<D>(rr, cc * 8)) = hi;
+    *reinterpret_cast<u32x4*>(Scl + swzv<D>(rr, cc * 8)) = lo;
+  }
 
   u32x4 qf[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
     qf[s] = valid ? *reinterpret_cast<const u32x4*>(qrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
 
-  // ---------------------------------------------------------------- exact branch again
-  f32x16 o[CT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) o[c] = f32x16{};
-  float m = kNegBig, l = 0.f;
-  uint16_t* Kt = smem;
-  uint16_t* Vt = smem + TILE;
-  const int32_t* sel = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f16x2 ones2 = {(_Float16)1.0f, (_Float16)1.0f};
-  for (int e = 0; e < a.topk; ++e) {
-    const int j = sel[e];
-    const int nval = min(kBlock, a.nkv - j * kBlock);
-    __syncthreads();
-    copy_tile<D, false>(Kt, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D, nval);
-    copy_tile<D, true>(Vt, a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
-    __syncthreads();
-    f32x16 sh[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        sh[mt] = mfma_bf16(row_frag<D, false>(Kt, 32 * mt + l32, 16 * ks + 8 * h), qf[ks], sh[mt]);
-    float r = kNegBig;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int el = 0; el < 16; ++el) {
-        const int key = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
-        sh[mt][el] = key < nval ? sh[mt][el] : -INFINITY;
-        r = fmaxf(r, sh[mt][el]);
-      }
-    r = fmaxf(r, swap_halves(r)) * qk_scale;
-    if (r > m) {
-      const float corr = __builtin_amdgcn_exp2f(m - r);
-      l *= corr;
-#pragma unroll
-      for (int c = 0; c < CT; ++c) o[c] *= corr;
-      m = r;
-    }
-    u32x4 pf[4];
-    float rs = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int el = 8 * hh + 2 * e2;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[mt][el], qk_scale, -m));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sh[mt][el + 1], qk_scale, -m));
-          const uint32_t pk = pack_f16(p0, p1);
-          pf[2 * mt + hh][e2] = pk;
-          rs = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), ones2, rs, false);
-        }
-    l += rs;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) o[c] = mfma_f16(vt_frag<D>(Vt, 32 * c, 16 * kk), pf[kk], o[c]);
-  }
-  l += swap_halves(l);
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  const float lse = (l > 0.f && valid) ? m + log2f(l) : kNoRow;
+  // the exact branch's output, saved by the forward's sparse kernel in this backward
+  const float* osr = a.os + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
 
   // ---------------------------------------------------------------- linear branch again
   const bool empty_c = a.topk >= a.nbk;
-  const float* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
   const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
   f32x16 lin[CT];
   float den = 0.f;
@@ -256,23 +228,20 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   }
   den += swap_halves(den);
   den += kEps;
+  barrier_vmem_lds_n<0>();   // S_c^T (stores) and the Q tile (loads into LDS) are in place
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     lin[c] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      u32x4 ah, alo;
-      split8(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h, ah, alo);
       const u32x4 qb = relu_bf16x8(qf[s]);
-      lin[c] = mfma_bf16(ah, qb, lin[c]);
-      lin[c] = mfma_bf16(alo, qb, lin[c]);
+      lin[c] = mfma_bf16(row_frag<D, true>(Sct, 32 * c + l32, 16 * s + 8 * h), qb, lin[c]);
+      lin[c] = mfma_bf16(row_frag<D, true>(Scl, 32 * c + l32, 16 * s + 8 * h), qb, lin[c]);
     }
   }
   const float inv_den = empty_c ? 0.f : 1.f / den;
 
   // ---------------------------------------------------------------- upstream gradient
-  __syncthreads();   // the tile buffers are free: X (dalpha terms) goes to smem as fp32
-  float* xs = reinterpret_cast<float*>(smem);     // [64][D]
   const float* al = a.alpha + (size_t)hd * D;
   float dsum = 0.f, hsum = 0.f;
   f32x16 gv[CT];                                  // g = dO_l / den, O^T layout
@@ -295,11 +264,12 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
         }
       }
       const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
+      const f32x4 osv = valid ? *reinterpret_cast<const f32x4*>(osr + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
       float dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ix = 4 * g4 + e;
-        const float os = o[c][ix] * inv_l;
+        const float os = osv[e];
         const float ol = lin[c][ix] * inv_den;
         dsv[e] = alv[e] * dov[e];
         const float dl = (1.f - alv[e]) * dov[e];
@@ -314,7 +284,6 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   hsum += swap_halves(hsum);
   const float hn = empty_c ? 0.f : -hsum * inv_den;
   if (h == 0) {
-    a.lse[(size_t)bh * a.nbq * kBlock + iq * kBlock + row] = lse;
     a.dr[(size_t)bh * a.nbq * kBlock + iq * kBlock + row] = valid ? dsum : 0.f;
     hh_s[row] = valid ? hn : 0.f;
   }
@@ -327,22 +296,6 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   __syncthreads();
 
   // ---------------------------------------------------------------- linear part of dQ
-  // smem: S_c^T [D][D] as bf16 high and low parts (V swizzle, read with vt_frag), then the
-  // Q tile and the g tiles (row swizzle, read with tr_nat)
-  uint16_t* Sct = smem;
-  uint16_t* Scl = smem + D * D;
-  uint16_t* Qt = smem + 2 * D * D;
-  uint16_t* Gt = Qt + TILE;     // g rounded to bf16
-  uint16_t* Gl = Gt + TILE;     // and its remainder, also bf16
-  for (int id = t; id < D * CH; id += 128) {
-    const int rr = id / CH, cc = id % CH;
-    u32x4 hi, lo;
-    split8(scb + (size_t)rr * D + cc * 8, hi, lo);
-    *reinterpret_cast<u32x4*>(Sct + swzv<D>(rr, cc * 8)) = hi;
-    *reinterpret_cast<u32x4*>(Scl + swzv<D>(rr, cc * 8)) = lo;
-  }
-  copy_tile<D, false>(Qt, a.q + ((size_t)bh * a.nq + (size_t)iq * kBlock) * D,
-                      min(kBlock, a.nq - iq * kBlock));
 #pragma unroll
   for (int c = 0; c < CT; ++c)
 #pragma unroll
@@ -463,8 +416,8 @@ __global__ __launch_bounds__(64) void bwd_gz_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   constexpr int KS = D / 16, CT = D / 32, TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE > 2 * D * D ? 2 * TILE : 2 * D * D];
-  __shared__ __attribute__((aligned(16))) float lse_s[64], dr_s[64];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE > 2 * D * D ? 4 * TILE : 2 * D * D];
+  __shared__ __attribute__((aligned(16))) float lse_s[2][64], dr_s[2][64];
   const int bh = blockIdx.x / a.nbk, j = blockIdx.x % a.nbk;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int key = j * kBlock + 32 * wv + l32;
@@ -482,23 +435,49 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   f32x16 dvt[CT], dkt[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) dvt[c] = dkt[c] = f32x16{};
-  uint16_t* Qs = smem;            // V swizzle: row reads and vt_frag reads
-  uint16_t* Os = smem + TILE;     // dO_s tile, f16, V swizzle
+  // Two slots of (Q tile, dO_s tile), both V-swizzled (row reads and vt_frag reads): the
+  // next routed query block's tiles load straight into LDS while this one is multiplied.
   const uint32_t* brow = a.bitsT + ((size_t)bh * a.nbk + j) * a.nwq;
-  for (int w = 0; w < a.nwq; ++w) {
-    uint32_t word = brow[w];
-    while (word) {
-      const int i = 32 * w + __builtin_ctz(word);
-      word &= word - 1u;
-      __syncthreads();
-      copy_tile<D, true>(Qs, a.q + ((size_t)bh * a.nq + (size_t)i * kBlock) * D,
+  auto next_routed = [&](int from) -> int {   // first query block >= from that routed j, or -1
+    for (int w = from >> 5; w < a.nwq; ++w) {
+      uint32_t word = brow[w];
+      if (w == (from >> 5)) word &= ~0u << (from & 31);
+      if (word) return 32 * w + __builtin_ctz(word);
+    }
+    return -1;
+  };
+  auto stage = [&](int i, int slot) __attribute__((always_inline)) {
+    dma_tile<D, true, 2>(smem + 2 * slot * TILE, a.q + ((size_t)bh * a.nq + (size_t)i * kBlock) * D,
                          min(kBlock, a.nq - i * kBlock));
-      copy_tile<D, true>(Os, a.dos + ((size_t)bh * a.nbq * kBlock + (size_t)i * kBlock) * D, kBlock);
+    dma_tile<D, true, 2>(smem + (2 * slot + 1) * TILE,
+                         a.dos + ((size_t)bh * a.nbq * kBlock + (size_t)i * kBlock) * D, kBlock);
+  };
+  const size_t rbase = (size_t)bh * a.nbq * kBlock;
+  int i = next_routed(0);
+  if (i >= 0) {
+    stage(i, 0);
+    if (t < 64) {
+      lse_s[0][t] = a.lse[rbase + i * kBlock + t];
+      dr_s[0][t] = a.dr[rbase + i * kBlock + t];
+    }
+  }
+  barrier_vmem_lds_n<0>();
+  int slot = 0;
+  while (i >= 0) {
+    const int inext = next_routed(i + 1);
+    float lnext = 0.f, dnext = 0.f;
+    if (inext >= 0) {
+      stage(inext, slot ^ 1);
       if (t < 64) {
-        lse_s[t] = a.lse[(size_t)bh * a.nbq * kBlock + i * kBlock + t];
-        dr_s[t] = a.dr[(size_t)bh * a.nbq * kBlock + i * kBlock + t];
+        lnext = a.lse[rbase + inext * kBlock + t];
+        dnext = a.dr[rbase + inext * kBlock + t];
       }
-      __syncthreads();
+    }
+    {
+      const uint16_t* Qs = smem + 2 * slot * TILE;
+      const uint16_t* Os = smem + (2 * slot + 1) * TILE;
+      const float* lsv = lse_s[slot];
+      const float* drv = dr_s[slot];
       // S = Q K^T and dP = dO_s V^T: rows n (two 32-row tiles), lane: key
       f32x16 sv[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -514,10 +493,10 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int nb0 = 32 * mt + 16 * hh + 4 * h;   // rows of elements 8 hh .. 8 hh + 3
-          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lse_s[nb0]);
-          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lse_s[nb0 + 8]);
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dr_s[nb0]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dr_s[nb0 + 8]);
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lsv[nb0]);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lsv[nb0 + 8]);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&drv[nb0]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&drv[nb0 + 8]);
           float pv[8], dsv[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -546,6 +525,13 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
           dkt[c] = mfma_bf16(qa, dl[kk], dkt[c]);
         }
     }
+    if (inext >= 0 && t < 64) {
+      lse_s[slot ^ 1][t] = lnext;
+      dr_s[slot ^ 1][t] = dnext;
+    }
+    barrier_vmem_lds_n<0>();   // the next tiles and their rows' lse / D are in place
+    slot ^= 1;
+    i = inext;
   }
   // linear parts: dV^T += G_j^T relu(K)^T (M = c, K = r), dK_lin^T = G_j V^T (M = r, K = c),
   // with G_j as bf16 high and low parts (V G^T + gz nearly cancels, like the query side)
@@ -606,7 +592,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   constexpr int KS = D / 16, CT = D / 32, TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
   const int bh = blockIdx.x / a.nbq, iq = blockIdx.x % a.nbq;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int row = 32 * wv + l32;
@@ -627,16 +613,25 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   f32x16 dqt[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) dqt[c] = f32x16{};
-  uint16_t* Ks = smem;          // V swizzle: row reads and vt_frag reads
-  uint16_t* Vs = smem + TILE;   // f16 V, row swizzle
+  // Two slots of (K tile, V-swizzled: row reads and vt_frag reads; f16 V tile, row swizzle):
+  // the next selected block's tiles load straight into LDS while this one is multiplied.
   const int32_t* sel = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
+  auto stage = [&](int e, int slot) __attribute__((always_inline)) {
+    const int j = sel[e];
+    dma_tile<D, true, 2>(smem + 2 * slot * TILE, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D,
+                         min(kBlock, a.nkv - j * kBlock));
+    dma_tile<D, false, 2>(smem + (2 * slot + 1) * TILE,
+                          a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
+  };
+  if (a.topk > 0) stage(0, 0);
+  barrier_vmem_n<0>();
+  int slot = 0;
   for (int e = 0; e < a.topk; ++e) {
+    if (e + 1 < a.topk) stage(e + 1, slot ^ 1);
     const int j = sel[e];
     const int nval = min(kBlock, a.nkv - j * kBlock);
-    __syncthreads();
-    copy_tile<D, true>(Ks, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D, nval);
-    copy_tile<D, false>(Vs, a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
-    __syncthreads();
+    const uint16_t* Ks = smem + 2 * slot * TILE;
+    const uint16_t* Vs = smem + (2 * slot + 1) * TILE;
     f32x16 st[2] = {f32x16{}, f32x16{}}, dpt[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < KS; ++s)
@@ -674,6 +669,8 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
         dqt[c] = mfma_bf16(ka, df[kk], dqt[c]);
         dqt[c] = mfma_bf16(ka, dl[kk], dqt[c]);
       }
+    barrier_vmem_n<0>();   // the next tiles have landed; this slot is free
+    slot ^= 1;
   }
   if (!valid) return;
   float* dqr = a.dq + ((size_t)bh * a.nq + n) * D;
@@ -718,6 +715,9 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
   if (e != hipSuccess) return e;
   e = launch_complement_z(s, a.idx, ws, st);
   if (e != hipSuccess) return e;
+  e = launch_sparse_save(s, a.q, a.k, a.idx, const_cast<float*>(a.os), const_cast<float*>(a.lse),
+                         ws, st);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_query_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
   e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + bp.bitsT), a.nwq, s.nbk,
                             s.nbq, 0, a.dsc, a.dsclo, const_cast<float*>(a.gt), st);
@@ -746,7 +746,8 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
   a.bitsT = reinterpret_cast<const uint32_t*>(ws + bp.bitsT);
   a.sc = reinterpret_cast<const float*>(ws + bp.scf);
   a.zc = reinterpret_cast<const float*>(ws + s.zc);
-  a.lse = reinterpret_cast<float*>(ws + bp.lse);
+  a.os = reinterpret_cast<const float*>(ws + bp.os);
+  a.lse = reinterpret_cast<const float*>(ws + bp.lse);
   a.dr = reinterpret_cast<float*>(ws + bp.dr);
   a.dos = reinterpret_cast<uint16_t*>(ws + bp.dos);
   a.dsc = reinterpret_cast<uint16_t*>(ws + bp.dsc);

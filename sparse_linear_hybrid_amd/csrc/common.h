@@ -29,6 +29,8 @@ constexpr int kMaxKeyBlocks = 8064;   // top-k keeps a row of 64-bit keys in 64 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;
+// Saved log-sum-exp of a row with no exact part (or past n_q): exp2(x - kNoRowLse) = 0.
+constexpr float kNoRowLse = 1.0e30f;
 
 // ----------------------------------------------------------------------------- conversions
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -348,7 +350,7 @@ inline Plan make_plan(const sla_problem& p) {
 // complement, bitmap), then the backward's own regions.
 struct BwdPlan {
   int nwq;                                      // 32-bit words of a query-block bitmap row
-  size_t bitsT, sblo, scf, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, bytes;
+  size_t bitsT, sblo, scf, os, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, bytes;
 };
 inline BwdPlan make_bwd_plan(const Plan& s) {
   BwdPlan b{};
@@ -359,6 +361,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   b.bitsT = take(BH * nbk * (size_t)b.nwq * 4);
   b.sblo = take(BH * nbk * D * D * 2);          // S_j - bf16(S_j), bf16, summary layout
   b.scf = take(BH * nbq * D * D * 4);           // S_c^T fp32
+  b.os = take(BH * (size_t)s.nq * D * 4);        // O_s fp32, saved by the sparse kernel
   b.lse = take(BH * nq64 * 4);
   b.dr = take(BH * nq64 * 4);
   b.dos = take(BH * nq64 * D * 2);

@@ -24,6 +24,11 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
 hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int32_t* idx,
                          const float* alpha, void* o, char* ws, hipStream_t st);
 
+// The sparse branch alone for the backward (bf16 inputs): O_s (fp32 [BH][n_q][D]) and each
+// row's log-sum-exp (base 2, scaled units; [BH][nbq*64]).
+hipError_t launch_sparse_save(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                              float* os, float* lse, char* ws, hipStream_t st);
+
 // Quantised branch: E4M3 copies of Q, K, V with power-of-two block exponents.
 hipError_t launch_quant(const Plan& s, const void* q, const void* k, const void* v, char* ws,
                         hipStream_t st);

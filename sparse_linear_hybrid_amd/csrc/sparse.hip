@@ -129,6 +129,9 @@ struct SparseArgs {
   const float* tail_d;     // its token-count-weighted row sum
   const float* tail_a;     // its plain row sum
   const float* tail_n;     // [BH][nbq * 64][D]: its numerator
+  // saved exact-branch state for the backward only
+  float* lse;              // [BH][nbq * 64]: m + log2(l) in base-2 scaled units (kNoRowLse
+                           // for a row with no exact part or past n_q)
 };
 
 template <typename T>
@@ -157,7 +160,10 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
   }
 }
 
-template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false>
+// SAVE (bf16 inputs, for the backward): instead of the linear apply and the mix, the
+// epilogue writes the exact branch's normalised output O_s (fp32, `out` [BH][n_q][D]) and each
+// row's log-sum-exp (`lse`).
+template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false, bool SAVE = false>
 __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
   constexpr bool DMA = !SPLIT;             // bf16 inputs: K/V tiles go global -> LDS directly
@@ -504,7 +510,7 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   // loads into LDS, so that no wave waits on several dependent global round trips. S_c^T of
   // query block qb takes two swizzled 64-row tiles at 2 qb TILE; z_c takes the 1 KB at 4 TILE
   // (each load into LDS writes 1 KB, lanes past the data write zeros), alpha the next 1 KB.
-  constexpr bool STAGE_EPI = DMA && !PISA;
+  constexpr bool STAGE_EPI = DMA && !PISA && !SAVE;
   if constexpr (STAGE_EPI) {
     __syncthreads();   // every wave has drained its ring loads (wait_vmem above)
     constexpr int SCP = D * D * 2 / 1024;           // 1-KB pieces of one S_c^T
@@ -535,6 +541,26 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
 
   // ---------------------------------------------------------------- epilogue
   l += swap_halves(l);
+  if constexpr (SAVE) {
+    const int q = qrow0 + l32;
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+    if (h == 0)
+      a.lse[(size_t)bh * a.nbq * kBlock + (size_t)iq * kBlock + 32 * (wv & 1) + l32] =
+          (l > 0.f && q < a.nq) ? m + log2f(l) : kNoRowLse;
+    if (q < a.nq) {
+      float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D;
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int ch = 32 * c + 8 * g + 4 * h;
+          *reinterpret_cast<f32x4*>(dst + ch) =
+              f32x4{o[c][4 * g] * inv_l, o[c][4 * g + 1] * inv_l, o[c][4 * g + 2] * inv_l,
+                    o[c][4 * g + 3] * inv_l};
+        }
+    }
+    return;
+  }
   if constexpr (PISA) {
     // Piecewise merge (PISA page, core algorithm): the exact part (o, l in the frame 2^m) and
     // the tail (N_U, D_U, A_U in the frame 2^m_U) share one normalisation; the first-order
@@ -880,7 +906,7 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_fp8_kernel(SparseArgs
 template <typename T, int D, int QB, bool FP8, bool PISA = false>
 hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const int32_t* idx,
                            const float* alpha, void* o, char* ws, hipStream_t st) {
-  SparseArgs a;
+  SparseArgs a{};
   a.q = q;
   a.k = k;
   a.v16 = reinterpret_cast<const uint16_t*>(ws + s.v16);
@@ -951,6 +977,33 @@ hipError_t launch_sparse_pisa(const Plan& s, const void* q, const void* k, const
   }
   if (s.D == 128) return launch_sparse_D<float, 128, false, true>(s, q, k, idx, nullptr, o, ws, st);
   return launch_sparse_D<float, 64, false, true>(s, q, k, idx, nullptr, o, ws, st);
+}
+
+hipError_t launch_sparse_save(const Plan& s, const void* q, const void* k, const int32_t* idx,
+                              float* os, float* lse, char* ws, hipStream_t st) {
+  if (!s.in_bf16) return hipErrorInvalidValue;
+  SparseArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v16 = reinterpret_cast<const uint16_t*>(ws + s.v16);
+  a.idx = idx;
+  a.out = os;
+  a.lse = lse;
+  a.nq = s.nq; a.nkv = s.nkv; a.nbq = s.nbq; a.nbk = s.nbk; a.topk = s.k; a.H = s.H;
+  auto go = [&](auto kern, int qb) {
+    a.ngroups = (s.nbq + qb - 1) / qb;
+    a.total = s.BH * a.ngroups;
+    hipLaunchKernelGGL(kern, dim3(a.total), dim3(128 * qb), 0, st, a);
+  };
+  const bool pair = s.nbq >= 2 && (long long)s.BH * s.nbq >= 1024;
+  if (s.D == 128) {
+    if (pair) go(sparse_attn_kernel<uint16_t, 128, 2, false, false, true>, 2);
+    else go(sparse_attn_kernel<uint16_t, 128, 1, false, false, true>, 1);
+  } else {
+    if (pair) go(sparse_attn_kernel<uint16_t, 64, 2, false, false, true>, 2);
+    else go(sparse_attn_kernel<uint16_t, 64, 1, false, false, true>, 1);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
