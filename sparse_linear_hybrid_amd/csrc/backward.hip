@@ -23,6 +23,7 @@
 //                       part of dQ, dS_c(i) (bf16 high and low parts, summary layout), dz_c(i);
 //   (complement, fp32)  G_j from the dS_c(i), roles of query and key blocks swapped;
 //   bwd_gz_kernel       gz_j;
+//   bwd_order_kernel    key-block tasks by number of routing query blocks, most first;
 //   bwd_key_kernel      per key block: dK, dV over the query blocks that selected it, plus
 //                       the linear parts;
 //   bwd_dq_kernel       per query block: the exact branch's dQ, added to the linear part;
@@ -32,7 +33,8 @@
 // complement), so S_c, g, dS_c and G are carried as bf16 high + low parts into the MFMAs.
 // Layout conventions follow the forward (transposed products so that an accumulator feeds
 // the next MFMA as an operand; transposing LDS reads supply the other operand in the same
-// permuted order). Everything is deterministic: no atomics, fixed reduction orders.
+// permuted order). Every result is deterministic: no atomics on values, fixed reduction
+// orders (the key kernel's task order comes from LDS atomics but changes no output bit).
 #include "common.h"
 #include "kernels.h"
 
@@ -62,6 +64,7 @@ struct BwdArgs {
   const float* gt;          // G_j^T [BH][nbk][D(c)][D(r)] fp32
   float* gz;                // [BH][nbk][D]
   float* dapart;            // [BH][nbq][D]
+  const int32_t* order;     // [BH*nbk]: key-block tasks, most routed query blocks first
   float* dq;                // [BH][nq][D]
   float* dk;                // [BH][nkv][D]
   float* dv;                // [BH][nkv][D]
@@ -134,7 +137,8 @@ __device__ __forceinline__ u32x4 row_frag(const uint16_t* M, int row, int col) {
 // bit i set iff j is routed to i. One workgroup per (batch*head, row).
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ idx,
                                                        uint32_t* __restrict__ selbits,
-                                                       uint32_t* __restrict__ bitsT, int nbq,
+                                                       uint32_t* __restrict__ bitsT,
+                                                       int32_t* __restrict__ counts, int nbq,
                                                        int nbk, int topk, int nwk, int nwq) {
   extern __shared__ uint32_t wbits[];
   const int bh = blockIdx.y, row = blockIdx.x, t = threadIdx.x;
@@ -150,6 +154,9 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict
     for (int w = t; w < nwk; w += 256) selbits[((size_t)bh * nbq + row) * nwk + w] = wbits[w];
   } else {           // transposed: key block j = row - nbq; binary search in each list
     const int j = row - nbq;
+    if (t == 0) wbits[0] = 0u;
+    __syncthreads();
+    int mine = 0;
     for (int w = t; w < nwq; w += 256) {
       uint32_t word = 0u;
       for (int b = 0; b < 32; ++b) {
@@ -164,7 +171,12 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict
         if (lo < topk && sel[lo] == j) word |= 1u << b;
       }
       bitsT[((size_t)bh * nbk + j) * nwq + w] = word;
+      mine += __builtin_popcount(word);
     }
+    // how many query blocks routed j (integer sum: the same whatever the order)
+    if (mine) atomicAdd(&wbits[0], (uint32_t)mine);
+    __syncthreads();
+    if (t == 0) counts[(size_t)bh * nbk + j] = (int32_t)wbits[0];
   }
 }
 
@@ -387,27 +399,65 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   }
 }
 
-// gz_j = sum over the query blocks i that did not select j of dz_c(i), in order of i
+// gz_j = sum over the query blocks i that did not select j of dz_c(i), in order of i.
+// One thread per channel; a workgroup takes kGzBlocks key blocks, so that each dz_c row is
+// read once for all of them.
+constexpr int kGzBlocks = 16;
 template <int D>
-__global__ __launch_bounds__(64) void bwd_gz_kernel(BwdArgs a) {
-  const int bh = blockIdx.x / a.nbk, j = blockIdx.x % a.nbk, lane = threadIdx.x;
-  const uint32_t* row = a.bitsT + ((size_t)bh * a.nbk + j) * a.nwq;
-  float acc[D / 64];
+__global__ __launch_bounds__(D) void bwd_gz_kernel(BwdArgs a) {
+  const int ngrp = (a.nbk + kGzBlocks - 1) / kGzBlocks;
+  const int bh = blockIdx.x / ngrp, j0 = (blockIdx.x % ngrp) * kGzBlocks, c = threadIdx.x;
+  const int nj = min(kGzBlocks, a.nbk - j0);
+  float acc[kGzBlocks];
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u) acc[u] = 0.f;
+  for (int u = 0; u < kGzBlocks; ++u) acc[u] = 0.f;
+  const uint32_t* rows = a.bitsT + ((size_t)bh * a.nbk + j0) * a.nwq;
+  const float* dz = a.dzc + (size_t)bh * a.nbq * D + c;
   for (int w = 0; w < a.nwq; ++w) {
-    const uint32_t word = row[w];
-    for (int b = 0; b < 32; ++b) {
-      const int i = 32 * w + b;
-      if (i >= a.nbq) break;
-      if ((word >> b) & 1u) continue;
+    uint32_t word[kGzBlocks];
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) acc[u] += a.dzc[((size_t)bh * a.nbq + i) * D + lane + 64 * u];
-    }
+    for (int u = 0; u < kGzBlocks; ++u) word[u] = u < nj ? rows[(size_t)u * a.nwq + w] : ~0u;
+    const int nb = min(32, a.nbq - 32 * w);
+    float v[32];   // the word's 32 rows of dz_c in flight together
+#pragma unroll
+    for (int b = 0; b < 32; ++b) v[b] = b < nb ? dz[(size_t)(32 * w + b) * D] : 0.f;
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+#pragma unroll
+      for (int u = 0; u < kGzBlocks; ++u)
+        if (b < nb && !((word[u] >> b) & 1u)) acc[u] += v[b];
   }
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u)
-    a.gz[((size_t)bh * a.nbk + j) * D + lane + 64 * u] = acc[u];
+  for (int u = 0; u < kGzBlocks; ++u)
+    if (u < nj) a.gz[((size_t)bh * a.nbk + j0 + u) * D + c] = acc[u];
+}
+
+// Key-block tasks ordered by the number of query blocks that routed them, most first (a
+// counting sort in one workgroup), so that the longest tasks of the key kernel start first
+// and its tail stays short. Tasks with the same count land in any order: each task's
+// results depend only on its own key block, so the order changes no output bit.
+constexpr int kOrderBins = 4096;
+__global__ __launch_bounds__(1024) void bwd_order_kernel(const int32_t* __restrict__ counts,
+                                                         int ntask, int nbq,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int bins[kOrderBins];
+  const int nbin = min(nbq + 1, kOrderBins);
+  for (int b = threadIdx.x; b < nbin; b += 1024) bins[b] = 0;
+  __syncthreads();
+  for (int task = threadIdx.x; task < ntask; task += 1024)
+    atomicAdd(&bins[min(counts[task], nbin - 1)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {   // exclusive offsets, largest count first
+    int off = 0;
+    for (int b = nbin - 1; b >= 0; --b) {
+      const int n = bins[b];
+      bins[b] = off;
+      off += n;
+    }
+  }
+  __syncthreads();
+  for (int task = threadIdx.x; task < ntask; task += 1024)
+    order[atomicAdd(&bins[min(counts[task], nbin - 1)], 1)] = task;
 }
 
 // ----------------------------------------------------------------------------- per key block
@@ -418,7 +468,8 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   constexpr int KS = D / 16, CT = D / 32, TILE = 64 * D;
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE > 2 * D * D ? 4 * TILE : 2 * D * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][64], dr_s[2][64];
-  const int bh = blockIdx.x / a.nbk, j = blockIdx.x % a.nbk;
+  const int task = a.order[blockIdx.x];
+  const int bh = task / a.nbk, j = task % a.nbk;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int key = j * kBlock + 32 * wv + l32;
   const bool kvalid = key < a.nkv;
@@ -686,16 +737,28 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
-// dalpha[h][c] = sum over batches and query blocks of the partials, in order
+// dalpha[h][c] = sum over batches and query blocks of the partials: eight interleaved
+// partial sums per channel (rows r = p, p + 8, ... in order), then the eight in order.
 template <int D>
-__global__ __launch_bounds__(D) void bwd_dalpha_kernel(const float* __restrict__ part,
-                                                       float* __restrict__ dalpha, int B, int H,
-                                                       int nbq) {
-  const int hd = blockIdx.x, c = threadIdx.x;
+__global__ __launch_bounds__(256) void bwd_dalpha_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ dalpha, int B, int H,
+                                                         int nbq) {
+  __shared__ float red[8][32];
+  const int hd = blockIdx.x, c = blockIdx.y * 32 + (threadIdx.x & 31), p = threadIdx.x >> 5;
+  const int rows = B * nbq;
   float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int i = 0; i < nbq; ++i) s += part[(((size_t)b * H + hd) * nbq + i) * D + c];
-  dalpha[(size_t)hd * D + c] = s;
+  for (int r = p; r < rows; r += 8) {
+    const int b = r / nbq, i = r % nbq;
+    s += part[(((size_t)b * H + hd) * nbq + i) * D + c];
+  }
+  red[p][threadIdx.x & 31] = s;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tot += red[q][threadIdx.x];
+    dalpha[(size_t)hd * D + c] = tot;
+  }
 }
 
 template <int D>
@@ -703,9 +766,10 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
                              hipStream_t st) {
   const int nwk = s.nwords;
   hipLaunchKernelGGL(bwd_bits_kernel, dim3(s.nbq + s.nbk, s.BH), dim3(256),
-                     (size_t)nwk * 4, st, a.idx,
+                     (size_t)(nwk > 1 ? nwk : 1) * 4, st, a.idx,
                      reinterpret_cast<uint32_t*>(ws + s.selbits),
-                     reinterpret_cast<uint32_t*>(ws + bp.bitsT), s.nbq, s.nbk, s.k, nwk, a.nwq);
+                     reinterpret_cast<uint32_t*>(ws + bp.bitsT),
+                     reinterpret_cast<int32_t*>(ws + bp.counts), s.nbq, s.nbk, s.k, nwk, a.nwq);
   uint16_t* sblo = reinterpret_cast<uint16_t*>(ws + bp.sblo);
   hipError_t e = launch_kv_summary(s, a.k, a.v, nullptr, ws, st, false, sblo);
   if (e != hipSuccess) return e;
@@ -722,7 +786,11 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
   e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + bp.bitsT), a.nwq, s.nbk,
                             s.nbq, 0, a.dsc, a.dsclo, const_cast<float*>(a.gt), st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_gz_kernel<D>, dim3(s.BH * s.nbk), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bwd_gz_kernel<D>, dim3(s.BH * ((s.nbk + kGzBlocks - 1) / kGzBlocks)),
+                     dim3(D), 0, st, a);
+  hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, st,
+                     reinterpret_cast<const int32_t*>(ws + bp.counts), s.BH * s.nbk, s.nbq,
+                     const_cast<int32_t*>(a.order));
   hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
   return hipGetLastError();
@@ -756,6 +824,7 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
   a.gt = reinterpret_cast<const float*>(ws + bp.gt);
   a.gz = reinterpret_cast<float*>(ws + bp.gz);
   a.dapart = reinterpret_cast<float*>(ws + bp.dapart);
+  a.order = reinterpret_cast<const int32_t*>(ws + bp.order);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -765,11 +834,11 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
                             : launch_backward_T<64>(s, bp, a, ws, st);
   if (e != hipSuccess) return e;
   if (s.D == 128)
-    hipLaunchKernelGGL(bwd_dalpha_kernel<128>, dim3(s.H), dim3(128), 0, st, a.dapart, dalpha,
-                       s.B, s.H, s.nbq);
+    hipLaunchKernelGGL(bwd_dalpha_kernel<128>, dim3(s.H, 128 / 32), dim3(256), 0, st, a.dapart,
+                       dalpha, s.B, s.H, s.nbq);
   else
-    hipLaunchKernelGGL(bwd_dalpha_kernel<64>, dim3(s.H), dim3(64), 0, st, a.dapart, dalpha,
-                       s.B, s.H, s.nbq);
+    hipLaunchKernelGGL(bwd_dalpha_kernel<64>, dim3(s.H, 64 / 32), dim3(256), 0, st, a.dapart,
+                       dalpha, s.B, s.H, s.nbq);
   return hipGetLastError();
 }
 

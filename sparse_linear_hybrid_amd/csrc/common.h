@@ -350,7 +350,8 @@ inline Plan make_plan(const sla_problem& p) {
 // complement, bitmap), then the backward's own regions.
 struct BwdPlan {
   int nwq;                                      // 32-bit words of a query-block bitmap row
-  size_t bitsT, sblo, scf, os, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, bytes;
+  size_t bitsT, counts, sblo, scf, os, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, order,
+      bytes;
 };
 inline BwdPlan make_bwd_plan(const Plan& s) {
   BwdPlan b{};
@@ -359,6 +360,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   size_t off = s.total_fwd;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   b.bitsT = take(BH * nbk * (size_t)b.nwq * 4);
+  b.counts = take(BH * nbk * 4);                // query blocks that routed each key block
   b.sblo = take(BH * nbk * D * D * 2);          // S_j - bf16(S_j), bf16, summary layout
   b.scf = take(BH * nbq * D * D * 4);           // S_c^T fp32
   b.os = take(BH * (size_t)s.nq * D * 4);        // O_s fp32, saved by the sparse kernel
@@ -371,6 +373,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   b.gt = take(BH * nbk * D * D * 4);            // G_j^T fp32
   b.gz = take(BH * nbk * D * 4);
   b.dapart = take(BH * nbq * D * 4);
+  b.order = take(BH * nbk * 4);                 // key-block task order of the key kernel
   b.bytes = off;
   return b;
 }
