@@ -183,11 +183,15 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict
 // ----------------------------------------------------------------------------- per query block
 // Two waves, wave w owns query rows 32 w .. 32 w + 31 of query block iq; the O^T accumulator
 // layout (lane: query row, elements: channels 32 c + 8 g + 4 h + e) is kept throughout.
+// LDS is used in three phases: S_c^T as bf16 high and low parts (O_l and the linear dQ),
+// then the dalpha terms (fp32 [64][D]), then g as bf16 high and low parts and the Q tile
+// (dS_c and dz_c): 64 KB at D = 128, so two workgroups share a CU.
 template <int D>
 __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   constexpr int KS = D / 16, CT = D / 32, CH = D / 8, TILE = 64 * D;
   constexpr int NCS = D * D / 128;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * D * D + 3 * TILE];
+  constexpr int SMEM = 2 * D * D > 3 * TILE ? 2 * D * D : 3 * TILE;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM];
   __shared__ float hh_s[64];
   const int bh = blockIdx.x / a.nbq, iq = blockIdx.x % a.nbq;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
@@ -197,18 +201,10 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   const int hd = bh % a.H;
   const uint16_t* qrow = a.q + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
 
-  // smem: S_c^T [D][D] as bf16 high and low parts (V swizzle: row reads and vt_frag), the
-  // Q tile (row swizzle, read with tr_nat), then two tiles that first hold the dalpha terms
-  // (fp32 [64][D]) and then g as bf16 high and low parts (row swizzle)
+  // phase 1: S_c^T [D][D] as bf16 high and low parts, V swizzle (row reads and vt_frag)
   uint16_t* Sct = smem;
   uint16_t* Scl = smem + D * D;
-  uint16_t* Qt = smem + 2 * D * D;
-  uint16_t* Gt = Qt + TILE;     // g rounded to bf16
-  uint16_t* Gl = Gt + TILE;     // and its remainder, also bf16
-  float* xs = reinterpret_cast<float*>(Gt);
   const float* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
-  dma_tile<D, false, 2>(Qt, a.q + ((size_t)bh * a.nq + (size_t)iq * kBlock) * D,
-                        min(kBlock, a.nq - iq * kBlock));
   for (int id = t; id < D * CH; id += 128) {
     const int rr = id / CH, cc = id % CH;
     u32x4 hi, lo;
@@ -224,6 +220,19 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
 
   // the exact branch's output, saved by the forward's sparse kernel in this backward
   const float* osr = a.os + ((size_t)bh * a.nq + (valid ? n : 0)) * D;
+  const float* dof = reinterpret_cast<const float*>(a.dout) + ((size_t)bh * a.nq + n) * D;
+  const uint16_t* dob = reinterpret_cast<const uint16_t*>(a.dout) + ((size_t)bh * a.nq + n) * D;
+  auto load_dout = [&](int ch, float (&dov)[4]) __attribute__((always_inline)) {
+    dov[0] = dov[1] = dov[2] = dov[3] = 0.f;
+    if (!valid) return;
+    if (a.dout_bf16) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(dob + ch);
+      dov[0] = bf16_lo(w[0]); dov[1] = bf16_hi(w[0]); dov[2] = bf16_lo(w[1]); dov[3] = bf16_hi(w[1]);
+    } else {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(dof + ch);
+      dov[0] = w[0]; dov[1] = w[1]; dov[2] = w[2]; dov[3] = w[3];
+    }
+  };
 
   // ---------------------------------------------------------------- linear branch again
   const bool empty_c = a.topk >= a.nbk;
@@ -240,7 +249,7 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
   }
   den += swap_halves(den);
   den += kEps;
-  barrier_vmem_lds_n<0>();   // S_c^T (stores) and the Q tile (loads into LDS) are in place
+  __syncthreads();   // S_c^T is in place
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
     lin[c] = f32x16{};
@@ -263,32 +272,20 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int ch = 32 * c + 8 * g4 + 4 * h;
-      float dov[4] = {0.f, 0.f, 0.f, 0.f};
-      if (valid) {
-        if (a.dout_bf16) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(
-              reinterpret_cast<const uint16_t*>(a.dout) + ((size_t)bh * a.nq + n) * D + ch);
-          dov[0] = bf16_lo(w[0]); dov[1] = bf16_hi(w[0]); dov[2] = bf16_lo(w[1]); dov[3] = bf16_hi(w[1]);
-        } else {
-          const f32x4 w = *reinterpret_cast<const f32x4*>(
-              reinterpret_cast<const float*>(a.dout) + ((size_t)bh * a.nq + n) * D + ch);
-          dov[0] = w[0]; dov[1] = w[1]; dov[2] = w[2]; dov[3] = w[3];
-        }
-      }
+      float dov[4];
+      load_dout(ch, dov);
       const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
       const f32x4 osv = valid ? *reinterpret_cast<const f32x4*>(osr + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
       float dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ix = 4 * g4 + e;
-        const float os = osv[e];
         const float ol = lin[c][ix] * inv_den;
         dsv[e] = alv[e] * dov[e];
         const float dl = (1.f - alv[e]) * dov[e];
-        dsum += dsv[e] * os;
+        dsum += dsv[e] * osv[e];
         hsum += dl * ol;
         gv[c][ix] = dl * inv_den;
-        xs[row * D + ch + e] = dov[e] * (os - ol);
       }
       *reinterpret_cast<u32x2*>(dosr + ch) = u32x2{pack_f16(dsv[0], dsv[1]), pack_f16(dsv[2], dsv[3])};
     }
@@ -299,28 +296,8 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
     a.dr[(size_t)bh * a.nbq * kBlock + iq * kBlock + row] = valid ? dsum : 0.f;
     hh_s[row] = valid ? hn : 0.f;
   }
-  __syncthreads();
-  for (int c = t; c < D; c += 128) {   // dalpha partial: the block's rows in order
-    float s = 0.f;
-    for (int r2 = 0; r2 < kBlock; ++r2) s += xs[r2 * D + c];
-    a.dapart[((size_t)bh * a.nbq + iq) * D + c] = s;
-  }
-  __syncthreads();
 
   // ---------------------------------------------------------------- linear part of dQ
-#pragma unroll
-  for (int c = 0; c < CT; ++c)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int ch = 32 * c + 8 * g4 + 4 * h;
-      const uint32_t h0 = pack_bf16(gv[c][4 * g4], gv[c][4 * g4 + 1]);
-      const uint32_t h1 = pack_bf16(gv[c][4 * g4 + 2], gv[c][4 * g4 + 3]);
-      *reinterpret_cast<u32x2*>(Gt + swz<D>(row, ch)) = u32x2{h0, h1};
-      *reinterpret_cast<u32x2*>(Gl + swz<D>(row, ch)) =
-          u32x2{pack_bf16(gv[c][4 * g4] - bf16_lo(h0), gv[c][4 * g4 + 1] - bf16_hi(h0)),
-                pack_bf16(gv[c][4 * g4 + 2] - bf16_lo(h1), gv[c][4 * g4 + 3] - bf16_hi(h1))};
-    }
-  __syncthreads();
   // da^T = S_c g^T: M = r, N = this wave's rows, K = c (g's elements in vt_frag's order).
   // S_c and g enter as bf16 high and low parts (the low x low product is below fp32's
   // rounding): g S_c^T and h z_c nearly cancel (their difference is the covariance of phi(k)
@@ -365,6 +342,51 @@ __global__ __launch_bounds__(128) void bwd_query_kernel(BwdArgs a) {
         *reinterpret_cast<f32x4*>(dqr + r0) = outv;
       }
   }
+
+  // ---------------------------------------------------------------- dalpha partial
+  // phase 2: the terms dO (.) (O_s - O_l) as fp32 [64][D], summed over the block's rows in order
+  __syncthreads();   // S_c^T is no longer read
+  float* xs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = 32 * c + 8 * g4 + 4 * h;
+      float dov[4];
+      load_dout(ch, dov);
+      const f32x4 osv = valid ? *reinterpret_cast<const f32x4*>(osr + ch) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xs[row * D + ch + e] = dov[e] * (osv[e] - lin[c][4 * g4 + e] * inv_den);
+    }
+  __syncthreads();
+  for (int c = t; c < D; c += 128) {
+    float sacc = 0.f;
+    for (int r2 = 0; r2 < kBlock; ++r2) sacc += xs[r2 * D + c];
+    a.dapart[((size_t)bh * a.nbq + iq) * D + c] = sacc;
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- dS_c and dz_c
+  // phase 3: g as bf16 high and low parts and the Q tile (row swizzle, read with tr_nat)
+  uint16_t* Gt = smem;          // g rounded to bf16
+  uint16_t* Gl = smem + TILE;   // and its remainder, also bf16
+  uint16_t* Qt = smem + 2 * TILE;
+  dma_tile<D, false, 2>(Qt, a.q + ((size_t)bh * a.nq + (size_t)iq * kBlock) * D,
+                        min(kBlock, a.nq - iq * kBlock));
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = 32 * c + 8 * g4 + 4 * h;
+      const uint32_t h0 = pack_bf16(gv[c][4 * g4], gv[c][4 * g4 + 1]);
+      const uint32_t h1 = pack_bf16(gv[c][4 * g4 + 2], gv[c][4 * g4 + 3]);
+      *reinterpret_cast<u32x2*>(Gt + swz<D>(row, ch)) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(Gl + swz<D>(row, ch)) =
+          u32x2{pack_bf16(gv[c][4 * g4] - bf16_lo(h0), gv[c][4 * g4 + 1] - bf16_hi(h0)),
+                pack_bf16(gv[c][4 * g4 + 2] - bf16_lo(h1), gv[c][4 * g4 + 3] - bf16_hi(h1))};
+    }
+  barrier_vmem_lds_n<0>();   // the g tiles (stores) and the Q tile (loads into LDS) are in place
   // dS_c(i)^T[c][r] = sum_n g[n][c] relu(q[n][r]): M = c, N = r, K = the block's 64 rows.
   // Wave w takes the c tiles w, w + 2, ...
   for (int ct = wv; ct < CT; ct += 2) {

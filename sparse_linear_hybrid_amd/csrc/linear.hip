@@ -505,13 +505,14 @@ __device__ __forceinline__ u32x4 bits_to_bf16x8(uint32_t m8) {
   return b;
 }
 
-// F32: the sums go out as fp32 (stored, or added to what `sc` holds when accum != 0) instead
-// of bf16; the backward sums the high and low bf16 parts of its summaries that way.
+// F32 (the backward): the stacked summaries come as bf16 high parts (sblk) and low parts
+// (sblk_lo); both are summed into the same accumulators (high parts first) and the sums go
+// out once, as fp32.
 template <int D, bool F32 = false>
 __global__ __launch_bounds__(256, 2) void complement_kernel(
     const uint32_t* __restrict__ selbits, int nwords, const uint16_t* __restrict__ sblk,
-    const float* __restrict__ stot, void* __restrict__ out, int nbq, int nbk, int k,
-    int nqt, int total, int ww, int accum) {
+    const uint16_t* __restrict__ sblk_lo, void* __restrict__ out, int nbq, int nbk, int k,
+    int nqt, int total, int ww) {
   uint16_t* sc = reinterpret_cast<uint16_t*>(out);
   float* scf = reinterpret_cast<float*>(out);
   constexpr int NCS = D * D / CN;      // column slices per (batch, head)
@@ -531,7 +532,6 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
 
   if (k >= nbk) {   // every block selected: the complement is empty, exactly zero
     if constexpr (F32) {
-      if (accum) return;
       for (int e = t; e < CQ * CN / 4; e += 256) {
         const int il = e / (CN / 4), c4 = e % (CN / 4);
         const int i = qt * CQ + il;
@@ -580,6 +580,8 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
     for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = f32x16{};
 
   const int win = ww * CK;
+  for (int pass = 0; pass < (F32 ? 2 : 1); ++pass) {
+  if (pass == 1) sbase = sblk_lo + ((size_t)bh * NCS + cs) * nbk * CN;
   for (int win0 = 0; win0 < nbk; win0 += win) {
     const int nstep = min(ww, (nbk - win0 + CK - 1) / CK);
     barrier_vmem_n<0>();   // the previous window's ring and bitmap are no longer in use
@@ -662,6 +664,7 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       slot = slot == 4 ? 0 : slot + 2;
     }
   }
+  }   // pass
   wait_vmem();   // no load into LDS outlives the workgroup
   if constexpr (F32) {
     // lane: query block 64 w + 32 tq + l32 of the group; elements 4 g .. 4 g + 3: the four
@@ -675,11 +678,9 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4* p = reinterpret_cast<f32x4*>(row + 32 * nt + 8 * g + 4 * h);
-          f32x4 v{acc[tq][nt][4 * g], acc[tq][nt][4 * g + 1], acc[tq][nt][4 * g + 2],
-                  acc[tq][nt][4 * g + 3]};
-          if (accum) v += *p;
-          *p = v;
+          *reinterpret_cast<f32x4*>(row + 32 * nt + 8 * g + 4 * h) =
+              f32x4{acc[tq][nt][4 * g], acc[tq][nt][4 * g + 1], acc[tq][nt][4 * g + 2],
+                    acc[tq][nt][4 * g + 3]};
         }
     }
     return;
@@ -869,8 +870,8 @@ hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const 
 hipError_t launch_complement_f32(const Plan& s, const uint32_t* bits, int nwords, int rows,
                                  int cols, int k, const uint16_t* hi, const uint16_t* lo,
                                  float* out, hipStream_t st) {
-  // out[row] = sum over the columns whose bit is clear of (hi + lo)[col], in fp32: the
-  // complement kernel on the high parts (stored), then on the low parts (added)
+  // out[row] = sum over the columns whose bit is clear of (hi + lo)[col], in fp32: one
+  // complement pass over the high parts and then the low parts into the same sums
   const int nqt = (rows + CQ - 1) / CQ;
   const int ncs = s.D * s.D / CN;
   const int total = s.BH * ncs * nqt;
@@ -883,10 +884,8 @@ hipError_t launch_complement_f32(const Plan& s, const uint32_t* bits, int nwords
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (err != hipSuccess) return;
     }
-    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, nwords, hi, nullptr,
-                       (void*)out, rows, cols, k, nqt, total, ww, 0);
-    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, nwords, lo, nullptr,
-                       (void*)out, rows, cols, k, nqt, total, ww, 1);
+    hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, nwords, hi, lo, (void*)out,
+                       rows, cols, k, nqt, total, ww);
   };
   if (s.D == 128) go(complement_kernel<128, true>);
   else go(complement_kernel<64, true>);
@@ -921,9 +920,8 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
       if (err != hipSuccess) return;
     }
     hipLaunchKernelGGL(kern, dim3(total), dim3(256), lds, st, bits, s.nwords,
-                       reinterpret_cast<const uint16_t*>(ws + s.sblk),
-                       reinterpret_cast<const float*>(ws + s.stot),
-                       (void*)(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww, 0);
+                       reinterpret_cast<const uint16_t*>(ws + s.sblk), nullptr,
+                       (void*)(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww);
     hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
                        reinterpret_cast<const float*>(ws + s.zblk),
                        reinterpret_cast<const float*>(ws + s.ztot),
