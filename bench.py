@@ -761,7 +761,8 @@ def main():
     line = {
         "metric": METRIC, "value": ms, "unit": "ms", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": False,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/bf16" if fp8 else "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": ("fp8-e4m3/bf16" if fp8 else "bf16" if p.dtype == "bf16"
+                  else "f32 (bf16 three-term split products)"),
         "data": "synthetic",
         "config": {"workload": p.name, "batch": p.batch, "heads": p.heads, "n_q": p.n_q,
                    "n_kv": p.n_kv, "head_dim": p.head_dim, "block": p.block,
@@ -769,7 +770,14 @@ def main():
                    "grid": "x".join(map(str, p.grid)) if p.grid else None,
                    "router": args.router, "path": "sla_forward_pisa" if pisa else None,
                    "parallelism": "single GPU"},
+        # dense-equivalent: what full attention on the same shape would compute, over this
+        # forward's time (it exceeds the MFMA peak whenever the speedup over dense does);
+        # executed: the sparse kernel's FLOPs (Q K^T, P.V, linear apply) plus the complement's
+        # masked product, over the same time
         "effective_tflops": w["dense_flops"] / (ms * 1e-3) / 1e12,
+        "effective_tflops_kind": "dense-equivalent FLOPs / forward time",
+        "executed_tflops": (w["sparse_flops"] + 2 * p.batch * p.heads * p.nbq * p.nbk
+                            * p.head_dim ** 2) / (ms * 1e-3) / 1e12,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "dense": dense,

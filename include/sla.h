@@ -270,8 +270,16 @@ sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k
  * Inputs as sla_forward (in_dtype must be SLA_BF16); dout has out_dtype and O's shape;
  * block_idx (required unless top_k is 0) is the forward's selection [B, H, ceil(n_q/64),
  * top_k], ascending.
- * Outputs, fp32: dq like Q, dk and dv like K and V, dalpha [heads, head_dim]. Products run on
- * bf16 / f16 MFMA with fp32 accumulation; results are bit-reproducible. */
+ * Outputs, fp32: dq like Q, dk and dv like K and V, dalpha [heads, head_dim]; every element
+ * is written. Products run on bf16 / f16 MFMA with fp32 accumulation; the quantities whose
+ * gradients are small differences of large terms (dS of the exact branch; S_j, S_c, g, dS_c
+ * and G of the linear branch) enter as bf16 high + low parts. Results are bit-reproducible.
+ * Errors, with nothing enqueued: an invalid problem (as sla_forward), SLA_ERR_DTYPE for fp32
+ * inputs, SLA_ERR_NULL for a missing pointer (block_idx may be NULL only when top_k is 0),
+ * SLA_ERR_WORKSPACE when workspace_bytes < sla_backward_workspace_size(p), SLA_ERR_ALIGN for
+ * an unaligned workspace. The workspace (caller-owned, device) holds the forward's per-block
+ * summaries and the backward's intermediates: about 2.3 GB at B = 1, H = 12, n = 32768,
+ * d = 128. */
 size_t sla_backward_workspace_size(const sla_problem* p);
 
 sla_status sla_backward(const sla_problem* p, const void* q, const void* k, const void* v,
