@@ -216,6 +216,7 @@ def test_tiny_workload(sla):
     ref, ref_idx = oracle.forward(x)
     assert np.array_equal(idx, ref_idx)
     err, _ = max_err_over_rms(out, ref)
+    print(f"tiny: max-abs/rms {err:.3e}", flush=True)
     assert err <= TOL
 
 
