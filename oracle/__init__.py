@@ -12,8 +12,9 @@ What pins each part to something other than itself (``-m "not gpu"`` tests):
   the projection's orientation, pooling over valid tokens only, permutation invariance,
   the direct complement against total minus selected, the mix's endpoints and affinity
   (tests/test_oracle_pins.py); boundary gaps and near-tie flags on hand-built score rows and
-  against a Python sort (tests/test_oracle_wrappers.py); stored values of the tiny workload
-  written by tests/golden/make_golden.py (tests/golden/tiny_oracle.json).
+  against a Python sort (tests/test_oracle_wrappers.py). tests/golden/tiny_oracle.json
+  (written by tests/golden/make_golden.py from this oracle) only guards against change; it
+  pins nothing by itself.
 * fp8 (quantised sparse branch, both readings): the E4M3 table and rounding rule
   exhaustively, the block-scale closed form, equal-logit and two-key closed forms, the
   visit-order-free definition against the online form (tests/test_oracle_fp8.py); a
