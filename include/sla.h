@@ -9,8 +9,10 @@
  *   - sparse branch, sections 1 and 2.B: exact softmax attention (scale 1/sqrt(d)) of
  *     each query block over the tokens of its routed key blocks;
  *   - linear branch (SALAD page, section 2; SPLA page, section 2.2): ReLU-kernel linear
- *     attention over the key blocks that were NOT routed, obtained as the total over all
- *     key blocks minus the routed ones; O_l = phi(q) S_c / (phi(q) . z_c + 1e-6);
+ *     attention over the key blocks that were NOT routed: S_c is the sum of the unrouted
+ *     blocks' phi(K_j)^T V_j (formed directly on the per-block path; as the total minus the
+ *     routed blocks' term on the cache path), z_c the total of phi(K) minus the routed
+ *     blocks'; O_l = phi(q) S_c / (phi(q) . z_c + 1e-6);
  *   - mix, section 2.A: O = alpha (.) O_s + (1 - alpha) (.) O_l with a per-head,
  *     per-channel ratio alpha;
  *   - quantised sparse branch, section 2.C: sla_forward_fp8 runs the sparse branch on
@@ -21,7 +23,10 @@
  *   - All tensor pointers are DEVICE pointers to contiguous row-major arrays.
  *     Q is [batch, heads, n_q, head_dim]; K and V are [batch, heads, n_kv, head_dim];
  *     O is [batch, heads, n_q, head_dim]; the channel index is the fastest.
- *   - Q, K, V have element type in_dtype (bf16 or f32); O has out_dtype.
+ *   - Q, K, V have element type in_dtype (bf16 or f32); O has out_dtype. With f32 inputs
+ *     the logits Q K^T come from three bf16 products (hi hi, hi lo, lo hi: near-fp32), but
+ *     P.V still multiplies f16 P by an f16 copy of V and the per-block summaries S_j, S_c are
+ *     bf16, so f32 inputs give no more accuracy than bf16 ones beyond the logits.
  *   - Range: the exact (sparse) branch multiplies the softmax weights, held in f16 in
  *     [0, 256], with an f16 copy of V, so entries of V beyond +-65504 saturate there; the
  *     piecewise forward's per-block value sums (64 tokens each) are f16 as well.
