@@ -54,6 +54,47 @@ def forward_at(q, k, v, alpha_h, idx, block):
     return mix(alpha_h, o_s, o_l), o_s, o_l
 
 
+def _query_block(q, k, v, alpha_h, toks, comp, S, z, rows, dO, tau):
+    """The terms of one query block with rows `rows`, the tokens `toks` of its selected key
+    blocks and complement indicator `comp` (1 for the key blocks it did not select): its dQ
+    rows, its sparse branch's dK, dV contributions on those tokens (toks, dk_t, dv_t),
+    dS_c(i), dz_c(i) and its dalpha part."""
+    d = k.shape[1]
+    dq = np.zeros((len(rows), d))
+    o_s = np.zeros((len(rows), d))
+    dk_t = dv_t = np.zeros((0, d))
+    if len(toks):
+        lg = tau * (q[rows] @ k[toks].T)
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        o_s = p @ v[toks]
+        dos = alpha_h[None, :] * dO
+        dv_t = p.T @ dos
+        dp = dos @ v[toks].T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        dq += tau * (ds @ k[toks])
+        dk_t = tau * (ds.T @ q[rows])
+    # linear branch over the complement
+    S_c = np.tensordot(comp, S, axes=(0, 0))
+    z_c = comp @ z
+    a = relu(q[rows])
+    num = a @ S_c
+    den = a @ z_c + EPS
+    o_l = num / den[:, None]
+    dol = (1.0 - alpha_h)[None, :] * dO
+    g = dol / den[:, None]
+    hh = -(dol * num).sum(axis=1) / den ** 2
+    dq += (g @ S_c.T + hh[:, None] * z_c[None, :]) * (q[rows] > 0)
+    dalpha = (dO * (o_s - o_l)).sum(axis=0)
+    return dq, toks, dk_t, dv_t, a.T @ g, a.T @ hh, dalpha
+
+
+def _tokens(blocks, n, block):
+    if len(blocks) == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate([np.arange(n)[block_slice(j, n, block)] for j in blocks])
+
+
 def backward_head(q, k, v, alpha_h, idx, block, dout):
     """Gradients (dq, dk, dv, dalpha) of sum(dout * O) for one (b, h) at selection idx."""
     nq, d = q.shape
@@ -70,36 +111,13 @@ def backward_head(q, k, v, alpha_h, idx, block, dout):
     dzc = np.zeros((nbq, d))
     for i in range(nbq):
         rows = np.arange(nq)[block_slice(i, nq, block)]
-        dO = dout[rows]
-        # sparse branch over the selected tokens
-        o_s = np.zeros((len(rows), d))
-        if len(idx[i]):
-            toks = np.concatenate([np.arange(nkv)[block_slice(j, nkv, block)] for j in idx[i]])
-            lg = tau * (q[rows] @ k[toks].T)
-            p = np.exp(lg - lg.max(axis=1, keepdims=True))
-            p /= p.sum(axis=1, keepdims=True)
-            o_s = p @ v[toks]
-            dos = alpha_h[None, :] * dO
-            dv[toks] += p.T @ dos
-            dp = dos @ v[toks].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-            dq[rows] += tau * (ds @ k[toks])
-            dk[toks] += tau * (ds.T @ q[rows])
-        # linear branch over the complement
-        comp = 1.0 - M[i]
-        S_c = np.tensordot(comp, S, axes=(0, 0))
-        z_c = comp @ z
-        a = relu(q[rows])
-        num = a @ S_c
-        den = a @ z_c + EPS
-        o_l = num / den[:, None]
-        dol = (1.0 - alpha_h)[None, :] * dO
-        g = dol / den[:, None]
-        hh = -(dol * num).sum(axis=1) / den ** 2
-        dq[rows] += (g @ S_c.T + hh[:, None] * z_c[None, :]) * (q[rows] > 0)
-        dSc[i] = a.T @ g
-        dzc[i] = a.T @ hh
-        dalpha += (dO * (o_s - o_l)).sum(axis=0)
+        toks = _tokens(idx[i], nkv, block)
+        dq_i, toks, dk_t, dv_t, dSc[i], dzc[i], da = _query_block(
+            q, k, v, alpha_h, toks, 1.0 - M[i], S, z, rows, dout[rows], tau)
+        dq[rows] += dq_i
+        dk[toks] += dk_t
+        dv[toks] += dv_t
+        dalpha += da
     # each key block collects the linear gradients of the query blocks that did not select it
     compT = (1.0 - M).T                               # [Nbk, Nbq]
     G = np.tensordot(compT, dSc, axes=(1, 0))         # [Nbk, d, d]
@@ -110,6 +128,24 @@ def backward_head(q, k, v, alpha_h, idx, block, dout):
         dv[toks] += fk @ G[j]
         dk[toks] += (v[toks] @ G[j].T + gz[j][None, :]) * (k[toks] > 0)
     return dq, dk, dv, dalpha
+
+
+def dq_blocks(q, k, v, alpha_h, idx, block, dout, blocks):
+    """dQ rows of the listed query blocks only (one (b, h)): the query block's own terms of
+    backward_head (its rows' dQ depends on nothing else), for checks at sizes where the
+    full backward would be too slow. Returns {i: dq rows of block i}."""
+    nq, d = q.shape
+    nkv = k.shape[0]
+    tau = 1.0 / math.sqrt(d)
+    S, z = block_summaries(k, v, block)
+    M = selection_mask(idx, n_blocks(nkv, block))
+    out = {}
+    for i in blocks:
+        rows = np.arange(nq)[block_slice(i, nq, block)]
+        toks = _tokens(idx[i], nkv, block)
+        out[i] = _query_block(q, k, v, alpha_h, toks, 1.0 - M[i], S, z, rows, dout[rows],
+                              tau)[0]
+    return out
 
 
 def backward(inputs, dout: np.ndarray, idx: Optional[np.ndarray] = None):

@@ -109,3 +109,32 @@ def test_backward_single_branch(sla, alpha_value):
     for name, (e, _) in errs.items():
         tol = TOL_LINEAR if alpha_value == 0.0 and name != "dalpha" else TOL
         assert e <= tol, f"{name}: max-abs/rms {e:.3e}"
+
+
+@pytest.mark.slow
+def test_backward_video95_sampled_dq(sla):
+    """Full video95 shape (B=1, H=12, 32768 tokens, d=128, top-k 26): the GPU's dQ on
+    sampled query blocks of two heads against the oracle's per-block dQ (which depends only
+    on the block's own rows, selection and complement)."""
+    from workloads import make_inputs
+    x = make_inputs("video95")
+    q, k, v, pq, pk, al = to_device(x)
+    _, idx = sla.sla_forward(q, k, v, pq, pk, al, x.problem.top_k)
+    rng = np.random.default_rng(95)
+    dout = rng.standard_normal(q.shape).astype(np.float32)
+    dq, _, _, _ = sla.sla_backward(q, k, v, al, torch.from_numpy(dout).cuda(), idx)
+    torch.cuda.synchronize()
+    dq = dq.cpu().numpy()
+    idx = idx.cpu().numpy()
+    got, want = [], []
+    for h in (0, 7):
+        blocks = sorted(rng.choice(x.problem.nbq, size=3, replace=False).tolist())
+        ref = bw.dq_blocks(x.as_f64("q")[0, h], x.as_f64("k")[0, h], x.as_f64("v")[0, h],
+                           x.alpha[h].astype(np.float64), idx[0, h], 64,
+                           dout[0, h].astype(np.float64), blocks)
+        for i in blocks:
+            got.append(dq[0, h, 64 * i:64 * i + 64])
+            want.append(ref[i])
+    err, rms = rel_err(np.concatenate(got), np.concatenate(want))
+    print(f"video95 backward, sampled dq: max-abs/rms {err:.2e} (rms {rms:.3g})", flush=True)
+    assert err <= TOL

@@ -135,3 +135,14 @@ def test_backward_wrapper_matches_head_function():
             assert np.array_equal(dv[b, h], g[2])
             want_dal[h] += g[3]
     assert np.allclose(dal, want_dal, rtol=1e-14, atol=0)
+
+
+def test_dq_blocks_equal_the_full_backward_rows():
+    """The per-block dQ used for sampled checks at full size is the full backward's."""
+    nq, nk, d, b = 200, 330, 16, 64
+    q, k, v, al = head(nq, nk, d)
+    idx = random_selection(so.n_blocks(nq, b), so.n_blocks(nk, b), 2)
+    dout = RNG.standard_normal((nq, d))
+    dq = bw.backward_head(q, k, v, al, idx, b, dout)[0]
+    got = bw.dq_blocks(q, k, v, al, idx, b, dout, [0, 3])
+    assert np.array_equal(got[0], dq[0:64]) and np.array_equal(got[3], dq[192:200])
