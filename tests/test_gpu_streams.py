@@ -1,6 +1,7 @@
 """Stream behaviour of the forwards, which enqueue all their work on the caller's stream.
 
-Checked: graph capture of each forward replays bit-identically to the eager call (several
+Checked: graph capture of each forward, and of the backward, replays bit-identically to the
+eager call (several
 replays, with eager library work and synchronisations between them; the library records
 no memset nodes); forwards on two caller streams at once give the results each gives
 alone; the profiled entry point writes exactly what the plain one writes, for every variant;
@@ -179,3 +180,49 @@ def test_binding_refuses_mismatched_tensors(sla):
             sla.sla_forward(q, k, a["v"], a["pq"], a["pk"], a["al"], 2, out=a["out"])
     with pytest.raises(TypeError, match="k has dtype"):
         sla.sla_forward(q, k.float(), v.float(), pq, pk, al, 2)
+
+
+def test_backward_graph_replay_matches_eager(sla):
+    """sla_backward captured in a graph replays bit-identically to the eager call (outputs and
+    workspace preallocated, called through the C ABI), with other library work between the
+    replays."""
+    dev = torch.device("cuda")
+    x, (q, k, v, pq, pk, al) = inputs(505, nq=450, nkv=900)
+    top_k = x.problem.top_k
+    _, idx = sla.sla_forward(q, k, v, pq, pk, al, top_k)
+    dout = torch.randn(q.shape, device=dev, generator=torch.Generator(device=dev).manual_seed(2))
+    p = sla.make_problem(q, k, top_k)
+    ws = torch.empty(sla.sla_backward_workspace_size(p), dtype=torch.uint8, device=dev)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=dev),
+             torch.empty(k.shape, dtype=torch.float32, device=dev),
+             torch.empty(v.shape, dtype=torch.float32, device=dev),
+             torch.empty(al.shape, dtype=torch.float32, device=dev)]
+    lib = sla.library()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())   # noqa: E731
+
+    def call():
+        st = lib.sla_backward(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(al), ptr(dout),
+                              ptr(idx), *(ptr(g_) for g_ in grads), ptr(ws),
+                              ctypes.c_size_t(ws.numel()),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+    call()
+    torch.cuda.synchronize()
+    eager = [g_.clone() for g_ in grads]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    _, t2 = inputs(606)
+    other, _ = runner(sla, "sla", dev, top_k)(t2)
+    for rep in range(3):
+        call()
+        other()
+        torch.cuda.synchronize()
+        for g_ in grads:
+            g_.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("dq", "dk", "dv", "dalpha"), grads, eager):
+            assert torch.equal(got, want), f"replay {rep}: {name}"
