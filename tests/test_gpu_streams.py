@@ -1,9 +1,8 @@
 """Stream behaviour of the forwards, which enqueue all their work on the caller's stream.
 
 Checked: graph capture of each forward, and of the backward, replays bit-identically to the
-eager call (several
-replays, with eager library work and synchronisations between them; the library records
-no memset nodes); forwards on two caller streams at once give the results each gives
+eager call (several replays, with eager library work and synchronisations between them; the
+library records no memset nodes); forwards on two caller streams at once give the results each gives
 alone; the profiled entry point writes exactly what the plain one writes, for every variant;
 junk in one head does not reach another head's output (ragged last blocks).
 """
