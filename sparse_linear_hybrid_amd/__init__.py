@@ -10,6 +10,7 @@ from .sla import (SlaError, STATUS, Problem, make_problem, workspace_size, sla_r
                   sla_forward_taylor, sla_forward_pisa, VARIANT_FORWARD, VARIANT_FP8,
                   VARIANT_PISA, VARIANT_TAYLOR, sla_forward_cached_noalloc, NOALLOC_SCRATCH_BYTES,
                   sla_backward, sla_backward_workspace_size, sla_diag_fp8_mfma)
+from .autograd import sla_attention, SLAAttention
 
 __all__ = ["SlaError", "STATUS", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
            "sla_forward_fp8", "sla_forward_profiled", "library", "LIB_PATH", "EXPORTS", "STAGES",
@@ -17,4 +18,5 @@ __all__ = ["SlaError", "STATUS", "Problem", "make_problem", "workspace_size", "s
            "cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
            "sla_forward_taylor", "sla_forward_pisa", "VARIANT_FORWARD", "VARIANT_FP8",
            "VARIANT_PISA", "VARIANT_TAYLOR", "sla_forward_cached_noalloc", "NOALLOC_SCRATCH_BYTES",
-           "sla_backward", "sla_backward_workspace_size", "sla_diag_fp8_mfma"]
+           "sla_backward", "sla_backward_workspace_size", "sla_diag_fp8_mfma",
+           "sla_attention", "SLAAttention"]
