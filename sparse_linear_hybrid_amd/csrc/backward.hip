@@ -576,9 +576,11 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
             const int el = 8 * hh + e;
             const float lv = e < 4 ? l0[e] : l1[e - 4];
             const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-            const float p = kvalid ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv[mt][el], qk_scale, -lv)) : 0.f;
+            // (no mask for a key past n_kv: every product below keeps a key's terms in that
+            // key's own column, and the lane's results are not stored)
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[mt][el], qk_scale, -lv));
             pv[e] = p;
-            dsv[e] = p * (dp[mt][el] - dv_) * tau;
+            dsv[e] = p * (dp[mt][el] - dv_);   // tau is applied to the sum
           }
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int ix = 4 * g4 + e;
-        ko[e] = dkt[c][ix] + (kv[e] > 0.f ? lk[c][ix] + z[e] : 0.f);
+        ko[e] = tau * dkt[c][ix] + (kv[e] > 0.f ? lk[c][ix] + z[e] : 0.f);
         vo[e] = dvt[c][ix];
       }
       *reinterpret_cast<f32x4*>(dkr + r0) = ko;
@@ -726,7 +728,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
             const int el = 8 * hh + 2 * e2 + u;
             const int kk = 32 * mt + 8 * (el >> 2) + 4 * h + (el & 3);
             const float p = kk < nval ? __builtin_amdgcn_exp2f(__builtin_fmaf(st[mt][el], qk_scale, -lse)) : 0.f;
-            dsv[u] = p * (dpt[mt][el] - dn) * tau;
+            dsv[u] = p * (dpt[mt][el] - dn);   // tau is applied to the sum
           }
           const uint32_t hi = pack_bf16(dsv[0], dsv[1]);
           df[2 * mt + hh][e2] = hi;
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
       const int r0 = 32 * c + 8 * g4 + 4 * h;
       f32x4 cur = *reinterpret_cast<const f32x4*>(dqr + r0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) cur[e] += dqt[c][4 * g4 + e];
+      for (int e = 0; e < 4; ++e) cur[e] += tau * dqt[c][4 * g4 + e];
       *reinterpret_cast<f32x4*>(dqr + r0) = cur;
     }
 }
