@@ -628,18 +628,24 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
       uint32_t word[2];
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) word[tq] = bits[(64 * w + 32 * tq + l32) * WW + st];
+      // all eight A fragments of the step are read before its first product
+      u32x4 a[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 a[4];
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) a[nt] = ring_frag(M, 32 * nt, 16 * kk);
+        for (int nt = 0; nt < 4; ++nt) a[kk][nt] = ring_frag(M, 32 * nt, 16 * kk);
+      u32x4 b[2][2];
 #pragma unroll
-        for (int tq = 0; tq < 2; ++tq) {
-          const u32x4 b = bits_to_bf16x8((word[tq] >> (16 * kk + 8 * h)) & 0xffu);
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = mfma_bf16(a[nt], b, acc[tq][nt]);
-        }
-      }
+        for (int tq = 0; tq < 2; ++tq)
+          b[kk][tq] = bits_to_bf16x8((word[tq] >> (16 * kk + 8 * h)) & 0xffu);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) acc[tq][nt] = mfma_bf16(a[kk][nt], b[kk][tq], acc[tq][nt]);
     };
     // the next six occupied steps (-1: none); st[0], st[1] is the pair being multiplied
     int st[6];
