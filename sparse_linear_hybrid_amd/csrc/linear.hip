@@ -14,8 +14,9 @@
 //              product of the 0/1 complement bitmap with the stacked S_j, slice by slice.
 //              It equals S_tot - sum_{j in sel(i)} S_j exactly in real arithmetic, without that
 //              difference's cancellation when the selected blocks hold most of the mass; an
-//              all-blocks selection gives exactly 0. z_c(i) = z_tot - sum_{j in sel(i)} z_j
-//              (fp32, d values per block, in the order of the index list).
+//              all-blocks selection gives exactly 0. z_c(i) (fp32, d values per block) is
+//              z_tot - sum_{j in sel(i)} z_j while at most half the blocks are selected, else
+//              the direct sum of the unselected z_j.
 #include "common.h"
 #include "kernels.h"
 
@@ -283,71 +284,121 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       zblk[((size_t)bh * nbk + j) * D + 32 * mt + l32] = zl;
     }
     zp += zl;
-    f32x16 accs[TILES_PER_WAVE];
+    // Plain forward at d = 128: S_j^T in two halves of 64 value columns, so that only two
+    // accumulator tiles are live at a time (fewer registers: three workgroups per CU instead
+    // of two, more loads in flight). Half 0 is staged over the K tile once every wave holds its
+    // A fragments, half 1 over the V tile after every wave's last product.
+    constexpr bool HALVES = BLOCKS && !PISA && !FP8 && !LO && NT == 4;
+    if constexpr (HALVES) {
+      f32x16 acc2[2];
+      auto product = [&](int half) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < TILES_PER_WAVE; ++u) {
-      const int nt = (NT == 4) ? u : (w & 1);
-      accs[u] = f32x16{};
+        for (int u = 0; u < 2; ++u) {
+          acc2[u] = f32x16{};
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        accs[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), accs[u]);
-      if constexpr (TOTALS) part[u] += accs[u];
-    }
-    if constexpr (BLOCKS && !PISA) {
-      // S_j^T[c][r] (bf16) goes out in whole 2D-byte rows: staged over the K and V tiles
-      // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
-      // Lane column c = 32 nt + l32 holds rows r in runs of 4.
-      __syncthreads();
-      if constexpr (FP8) {   // the V8 tile (complete after the barrier) goes out
-        uint8_t* dst = f8.v8 + ((size_t)bh * nbk + j) * D * 64;
-        for (int id = t; id < D * 64 / 16; id += 256)
-          *reinterpret_cast<u32x4*>(dst + id * 16) = *reinterpret_cast<const u32x4*>(&vt8[id * 16]);
-      }
-#pragma unroll
-      for (int u = 0; u < TILES_PER_WAVE; ++u) {
-        const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 32 * mt + 8 * q + 4 * h;
-          *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
-              u32x2{pack_bf16(accs[u][4 * q], accs[u][4 * q + 1]),
-                    pack_bf16(accs[u][4 * q + 2], accs[u][4 * q + 3])};
+          for (int s4 = 0; s4 < 4; ++s4)
+            acc2[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * (2 * half + u), 16 * s4), acc2[u]);
         }
-      }
-      __syncthreads();
+      };
+      auto stage_half = [&](int half) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = t; e < D * D / 8; e += 256) {
-        const int c = e / (D / 8), ch = e % (D / 8);
-        const int f = c * D + ch * 8;             // flattened index of the chunk
-        uint16_t* dst = sblk + (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
-                        f % kSlice;
-        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
-      }
-      if constexpr (LO) {   // S_j - bf16(S_j), rounded to bf16, in the same layout
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < TILES_PER_WAVE; ++u) {
-          const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
+        for (int u = 0; u < 2; ++u) {
+          const int c = 32 * (2 * half + u) + l32;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int r = 32 * mt + 8 * q + 4 * h;
-            float lo[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              lo[e] = accs[u][4 * q + e] - bf16_lo(pack_bf16(accs[u][4 * q + e], 0.f));
             *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
-                u32x2{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
+                u32x2{pack_bf16(acc2[u][4 * q], acc2[u][4 * q + 1]),
+                      pack_bf16(acc2[u][4 * q + 2], acc2[u][4 * q + 3])};
+          }
+        }
+      };
+      auto store_half = [&](int half) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = t; e < D * D / 16; e += 256) {
+          const int c = 64 * half + e / (D / 8), ch = e % (D / 8);
+          const int f = c * D + ch * 8;
+          uint16_t* dst = sblk + (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
+                          f % kSlice;
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
+        }
+      };
+      product(0);
+      __syncthreads();   // every wave has its A fragments: the K tile is free
+      stage_half(0);
+      product(1);
+      __syncthreads();   // half 0 is staged and every wave is done with the V tile
+      store_half(0);
+      stage_half(1);
+      __syncthreads();
+      store_half(1);
+    } else {
+      f32x16 accs[TILES_PER_WAVE];
+  #pragma unroll
+      for (int u = 0; u < TILES_PER_WAVE; ++u) {
+        const int nt = (NT == 4) ? u : (w & 1);
+        accs[u] = f32x16{};
+  #pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          accs[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), accs[u]);
+        if constexpr (TOTALS) part[u] += accs[u];
+      }
+      if constexpr (BLOCKS && !PISA) {
+        // S_j^T[c][r] (bf16) goes out in whole 2D-byte rows: staged over the K and V tiles
+        // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
+        // Lane column c = 32 nt + l32 holds rows r in runs of 4.
+        __syncthreads();
+        if constexpr (FP8) {   // the V8 tile (complete after the barrier) goes out
+          uint8_t* dst = f8.v8 + ((size_t)bh * nbk + j) * D * 64;
+          for (int id = t; id < D * 64 / 16; id += 256)
+            *reinterpret_cast<u32x4*>(dst + id * 16) = *reinterpret_cast<const u32x4*>(&vt8[id * 16]);
+        }
+  #pragma unroll
+        for (int u = 0; u < TILES_PER_WAVE; ++u) {
+          const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 32 * mt + 8 * q + 4 * h;
+            *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
+                u32x2{pack_bf16(accs[u][4 * q], accs[u][4 * q + 1]),
+                      pack_bf16(accs[u][4 * q + 2], accs[u][4 * q + 3])};
           }
         }
         __syncthreads();
-#pragma unroll
+  #pragma unroll
         for (int e = t; e < D * D / 8; e += 256) {
           const int c = e / (D / 8), ch = e % (D / 8);
-          const int f = c * D + ch * 8;
-          uint16_t* dst = sblk_lo +
-                          (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
+          const int f = c * D + ch * 8;             // flattened index of the chunk
+          uint16_t* dst = sblk + (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
                           f % kSlice;
           *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
+        }
+        if constexpr (LO) {   // S_j - bf16(S_j), rounded to bf16, in the same layout
+          __syncthreads();
+  #pragma unroll
+          for (int u = 0; u < TILES_PER_WAVE; ++u) {
+            const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 32 * mt + 8 * q + 4 * h;
+              float lo[4];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                lo[e] = accs[u][4 * q + e] - bf16_lo(pack_bf16(accs[u][4 * q + e], 0.f));
+              *reinterpret_cast<u32x2*>(&KVs[c * LS + r]) =
+                  u32x2{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
+            }
+          }
+          __syncthreads();
+  #pragma unroll
+          for (int e = t; e < D * D / 8; e += 256) {
+            const int c = e / (D / 8), ch = e % (D / 8);
+            const int f = c * D + ch * 8;
+            uint16_t* dst = sblk_lo +
+                            (((size_t)bh * (D * D / kSlice) + f / kSlice) * nbk + j) * kSlice +
+                            f % kSlice;
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(&KVs[c * LS + ch * 8]);
+          }
         }
       }
     }
@@ -723,9 +774,15 @@ __global__ __launch_bounds__(256, 2) void complement_kernel(
   }
 }
 
-// Complement, normaliser part: z_c(i) = z_tot - sum_{j in sel(i)} z_j (fp32, fixed order).
+// Complement, normaliser part (fp32, fixed order). With at most half the key blocks selected,
+// z_c(i) = z_tot - sum_{j in sel(i)} z_j (at most k + 1 terms, and the unselected blocks are
+// at least half of them); with more than half selected, the unselected z_j are added directly
+// in ascending block order from the routed-block bitmap, so that z_c never comes out of a
+// difference of nearly equal sums (a selection of all but one block leaves one block's z).
 template <int D>
 __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restrict__ idx,
+                                                         const uint32_t* __restrict__ selbits,
+                                                         int nwords,
                                                          const float* __restrict__ zblk,
                                                          const float* __restrict__ ztot,
                                                          float* __restrict__ zc, int nbq, int nbk,
@@ -736,8 +793,23 @@ __global__ __launch_bounds__(D) void complement_z_kernel(const int32_t* __restri
     out[r] = 0.f;
     return;
   }
-  const int32_t* sel = idx + ((size_t)bh * nbq + i) * k;
   const float* zb = zblk + (size_t)bh * nbk * D + r;
+  if (2 * k > nbk) {
+    const uint32_t* brow = selbits + ((size_t)bh * nbq + i) * nwords;
+    float z = 0.f;
+    for (int wi = 0; wi < nwords; ++wi) {
+      const int jb = 32 * wi;
+      uint32_t m = ~brow[wi];
+      if (nbk - jb < 32) m &= (1u << (nbk - jb)) - 1u;   // bits past the last block
+      while (m) {
+        z += zb[(size_t)(jb + __builtin_ctz(m)) * D];
+        m &= m - 1u;
+      }
+    }
+    out[r] = z;
+    return;
+  }
+  const int32_t* sel = idx + ((size_t)bh * nbq + i) * k;
   // selected blocks are added in list order (deterministic); loads go out 32 at a time, so a
   // row of k selections waits for about k / 32 round trips
   float z = 0.f;
@@ -901,6 +973,7 @@ hipError_t launch_complement_f32(const Plan& s, const uint32_t* bits, int nwords
 hipError_t launch_complement_z(const Plan& s, const int32_t* idx, char* ws, hipStream_t st) {
   auto go = [&](auto zkern) {
     hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
+                       reinterpret_cast<const uint32_t*>(ws + s.selbits), s.nwords,
                        reinterpret_cast<const float*>(ws + s.zblk),
                        reinterpret_cast<const float*>(ws + s.ztot),
                        reinterpret_cast<float*>(ws + s.zc), s.nbq, s.nbk, s.k);
@@ -929,6 +1002,7 @@ hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStr
                        reinterpret_cast<const uint16_t*>(ws + s.sblk), nullptr,
                        (void*)(ws + s.sc), s.nbq, s.nbk, s.k, nqt, total, ww);
     hipLaunchKernelGGL(zkern, dim3(s.nbq, s.BH), dim3(s.D), 0, st, idx,
+                       reinterpret_cast<const uint32_t*>(ws + s.selbits), s.nwords,
                        reinterpret_cast<const float*>(ws + s.zblk),
                        reinterpret_cast<const float*>(ws + s.ztot),
                        reinterpret_cast<float*>(ws + s.zc), s.nbq, s.nbk, s.k);
