@@ -110,9 +110,11 @@ def spread(vals):
             "p90": float(np.percentile(v, 90))}
 
 
-def achievable_peaks(torch, dev):
+def achievable_peaks(torch, dev, sla=None):
     """What this GPU reaches in practice: a 1 GiB device-to-device copy (bytes read plus
-    written per second) and an 8192^3 bf16 GEMM through torch (dense MFMA work)."""
+    written per second), an 8192^3 bf16 GEMM through torch (dense MFMA work) and, with the
+    library, its matrix-instruction throughput loop (independent 32x32x16 bf16 products on
+    every SIMD: the rate of the matrix cores at the clock they run under that load)."""
     def timed(fn, n):
         for _ in range(2):
             fn()
@@ -133,9 +135,13 @@ def achievable_peaks(torch, dev):
     b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
     t_mm = timed(lambda: torch.mm(a, b), 5)
     del a, b
-    return {"copy_GBps": 2 * COPY_BYTES / t_copy / 1e9,
-            "bf16_gemm_TFLOPs": 2 * n ** 3 / t_mm / 1e12,
-            "how": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.mm"}
+    out = {"copy_GBps": 2 * COPY_BYTES / t_copy / 1e9,
+           "bf16_gemm_TFLOPs": 2 * n ** 3 / t_mm / 1e12,
+           "how": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.mm"}
+    if sla is not None:
+        out["mfma_bf16_TFLOPs"] = sla.sla_diag_mfma_rate(dev)
+        out["how"] += "; sla_diag_mfma_rate (bf16 32x32x16 products, 512 workgroups)"
+    return out
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -647,7 +653,7 @@ def main():
     torch.cuda.synchronize()
     warm_steps = [a.elapsed_time(b) for a, b in marks]
     del flush
-    peaks = None if args.no_peaks else achievable_peaks(torch, dev)
+    peaks = None if args.no_peaks else achievable_peaks(torch, dev, sla)
 
     w = work(p, fp8)
     sparse_s = stage_ms["sparse"] * 1e-3
@@ -661,6 +667,8 @@ def main():
     if peaks and not fp8:
         roofline["achievable_peak"] = peaks["bf16_gemm_TFLOPs"]
         roofline["frac_of_achievable"] = achieved / 1e12 / peaks["bf16_gemm_TFLOPs"]
+        roofline["mfma_rate"] = peaks["mfma_bf16_TFLOPs"]
+        roofline["frac_of_mfma_rate"] = achieved / 1e12 / peaks["mfma_bf16_TFLOPs"]
     # algorithmic HBM rate of the memory-bound stages (the key/value pass, the router, the
     # complement), against the 8 TB/s peak; the f16 V copy is shown apart
     hbm = {}

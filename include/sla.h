@@ -323,6 +323,15 @@ sla_status sla_forward_cached_noalloc(const sla_problem* p, const void* q, const
 sla_status sla_diag_fp8_mfma(const uint8_t* a, const uint8_t* b, float* c_fp8, float* c_bf16,
                              hipStream_t stream);
 
+/* Not part of the method: the matrix-core throughput this GPU reaches, for rooflines measured
+ * against the instruction rather than the published peak. Launches `blocks` workgroups of four
+ * waves; each wave issues 4 * iters 32x32x16 bf16 matrix products in four independent chains
+ * (32768 FLOP each: blocks * 16 * iters * 32768 FLOP in all) and every thread writes one
+ * float to sink (device, blocks * 256 floats, caller-owned). The caller times the launch on
+ * `stream` (for example with events). SLA_ERR_NULL for a NULL sink, SLA_ERR_SHAPE for blocks or
+ * iters <= 0; nothing is enqueued then. */
+sla_status sla_diag_mfma_rate(float* sink, int blocks, int iters, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* sla_status_string(sla_status s);
 

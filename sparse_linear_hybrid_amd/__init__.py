@@ -9,7 +9,8 @@ from .sla import (SlaError, STATUS, Problem, make_problem, workspace_size, sla_r
                   cached_workspace_size, sla_forward_cached, sla_route_taylor,
                   sla_forward_taylor, sla_forward_pisa, VARIANT_FORWARD, VARIANT_FP8,
                   VARIANT_PISA, VARIANT_TAYLOR, sla_forward_cached_noalloc, NOALLOC_SCRATCH_BYTES,
-                  sla_backward, sla_backward_workspace_size, sla_diag_fp8_mfma)
+                  sla_backward, sla_backward_workspace_size, sla_diag_fp8_mfma,
+                  sla_diag_mfma_rate)
 from .autograd import sla_attention, SLAAttention
 
 __all__ = ["SlaError", "STATUS", "Problem", "make_problem", "workspace_size", "sla_route", "sla_forward",
@@ -19,4 +20,4 @@ __all__ = ["SlaError", "STATUS", "Problem", "make_problem", "workspace_size", "s
            "sla_forward_taylor", "sla_forward_pisa", "VARIANT_FORWARD", "VARIANT_FP8",
            "VARIANT_PISA", "VARIANT_TAYLOR", "sla_forward_cached_noalloc", "NOALLOC_SCRATCH_BYTES",
            "sla_backward", "sla_backward_workspace_size", "sla_diag_fp8_mfma",
-           "sla_attention", "SLAAttention"]
+           "sla_diag_mfma_rate", "sla_attention", "SLAAttention"]

@@ -1,7 +1,11 @@
-// Diagnostic entry point (include/sla.h, sla_diag_fp8_mfma): one 32 x 32 x 64 product of
-// E4M3 operands on the scaled fp8 matrix instruction that the quantised forward uses for P.V,
-// and the same product on the bf16 instruction (every E4M3 value and every product of two is
-// exact in bf16 / fp32), so that a test can measure how the fp8 instruction accumulates.
+// Diagnostic entry points (include/sla.h):
+// * sla_diag_fp8_mfma: one 32 x 32 x 64 product of E4M3 operands on the scaled fp8 matrix
+//   instruction that the quantised forward uses for P.V, and the same product on the bf16
+//   instruction (every E4M3 value and every product of two is exact in bf16 / fp32), so that
+//   a test can measure how the fp8 instruction accumulates.
+// * sla_diag_mfma_rate: a matrix-instruction throughput loop (the 32x32x16 bf16 product of the
+//   exact branch's Q K^T), timed by the caller, which gives the rate the matrix cores reach on
+//   this GPU at the clock they run under that load.
 #include "common.h"
 
 namespace sla {
@@ -52,8 +56,47 @@ __global__ __launch_bounds__(64) void fp8_mfma_probe_kernel(const uint8_t* __res
   }
 }
 
+// Every wave runs four independent accumulator chains of 32x32x16 bf16 products, `iters`
+// rounds (4 iters products per wave); each thread writes one sum to `sink` so that nothing is
+// optimised away.
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ sink, int iters) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = pack_bf16(1e-3f * (float)(lane + e), 1e-3f * (float)(lane - e));
+    b[e] = pack_bf16(2e-3f * (float)(e + 1), -1e-3f * (float)lane);
+  }
+  // distinct starting values keep the four chains distinct computations
+  f32x16 c0, c1, c2, c3;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    c0[e] = (float)e;
+    c1[e] = (float)(e + lane);
+    c2[e] = (float)(2 * e - lane);
+    c3[e] = (float)(3 * e + 1);
+  }
+  for (int it = 0; it < iters; ++it) {
+    c0 = mfma_bf16(a, b, c0);
+    c1 = mfma_bf16(a, b, c1);
+    c2 = mfma_bf16(a, b, c2);
+    c3 = mfma_bf16(a, b, c3);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += c0[e] + c1[e] + c2[e] + c3[e];
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 }  // namespace sla
+
+extern "C" sla_status sla_diag_mfma_rate(float* sink, int blocks, int iters, hipStream_t stream) {
+  if (!sink) return SLA_ERR_NULL;
+  if (blocks <= 0 || iters <= 0) return SLA_ERR_SHAPE;
+  hipLaunchKernelGGL(sla::mfma_rate_kernel, dim3(blocks), dim3(256), 0, stream, sink, iters);
+  return hipGetLastError() == hipSuccess ? SLA_OK : SLA_ERR_HIP;
+}
 
 extern "C" sla_status sla_diag_fp8_mfma(const uint8_t* a, const uint8_t* b, float* c_fp8,
                                         float* c_bf16, hipStream_t stream) {

@@ -26,7 +26,8 @@ EXPORTS = ("sla_workspace_size", "sla_route", "sla_forward", "sla_forward_fp8",
            "sla_kv_cache_size", "sla_kv_cache_workspace_size", "sla_kv_cache_update",
            "sla_cached_workspace_size", "sla_forward_cached", "sla_route_taylor",
            "sla_forward_taylor", "sla_forward_pisa", "sla_forward_cached_noalloc",
-           "sla_backward_workspace_size", "sla_backward", "sla_diag_fp8_mfma")
+           "sla_backward_workspace_size", "sla_backward", "sla_diag_fp8_mfma",
+           "sla_diag_mfma_rate")
 WS_REGIONS = {"q8": 0, "k8": 1, "v8": 2, "eq": 3, "ek": 4, "ev": 5, "scores": 6, "sc": 7, "zc": 8,
               "hbar": 9, "cent_hi": 10, "cent_lo": 11, "vsum": 12}
 # workspace layouts (sla_workspace_size / sla_workspace_region)
@@ -89,6 +90,8 @@ def _load() -> ctypes.CDLL:
     lib.sla_forward_cached.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sla_diag_fp8_mfma.argtypes = [vp, vp, vp, vp, vp]
     lib.sla_diag_fp8_mfma.restype = ctypes.c_int
+    lib.sla_diag_mfma_rate.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.sla_diag_mfma_rate.restype = ctypes.c_int
     lib.sla_backward_workspace_size.argtypes = [pp]
     lib.sla_backward_workspace_size.restype = sz
     lib.sla_backward.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -427,6 +430,30 @@ def sla_diag_fp8_mfma(a: torch.Tensor, b: torch.Tensor):
     if st != 0:
         raise SlaError(st, "sla_diag_fp8_mfma")
     return c8, c16
+
+
+def sla_diag_mfma_rate(device, blocks: int = 512, iters: int = 4096, repeats: int = 3) -> float:
+    """Diagnostic: the bf16 matrix-instruction rate (TFLOP/s) this GPU reaches: the median of
+    `repeats` timed launches of the throughput loop, after one untimed launch."""
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=device)
+    stream = _stream(torch.device(device))
+    flops = blocks * 16 * iters * 32768        # four waves, four products per iteration each
+
+    def launch():
+        st = library().sla_diag_mfma_rate(_ptr(sink), blocks, iters, stream)
+        if st != 0:
+            raise SlaError(st, "sla_diag_mfma_rate")
+    launch()
+    times = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    times.sort()
+    return flops / times[len(times) // 2] / 1e12
 
 
 # ----------------------------------------------------------------------------- Taylor router

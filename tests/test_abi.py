@@ -345,3 +345,13 @@ def test_pisa_validation(lib):
     assert fwd(ws=MISALIGNED) == 5 and fwd(idx=MISALIGNED) == 5
     assert fwd(prob_=prob(head_dim=96)) == 7
     assert fwd(prob_=prob(top_k=12)) == 4
+
+
+def test_mfma_rate_validation(lib):
+    """The throughput diagnostic rejects a NULL sink and empty launches before enqueuing."""
+    fn = lib.sla_diag_mfma_rate
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 512, 16, None) == 1                      # SLA_ERR_NULL
+    assert fn(ctypes.c_void_p(FAKE), 0, 16, None) == 2       # SLA_ERR_SHAPE
+    assert fn(ctypes.c_void_p(FAKE), 512, 0, None) == 2

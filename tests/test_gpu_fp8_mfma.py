@@ -45,3 +45,11 @@ def test_fp8_instruction_accumulation(sla, spread):
           f"sum|products| (mean {e8.mean():.2e}); bf16 instruction {e16.max():.2e}", flush=True)
     assert np.isfinite(c8.cpu().numpy()).all()
     assert e16.max() <= 2e-7                        # fp32 accumulation of exact products
+
+
+def test_mfma_rate_diagnostic(sla):
+    """The matrix-instruction throughput loop runs and reports a rate between a tenth of and the
+    published dense bf16 peak (2.5 PFLOP/s at 2.4 GHz)."""
+    tf = sla.sla_diag_mfma_rate("cuda", blocks=512, iters=1024)
+    print(f"bf16 32x32x16 matrix-instruction rate: {tf:.0f} TFLOP/s", flush=True)
+    assert 250.0 < tf <= 2500.0 * 1.02
