@@ -2,7 +2,8 @@
 forward forms Q K^T on the bf16 instruction over the E4M3 values and uses the fp8 one only for
 P.V). E4M3 operands whose products span many binades are multiplied on both instructions and
 compared with the exact float64 product; the bf16 instruction (exact operands, fp32
-accumulation) must be exact to fp32 rounding, the fp8 one is reported."""
+accumulation) must be exact to fp32 rounding, the fp8 one is reported. Also the bf16
+matrix-instruction throughput diagnostic that the bench's roofline is measured against."""
 import numpy as np
 import pytest
 
