@@ -21,7 +21,9 @@
 //                       row's log-sum-exp instead of mixing;
 //   bwd_query_kernel    per query block: O_l, D, dO_s (f16), dalpha partials, the linear
 //                       part of dQ, dS_c(i) (bf16 high and low parts, summary layout), dz_c(i);
-//   (complement, fp32)  G_j from the dS_c(i), roles of query and key blocks swapped;
+//   (complement, fp32)  G_j from the dS_c(i), roles of query and key blocks swapped (with at
+//                       most kFewBwdRows query blocks per head the key kernel sums each G_j
+//                       from the dS_c(i) itself instead);
 //   bwd_gz_kernel       gz_j;
 //   bwd_order_kernel    key-block tasks by number of routing query blocks, most first;
 //   bwd_key_kernel      per key block: dK, dV over the query blocks that selected it, plus
@@ -611,15 +613,45 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   // linear parts: dV^T += G_j^T relu(K)^T (M = c, K = r), dK_lin^T = G_j V^T (M = r, K = c),
   // with G_j as bf16 high and low parts (V G^T + gz nearly cancels, like the query side)
   __syncthreads();
-  const float* gtb = a.gt + ((size_t)bh * a.nbk + j) * D * D;
   uint16_t* Gs = smem;           // G_j^T [c][r], row swizzle (tr_nat gives G[r][c] fragments)
   uint16_t* Gl = smem + D * D;   // its low parts
-  for (int id = t; id < D * (D / 8); id += 128) {
-    const int rr = id / (D / 8), cc = id % (D / 8);
-    u32x4 hi, lo;
-    split8(gtb + (size_t)rr * D + cc * 8, hi, lo);
-    *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
-    *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
+  if (a.gt) {
+    const float* gtb = a.gt + ((size_t)bh * a.nbk + j) * D * D;
+    for (int id = t; id < D * (D / 8); id += 128) {
+      const int rr = id / (D / 8), cc = id % (D / 8);
+      u32x4 hi, lo;
+      split8(gtb + (size_t)rr * D + cc * 8, hi, lo);
+      *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
+      *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
+    }
+  } else {
+    // Few query blocks (no G_j region): G_j^T is the sum of dS_c(i)^T over the query blocks i
+    // that did not route j, each as its high plus low part in fp32, in ascending i; then
+    // split into bf16 high and low parts as above.
+    for (int id = t; id < D * (D / 8); id += 128) {
+      const int rr = id / (D / 8), cc = id % (D / 8);
+      const int f = rr * D + cc * 8;   // flattened [c][r] index, summary layout of 128-slices
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < a.nbq; ++i) {
+        if ((brow[i >> 5] >> (i & 31)) & 1u) continue;   // i routed j: j is not in its complement
+        const size_t o = (((size_t)bh * (D * D / 128) + (f >> 7)) * a.nbq + i) * 128 + (f & 127);
+        const u32x4 hv = *reinterpret_cast<const u32x4*>(a.dsc + o);
+        const u32x4 lv = *reinterpret_cast<const u32x4*>(a.dsclo + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] += bf16_lo(hv[e]) + bf16_lo(lv[e]);
+          x[2 * e + 1] += bf16_hi(hv[e]) + bf16_hi(lv[e]);
+        }
+      }
+      u32x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hi[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+        lo[e] = pack_bf16(x[2 * e] - bf16_lo(hi[e]), x[2 * e + 1] - bf16_hi(hi[e]));
+      }
+      *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
+      *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
+    }
   }
   __syncthreads();
   const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
@@ -629,8 +661,9 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
     lk[c] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      u32x4 gh, glo;
-      split8(gtb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h, gh, glo);
+      // G^T rows 32 c + l32, columns 16 s + 8 h .. +7, from the staged high and low parts
+      const u32x4 gh = *reinterpret_cast<const u32x4*>(Gs + swz<D>(32 * c + l32, 16 * s + 8 * h));
+      const u32x4 glo = *reinterpret_cast<const u32x4*>(Gl + swz<D>(32 * c + l32, 16 * s + 8 * h));
       const u32x4 kb = relu_bf16x8(kf[s]);
       dvt[c] = mfma_bf16(gh, kb, dvt[c]);
       dvt[c] = mfma_bf16(glo, kb, dvt[c]);
@@ -807,9 +840,11 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
                          ws, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_query_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
-  e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + bp.bitsT), a.nwq, s.nbk,
-                            s.nbq, 0, a.dsc, a.dsclo, const_cast<float*>(a.gt), st);
-  if (e != hipSuccess) return e;
+  if (a.gt) {   // else the key kernel sums each G_j from the few dS_c(i) itself
+    e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + bp.bitsT), a.nwq, s.nbk,
+                              s.nbq, 0, a.dsc, a.dsclo, const_cast<float*>(a.gt), st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd_gz_kernel<D>, dim3(s.BH * ((s.nbk + kGzBlocks - 1) / kGzBlocks)),
                      dim3(D), 0, st, a);
   hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, st,
@@ -845,7 +880,7 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
   a.dsc = reinterpret_cast<uint16_t*>(ws + bp.dsc);
   a.dsclo = reinterpret_cast<uint16_t*>(ws + bp.dsclo);
   a.dzc = reinterpret_cast<float*>(ws + bp.dzc);
-  a.gt = reinterpret_cast<const float*>(ws + bp.gt);
+  a.gt = s.nbq <= kFewBwdRows ? nullptr : reinterpret_cast<const float*>(ws + bp.gt);
   a.gz = reinterpret_cast<float*>(ws + bp.gz);
   a.dapart = reinterpret_cast<float*>(ws + bp.dapart);
   a.order = reinterpret_cast<const int32_t*>(ws + bp.order);

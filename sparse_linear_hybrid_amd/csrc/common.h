@@ -348,6 +348,9 @@ inline Plan make_plan(const sla_problem& p) {
 
 // Workspace of the backward (sla_backward): the forward's per-block layout (key/value pass,
 // complement, bitmap), then the backward's own regions.
+// The backward for at most this many query blocks per head forms each key block's G_j in the
+// key kernel from the few dS_c(i) instead of materialising every G_j (no G_j region).
+constexpr int kFewBwdRows = 8;
 struct BwdPlan {
   int nwq;                                      // 32-bit words of a query-block bitmap row
   size_t bitsT, counts, sblo, scf, os, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, order,
@@ -370,7 +373,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   b.dsc = take(BH * nbq * D * D * 2);           // dS_c(i)^T, bf16 high part, summary layout
   b.dsclo = take(BH * nbq * D * D * 2);         // and its low part
   b.dzc = take(BH * nbq * D * 4);
-  b.gt = take(BH * nbk * D * D * 4);            // G_j^T fp32
+  b.gt = take(s.nbq <= kFewBwdRows ? 0 : BH * nbk * D * D * 4);   // G_j^T fp32
   b.gz = take(BH * nbk * D * 4);
   b.dapart = take(BH * nbq * D * 4);
   b.order = take(BH * nbk * 4);                 // key-block task order of the key kernel

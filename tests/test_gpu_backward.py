@@ -49,6 +49,11 @@ CASES = [
     (1, 2, 130, 400, 128, 0, "normal", "f32"),      # nothing routed: linear branch alone
     (1, 1, 190, 300, 128, 5, "smooth", "f32"),      # every block routed: no linear branch
     (1, 2, 320, 448, 128, 3, "smooth", "bf16"),     # bf16 upstream gradient
+    # at most 8 query blocks per head (all the cases above): the key kernel sums each G_j
+    # from the dS_c(i) itself; more: G_j from the transposed complement
+    (1, 2, 128, 64 * 40 - 9, 128, 3, "normal", "f32"),  # 2 query blocks over 40 key blocks
+    (1, 2, 670, 700, 128, 3, "smooth", "f32"),      # 11 query blocks, ragged
+    (1, 1, 64 * 9, 64 * 12, 64, 4, "normal", "f32"),  # 9 query blocks, d = 64
 ]
 
 
