@@ -15,7 +15,10 @@
 // Kernels, in launch order:
 //   bwd_bits_kernel     routed-block bitmaps of both orientations from the index lists;
 //   (key/value pass)    S_j as bf16 high and low parts, z_j, z_tot and the f16 copy of V;
-//   (complement, fp32)  S_c(i) = sum of the unselected S_j, high and low parts summed in fp32;
+//   (complement, fp32)  S_c(i) = sum of the unselected S_j, high and low parts summed in fp32
+//                       (with at most kFewBwdRows query blocks per head selecting at most half
+//                       the key blocks: a key/value pass that keeps S_tot instead of every
+//                       S_j, and S_c(i) = S_tot - the selected S_j in fp32);
 //                       z_c(i);
 //   (sparse kernel)     the exact branch of the forward again, saving O_s (fp32) and each
 //                       row's log-sum-exp instead of mixing;
@@ -827,13 +830,22 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
                      reinterpret_cast<uint32_t*>(ws + s.selbits),
                      reinterpret_cast<uint32_t*>(ws + bp.bitsT),
                      reinterpret_cast<int32_t*>(ws + bp.counts), s.nbq, s.nbk, s.k, nwk, a.nwq);
-  uint16_t* sblo = reinterpret_cast<uint16_t*>(ws + bp.sblo);
-  hipError_t e = launch_kv_summary(s, a.k, a.v, nullptr, ws, st, false, sblo);
-  if (e != hipSuccess) return e;
-  e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + s.selbits), nwk, s.nbq,
-                            s.nbk, s.k, reinterpret_cast<const uint16_t*>(ws + s.sblk), sblo,
-                            const_cast<float*>(a.sc), st);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (bwd_few_sc(s)) {   // S_c(i) = S_tot - the selected blocks' summaries
+    e = launch_kv_totals_blocks(s, a.k, a.v, ws, st);
+    if (e != hipSuccess) return e;
+    e = launch_sc_subtract(s, a.k, a.v, a.idx, reinterpret_cast<const float*>(ws + s.stot),
+                           const_cast<float*>(a.sc), st);
+    if (e != hipSuccess) return e;
+  } else {
+    uint16_t* sblo = reinterpret_cast<uint16_t*>(ws + bp.sblo);
+    e = launch_kv_summary(s, a.k, a.v, nullptr, ws, st, false, sblo);
+    if (e != hipSuccess) return e;
+    e = launch_complement_f32(s, reinterpret_cast<const uint32_t*>(ws + s.selbits), nwk, s.nbq,
+                              s.nbk, s.k, reinterpret_cast<const uint16_t*>(ws + s.sblk), sblo,
+                              const_cast<float*>(a.sc), st);
+    if (e != hipSuccess) return e;
+  }
   e = launch_complement_z(s, a.idx, ws, st);
   if (e != hipSuccess) return e;
   e = launch_sparse_save(s, a.q, a.k, a.idx, const_cast<float*>(a.os), const_cast<float*>(a.lse),
@@ -880,7 +892,7 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
   a.dsc = reinterpret_cast<uint16_t*>(ws + bp.dsc);
   a.dsclo = reinterpret_cast<uint16_t*>(ws + bp.dsclo);
   a.dzc = reinterpret_cast<float*>(ws + bp.dzc);
-  a.gt = s.nbq <= kFewBwdRows ? nullptr : reinterpret_cast<const float*>(ws + bp.gt);
+  a.gt = bwd_few_g(s) ? nullptr : reinterpret_cast<const float*>(ws + bp.gt);
   a.gz = reinterpret_cast<float*>(ws + bp.gz);
   a.dapart = reinterpret_cast<float*>(ws + bp.dapart);
   a.order = reinterpret_cast<const int32_t*>(ws + bp.order);

@@ -349,8 +349,12 @@ inline Plan make_plan(const sla_problem& p) {
 // Workspace of the backward (sla_backward): the forward's per-block layout (key/value pass,
 // complement, bitmap), then the backward's own regions.
 // The backward for at most this many query blocks per head forms each key block's G_j in the
-// key kernel from the few dS_c(i) instead of materialising every G_j (no G_j region).
+// key kernel from the few dS_c(i) instead of materialising every G_j (no G_j region); when
+// those query blocks also select at most half the key blocks, S_c(i) is S_tot minus the
+// selected blocks' summaries (no per-block S_j and no low parts).
 constexpr int kFewBwdRows = 8;
+inline bool bwd_few_g(const Plan& s) { return s.nbq <= kFewBwdRows; }
+inline bool bwd_few_sc(const Plan& s) { return s.nbq <= kFewBwdRows && 2 * s.k <= s.nbk; }
 struct BwdPlan {
   int nwq;                                      // 32-bit words of a query-block bitmap row
   size_t bitsT, counts, sblo, scf, os, lse, dr, dos, dsc, dsclo, dzc, gt, gz, dapart, order,
@@ -364,7 +368,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   b.bitsT = take(BH * nbk * (size_t)b.nwq * 4);
   b.counts = take(BH * nbk * 4);                // query blocks that routed each key block
-  b.sblo = take(BH * nbk * D * D * 2);          // S_j - bf16(S_j), bf16, summary layout
+  b.sblo = take(bwd_few_sc(s) ? 0 : BH * nbk * D * D * 2);   // S_j - bf16(S_j), bf16
   b.scf = take(BH * nbq * D * D * 4);           // S_c^T fp32
   b.os = take(BH * (size_t)s.nq * D * 4);        // O_s fp32, saved by the sparse kernel
   b.lse = take(BH * nq64 * 4);
@@ -373,7 +377,7 @@ inline BwdPlan make_bwd_plan(const Plan& s) {
   b.dsc = take(BH * nbq * D * D * 2);           // dS_c(i)^T, bf16 high part, summary layout
   b.dsclo = take(BH * nbq * D * D * 2);         // and its low part
   b.dzc = take(BH * nbq * D * 4);
-  b.gt = take(s.nbq <= kFewBwdRows ? 0 : BH * nbk * D * D * 4);   // G_j^T fp32
+  b.gt = take(bwd_few_g(s) ? 0 : BH * nbk * D * D * 4);   // G_j^T fp32
   b.gz = take(BH * nbk * D * 4);
   b.dapart = take(BH * nbq * D * 4);
   b.order = take(BH * nbk * 4);                 // key-block task order of the key kernel

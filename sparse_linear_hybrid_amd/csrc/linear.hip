@@ -61,8 +61,10 @@ constexpr int kSlice = 128;
 // to E4M3 exactly as the quantiser does (block absmax over the valid tokens, power-of-two
 // scale, one rounding), from the tiles it has staged in LDS, and writes K8, the V8 tiles and
 // the block exponents (Fp8Out).
+// NOSJ (the few-query-block backward, bf16 inputs): no S_j is stored; the pass keeps the d x d
+// chunk totals instead (z_j, the f16 V copy and the z partials as usual).
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false,
-          bool LO = false>
+          bool LO = false, bool NOSJ = false>
 __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
@@ -73,9 +75,11 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
   static_assert(!PISA || BLOCKS, "the piecewise pass is a full-forward pass");
   static_assert(!FP8 || (BLOCKS && !PISA && sizeof(T) == 2), "fused E4M3: bf16 full forward");
   static_assert(!LO || (BLOCKS && !PISA && !FP8), "low parts of S_j: plain full pass");
+  static_assert(!NOSJ || (BLOCKS && !PISA && !FP8 && !LO), "totals instead of S_j: plain pass");
   // The SLA2 forward's complement sums the unselected S_j itself, so its pass keeps no d x d
-  // chunk totals (only the z partials); the cache update and the piecewise pass do.
-  constexpr bool TOTALS = !BLOCKS || PISA;
+  // chunk totals (only the z partials); the cache update, the piecewise pass and the
+  // few-query-block backward do.
+  constexpr bool TOTALS = !BLOCKS || PISA || NOSJ;
   constexpr int LS = D + 8;                  // padded LDS row (elements)
   constexpr int TPR = D / 8, RPP = 256 / TPR;
   constexpr int CPT = 64 * TPR / 256;        // 16-byte chunks per thread per tensor
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     // accumulator tiles are live at a time (fewer registers: three workgroups per CU instead
     // of two, more loads in flight). Half 0 is staged over the K tile once every wave holds its
     // A fragments, half 1 over the V tile after every wave's last product.
-    constexpr bool HALVES = BLOCKS && !PISA && !FP8 && !LO && NT == 4;
+    constexpr bool HALVES = BLOCKS && !PISA && !FP8 && !LO && !NOSJ && NT == 4;
     if constexpr (HALVES) {
       f32x16 acc2[2];
       auto product = [&](int half) __attribute__((always_inline)) {
@@ -343,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
           accs[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), accs[u]);
         if constexpr (TOTALS) part[u] += accs[u];
       }
-      if constexpr (BLOCKS && !PISA) {
+      if constexpr (BLOCKS && !PISA && !NOSJ) {
         // S_j^T[c][r] (bf16) goes out in whole 2D-byte rows: staged over the K and V tiles
         // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
         // Lane column c = 32 nt + l32 holds rows r in runs of 4.
@@ -877,6 +881,99 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
 }
 
 template <int D>
+static hipError_t launch_kv_totals_blocks_T(const Plan& s, const void* k, const void* v, char* ws,
+                                            hipStream_t st) {
+  const dim3 grid(s.nchunk, s.BH);
+  float* spart = reinterpret_cast<float*>(ws + s.spart);
+  float* zpart = reinterpret_cast<float*>(ws + s.zpart);
+  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, false, false, false, true>),
+                     grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, nullptr,
+                     nullptr, (size_t)0, (size_t)0, reinterpret_cast<uint16_t*>(ws + s.v16), nullptr,
+                     nullptr, reinterpret_cast<float*>(ws + s.zblk), spart, zpart, s.nkv, s.nbk, 0,
+                     0, nullptr, nullptr, nullptr, 0, Fp8Out{});
+  hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
+                     zpart, reinterpret_cast<float*>(ws + s.stot),
+                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f, 0);
+  return hipGetLastError();
+}
+
+// S_c(i)^T = S_tot^T - sum_{j in sel(i)} S_j^T in fp32 (SPLA page, section 2.2: the linear state
+// of the unselected blocks is the total minus that of the selected ones), one workgroup per
+// query block; S_j = relu(K_j)^T V_j on bf16 MFMA with fp32 accumulation (the products of the
+// key/value pass), summed over the selected blocks in the same accumulators. The next selected
+// block's K and V rows load into registers while the current one is multiplied.
+template <int D>
+__global__ __launch_bounds__(256) void sc_subtract_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const int32_t* __restrict__ idx,
+                                                          const float* __restrict__ stot,
+                                                          float* __restrict__ sc, int nkv, int nbq,
+                                                          int topk) {
+  constexpr int LS = D + 8, TPR = D / 8, CPT = 64 * TPR / 256, NT = D / 32;
+  constexpr int TPW = NT * NT / 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[64 * LS];
+  const int bh = blockIdx.x / nbq, i = blockIdx.x % nbq;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int mt = NT == 4 ? w : (w >> 1);   // this wave's 32-row strip r of S_j
+  const uint16_t* kb = k + (size_t)bh * nkv * D;
+  const uint16_t* vb = v + (size_t)bh * nkv * D;
+  const int32_t* sel = idx + ((size_t)bh * nbq + i) * topk;
+  u32x4 kraw[CPT], vraw[CPT];
+  auto load = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = t + 256 * u, r = cidx / TPR, c8 = cidx % TPR;
+      const int row = j * kBlock + r;
+      const bool ok = row < nkv;               // padded keys: zero K and V
+      const size_t off = (size_t)(ok ? row : 0) * D + c8 * 8;
+      kraw[u] = ok ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
+      vraw[u] = ok ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
+    }
+  };
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+  if (topk > 0) load(sel[0]);
+  for (int e = 0; e < topk; ++e) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int cidx = t + 256 * u, r = cidx / TPR, c8 = cidx % TPR;
+      *reinterpret_cast<u32x4*>(&Ks[r * LS + c8 * 8]) = kraw[u];
+      *reinterpret_cast<u32x4*>(&Vs[r * LS + c8 * 8]) = vraw[u];
+    }
+    __syncthreads();
+    if (e + 1 < topk) load(sel[e + 1]);
+    u32x4 af[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) af[s4] = relu_bf16x8(frag_tr(Ks, LS, 32 * mt, 16 * s4));
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int nt = NT == 4 ? u : (w & 1);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc[u] = mfma_bf16(af[s4], frag_tr(Vs, LS, 32 * nt, 16 * s4), acc[u]);
+    }
+    __syncthreads();   // the tiles are rewritten next
+  }
+  // element 4 q + e of tile u: r = 32 mt + 8 q + 4 h + e, c = 32 nt + l32 ([c][r] layouts)
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int c = 32 * (NT == 4 ? u : (w & 1)) + l32;
+    const float* tot = stot + ((size_t)bh * D + c) * D;
+    float* dst = sc + (((size_t)bh * nbq + i) * D + c) * D;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 32 * mt + 8 * q + 4 * h;
+      const f32x4 tv = *reinterpret_cast<const f32x4*>(tot + r);
+      *reinterpret_cast<f32x4*>(dst + r) =
+          f32x4{tv[0] - acc[u][4 * q], tv[1] - acc[u][4 * q + 1], tv[2] - acc[u][4 * q + 2],
+                tv[3] - acc[u][4 * q + 3]};
+    }
+  }
+}
+
+template <int D>
 static hipError_t launch_pisa_stats_T(const Plan& s, const void* k, const void* v, const float* pk,
                                       char* ws, hipStream_t st) {
   double* kt = reinterpret_cast<double*>(ws + s.kt);
@@ -937,6 +1034,26 @@ hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const 
   if (sblk_lo && (fp8 || !s.in_bf16)) return hipErrorInvalidValue;
   if (s.D == 128) return launch_kv_summary_T<128>(s, k, v, pk, ws, st, fp8, sblk_lo);
   return launch_kv_summary_T<64>(s, k, v, pk, ws, st, fp8, sblk_lo);
+}
+
+hipError_t launch_kv_totals_blocks(const Plan& s, const void* k, const void* v, char* ws,
+                                   hipStream_t st) {
+  if (!s.in_bf16) return hipErrorInvalidValue;
+  if (s.D == 128) return launch_kv_totals_blocks_T<128>(s, k, v, ws, st);
+  return launch_kv_totals_blocks_T<64>(s, k, v, ws, st);
+}
+
+hipError_t launch_sc_subtract(const Plan& s, const void* k, const void* v, const int32_t* idx,
+                              const float* stot, float* sc, hipStream_t st) {
+  if (!s.in_bf16) return hipErrorInvalidValue;
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(s.BH * s.nbq), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
+                       idx, stot, sc, s.nkv, s.nbq, s.k);
+  };
+  if (s.D == 128) go(sc_subtract_kernel<128>);
+  else go(sc_subtract_kernel<64>);
+  return hipGetLastError();
 }
 
 hipError_t launch_pisa_stats(const Plan& s, const void* k, const void* v, const float* pk,
