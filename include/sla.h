@@ -284,7 +284,9 @@ sla_status sla_forward_cached(const sla_problem* p, const void* q, const void* k
  * SLA_ERR_WORKSPACE when workspace_bytes < sla_backward_workspace_size(p), SLA_ERR_ALIGN for
  * an unaligned workspace. The workspace (caller-owned, device) holds the forward's per-block
  * summaries and the backward's intermediates: about 2.3 GB at B = 1, H = 12, n = 32768,
- * d = 128. */
+ * d = 128. With at most 8 query blocks per head no per-key-block G_j is kept (and, when they
+ * also select at most half the key blocks, no per-block summaries either): 15.9 GB at B = 4,
+ * H = 32, 64 queries over 131072 keys, d = 128. */
 size_t sla_backward_workspace_size(const sla_problem* p);
 
 sla_status sla_backward(const sla_problem* p, const void* q, const void* k, const void* v,
