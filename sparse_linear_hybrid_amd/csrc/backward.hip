@@ -30,7 +30,8 @@
 //   bwd_gz_kernel       gz_j;
 //   bwd_order_kernel    key-block tasks by number of routing query blocks, most first;
 //   bwd_key_kernel      per key block: dK, dV over the query blocks that selected it, plus
-//                       the linear parts;
+//                       the linear parts (with few query blocks: only the routed key blocks;
+//                       bwd_key_linear_kernel does the others);
 //   bwd_dq_kernel       per query block: the exact branch's dQ, added to the linear part;
 //   bwd_dalpha_kernel   dalpha from the per-query-block partials (fixed order).
 // The linear gradients are differences of nearly equal terms (g S_c^T against h z_c, and
@@ -70,6 +71,7 @@ struct BwdArgs {
   float* gz;                // [BH][nbk][D]
   float* dapart;            // [BH][nbq][D]
   const int32_t* order;     // [BH*nbk]: key-block tasks, most routed query blocks first
+  const int32_t* counts;    // [BH*nbk]: query blocks that routed each key block
   float* dq;                // [BH][nq][D]
   float* dk;                // [BH][nkv][D]
   float* dv;                // [BH][nkv][D]
@@ -488,6 +490,39 @@ __global__ __launch_bounds__(1024) void bwd_order_kernel(const int32_t* __restri
 }
 
 // ----------------------------------------------------------------------------- per key block
+// Few query blocks (no G_j region): G_j^T is the sum of dS_c(i)^T over the query blocks i that
+// did not route j (brow: j's row of the transposed bitmap; nullptr: every query block), each
+// as its high plus low part in fp32, in ascending i; then split into bf16 high and low parts,
+// staged into Gs / Gl (row swizzle) by the workgroup's 128 threads.
+template <int D>
+__device__ __forceinline__ void stage_g_sum(const BwdArgs& a, int bh, const uint32_t* brow,
+                                            uint16_t* Gs, uint16_t* Gl) {
+  for (int id = threadIdx.x; id < D * (D / 8); id += 128) {
+    const int rr = id / (D / 8), cc = id % (D / 8);
+    const int f = rr * D + cc * 8;   // flattened [c][r] index, summary layout of 128-slices
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < a.nbq; ++i) {
+      if (brow && ((brow[i >> 5] >> (i & 31)) & 1u)) continue;   // i routed j
+      const size_t o = (((size_t)bh * (D * D / 128) + (f >> 7)) * a.nbq + i) * 128 + (f & 127);
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(a.dsc + o);
+      const u32x4 lv = *reinterpret_cast<const u32x4*>(a.dsclo + o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] += bf16_lo(hv[e]) + bf16_lo(lv[e]);
+        x[2 * e + 1] += bf16_hi(hv[e]) + bf16_hi(lv[e]);
+      }
+    }
+    u32x4 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hi[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+      lo[e] = pack_bf16(x[2 * e] - bf16_lo(hi[e]), x[2 * e + 1] - bf16_hi(hi[e]));
+    }
+    *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
+    *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
+  }
+}
+
 // Two waves, wave w owns keys 32 w .. 32 w + 31 of key block j. Products are oriented so that
 // the score accumulator (rows: queries, lane: key) feeds the dV^T and dK^T products directly.
 template <int D>
@@ -496,6 +531,8 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE > 2 * D * D ? 4 * TILE : 2 * D * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][64], dr_s[2][64];
   const int task = a.order[blockIdx.x];
+  // few query blocks: the key blocks no query block routed are bwd_key_linear_kernel's
+  if (!a.gt && a.counts[task] == 0) return;
   const int bh = task / a.nbk, j = task % a.nbk;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int key = j * kBlock + 32 * wv + l32;
@@ -628,33 +665,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
     }
   } else {
-    // Few query blocks (no G_j region): G_j^T is the sum of dS_c(i)^T over the query blocks i
-    // that did not route j, each as its high plus low part in fp32, in ascending i; then
-    // split into bf16 high and low parts as above.
-    for (int id = t; id < D * (D / 8); id += 128) {
-      const int rr = id / (D / 8), cc = id % (D / 8);
-      const int f = rr * D + cc * 8;   // flattened [c][r] index, summary layout of 128-slices
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int i = 0; i < a.nbq; ++i) {
-        if ((brow[i >> 5] >> (i & 31)) & 1u) continue;   // i routed j: j is not in its complement
-        const size_t o = (((size_t)bh * (D * D / 128) + (f >> 7)) * a.nbq + i) * 128 + (f & 127);
-        const u32x4 hv = *reinterpret_cast<const u32x4*>(a.dsc + o);
-        const u32x4 lv = *reinterpret_cast<const u32x4*>(a.dsclo + o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[2 * e] += bf16_lo(hv[e]) + bf16_lo(lv[e]);
-          x[2 * e + 1] += bf16_hi(hv[e]) + bf16_hi(lv[e]);
-        }
-      }
-      u32x4 hi, lo;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hi[e] = pack_bf16(x[2 * e], x[2 * e + 1]);
-        lo[e] = pack_bf16(x[2 * e] - bf16_lo(hi[e]), x[2 * e + 1] - bf16_hi(hi[e]));
-      }
-      *reinterpret_cast<u32x4*>(Gs + swz<D>(rr, cc * 8)) = hi;
-      *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
-    }
+    stage_g_sum<D>(a, bh, brow, Gs, Gl);
   }
   __syncthreads();
   const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
@@ -697,6 +708,79 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       *reinterpret_cast<f32x4*>(dkr + r0) = ko;
       *reinterpret_cast<f32x4*>(dvr + r0) = vo;
     }
+}
+
+// Few query blocks per head: the key blocks that no query block routed only have the linear
+// gradients, all with the same G (the sum of every dS_c(i)) within a head. A workgroup takes
+// kLinBlocks consecutive key blocks of one head, stages that G once and computes dV = phi(K)
+// G and dK = (V G^T + gz) (.) 1[k > 0] for its unrouted blocks, as bwd_key_kernel's linear
+// part does (the routed ones are bwd_key_kernel's).
+constexpr int kLinBlocks = 16;
+template <int D>
+__global__ __launch_bounds__(128) void bwd_key_linear_kernel(BwdArgs a) {
+  constexpr int KS = D / 16, CT = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[D * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Gl[D * D];
+  const int chunks = (a.nbk + kLinBlocks - 1) / kLinBlocks;
+  const int bh = blockIdx.x / chunks, j0 = (blockIdx.x % chunks) * kLinBlocks;
+  const int j1 = min(j0 + kLinBlocks, a.nbk);
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
+  const int32_t* cnt = a.counts + (size_t)bh * a.nbk;
+  bool any = false;
+  for (int j = j0; j < j1; ++j) any = any || cnt[j] == 0;
+  if (!any) return;   // uniform: every block here was routed
+  stage_g_sum<D>(a, bh, nullptr, Gs, Gl);
+  __syncthreads();
+  for (int j = j0; j < j1; ++j) {
+    if (cnt[j] != 0) continue;   // uniform
+    const int key = j * kBlock + 32 * wv + l32;
+    const bool kvalid = key < a.nkv;
+    const uint16_t* krow = a.k + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
+    const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
+    u32x4 kf[KS], vf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(krow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+      vf[s] = kvalid ? *reinterpret_cast<const u32x4*>(vrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+    }
+    f32x16 dvt[CT], lk[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      dvt[c] = lk[c] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 gh = *reinterpret_cast<const u32x4*>(Gs + swz<D>(32 * c + l32, 16 * s + 8 * h));
+        const u32x4 glo = *reinterpret_cast<const u32x4*>(Gl + swz<D>(32 * c + l32, 16 * s + 8 * h));
+        const u32x4 kb = relu_bf16x8(kf[s]);
+        dvt[c] = mfma_bf16(gh, kb, dvt[c]);
+        dvt[c] = mfma_bf16(glo, kb, dvt[c]);
+        lk[c] = mfma_bf16(tr_nat<D>(Gs, 32 * c, 16 * s), vf[s], lk[c]);
+        lk[c] = mfma_bf16(tr_nat<D>(Gl, 32 * c, 16 * s), vf[s], lk[c]);
+      }
+    }
+    if (!kvalid) continue;
+    const float* gzb = a.gz + ((size_t)bh * a.nbk + j) * D;
+    float* dkr = a.dk + ((size_t)bh * a.nkv + key) * D;
+    float* dvr = a.dv + ((size_t)bh * a.nkv + key) * D;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int r0 = 32 * c + 8 * g4 + 4 * h;
+        const f32x4 z = *reinterpret_cast<const f32x4*>(gzb + r0);
+        const u32x2 kw = *reinterpret_cast<const u32x2*>(krow + r0);
+        const float kv[4] = {bf16_lo(kw[0]), bf16_hi(kw[0]), bf16_lo(kw[1]), bf16_hi(kw[1])};
+        f32x4 ko, vo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ix = 4 * g4 + e;
+          ko[e] = kv[e] > 0.f ? lk[c][ix] + z[e] : 0.f;
+          vo[e] = dvt[c][ix];
+        }
+        *reinterpret_cast<f32x4*>(dkr + r0) = ko;
+        *reinterpret_cast<f32x4*>(dvr + r0) = vo;
+      }
+  }
 }
 
 // ----------------------------------------------------------------------------- dQ of the exact branch
@@ -863,6 +947,9 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
                      reinterpret_cast<const int32_t*>(ws + bp.counts), s.BH * s.nbk, s.nbq,
                      const_cast<int32_t*>(a.order));
   hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
+  if (!a.gt)
+    hipLaunchKernelGGL(bwd_key_linear_kernel<D>,
+                       dim3((s.nbk + kLinBlocks - 1) / kLinBlocks * s.BH), dim3(128), 0, st, a);
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
   return hipGetLastError();
 }
@@ -896,6 +983,7 @@ hipError_t launch_backward(const Plan& s, const void* q, const void* k, const vo
   a.gz = reinterpret_cast<float*>(ws + bp.gz);
   a.dapart = reinterpret_cast<float*>(ws + bp.dapart);
   a.order = reinterpret_cast<const int32_t*>(ws + bp.order);
+  a.counts = reinterpret_cast<const int32_t*>(ws + bp.counts);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
