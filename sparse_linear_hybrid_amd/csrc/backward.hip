@@ -28,7 +28,8 @@
 //                       most kFewBwdRows query blocks per head the key kernel sums each G_j
 //                       from the dS_c(i) itself instead);
 //   bwd_gz_kernel       gz_j;
-//   bwd_order_kernel    key-block tasks by number of routing query blocks, most first;
+//   bwd_order_kernel    key-block tasks by number of routing query blocks, most first (with
+//                       few query blocks, bwd_routed_kernel lists the routed ones instead);
 //   bwd_key_kernel      per key block: dK, dV over the query blocks that selected it, plus
 //                       the linear parts (with few query blocks: only the routed key blocks;
 //                       bwd_key_linear_kernel does the others);
@@ -489,15 +490,48 @@ __global__ __launch_bounds__(1024) void bwd_order_kernel(const int32_t* __restri
     order[atomicAdd(&bins[min(counts[task], nbin - 1)], 1)] = task;
 }
 
+// Few query blocks per head: the key kernel's tasks are the routed key blocks only, at most
+// cap = min(nbk, nbq k) per head (each query block routes at most k). One workgroup per head
+// lists them in index order at order[bh cap ..] and fills the rest of its cap slots with -1.
+__global__ __launch_bounds__(256) void bwd_routed_kernel(const int32_t* __restrict__ counts,
+                                                         int nbk, int cap,
+                                                         int32_t* __restrict__ order) {
+  __shared__ int wsum[4];
+  const int bh = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int32_t* cnt = counts + (size_t)bh * nbk;
+  int32_t* out = order + (size_t)bh * cap;
+  int base = 0;
+  for (int j0 = 0; j0 < nbk; j0 += 256) {
+    const int j = j0 + t;
+    const bool routed = j < nbk && cnt[j] > 0;
+    const unsigned long long m = __ballot(routed);
+    if (lane == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int off = base + __popcll(m & ((1ull << lane) - 1ull)), tot = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      off += q < w ? wsum[q] : 0;
+      tot += wsum[q];
+    }
+    if (routed && off < cap) out[off] = bh * nbk + j;
+    base += tot;
+    __syncthreads();   // wsum is rewritten next round
+  }
+  for (int p = base + t; p < cap; p += 256) out[p] = -1;
+}
+
 // ----------------------------------------------------------------------------- per key block
 // Few query blocks (no G_j region): G_j^T is the sum of dS_c(i)^T over the query blocks i that
 // did not route j (brow: j's row of the transposed bitmap; nullptr: every query block), each
 // as its high plus low part in fp32, in ascending i; then split into bf16 high and low parts,
-// staged into Gs / Gl (row swizzle) by the workgroup's 128 threads.
-template <int D>
+// staged into Gs / Gl (row swizzle) by the workgroup's NT threads.
+template <int D, int NT>
 __device__ __forceinline__ void stage_g_sum(const BwdArgs& a, int bh, const uint32_t* brow,
                                             uint16_t* Gs, uint16_t* Gl) {
-  for (int id = threadIdx.x; id < D * (D / 8); id += 128) {
+  static_assert(D * (D / 8) % NT == 0, "whole rounds of ids");
+#pragma unroll 4
+  for (int u = 0; u < D * (D / 8) / NT; ++u) {
+    const int id = threadIdx.x + u * NT;
     const int rr = id / (D / 8), cc = id % (D / 8);
     const int f = rr * D + cc * 8;   // flattened [c][r] index, summary layout of 128-slices
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -531,8 +565,9 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE > 2 * D * D ? 4 * TILE : 2 * D * D];
   __shared__ __attribute__((aligned(16))) float lse_s[2][64], dr_s[2][64];
   const int task = a.order[blockIdx.x];
-  // few query blocks: the key blocks no query block routed are bwd_key_linear_kernel's
-  if (!a.gt && a.counts[task] == 0) return;
+  // few query blocks: the routed key blocks only, -1 past a head's last one (the key blocks
+  // no query block routed are bwd_key_linear_kernel's)
+  if (task < 0) return;
   const int bh = task / a.nbk, j = task % a.nbk;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
   const int key = j * kBlock + 32 * wv + l32;
@@ -665,7 +700,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
     }
   } else {
-    stage_g_sum<D>(a, bh, brow, Gs, Gl);
+    stage_g_sum<D, 128>(a, bh, brow, Gs, Gl);
   }
   __syncthreads();
   const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
@@ -714,72 +749,187 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
 // gradients, all with the same G (the sum of every dS_c(i)) within a head. A workgroup takes
 // kLinBlocks consecutive key blocks of one head, stages that G once and computes dV = phi(K)
 // G and dK = (V G^T + gz) (.) 1[k > 0] for its unrouted blocks, as bwd_key_kernel's linear
-// part does (the routed ones are bwd_key_kernel's).
+// part does (the routed ones are bwd_key_kernel's). Four waves (two per SIMD with two
+// workgroups per CU) take the 32-key halves of those blocks in turn. The epilogue reads gz
+// from LDS and k > 0 from the K fragments in registers: its only memory accesses are the
+// stores, so no wait on them stalls the next item.
 constexpr int kLinBlocks = 16;
 template <int D>
-__global__ __launch_bounds__(128) void bwd_key_linear_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_key_linear_kernel(BwdArgs a) {
   constexpr int KS = D / 16, CT = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Gs[D * D];
   __shared__ __attribute__((aligned(16))) uint16_t Gl[D * D];
+  __shared__ __attribute__((aligned(16))) float zs[kLinBlocks * D];   // gz of the blocks here
+  __shared__ int items[2 * kLinBlocks];
+  __shared__ int nitems;
+  static_assert(kLinBlocks <= 64, "one ballot lists the blocks");
   const int chunks = (a.nbk + kLinBlocks - 1) / kLinBlocks;
   const int bh = blockIdx.x / chunks, j0 = (blockIdx.x % chunks) * kLinBlocks;
   const int j1 = min(j0 + kLinBlocks, a.nbk);
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
-  const int32_t* cnt = a.counts + (size_t)bh * a.nbk;
-  bool any = false;
-  for (int j = j0; j < j1; ++j) any = any || cnt[j] == 0;
-  if (!any) return;   // uniform: every block here was routed
-  stage_g_sum<D>(a, bh, nullptr, Gs, Gl);
+  if (wv == 0) {   // the halves of the unrouted blocks, in order
+    const int j = j0 + lane;
+    const bool un = j < j1 && a.counts[(size_t)bh * a.nbk + j] == 0;
+    const unsigned long long m = __ballot(un);
+    if (un) {
+      const int pos = __popcll(m & ((1ull << lane) - 1ull));
+      items[2 * pos] = 2 * j;
+      items[2 * pos + 1] = 2 * j + 1;
+    }
+    if (lane == 0) nitems = 2 * __popcll(m);
+  }
+  for (int e = t; e < (j1 - j0) * D; e += 256)
+    zs[e] = a.gz[((size_t)bh * a.nbk + j0) * D + e];
   __syncthreads();
-  for (int j = j0; j < j1; ++j) {
-    if (cnt[j] != 0) continue;   // uniform
-    const int key = j * kBlock + 32 * wv + l32;
-    const bool kvalid = key < a.nkv;
-    const uint16_t* krow = a.k + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
-    const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
-    u32x4 kf[KS], vf[KS];
+  const int n = __builtin_amdgcn_readfirstlane(nitems);
+  if (n == 0) return;   // uniform: every block here was routed
+  stage_g_sum<D, 256>(a, bh, nullptr, Gs, Gl);
+  __syncthreads();
+  // Item it covers keys 32 items[it] .. + 31 (block items[it] / 2, half items[it] % 2), of
+  // which nrows(it) exist. Its loads and stores go through buffer resources that end at the
+  // last existing key: rows past it read as zero and are not written, with no branch (a
+  // branch around a load or store leaves the compiler's wait counts at their most cautious).
+  // (item, wave and count are wave-uniform: read as such, the resources stay scalar)
+  auto first = [&](int it) { return min(32 * __builtin_amdgcn_readfirstlane(items[it]), a.nkv); };
+  auto nrows = [&](int it) { return min(a.nkv - first(it), 32); };
+  const uint16_t* kbase = a.k + (size_t)bh * a.nkv * D;
+  const uint16_t* vbase = a.v + (size_t)bh * a.nkv * D;
+  // this lane's 8-channel pieces 16 s + 8 h .. of its key's row of K or V
+  auto load = [&](const uint16_t* base, int it, u32x4* f) {
+    const auto rs = buf_rsrc(base + (size_t)first(it) * D, nrows(it) * D * 2);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      kf[s] = kvalid ? *reinterpret_cast<const u32x4*>(krow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
-      vf[s] = kvalid ? *reinterpret_cast<const u32x4*>(vrow + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
-    }
-    f32x16 dvt[CT], lk[CT];
+    for (int s = 0; s < KS; ++s)
+      f[s] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (l32 * D + 16 * s + 8 * h) * 2, 0, 0));
+  };
+  // LDS element offsets of this lane's G fragments. Row reads (G^T row 32 c + l32, columns
+  // 16 s + 8 h ..): the swizzle XORs the chunk with row % (D / 8), the same for every c, so
+  // c is a constant offset and s picks one of KS bases. Transposing reads (tr_nat at x0 =
+  // 32 c, k0 = 16 s): rows 16 s + 8 (g / 2) + L / 4 (+ 4) keep row % 16 for every s, so s is a
+  // constant offset and (c, upper four rows) picks one of 2 CT bases.
+  static_assert(D / 8 <= 16, "row % chunks is independent of the 16-row step");
+  static_assert(CT % 2 == 0, "slices go in pairs");
+  int rb[KS], tb[CT][2];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      dvt[c] = lk[c] = f32x16{};
+  for (int s = 0; s < KS; ++s) rb[s] = swz<D>(l32, 16 * s + 8 * h);
+  {
+    const int g = lane >> 4, L = lane & 15;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 gh = *reinterpret_cast<const u32x4*>(Gs + swz<D>(32 * c + l32, 16 * s + 8 * h));
-        const u32x4 glo = *reinterpret_cast<const u32x4*>(Gl + swz<D>(32 * c + l32, 16 * s + 8 * h));
-        const u32x4 kb = relu_bf16x8(kf[s]);
-        dvt[c] = mfma_bf16(gh, kb, dvt[c]);
-        dvt[c] = mfma_bf16(glo, kb, dvt[c]);
-        lk[c] = mfma_bf16(tr_nat<D>(Gs, 32 * c, 16 * s), vf[s], lk[c]);
-        lk[c] = mfma_bf16(tr_nat<D>(Gl, 32 * c, 16 * s), vf[s], lk[c]);
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        tb[c][u] = swz<D>(8 * (g >> 1) + (L >> 2) + 4 * u, 32 * c + 16 * (g & 1) + 4 * (L & 3));
+  }
+  auto tr_frag = [&](const uint16_t* M, int c, int s) {
+    const u32x2 lo = lds_read_tr16(M + tb[c][0] + 16 * s * D);
+    const u32x2 hi = lds_read_tr16(M + tb[c][1] + 16 * s * D);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // Per item: dV^T = G^T relu(K)^T first (K only), then dK^T = G V^T (V only), so that V's
+  // load is in flight during the dV half; the next item's K loads during this one.
+  // k > 0 of this lane's key at channels 16 s + 8 h + e (bit 8 s + e); the partner lane
+  // (lane ^ 32) holds the channels 16 s + 8 (1 - h) + e
+  auto kmask = [&](const u32x4* f) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m |= (uint64_t)(bf16_lo(f[s][e]) > 0.f) << (8 * s + 2 * e);
+        m |= (uint64_t)(bf16_hi(f[s][e]) > 0.f) << (8 * s + 2 * e + 1);
       }
-    }
-    if (!kvalid) continue;
-    const float* gzb = a.gz + ((size_t)bh * a.nbk + j) * D;
-    float* dkr = a.dk + ((size_t)bh * a.nkv + key) * D;
-    float* dvr = a.dv + ((size_t)bh * a.nkv + key) * D;
+    return m;
+  };
+  // K of an item and its mask are both ready at the loop head on every path into it (the
+  // mask consumes the load), so the compiler's wait there does not hold for the stores
+  // issued after the next item's K load.
+  const int w0 = __builtin_amdgcn_readfirstlane(wv);
+  u32x4 kf[KS];
+  uint64_t own = 0;
+  if (w0 < n) {
+    load(kbase, w0, kf);
+    own = kmask(kf);
+  }
+  for (int it = w0; it < n; it += 4) {
+    // keeps the G fragment reads inside the loop (hoisted, they would not fit in registers)
+    asm volatile("" ::: "memory");
+    const uint64_t other = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(own >> 32), 32, 64) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)own, 32, 64);
+    // bit 16 c + 4 g4 + e: k > 0 at output row 32 c + 8 g4 + 4 h + e of the epilogue (16-channel
+    // group 2 c + g4 / 2, half g4 & 1, element 4 h + e within it)
+    uint64_t need = 0;
 #pragma unroll
     for (int c = 0; c < CT; ++c)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int r0 = 32 * c + 8 * g4 + 4 * h;
-        const f32x4 z = *reinterpret_cast<const f32x4*>(gzb + r0);
-        const u32x2 kw = *reinterpret_cast<const u32x2*>(krow + r0);
-        const float kv[4] = {bf16_lo(kw[0]), bf16_hi(kw[0]), bf16_lo(kw[1]), bf16_hi(kw[1])};
-        f32x4 ko, vo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ix = 4 * g4 + e;
-          ko[e] = kv[e] > 0.f ? lk[c][ix] + z[e] : 0.f;
-          vo[e] = dvt[c][ix];
-        }
-        *reinterpret_cast<f32x4*>(dkr + r0) = ko;
-        *reinterpret_cast<f32x4*>(dvr + r0) = vo;
+        const uint64_t pm = ((g4 & 1) == h) ? own : other;
+        need |= ((pm >> (8 * (2 * c + (g4 >> 1)) + 4 * h)) & 15u) << (16 * c + 4 * g4);
       }
+    u32x4 kb[KS], vf[KS], kn[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kb[s] = relu_bf16x8(kf[s]);
+    load(vbase, it, vf);
+    load(kbase, min(it + 4, n - 1), kn);   // the last item's K again after the last item
+    const int jl = (__builtin_amdgcn_readfirstlane(items[it]) >> 1) - j0;
+    const size_t o = (size_t)bh * a.nkv + first(it);
+    const auto rdk = buf_rsrc(a.dk + o * D, nrows(it) * D * 4);
+    const auto rdv = buf_rsrc(a.dv + o * D, nrows(it) * D * 4);
+    // dV^T rows 32 c .. 32 c + 31, two slices at a time
+#pragma unroll
+    for (int c0 = 0; c0 < CT; c0 += 2) {
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s % 2 == 0) asm volatile("" ::: "memory");   // two 16-channel groups in flight
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int c = c0 + u;
+          const u32x4 gh = *reinterpret_cast<const u32x4*>(Gs + rb[s] + 32 * c * D);
+          const u32x4 glo = *reinterpret_cast<const u32x4*>(Gl + rb[s] + 32 * c * D);
+          acc[u] = mfma_bf16(gh, kb[s], acc[u]);
+          acc[u] = mfma_bf16(glo, kb[s], acc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int r0 = 32 * (c0 + u) + 8 * g4 + 4 * h;
+          const f32x4 vo{acc[u][4 * g4], acc[u][4 * g4 + 1], acc[u][4 * g4 + 2], acc[u][4 * g4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vo), rdv,
+                                                 (l32 * D + r0) * 4, 0, 0);
+        }
+    }
+    own = kmask(kn);   // the next item's
+    // dK^T rows (V G^T + gz) (.) 1[k > 0], two slices at a time
+#pragma unroll
+    for (int c0 = 0; c0 < CT; c0 += 2) {
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s % 2 == 0) asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          acc[u] = mfma_bf16(tr_frag(Gs, c0 + u, s), vf[s], acc[u]);
+          acc[u] = mfma_bf16(tr_frag(Gl, c0 + u, s), vf[s], acc[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c = c0 + u, r0 = 32 * c + 8 * g4 + 4 * h;
+          const f32x4 z = *reinterpret_cast<const f32x4*>(zs + jl * D + r0);
+          const uint32_t bits = (uint32_t)(need >> (16 * c + 4 * g4)) & 15u;
+          f32x4 ko;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ko[e] = (bits >> e) & 1u ? acc[u][4 * g4 + e] + z[e] : 0.f;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ko), rdk,
+                                                 (l32 * D + r0) * 4, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = kn[s];
   }
 }
 
@@ -919,7 +1069,7 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
     e = launch_kv_totals_blocks(s, a.k, a.v, ws, st);
     if (e != hipSuccess) return e;
     e = launch_sc_subtract(s, a.k, a.v, a.idx, reinterpret_cast<const float*>(ws + s.stot),
-                           const_cast<float*>(a.sc), st);
+                           const_cast<float*>(a.sc), ws, st);
     if (e != hipSuccess) return e;
   } else {
     uint16_t* sblo = reinterpret_cast<uint16_t*>(ws + bp.sblo);
@@ -943,13 +1093,22 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
   }
   hipLaunchKernelGGL(bwd_gz_kernel<D>, dim3(s.BH * ((s.nbk + kGzBlocks - 1) / kGzBlocks)),
                      dim3(D), 0, st, a);
-  hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, st,
-                     reinterpret_cast<const int32_t*>(ws + bp.counts), s.BH * s.nbk, s.nbq,
-                     const_cast<int32_t*>(a.order));
-  hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
-  if (!a.gt)
+  if (a.gt) {
+    hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, st,
+                       reinterpret_cast<const int32_t*>(ws + bp.counts), s.BH * s.nbk, s.nbq,
+                       const_cast<int32_t*>(a.order));
+    hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
+  } else {   // few query blocks: routed key blocks in bwd_key_kernel, the others linear only
+    const int cap = s.nbk < s.nbq * s.k ? s.nbk : s.nbq * s.k;
+    if (cap > 0) {
+      hipLaunchKernelGGL(bwd_routed_kernel, dim3(s.BH), dim3(256), 0, st,
+                         reinterpret_cast<const int32_t*>(ws + bp.counts), s.nbk, cap,
+                         const_cast<int32_t*>(a.order));
+      hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * cap), dim3(128), 0, st, a);
+    }
     hipLaunchKernelGGL(bwd_key_linear_kernel<D>,
-                       dim3((s.nbk + kLinBlocks - 1) / kLinBlocks * s.BH), dim3(128), 0, st, a);
+                       dim3((s.nbk + kLinBlocks - 1) / kLinBlocks * s.BH), dim3(256), 0, st, a);
+  }
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
   return hipGetLastError();
 }

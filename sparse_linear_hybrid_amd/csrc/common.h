@@ -96,6 +96,11 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
   return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
+// The same as a compiler buffer resource, for its buffer load and store builtins: loads at
+// offsets >= bytes return 0 and stores there are dropped, without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
 // LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

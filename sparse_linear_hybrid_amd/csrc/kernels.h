@@ -17,12 +17,12 @@ hipError_t launch_kv_summary(const Plan& s, const void* k, const void* v, const 
                              hipStream_t st, bool fp8 = false, uint16_t* sblk_lo = nullptr);
 
 // Few-query-block backward (bf16): the key/value pass with S_tot and z_tot instead of the
-// per-block S_j (z_j and the f16 V copy as usual), and S_c(i)^T = S_tot^T - sum of the selected
-// S_j^T in fp32 from the selected K and V tiles.
+// per-block S_j and the f16 V copy (z_j as usual), and S_c(i)^T = S_tot^T - sum of the selected
+// S_j^T in fp32 from the selected K and V tiles, which also writes the selected blocks' f16 V.
 hipError_t launch_kv_totals_blocks(const Plan& s, const void* k, const void* v, char* ws,
                                    hipStream_t st);
 hipError_t launch_sc_subtract(const Plan& s, const void* k, const void* v, const int32_t* idx,
-                              const float* stot, float* sc, hipStream_t st);
+                              const float* stot, float* sc, char* ws, hipStream_t st);
 
 // Linear branch, part 2: complement = total - selected, per query block.
 hipError_t launch_complement(const Plan& s, const int32_t* idx, char* ws, hipStream_t st);

@@ -61,8 +61,9 @@ constexpr int kSlice = 128;
 // to E4M3 exactly as the quantiser does (block absmax over the valid tokens, power-of-two
 // scale, one rounding), from the tiles it has staged in LDS, and writes K8, the V8 tiles and
 // the block exponents (Fp8Out).
-// NOSJ (the few-query-block backward, bf16 inputs): no S_j is stored; the pass keeps the d x d
-// chunk totals instead (z_j, the f16 V copy and the z partials as usual).
+// NOSJ (the few-query-block backward, bf16 inputs): no S_j and no f16 copy of V are stored
+// (sc_subtract_kernel writes that of the selected blocks); the pass keeps the d x d chunk
+// totals instead (z_j and the z partials as usual).
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false,
           bool LO = false, bool NOSJ = false>
 __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       }
       *reinterpret_cast<u32x4*>(&Ks[r * LS + c8 * 8]) = kw;
       *reinterpret_cast<u32x4*>(&Vs[r * LS + c8 * 8]) = vw;
-      if constexpr (BLOCKS) {
+      if constexpr (BLOCKS && !NOSJ) {
         u32x4 v16w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v16w[e] = f16_sat_pack(vf[2 * e], vf[2 * e + 1]);
@@ -880,20 +881,24 @@ static hipError_t launch_kv_summary_T(const Plan& s, const void* k, const void* 
   return hipGetLastError();
 }
 
+// The few-query-block totals pass takes kTotalsChunk key blocks per workgroup: a quarter of
+// the usual pass's d x d partial totals to write and reduce (they fit in its partials region).
+constexpr int kTotalsChunk = 4 * kSummaryChunk;
 template <int D>
 static hipError_t launch_kv_totals_blocks_T(const Plan& s, const void* k, const void* v, char* ws,
                                             hipStream_t st) {
-  const dim3 grid(s.nchunk, s.BH);
+  const int nchunk = (s.nbk + kTotalsChunk - 1) / kTotalsChunk;
+  const dim3 grid(nchunk, s.BH);
   float* spart = reinterpret_cast<float*>(ws + s.spart);
   float* zpart = reinterpret_cast<float*>(ws + s.zpart);
-  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kSummaryChunk, false, false, false, true>),
+  hipLaunchKernelGGL((kv_summary_kernel<uint16_t, D, true, kTotalsChunk, false, false, false, true>),
                      grid, dim3(256), 0, st, (const uint16_t*)k, (const uint16_t*)v, nullptr,
-                     nullptr, (size_t)0, (size_t)0, reinterpret_cast<uint16_t*>(ws + s.v16), nullptr,
-                     nullptr, reinterpret_cast<float*>(ws + s.zblk), spart, zpart, s.nkv, s.nbk, 0,
-                     0, nullptr, nullptr, nullptr, 0, Fp8Out{});
+                     nullptr, (size_t)0, (size_t)0, nullptr, nullptr, nullptr,
+                     reinterpret_cast<float*>(ws + s.zblk), spart, zpart, s.nkv, s.nbk, 0, 0,
+                     nullptr, nullptr, nullptr, 0, Fp8Out{});
   hipLaunchKernelGGL((reduce_totals_kernel<D>), dim3(D * D / 32, s.BH), dim3(256), 0, st, spart,
                      zpart, reinterpret_cast<float*>(ws + s.stot),
-                     reinterpret_cast<float*>(ws + s.ztot), s.nchunk, 0, nullptr, 0.f, 0);
+                     reinterpret_cast<float*>(ws + s.ztot), nchunk, 0, nullptr, 0.f, 0);
   return hipGetLastError();
 }
 
@@ -901,14 +906,17 @@ static hipError_t launch_kv_totals_blocks_T(const Plan& s, const void* k, const 
 // of the unselected blocks is the total minus that of the selected ones), one workgroup per
 // query block; S_j = relu(K_j)^T V_j on bf16 MFMA with fp32 accumulation (the products of the
 // key/value pass), summed over the selected blocks in the same accumulators. The next selected
-// block's K and V rows load into registers while the current one is multiplied.
+// block's K and V rows load into registers while the current one is multiplied. Each selected
+// block's f16 copy of V (padded rows zero) goes to v16 [BH][nbk*64][D] on the way; a block
+// that several query blocks select is written with the same values by each.
 template <int D>
 __global__ __launch_bounds__(256) void sc_subtract_kernel(const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ idx,
                                                           const float* __restrict__ stot,
-                                                          float* __restrict__ sc, int nkv, int nbq,
-                                                          int topk) {
+                                                          float* __restrict__ sc,
+                                                          uint16_t* __restrict__ v16, int nkv,
+                                                          int nbk, int nbq, int topk) {
   constexpr int LS = D + 8, TPR = D / 8, CPT = 64 * TPR / 256, NT = D / 32;
   constexpr int TPW = NT * NT / 4;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * LS];
@@ -936,11 +944,16 @@ __global__ __launch_bounds__(256) void sc_subtract_kernel(const uint16_t* __rest
   for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
   if (topk > 0) load(sel[0]);
   for (int e = 0; e < topk; ++e) {
+    uint16_t* v16b = v16 + ((size_t)bh * nbk + sel[e]) * kBlock * D;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = t + 256 * u, r = cidx / TPR, c8 = cidx % TPR;
       *reinterpret_cast<u32x4*>(&Ks[r * LS + c8 * 8]) = kraw[u];
       *reinterpret_cast<u32x4*>(&Vs[r * LS + c8 * 8]) = vraw[u];
+      u32x4 hw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hw[q] = f16_sat_pack(bf16_lo(vraw[u][q]), bf16_hi(vraw[u][q]));
+      *reinterpret_cast<u32x4*>(v16b + (size_t)r * D + c8 * 8) = hw;
     }
     __syncthreads();
     if (e + 1 < topk) load(sel[e + 1]);
@@ -1044,12 +1057,13 @@ hipError_t launch_kv_totals_blocks(const Plan& s, const void* k, const void* v, 
 }
 
 hipError_t launch_sc_subtract(const Plan& s, const void* k, const void* v, const int32_t* idx,
-                              const float* stot, float* sc, hipStream_t st) {
+                              const float* stot, float* sc, char* ws, hipStream_t st) {
   if (!s.in_bf16) return hipErrorInvalidValue;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(s.BH * s.nbq), dim3(256), 0, st,
                        reinterpret_cast<const uint16_t*>(k), reinterpret_cast<const uint16_t*>(v),
-                       idx, stot, sc, s.nkv, s.nbq, s.k);
+                       idx, stot, sc, reinterpret_cast<uint16_t*>(ws + s.v16), s.nkv, s.nbk,
+                       s.nbq, s.k);
   };
   if (s.D == 128) go(sc_subtract_kernel<128>);
   else go(sc_subtract_kernel<64>);
