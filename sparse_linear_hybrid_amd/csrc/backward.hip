@@ -13,7 +13,8 @@
 //            blocks swapped) and gz_j likewise: dV += phi(K_j) G_j,
 //            dK += (V_j G_j^T + gz_j) (.) 1[k > 0].
 // Kernels, in launch order:
-//   bwd_bits_kernel     routed-block bitmaps of both orientations from the index lists;
+//   bwd_bits_kernel     routed-block bitmaps of both orientations and the per-key-block
+//                       counts from the index lists (into rows bwd_clear_kernel cleared);
 //   (key/value pass)    S_j as bf16 high and low parts, z_j, z_tot and the f16 copy of V;
 //   (complement, fp32)  S_c(i) = sum of the unselected S_j, high and low parts summed in fp32
 //                       (with at most kFewBwdRows query blocks per head selecting at most half
@@ -142,7 +143,19 @@ __device__ __forceinline__ u32x4 row_frag(const uint16_t* M, int row, int col) {
 
 // ----------------------------------------------------------------------------- bitmaps
 // Row i of selbits: bit j set iff key block j is routed to query block i; row j of bitsT:
-// bit i set iff j is routed to i. One workgroup per (batch*head, row).
+// bit i set iff j is routed to i; counts[j]: how many query blocks routed j. bitsT and counts
+// start cleared (bwd_clear_kernel); one workgroup per (batch*head, query block) builds its
+// selbits row in LDS, then ORs its bit into the bitsT row of each key block it routed and
+// adds one to that block's count (integer OR and sum: the same whatever the order).
+__global__ __launch_bounds__(256) void bwd_clear_kernel(uint32_t* __restrict__ bitsT,
+                                                        size_t nwords,
+                                                        int32_t* __restrict__ counts,
+                                                        size_t ncounts) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < nwords; e += stride) bitsT[e] = 0u;
+  for (size_t e = blockIdx.x * 256 + threadIdx.x; e < ncounts; e += stride) counts[e] = 0;
+}
+
 __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict__ idx,
                                                        uint32_t* __restrict__ selbits,
                                                        uint32_t* __restrict__ bitsT,
@@ -150,41 +163,23 @@ __global__ __launch_bounds__(256) void bwd_bits_kernel(const int32_t* __restrict
                                                        int nbk, int topk, int nwk, int nwq) {
   extern __shared__ uint32_t wbits[];
   const int bh = blockIdx.y, row = blockIdx.x, t = threadIdx.x;
-  if (row < nbq) {   // forward orientation
-    for (int w = t; w < nwk; w += 256) wbits[w] = 0u;
-    __syncthreads();
-    const int32_t* sel = idx + ((size_t)bh * nbq + row) * topk;
-    for (int e = t; e < topk; e += 256) {
-      const int j = sel[e];
-      atomicOr(&wbits[j >> 5], 1u << (j & 31));
+  for (int w = t; w < nwk; w += 256) wbits[w] = 0u;
+  __syncthreads();
+  const int32_t* sel = idx + ((size_t)bh * nbq + row) * topk;
+  for (int e = t; e < topk; e += 256) {
+    const int j = sel[e];
+    atomicOr(&wbits[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  for (int w = t; w < nwk; w += 256) {
+    uint32_t word = wbits[w];
+    selbits[((size_t)bh * nbq + row) * nwk + w] = word;
+    while (word) {
+      const int j = 32 * w + __builtin_ctz(word);
+      word &= word - 1u;
+      atomicOr(&bitsT[((size_t)bh * nbk + j) * nwq + (row >> 5)], 1u << (row & 31));
+      atomicAdd(&counts[(size_t)bh * nbk + j], 1);
     }
-    __syncthreads();
-    for (int w = t; w < nwk; w += 256) selbits[((size_t)bh * nbq + row) * nwk + w] = wbits[w];
-  } else {           // transposed: key block j = row - nbq; binary search in each list
-    const int j = row - nbq;
-    if (t == 0) wbits[0] = 0u;
-    __syncthreads();
-    int mine = 0;
-    for (int w = t; w < nwq; w += 256) {
-      uint32_t word = 0u;
-      for (int b = 0; b < 32; ++b) {
-        const int i = 32 * w + b;
-        if (i >= nbq) break;
-        const int32_t* sel = idx + ((size_t)bh * nbq + i) * topk;
-        int lo = 0, hi = topk;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (sel[mid] < j) lo = mid + 1; else hi = mid;
-        }
-        if (lo < topk && sel[lo] == j) word |= 1u << b;
-      }
-      bitsT[((size_t)bh * nbk + j) * nwq + w] = word;
-      mine += __builtin_popcount(word);
-    }
-    // how many query blocks routed j (integer sum: the same whatever the order)
-    if (mine) atomicAdd(&wbits[0], (uint32_t)mine);
-    __syncthreads();
-    if (t == 0) counts[(size_t)bh * nbk + j] = (int32_t)wbits[0];
   }
 }
 
@@ -1059,7 +1054,10 @@ template <int D>
 hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* ws,
                              hipStream_t st) {
   const int nwk = s.nwords;
-  hipLaunchKernelGGL(bwd_bits_kernel, dim3(s.nbq + s.nbk, s.BH), dim3(256),
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3(512), dim3(256), 0, st,
+                     reinterpret_cast<uint32_t*>(ws + bp.bitsT), (size_t)s.BH * s.nbk * a.nwq,
+                     reinterpret_cast<int32_t*>(ws + bp.counts), (size_t)s.BH * s.nbk);
+  hipLaunchKernelGGL(bwd_bits_kernel, dim3(s.nbq, s.BH), dim3(256),
                      (size_t)(nwk > 1 ? nwk : 1) * 4, st, a.idx,
                      reinterpret_cast<uint32_t*>(ws + s.selbits),
                      reinterpret_cast<uint32_t*>(ws + bp.bitsT),
