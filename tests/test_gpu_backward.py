@@ -143,3 +143,52 @@ def test_backward_video95_sampled_dq(sla):
     err, rms = rel_err(np.concatenate(got), np.concatenate(want))
     print(f"video95 backward, sampled dq: max-abs/rms {err:.2e} (rms {rms:.3g})", flush=True)
     assert err <= TOL
+
+
+@pytest.mark.slow
+def test_backward_longctx_sampled_heads(sla):
+    """Full longctx shape (B=4, H=32, 64 queries over 131072 keys, d=128, top-k 64: one query
+    block per head, so the few-query-block path with its linear-only key kernel): every
+    gradient of head 5 in all four batches (hence dalpha[5] too) and of (b=2, h=20), all
+    131072 keys of each, against the oracle's per-head backward at the GPU's selection.
+    dK and dV hold two populations: the 4096 keys of the routed blocks carry the exact
+    branch's gradients, the other 126976 only the linear branch's, orders of magnitude
+    smaller. Each is held to its own RMS: TOL for the routed keys, TOL_LINEAR for the others
+    (the linear branch alone, as with top-k = 0)."""
+    from workloads import make_inputs, bf16_bits_to_f32
+    x = make_inputs("longctx")
+    p = x.problem
+    q, k, v, pq, pk, al = to_device(x)
+    _, idx = sla.sla_forward(q, k, v, pq, pk, al, p.top_k)
+    rng = np.random.default_rng(131)
+    dout = rng.standard_normal(q.shape).astype(np.float32)
+    dq, dk, dv, dal = sla.sla_backward(q, k, v, al, torch.from_numpy(dout).cuda(), idx)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    f64 = lambda a, b, h: bf16_bits_to_f32(a[b, h]).astype(np.float64)   # noqa: E731
+    ral = np.zeros(p.head_dim)
+    worst = {}
+    for b, h in ((0, 5), (1, 5), (2, 5), (3, 5), (2, 20)):
+        rq, rk, rv, ra = bw.backward_head(f64(x.q, b, h), f64(x.k, b, h), f64(x.v, b, h),
+                                          x.alpha[h].astype(np.float64), idx[b, h], p.block,
+                                          dout[b, h].astype(np.float64))
+        if h == 5:
+            ral += ra
+        routed = np.zeros(p.n_kv, dtype=bool)
+        for j in np.unique(idx[b, h]):
+            routed[p.block * j:p.block * (j + 1)] = True
+        checks = [("dq", dq[b, h].cpu().numpy(), rq)]
+        for name, got, ref in (("dk", dk[b, h], rk), ("dv", dv[b, h], rv)):
+            g = got.cpu().numpy()
+            checks += [(name + " routed", g[routed], ref[routed]),
+                       (name + " linear-only", g[~routed], ref[~routed])]
+        for name, got, ref in checks:
+            e, rms = rel_err(got, ref)
+            if e > worst.get(name, (0.0, 0.0))[0]:
+                worst[name] = (e, rms)
+    worst["dalpha"] = rel_err(dal[5].cpu().numpy(), ral)
+    print("longctx backward, sampled heads: " +
+          ", ".join(f"{n} {e:.2e} (rms {r:.3g})" for n, (e, r) in worst.items()), flush=True)
+    for name, (e, _) in worst.items():
+        tol = TOL_LINEAR if name.endswith("linear-only") else TOL
+        assert e <= tol, f"{name}: max-abs/rms {e:.3e}"
