@@ -141,6 +141,15 @@ __device__ __forceinline__ u32x4 row_frag(const uint16_t* M, int row, int col) {
   return *reinterpret_cast<const u32x4*>(M + (SWZV ? swzv<D>(row, col) : swz<D>(row, col)));
 }
 
+// Wait for every memory operation of this wave (loads into LDS included), then a workgroup
+// barrier. Unlike a wait written in asm, the compiler sees this one: no load is pending for
+// it afterwards, so it places no wait for the loop's register operands inside the loop,
+// where its count would also cover the next block's tile loads issued on each pass.
+__device__ __forceinline__ void drain_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 // ----------------------------------------------------------------------------- bitmaps
 // Row i of selbits: bit j set iff key block j is routed to query block i; row j of bitsT:
 // bit i set iff j is routed to i; counts[j]: how many query blocks routed j. bitsT and counts
@@ -582,10 +591,15 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
   for (int c = 0; c < CT; ++c) dvt[c] = dkt[c] = f32x16{};
   // Two slots of (Q tile, dO_s tile), both V-swizzled (row reads and vt_frag reads): the
   // next routed query block's tiles load straight into LDS while this one is multiplied.
+  // j's row of the transposed bitmap, staged in LDS (nwq words of dynamic shared memory) so
+  // that finding the next routed query block is no memory round trip inside the loop
   const uint32_t* brow = a.bitsT + ((size_t)bh * a.nbk + j) * a.nwq;
+  extern __shared__ uint32_t brow_s[];
+  for (int w = t; w < a.nwq; w += 128) brow_s[w] = brow[w];
+  __syncthreads();
   auto next_routed = [&](int from) -> int {   // first query block >= from that routed j, or -1
     for (int w = from >> 5; w < a.nwq; ++w) {
-      uint32_t word = brow[w];
+      uint32_t word = brow_s[w];
       if (w == (from >> 5)) word &= ~0u << (from & 31);
       if (word) return 32 * w + __builtin_ctz(word);
     }
@@ -606,7 +620,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       dr_s[0][t] = a.dr[rbase + i * kBlock + t];
     }
   }
-  barrier_vmem_lds_n<0>();
+  drain_barrier();
   int slot = 0;
   while (i >= 0) {
     const int inext = next_routed(i + 1);
@@ -676,7 +690,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       lse_s[slot ^ 1][t] = lnext;
       dr_s[slot ^ 1][t] = dnext;
     }
-    barrier_vmem_lds_n<0>();   // the next tiles and their rows' lse / D are in place
+    drain_barrier();   // the next tiles and their rows' lse / D are in place
     slot ^= 1;
     i = inext;
   }
@@ -695,7 +709,7 @@ __global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(Gl + swz<D>(rr, cc * 8)) = lo;
     }
   } else {
-    stage_g_sum<D, 128>(a, bh, brow, Gs, Gl);
+    stage_g_sum<D, 128>(a, bh, brow_s, Gs, Gl);
   }
   __syncthreads();
   const uint16_t* vrow = a.v + ((size_t)bh * a.nkv + (kvalid ? key : 0)) * D;
@@ -955,7 +969,12 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
   for (int c = 0; c < CT; ++c) dqt[c] = f32x16{};
   // Two slots of (K tile, V-swizzled: row reads and vt_frag reads; f16 V tile, row swizzle):
   // the next selected block's tiles load straight into LDS while this one is multiplied.
-  const int32_t* sel = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
+  // the selection, staged in LDS (topk words of dynamic shared memory) so that the next
+  // block's address is no memory round trip inside the loop
+  const int32_t* selg = a.idx + ((size_t)bh * a.nbq + iq) * a.topk;
+  extern __shared__ int32_t sel[];
+  for (int e = t; e < a.topk; e += 128) sel[e] = selg[e];
+  __syncthreads();
   auto stage = [&](int e, int slot) __attribute__((always_inline)) {
     const int j = sel[e];
     dma_tile<D, true, 2>(smem + 2 * slot * TILE, a.k + ((size_t)bh * a.nkv + (size_t)j * kBlock) * D,
@@ -964,7 +983,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
                           a.v16 + ((size_t)bh * a.nbk * kBlock + (size_t)j * kBlock) * D, kBlock);
   };
   if (a.topk > 0) stage(0, 0);
-  barrier_vmem_n<0>();
+  drain_barrier();
   int slot = 0;
   for (int e = 0; e < a.topk; ++e) {
     if (e + 1 < a.topk) stage(e + 1, slot ^ 1);
@@ -1009,7 +1028,7 @@ __global__ __launch_bounds__(128) void bwd_dq_kernel(BwdArgs a) {
         dqt[c] = mfma_bf16(ka, df[kk], dqt[c]);
         dqt[c] = mfma_bf16(ka, dl[kk], dqt[c]);
       }
-    barrier_vmem_n<0>();   // the next tiles have landed; this slot is free
+    drain_barrier();   // the next tiles have landed; this slot is free
     slot ^= 1;
   }
   if (!valid) return;
@@ -1095,19 +1114,21 @@ hipError_t launch_backward_T(const Plan& s, const BwdPlan& bp, BwdArgs a, char* 
     hipLaunchKernelGGL(bwd_order_kernel, dim3(1), dim3(1024), 0, st,
                        reinterpret_cast<const int32_t*>(ws + bp.counts), s.BH * s.nbk, s.nbq,
                        const_cast<int32_t*>(a.order));
-    hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), 0, st, a);
+    hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * s.nbk), dim3(128), (size_t)a.nwq * 4, st,
+                       a);
   } else {   // few query blocks: routed key blocks in bwd_key_kernel, the others linear only
     const int cap = s.nbk < s.nbq * s.k ? s.nbk : s.nbq * s.k;
     if (cap > 0) {
       hipLaunchKernelGGL(bwd_routed_kernel, dim3(s.BH), dim3(256), 0, st,
                          reinterpret_cast<const int32_t*>(ws + bp.counts), s.nbk, cap,
                          const_cast<int32_t*>(a.order));
-      hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * cap), dim3(128), 0, st, a);
+      hipLaunchKernelGGL(bwd_key_kernel<D>, dim3(s.BH * cap), dim3(128), (size_t)a.nwq * 4, st,
+                         a);
     }
     hipLaunchKernelGGL(bwd_key_linear_kernel<D>,
                        dim3((s.nbk + kLinBlocks - 1) / kLinBlocks * s.BH), dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), 0, st, a);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(s.BH * s.nbq), dim3(128), (size_t)s.k * 4, st, a);
   return hipGetLastError();
 }
 
