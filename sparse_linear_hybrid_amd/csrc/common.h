@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -241,15 +242,18 @@ __device__ __forceinline__ void e4m3x8(const float (&v)[8], int e, uint32_t& w0,
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[4], -e), ldexpf(v[5], -e), 0u, false);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(v[6], -e), ldexpf(v[7], -e), w1, true);
 }
-// 8 E4M3 bytes (w0, w1) as 8 bf16 values
+// 8 E4M3 bytes (w0, w1) as 8 bf16 values: the hardware conversion to fp32 is exact, and the
+// top 16 bits of the result are the same value in bf16 (E4M3 has at most 4 significant bits
+// and its exponent range lies inside bf16's).
 __device__ __forceinline__ u32x4 e4m3x8_as_bf16(uint32_t w0, uint32_t w1) {
-  u32x4 o;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    o[b] = e4m3_to_bf16((w0 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w0 >> (16 * b + 8)) & 0xffu) << 16);
-    o[2 + b] = e4m3_to_bf16((w1 >> (16 * b)) & 0xffu) | (e4m3_to_bf16((w1 >> (16 * b + 8)) & 0xffu) << 16);
-  }
-  return o;
+  // bytes 0, 1 (false) or 2, 3 (true) of w as two bf16 in one word
+  auto two = [](uint32_t w, auto hi) __attribute__((always_inline)) {
+    const auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, decltype(hi)::value);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  };
+  const std::false_type lo{};
+  const std::true_type hi{};
+  return u32x4{two(w0, lo), two(w0, hi), two(w1, lo), two(w1, hi)};
 }
 // Outputs of the E4M3 quantisation of K and V when the key/value pass does it (fp8 forward):
 // K8 [BH][nb*64][D] bf16-held, V8 tiles [BH][nb][D][64] bytes, block exponents [BH][nb].

@@ -37,10 +37,6 @@ hipError_t launch_sparse(const Plan& s, const void* q, const void* k, const int3
 hipError_t launch_sparse_save(const Plan& s, const void* q, const void* k, const int32_t* idx,
                               float* os, float* lse, char* ws, hipStream_t st);
 
-// Quantised branch: E4M3 copies of Q, K, V with power-of-two block exponents.
-hipError_t launch_quant(const Plan& s, const void* q, const void* k, const void* v, char* ws,
-                        hipStream_t st);
-
 // Quantised sparse branch (fp8 MFMA) with the same epilogue as launch_sparse.
 hipError_t launch_sparse_fp8(const Plan& s, const void* q, const int32_t* idx,
                              const float* alpha, void* o, char* ws, hipStream_t st);

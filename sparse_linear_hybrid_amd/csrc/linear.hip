@@ -58,9 +58,14 @@ __device__ __forceinline__ uint32_t f16_sat_pack(float a, float b) {
 constexpr int kSlice = 128;
 
 // FP8 (fp8 forward, bf16 inputs; needs BLOCKS): the pass also quantises each block of K and V
-// to E4M3 exactly as the quantiser does (block absmax over the valid tokens, power-of-two
-// scale, one rounding), from the tiles it has staged in LDS, and writes K8, the V8 tiles and
-// the block exponents (Fp8Out).
+// to E4M3 (SLA2 page, section 2.C) by the rule the quantised sparse kernel applies to Q: e =
+// the smallest integer with 448 2^e >= the block's absmax over its valid tokens (0 for an
+// all-zero block), x8 = E4M3(x 2^-e), one round-to-nearest-even of an exactly scaled value.
+// It works from the tiles it has staged in LDS and writes K8 ([BH][nbk*64][D], the E4M3 values
+// held as bf16, padded rows zero), the V8 tiles ([BH][nbk][D][64] bytes, channel-major, byte
+// 32 hh + slot of a channel holding key 32 (slot / 16) + 8 ((slot % 16) / 4) + 4 hh + slot % 4:
+// the order of the P8 operand of the P.V product) and the block exponents (Fp8Out). The f16
+// copy of V, which only the bf16 exact branch reads, is not written on this path.
 // NOSJ (the few-query-block backward, bf16 inputs): no S_j and no f16 copy of V are stored
 // (sc_subtract_kernel writes that of the selected blocks); the pass keeps the d x d chunk
 // totals instead (z_j and the z partials as usual).
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       }
       *reinterpret_cast<u32x4*>(&Ks[r * LS + c8 * 8]) = kw;
       *reinterpret_cast<u32x4*>(&Vs[r * LS + c8 * 8]) = vw;
-      if constexpr (BLOCKS && !NOSJ) {
+      if constexpr (BLOCKS && !NOSJ && !FP8) {   // the quantised branch reads V8 instead
         u32x4 v16w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v16w[e] = f16_sat_pack(vf[2 * e], vf[2 * e + 1]);

@@ -132,11 +132,9 @@ sla_status forward_impl(const sla_problem* p, const void* q, const void* k, cons
     return SLA_ERR_HIP;
   }
   if (!ok(mark(2 * SLA_STAGE_COMPLEMENT + 1))) return SLA_ERR_HIP;
+  // fp8: K and V were quantised by the key/value pass, and the quantised sparse kernel
+  // quantises Q itself, so the quantisation stage is empty on every path
   if (!ok(mark(2 * SLA_STAGE_QUANT))) return SLA_ERR_HIP;
-  // fp8: Q is quantised here; K and V already were, by the key/value pass (bf16 inputs)
-  if (mode == Fwd::kFp8 && !ok(launch_quant(s, q, s.in_bf16 ? nullptr : k,
-                                            s.in_bf16 ? nullptr : v, ws, stream)))
-    return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_QUANT + 1))) return SLA_ERR_HIP;
   if (!ok(mark(2 * SLA_STAGE_SPARSE))) return SLA_ERR_HIP;
   hipError_t e;

@@ -86,6 +86,14 @@ struct UnionWalk {
   // -1 past the end), so the per-step read is a readlane and any list reload, with its wait
   // on all outstanding loads, happens once per 64 steps.
   int uvec = -1, upos = 64;
+  // Quantised branch: each buffered entry's key-block exponents (e_K low 16 bits, e_V high,
+  // both signed) are gathered with the entries, so no step waits on a load of its own.
+  const int32_t* ekp = nullptr;
+  const int32_t* evp = nullptr;
+  int evec = 0, ex = 0;
+  __device__ __forceinline__ int exps(int j) const {
+    return (ekp[j] & 0xffff) | (evp[j] << 16);
+  }
   __device__ __forceinline__ void fill() {
     uvec = -1;
 #pragma unroll 1
@@ -94,11 +102,13 @@ struct UnionWalk {
       if (!next_direct(j, f)) break;     // lanes past the end of the walk stay -1
       uvec = (int)(threadIdx.x & 63) == i ? (j | (f << 24)) : uvec;
     }
+    if (ekp != nullptr) evec = uvec >= 0 ? exps(uvec & 0xffffff) : 0;
     upos = 0;
   }
   __device__ __forceinline__ bool next(int& j, int& flags) {
     if (upos == 64) fill();
     const int e = __builtin_amdgcn_readlane(uvec, upos);
+    if (ekp != nullptr) ex = __builtin_amdgcn_readlane(evec, upos);
     ++upos;
     j = e & 0xffffff;
     flags = e < 0 ? 0 : e >> 24;
@@ -117,10 +127,10 @@ struct SparseArgs {
   void* out;
   int nq, nkv, nbq, nbk, topk, H, ngroups, total;
   // quantised branch only
-  const uint16_t* q8;      // E4M3 values as bf16 [BH][nbq*64][D]
+  uint16_t* q8;            // E4M3 values of Q as bf16 [BH][nbq*64][D] (written here)
   const uint16_t* k8;      // E4M3 values as bf16 [BH][nbk*64][D]
   const uint8_t* v8;       // E4M3 [BH][nbk][D][64], keys in P8 slot order
-  const int32_t* eq;       // block exponents [BH][nbq]
+  int32_t* eq;             // Q's block exponents [BH][nbq] (written here)
   const int32_t* ek;       // [BH][nbk]
   const int32_t* ev;       // [BH][nbk]
   // piecewise epilogue only
@@ -163,10 +173,12 @@ __device__ __forceinline__ void load_split_bf16x8(const float* p, u32x4& hi, u32
 // SAVE (bf16 inputs, for the backward): instead of the linear apply and the mix, the
 // epilogue writes the exact branch's normalised output O_s (fp32, `out` [BH][n_q][D]) and each
 // row's log-sum-exp (`lse`).
-template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false, bool SAVE = false>
-__global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) {
+// The exact branch's body, shared by the bf16/fp32 kernel and the quantised one (FP8).
+template <typename T, int D, int QB, bool OUT_BF16, bool PISA, bool SAVE, bool FP8>
+__device__ __forceinline__ void sparse_attn_body(const SparseArgs& a) {
   constexpr bool SPLIT = sizeof(T) == 4;   // fp32 inputs: three-term bf16 product
   constexpr bool DMA = !SPLIT;             // bf16 inputs: K/V tiles go global -> LDS directly
+  static_assert(!FP8 || (DMA && !PISA && !SAVE), "quantised branch: bf16-input SLA2 forward");
   constexpr int NT = 128 * QB;             // threads
   constexpr int NW = 2 * QB;               // waves
   constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
@@ -175,6 +187,8 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   constexpr int CPT = SPLIT ? 64 * CH / NT : 1;   // chunks per thread per tile (register path)
   constexpr int KPW = 64 * D * 2 / 1024 / NW;     // 1-KB pieces per wave per tile (LDS DMA)
   constexpr int TILE = 64 * D;             // elements of one K or V tile
+  constexpr int VT = FP8 ? TILE / 2 : TILE;   // 16-bit elements of one V slot (V8: 1 byte each)
+  constexpr int VPW = FP8 ? D * 64 / 1024 / NW : KPW;   // 1-KB pieces per wave of a V tile
   // LDS DMA path: K ring of 3 tiles, then V ring of 2. Register path: K[2], V[2], Klo[2].
   __shared__ __attribute__((aligned(16))) uint16_t smem[(DMA ? 5 : 6) * TILE];
 
@@ -186,10 +200,14 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   const bool active = iq < a.nbq;
   const int qrow0 = iq * kBlock + 32 * (wv & 1);
   const T* qb_ptr = reinterpret_cast<const T*>(a.q) + (size_t)bh * a.nq * D;
-  const T* kb = reinterpret_cast<const T*>(a.k) + (size_t)bh * a.nkv * D;
+  // quantised branch: K8 (E4M3 values held as bf16) and V8 tiles of 64 padded key rows
+  const T* kb = FP8 ? reinterpret_cast<const T*>(a.k8) + (size_t)bh * a.nbk * kBlock * D
+                    : reinterpret_cast<const T*>(a.k) + (size_t)bh * a.nkv * D;
   const uint16_t* vb = a.v16 + (size_t)bh * a.nbk * kBlock * D;
+  const uint8_t* v8b = a.v8 + (size_t)bh * a.nbk * kBlock * D;
 
   // Q^T fragments (B operand): lane column q = qrow0 + l32, channels 16 s + 8 h .. +7
+  // (the quantised branch turns them into Q8 below and reloads Q for the epilogue)
   u32x4 qf[KS];
   u32x4 ql[SPLIT ? KS : 1];
   {
@@ -212,11 +230,56 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   // the selection lists load after Q, so that both round trips overlap
   UnionWalk<QB> walk;
   walk.init(a.idx, bh, a.nbq, grp, a.topk);
+  if constexpr (FP8) {
+    walk.ekp = a.ek + (size_t)bh * a.nbk;
+    walk.evp = a.ev + (size_t)bh * a.nbk;
+  }
+  // Quantised branch: Q's E4M3 block quantisation (SLA2 page, section 2.C) from the
+  // register-held fragments. e_Q is the smallest integer with 448 2^e_Q >= the query block's
+  // absmax over its valid tokens (0 for an all-zero block); Q8 = E4M3(Q 2^-e_Q), one
+  // round-to-nearest-even of an exactly scaled value, held as bf16 (exact). The two waves of
+  // a query block meet through LDS for the absmax. Q8 (rows past n_q zero) and e_Q are also
+  // written to the workspace.
+  int eq = 0;
+  if constexpr (FP8) {
+    // the last 128 bytes of the LDS array, which neither the tile rings nor the epilogue's
+    // staging reach (a separate array would take the footprint past two workgroups per CU)
+    float* const qmax_lds = reinterpret_cast<float*>(smem + 5 * TILE - 64);
+    static_assert(4 * TILE + 1024 <= 5 * TILE - 64, "ring and epilogue staging stay below");
+    float amax = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(qf[s][e])), fabsf(bf16_hi(qf[s][e]))));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if (lane == 0) qmax_lds[wv] = amax;
+    __syncthreads();
+    eq = e8m0_exponent(fmaxf(qmax_lds[2 * qb], qmax_lds[2 * qb + 1]));
+    uint16_t* q8row = a.q8 + ((size_t)bh * a.nbq * kBlock + (active ? qrow0 + l32 : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16_lo(qf[s][e]);
+        v[2 * e + 1] = bf16_hi(qf[s][e]);
+      }
+      uint32_t w0, w1;
+      e4m3x8(v, eq, w0, w1);
+      qf[s] = e4m3x8_as_bf16(w0, w1);
+      if (active) *reinterpret_cast<u32x4*>(q8row + 16 * s + 8 * h) = qf[s];
+    }
+    if (active && (wv & 1) == 0 && lane == 0)
+      a.eq[(size_t)bh * a.nbq + iq] = eq;
+  }
 
   f32x16 o[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) o[c] = f32x16{};
-  float m = kNegBig, l = 0.f;
+  // quantised branch: the running maximum is an integer, far below any logit at the start
+  float m = FP8 ? -16384.f : kNegBig, l = 0.f;
   const float qk_scale = kLog2e / sqrtf((float)D);
 
   // LDS DMA: wave w moves the 1-KB pieces p = KPW w .. KPW w + KPW - 1 of the swizzled tile
@@ -231,6 +294,13 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
     const int lr = lane / CH, pc = lane % CH;
     klane = (uint32_t)(lr * D * 2 + ((pc ^ lr) & (CH - 1)) * 16);
     vlane = (uint32_t)(lr * D * 2 + ((pc ^ swzv_f<D>(lr)) & (CH - 1)) * 16);
+    if constexpr (FP8) {
+      // V8 tile: D rows (channels) of 64 key bytes; 16-byte chunk c of row r sits at chunk
+      // c ^ ((r / 4) % 4), so that the 16 lanes of a fragment read (16 consecutive rows, one
+      // logical chunk) hit 16 distinct 16-byte bank groups. Lane l lands at row 16 p + l / 4,
+      // physical chunk l % 4 of piece p.
+      vlane = (uint32_t)((lane >> 2) * 64 + (((lane & 3) ^ ((lane >> 4) & 3)) * 16));
+    }
   }
   // j < 0: an absent tile; the loads then cover an empty range (no memory access) so that
   // every step issues the same number of loads, which the vmcnt waits below rely on.
@@ -250,10 +320,11 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   auto stage_v = [&](int j, uint16_t* slot, int u0, int u1)
                      __attribute__((always_inline)) {
     const int row0 = j < 0 ? 0 : j * kBlock;
-    const auto r = make_rsrc(vb + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D * 2));
+    const auto r = FP8 ? make_rsrc(v8b + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D))
+                       : make_rsrc(vb + (size_t)row0 * D, j < 0 ? 0u : (uint32_t)(kBlock * D * 2));
 #pragma unroll
     for (int u = u0; u < u1; ++u) {
-      const int pp = wvs * KPW + u;
+      const int pp = wvs * VPW + u;
       load_lds16(r, lds_addr(slot) + pp * 1024, (uint32_t)(pp * 1024) + vlane);
     }
   };
@@ -430,6 +501,104 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
         for (int c = 0; c < CT; ++c) o[c] = mfma_f16(vb[kk * CT + c], pf[2 + kk], o[c]);
     }
   };
+  // Quantised branch (SLA2 page, section 2.C), one routed tile of this wave:
+  //   S^T = K8 Q8^T on the bf16 MFMA over the E4M3 values (exact products, fp32 sums),
+  //   y = S 2^(eQ + eK) log2(e) / sqrt(d);
+  //   per (row, tile): T = floor(max y), P8 = E4M3(2^(y - T + 7)) in (0, 256);
+  //   O^T += 2^(T - 7 - m + eV) V8^T P8^T on the scaled fp8 MFMA 32x32x64, the power-of-two
+  //   weight applied through its E8M0 scale on P8.
+  // The logits stay off the fp8 MFMA: on gfx950 it keeps only about 12-13 significant bits
+  // when products of very different magnitude are summed, which the exponential turns into
+  // errors of several percent for logits of a few hundred; for P.V the same relative error
+  // stays about 1e-4 of sum p |v|. m is the row's running maximum kept on integers, so every
+  // rescale is an exact power of two; the row sum adds the unquantised probabilities. In the
+  // 32x32x64 MFMA each lane half holds 32 of the 64 reduction elements (the V8 rows are
+  // stored in that key order); the two 32-element scale blocks take their E8M0 scale from
+  // lanes x and x + 32, which always carry the same value here.
+  auto compute_tile_fp8 = [&](const uint16_t* Kt, const uint8_t* Vt, int j, int exw,
+                              auto&& ld) __attribute__((always_inline)) {
+    u32x4 ka[KS], kb2[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(l32, 16 * ks + 8 * h)]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kb2[ks] = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(32 + l32, 16 * ks + 8 * h)]);
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    ld(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sacc[0] = mfma_bf16(ka[ks], qf[ks], sacc[0]);
+    ld(1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sacc[1] = mfma_bf16(kb2[ks], qf[ks], sacc[1]);
+    // V8^T fragments: row 32 c + l32, key bytes 32 h .. 32 h + 31 (logical chunks 2h, 2h+1)
+    i32x8 vf[CT];
+    {
+      const int x = (l32 >> 2) & 3;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        const uint8_t* row = Vt + (32 * c + l32) * 64;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(row + (((2 * h) ^ x) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(row + (((2 * h + 1) ^ x) << 4));
+        vf[c] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+    }
+    ld(2);
+    const int ekj = (exw << 16) >> 16, evj = exw >> 16;
+    const float cj = ldexpf(qk_scale, eq + ekj);
+    if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
+          sacc[mt][e] = key < a.nkv ? sacc[mt][e] : -INFINITY;
+        }
+    }
+    float r = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[mt][e]);
+    r = fmaxf(r, swap_halves(r)) * cj;          // row max of y over the tile
+    const float tmax = floorf(r);
+    if (__ballot(r > m + kRescaleSlack)) {
+      const float mn = fmaxf(m, ceilf(r));
+      const float corr = ldexpf(1.f, (int)fmaxf(m - mn, -200.f));
+      l *= corr;
+#pragma unroll
+      for (int c = 0; c < CT; ++c) o[c] *= corr;
+      m = mn;
+    }
+    // P8 = E4M3(2^(y - T + 7)); slot 16 mt + e of this lane half holds accumulator element e
+    // of key tile half mt
+    const int wexp = (int)(tmax - 7.f - m) + evj;
+    const bool live = wexp >= -127;   // weights below 2^-127 contribute nothing in fp32
+    i32x8 pf8;
+    float rs = 0.f;
+    const float off = 7.f - tmax;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int mt = w >> 2, e0 = 4 * (w & 3);
+      float p4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p4[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e0 + i], cj, off));
+        rs += p4[i];
+      }
+      int pk = 0;
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], pk, false);
+      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
+      pf8[w] = live ? pk : 0;
+    }
+    l += ldexpf(rs, (int)(tmax - 7.f - m));
+    const int sb = min(max(127 + wexp, 0), 254);
+    ld(3);
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[c], pf8, o[c], 0, 0, 0, 127, 0, sb);
+  };
   auto no_loads = [](int) __attribute__((always_inline)) {};
 
   if constexpr (DMA) {
@@ -445,33 +614,43 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
     int j0, f0, j1, f1;
     bool have0 = walk.next_direct(j0, f0);
     bool have1 = walk.next_direct(j1, f1);
+    int ex0 = 0, ex1 = 0;   // quantised branch: the key blocks' exponents
+    if constexpr (FP8) {
+      ex0 = have0 ? walk.exps(j0) : 0;
+      ex1 = have1 ? walk.exps(j1) : 0;
+    }
     stage_k(have0 ? j0 : -1, kring, 0, KPW);
     stage_k(have1 ? j1 : -1, kring + TILE, 0, KPW);
-    stage_v(have0 ? j0 : -1, vring, 0, KPW);
+    stage_v(have0 ? j0 : -1, vring, 0, VPW);
     walk.fill();
     barrier_vmem_n<0>();
     int ks = 0, vs = 0;
     while (have0) {
       int j2, f2;
       const bool have2 = walk.next(j2, f2);
+      const int ex2 = walk.ex;
       const int ks2 = ks == 0 ? 2 : ks - 1;          // (ks + 2) % 3
       // V(s + 1) pieces first, then K(s + 2): the wait below counts on that order
       const int jv = have1 ? j1 : -1, jk = have2 ? j2 : -1;
-      uint16_t* const vdst = vring + (vs ^ 1) * TILE;
+      uint16_t* const vdst = vring + (vs ^ 1) * VT;
       uint16_t* const kdst = kring + ks2 * TILE;
+      auto ld = [&](int p) __attribute__((always_inline)) {
+        if (p < 2) stage_v(jv, vdst, p * VPW / 2, (p + 1) * VPW / 2);
+        else stage_k(jk, kdst, (p - 2) * KPW / 2, (p - 1) * KPW / 2);
+      };
       if ((f0 >> qb) & 1) {
-        compute_tile(kring + ks * TILE, nullptr, vring + vs * TILE, j0,
-                     [&](int p) __attribute__((always_inline)) {
-                       if (p < 2) stage_v(jv, vdst, p * KPW / 2, (p + 1) * KPW / 2);
-                       else stage_k(jk, kdst, (p - 2) * KPW / 2, (p - 1) * KPW / 2);
-                     });
+        if constexpr (FP8)
+          compute_tile_fp8(kring + ks * TILE, reinterpret_cast<const uint8_t*>(vring + vs * VT),
+                           j0, ex0, ld);
+        else
+          compute_tile(kring + ks * TILE, nullptr, vring + vs * VT, j0, ld);
       } else {
-        stage_v(jv, vdst, 0, KPW);
+        stage_v(jv, vdst, 0, VPW);
         stage_k(jk, kdst, 0, KPW);
       }
       barrier_vmem_n<KPW>();
-      j0 = j1; f0 = f1; have0 = have1;
-      j1 = j2; f1 = f2; have1 = have2;
+      j0 = j1; f0 = f1; have0 = have1; ex0 = ex1;
+      j1 = j2; f1 = f2; have1 = have2; ex1 = ex2;
       ks = ks == 2 ? 0 : ks + 1;
       vs ^= 1;
     }
@@ -538,6 +717,13 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
     __syncthreads();
   }
   if (!active) return;   // no barrier follows
+  if constexpr (FP8) {
+    // the epilogue's phi(Q) takes the unquantised Q
+    const int q = qrow0 + l32;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = q < a.nq ? load_bf16x8(qb_ptr + (size_t)q * D + 16 * s + 8 * h) : u32x4{0, 0, 0, 0};
+  }
 
   // ---------------------------------------------------------------- epilogue
   l += swap_halves(l);
@@ -663,244 +849,14 @@ __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) 
   }
 }
 
-// ------------------------------------------------------------------------------------
-// Quantised sparse branch (SLA2 page, section 2.C). Same structure as sparse_attn_kernel,
-// on E4M3 operands with power-of-two block scales:
-//   S^T = K8 Q8^T                   bf16 MFMA 32x32x16 on the E4M3 values (held exactly in
-//                                   bf16; every product is exact and the sum is accumulated
-//                                   in fp32), logits y = S * 2^(eQ+eK) log2(e)/sqrt(d)
-//   per (row, tile): T = floor(max y), P8 = E4M3(2^(y - T + 7)) in (0, 256)
-//   O^T += 2^(T - 7 - m + eV) (V8^T P8^T)   fp8 MFMA 32x32x64 with the power-of-two weight
-//                                           applied by the MFMA's E8M0 scale on P8
-// The logits do not use the fp8 MFMA: on gfx950 it keeps only about 12-13 significant bits
-// when products of very different magnitude are summed, and the exponential turns that into
-// errors of several percent for logits of a few hundred. For P.V the same relative error
-// is harmless (it stays about 1e-4 of sum p |v|).
-// m is the row's running maximum kept on integers, so every rescale is an exact power of
-// two; the row sum uses the unquantised probabilities. In the 32x32x64 MFMA each lane half
-// holds 32 of the 64 reduction elements; the two 32-element scale blocks take their E8M0
-// scale from lanes x and x+32, which here always carry the same value.
+template <typename T, int D, int QB, bool OUT_BF16, bool PISA = false, bool SAVE = false>
+__global__ __launch_bounds__(128 * QB, 2) void sparse_attn_kernel(SparseArgs a) {
+  sparse_attn_body<T, D, QB, OUT_BF16, PISA, SAVE, false>(a);
+}
+
 template <int D, int QB, bool OUT_BF16>
 __global__ __launch_bounds__(128 * QB, 2) void sparse_attn_fp8_kernel(SparseArgs a) {
-  constexpr int NT = 128 * QB;
-  constexpr int KS = D / 16;               // 16-channel reduction steps for Q K^T
-  constexpr int CT = D / 32;
-  constexpr int CH = D / 8;                // 16-byte chunks per K row
-  constexpr int VROW = 64 + 16;            // padded LDS row of the V8 tile (bytes)
-  constexpr int KPT = 64 * CH / NT;        // K chunks per thread per tile
-  constexpr int VPT = D * 64 / 16 / NT;    // V8 chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][64 * D];
-  __shared__ __attribute__((aligned(16))) uint8_t V8s[2][D * VROW];
-
-  const int wid = xcd_remap(blockIdx.x, a.total);
-  const int bh = wid / a.ngroups, grp = wid % a.ngroups;
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63, h = lane >> 5, l32 = lane & 31;
-  const int qb = wv >> 1;
-  const int iq = grp * QB + qb;
-  const bool active = iq < a.nbq;
-  const int qrow0 = iq * kBlock + 32 * (wv & 1);
-  const uint16_t* k8b = a.k8 + (size_t)bh * a.nbk * kBlock * D;
-  const uint8_t* v8b = a.v8 + (size_t)bh * a.nbk * kBlock * D;
-  UnionWalk<QB> walk;
-  walk.init(a.idx, bh, a.nbq, grp, a.topk);
-
-  // Q8^T fragments (B operand): lane column q, channels 16 s + 8 h .. +7
-  u32x4 qf8[KS];
-  {
-    const int q = qrow0 + l32;
-    const int qc = (active && q < a.nq) ? q : 0;
-    const uint16_t* src = a.q8 + ((size_t)bh * a.nbq * kBlock + qc) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf8[s] = *reinterpret_cast<const u32x4*>(src + 16 * s + 8 * h);
-  }
-  const int eq = active ? a.eq[(size_t)bh * a.nbq + iq] : 0;
-  const float base_scale = kLog2e / sqrtf((float)D);
-
-  f32x16 o[CT];
-#pragma unroll
-  for (int c = 0; c < CT; ++c) o[c] = f32x16{};
-  float m = -16384.f;     // running maximum (an integer), far below any logit
-  float l = 0.f;
-
-  u32x4 kreg[KPT], vreg[VPT];
-  auto load_tile = [&](int j) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u)
-      kreg[u] = *reinterpret_cast<const u32x4*>(k8b + (size_t)j * kBlock * D + (t + NT * u) * 8);
-#pragma unroll
-    for (int u = 0; u < VPT; ++u)
-      vreg[u] = *reinterpret_cast<const u32x4*>(v8b + (size_t)j * kBlock * D + (t + NT * u) * 16);
-  };
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int id = t + NT * u, r = id / CH, c = id % CH;
-      *reinterpret_cast<u32x4*>(&Ks[buf][swz<D>(r, c * 8)]) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int id = t + NT * u, vr = id / 4, vc = id % 4;
-      *reinterpret_cast<u32x4*>(&V8s[buf][vr * VROW + vc * 16]) = vreg[u];
-    }
-  };
-  auto frag32 = [&](const uint8_t* p) __attribute__((always_inline)) {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
-    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  };
-
-  auto compute_tile = [&](const uint16_t* Kt, const uint8_t* Vt, int j) __attribute__((always_inline)) {
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const u32x4 af = *reinterpret_cast<const u32x4*>(&Kt[swz<D>(32 * mt + l32, 16 * ks + 8 * h)]);
-        sacc[mt] = mfma_bf16(af, qf8[ks], sacc[mt]);
-      }
-    }
-    const float cj = ldexpf(base_scale, eq + a.ek[(size_t)bh * a.nbk + j]);
-    if (__builtin_amdgcn_readfirstlane((j + 1) * kBlock > a.nkv ? 1 : 0)) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = j * kBlock + 32 * mt + 8 * (e >> 2) + 4 * h + (e & 3);
-          sacc[mt][e] = key < a.nkv ? sacc[mt][e] : -INFINITY;
-        }
-    }
-    float r = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) r = fmaxf(r, sacc[mt][e]);
-    r = fmaxf(r, swap_halves(r)) * cj;          // row max of y over the tile
-    const float T = floorf(r);
-    if (__ballot(r > m + kRescaleSlack)) {
-      const float mn = fmaxf(m, ceilf(r));
-      const float corr = ldexpf(1.f, (int)fmaxf(m - mn, -200.f));
-      l *= corr;
-#pragma unroll
-      for (int c = 0; c < CT; ++c) o[c] *= corr;
-      m = mn;
-    }
-    // P8 = E4M3(2^(y - T + 7)); slot 16 mt + e of this lane half holds accumulator element e
-    // of key tile half mt
-    const int wexp = (int)(T - 7.f - m) + a.ev[(size_t)bh * a.nbk + j];
-    const bool live = wexp >= -127;   // weights below 2^-127 contribute nothing in fp32
-    i32x8 pf8;
-    float rs = 0.f;
-    const float off = 7.f - T;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int mt = w >> 2, e0 = 4 * (w & 3);
-      float p4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p4[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][e0 + i], cj, off));
-        rs += p4[i];
-      }
-      int pk = 0;
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[0], p4[1], pk, false);
-      pk = __builtin_amdgcn_cvt_pk_fp8_f32(p4[2], p4[3], pk, true);
-      pf8[w] = live ? pk : 0;
-    }
-    l += ldexpf(rs, (int)(T - 7.f - m));
-    const int sb = min(max(127 + wexp, 0), 254);
-#pragma unroll
-    for (int c = 0; c < CT; ++c) {
-      const i32x8 vf = frag32(&Vt[(32 * c + l32) * VROW + 32 * h]);
-      o[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf8, o[c], 0, 0, 0, 127, 0, sb);
-    }
-  };
-
-  int j_cur, f_cur;
-  bool have = walk.next(j_cur, f_cur);
-  if (have) {
-    load_tile(j_cur);
-    store_tile(0);
-  }
-  __syncthreads();
-  auto step = [&](auto bufc) __attribute__((always_inline)) {
-    constexpr int B = decltype(bufc)::value;
-    int j_nxt, f_nxt;
-    const bool have_nxt = walk.next(j_nxt, f_nxt);
-    if (have_nxt) load_tile(j_nxt);
-    if ((f_cur >> qb) & 1) compute_tile(Ks[B], V8s[B], j_cur);
-    if (have_nxt) store_tile(B ^ 1);
-    __syncthreads();
-    j_cur = j_nxt;
-    f_cur = f_nxt;
-    have = have_nxt;
-  };
-  while (have) {
-    step(std::integral_constant<int, 0>{});
-    if (!have) break;
-    step(std::integral_constant<int, 1>{});
-  }
-  if (!active) return;
-
-  // ---------------------------------------------------------------- epilogue (as bf16)
-  l += swap_halves(l);
-  const float inv_l = l > 0.f ? 1.f / l : 0.f;
-  const uint16_t* qsrc = reinterpret_cast<const uint16_t*>(a.q) + (size_t)bh * a.nq * D;
-  u32x4 qf[KS];
-  {
-    const int q = qrow0 + l32;
-    const bool ok = q < a.nq;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = ok ? *reinterpret_cast<const u32x4*>(qsrc + (size_t)q * D + 16 * s + 8 * h)
-                 : u32x4{0, 0, 0, 0};
-  }
-  const uint16_t* scb = a.sc + ((size_t)bh * a.nbq + iq) * D * D;
-  const float* zcb = a.zc + ((size_t)bh * a.nbq + iq) * D;
-  float d = 0.f;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const f32x4 z0 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h);
-    const f32x4 z1 = *reinterpret_cast<const f32x4*>(zcb + 16 * s + 8 * h + 4);
-    const u32x4 w = qf[s];
-    d += fmaxf(bf16_lo(w[0]), 0.f) * z0[0] + fmaxf(bf16_hi(w[0]), 0.f) * z0[1] +
-         fmaxf(bf16_lo(w[1]), 0.f) * z0[2] + fmaxf(bf16_hi(w[1]), 0.f) * z0[3] +
-         fmaxf(bf16_lo(w[2]), 0.f) * z1[0] + fmaxf(bf16_hi(w[2]), 0.f) * z1[1] +
-         fmaxf(bf16_lo(w[3]), 0.f) * z1[2] + fmaxf(bf16_hi(w[3]), 0.f) * z1[3];
-  }
-  d += swap_halves(d);
-  const float inv_den = 1.f / (d + kEps);
-  const float* al = a.alpha + (size_t)(bh % a.H) * D;
-  const int q = qrow0 + l32;
-#pragma unroll
-  for (int c = 0; c < CT; ++c) {
-    f32x16 lin = f32x16{};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const u32x4 af =
-          *reinterpret_cast<const u32x4*>(scb + (size_t)(32 * c + l32) * D + 16 * s + 8 * h);
-      lin = mfma_bf16(af, relu_bf16x8(qf[s]), lin);
-    }
-    if (q < a.nq) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int ch = 32 * c + 8 * g + 4 * h;
-        const f32x4 alv = *reinterpret_cast<const f32x4*>(al + ch);
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ix = 4 * g + e;
-          r[e] = alv[e] * (o[c][ix] * inv_l) + (1.f - alv[e]) * (lin[ix] * inv_den);
-        }
-        if constexpr (OUT_BF16) {
-          uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-          *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16(r[0], r[1]), pack_bf16(r[2], r[3])};
-        } else {
-          float* dst = reinterpret_cast<float*>(a.out) + ((size_t)bh * a.nq + q) * D + ch;
-          *reinterpret_cast<f32x4*>(dst) = f32x4{r[0], r[1], r[2], r[3]};
-        }
-      }
-    }
-  }
+  sparse_attn_body<uint16_t, D, QB, OUT_BF16, false, false, true>(a);
 }
 
 template <typename T, int D, int QB, bool FP8, bool PISA = false>
@@ -918,10 +874,10 @@ hipError_t launch_sparse_T(const Plan& s, const void* q, const void* k, const in
   a.nq = s.nq; a.nkv = s.nkv; a.nbq = s.nbq; a.nbk = s.nbk; a.topk = s.k; a.H = s.H;
   a.ngroups = (s.nbq + QB - 1) / QB;
   a.total = s.BH * a.ngroups;
-  a.q8 = reinterpret_cast<const uint16_t*>(ws + s.q8);
+  a.q8 = reinterpret_cast<uint16_t*>(ws + s.q8);
   a.k8 = reinterpret_cast<const uint16_t*>(ws + s.k8);
   a.v8 = reinterpret_cast<const uint8_t*>(ws + s.v8);
-  a.eq = reinterpret_cast<const int32_t*>(ws + s.sq8);
+  a.eq = reinterpret_cast<int32_t*>(ws + s.sq8);
   a.ek = reinterpret_cast<const int32_t*>(ws + s.sk8);
   a.ev = reinterpret_cast<const int32_t*>(ws + s.sv8);
   a.hbar = reinterpret_cast<const uint16_t*>(ws + s.hbar);
