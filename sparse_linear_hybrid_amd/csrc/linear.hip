@@ -71,7 +71,7 @@ constexpr int kSlice = 128;
 // totals instead (z_j and the z partials as usual).
 template <typename T, int D, bool BLOCKS, int CHUNK, bool PISA = false, bool FP8 = false,
           bool LO = false, bool NOSJ = false>
-__global__ __launch_bounds__(256, 2) void kv_summary_kernel(
+__global__ __launch_bounds__(256, FP8 && D == 128 ? 3 : 2) void kv_summary_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ Pk,
     double* __restrict__ kt, size_t kbh, size_t kj, uint16_t* __restrict__ v16,
     uint16_t* __restrict__ sblk, uint16_t* __restrict__ sblk_lo, float* __restrict__ zblk, float* __restrict__ spart,
@@ -100,7 +100,6 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
   __shared__ double pool_lds[4 * D];          // per-wave block sums (rows folded by shuffles)
   __shared__ double means[kSummaryChunk][D];   // pooled means of the current group of blocks
   __shared__ double vpool_lds[PISA ? 4 * D : 1];
-  __shared__ __attribute__((aligned(16))) uint8_t vt8[FP8 ? D * 64 : 16];   // V8 tile
   __shared__ float amax_lds[8];                                             // per wave: K, V
 
   const int chunk = blockIdx.x, bh = blockIdx.y;
@@ -139,7 +138,6 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     double pacc[8], vacc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pacc[e] = vacc[e] = 0.0;
-    float kmx = 0.f, vmx = 0.f;   // FP8: absmax of the valid tokens
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int cidx = t + 256 * u;
@@ -166,10 +164,6 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         kf[e] = ok_sum ? kf[e] : 0.f;
         vf[e] = ok_sum ? vf[e] : 0.f;
         if constexpr (PISA) vacc[e] += (double)vf[e];
-        if constexpr (FP8) {
-          kmx = fmaxf(kmx, fabsf(kf[e]));
-          vmx = fmaxf(vmx, fabsf(vf[e]));
-        }
       }
       u32x4 kw, vw;
 #pragma unroll
@@ -206,17 +200,6 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         }
       }
     }
-    if constexpr (FP8) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
-        vmx = fmaxf(vmx, __shfl_xor(vmx, o, 64));
-      }
-      if (lane == 0) {
-        amax_lds[2 * w] = kmx;
-        amax_lds[2 * w + 1] = vmx;
-      }
-    }
     if (j + 1 < j1) load_block(j + 1);   // in flight during this block's compute
     __syncthreads();
     if (t < D) {
@@ -235,7 +218,40 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
       }
     }
     if constexpr (FP8) {
-      // E4M3 of this thread's chunks, read back from the staged (masked) tiles
+      // E4M3 of the staged (masked) tiles: K8 in this thread's row chunks, the V8 tile in
+      // 16-byte chunks of one channel's key slots, so that it goes out in whole chunks.
+      // The block absmax comes from the same reads in a first pass (not from the staging
+      // loop, whose registers it would add to).
+      float kmx = 0.f, vmx = 0.f;
+#pragma unroll 1
+      for (int u = 0; u < CPT; ++u) {
+        const int cidx = t + 256 * u;
+        const u32x4 kw = *reinterpret_cast<const u32x4*>(&Ks[(cidx / TPR) * LS + (cidx % TPR) * 8]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kmx = fmaxf(kmx, fmaxf(fabsf(bf16_lo(kw[e])), fabsf(bf16_hi(kw[e]))));
+      }
+#pragma unroll 1
+      for (int u = 0; u < D * 4 / 256; ++u) {
+        const int id = t + 256 * u, c = id >> 2, pq = id & 3;
+        const int mt = pq & 1, hh = pq >> 1;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vmx = fmaxf(vmx, fabsf(__uint_as_float(
+                                 (uint32_t)Vs[(32 * mt + 8 * g + 4 * hh + i) * LS + c] << 16)));
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        kmx = fmaxf(kmx, __shfl_xor(kmx, o, 64));
+        vmx = fmaxf(vmx, __shfl_xor(vmx, o, 64));
+      }
+      if (lane == 0) {
+        amax_lds[2 * w] = kmx;
+        amax_lds[2 * w + 1] = vmx;
+      }
+      __syncthreads();
       const int ek = e8m0_exponent(fmaxf(fmaxf(amax_lds[0], amax_lds[2]),
                                          fmaxf(amax_lds[4], amax_lds[6])));
       const int ev = e8m0_exponent(fmaxf(fmaxf(amax_lds[1], amax_lds[3]),
@@ -244,28 +260,38 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         f8.ek[(size_t)bh * nbk + j] = ek;
         f8.ev[(size_t)bh * nbk + j] = ev;
       }
-#pragma unroll
+#pragma unroll 1
       for (int u = 0; u < CPT; ++u) {
         const int cidx = t + 256 * u;
         const int r = cidx / TPR, c8 = cidx % TPR;
         const u32x4 kw = *reinterpret_cast<const u32x4*>(&Ks[r * LS + c8 * 8]);
-        const u32x4 vw = *reinterpret_cast<const u32x4*>(&Vs[r * LS + c8 * 8]);
-        float kf[8], vf[8];
+        float kf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kf[2 * e] = bf16_lo(kw[e]); kf[2 * e + 1] = bf16_hi(kw[e]);
-          vf[2 * e] = bf16_lo(vw[e]); vf[2 * e + 1] = bf16_hi(vw[e]);
         }
         uint32_t w0, w1;
         e4m3x8(kf, ek, w0, w1);
         *reinterpret_cast<u32x4*>(f8.k8 + (((size_t)bh * nbk * kBlock + row0 + r) * D + c8 * 8) * 2) =
             e4m3x8_as_bf16(w0, w1);
-        e4m3x8(vf, ev, w0, w1);
-        const int pos = v8_slot_pos(r);
+      }
+      // chunk (channel c, slot quarter pq = 2 hh + mt): slot 16 pq + 4 g + i holds key
+      // 32 mt + 8 g + 4 hh + i
+      uint8_t* v8t = f8.v8 + ((size_t)bh * nbk + j) * D * 64;
+#pragma unroll 1
+      for (int u = 0; u < D * 4 / 256; ++u) {
+        const int id = t + 256 * u, c = id >> 2, pq = id & 3;
+        const int mt = pq & 1, hh = pq >> 1;
+#pragma unroll 1
+        for (int g2 = 0; g2 < 4; g2 += 2) {   // slots 4 g2 .. 4 g2 + 7
+          float va[8];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          vt8[(c8 * 8 + b) * 64 + pos] = (uint8_t)(w0 >> (8 * b));
-          vt8[(c8 * 8 + 4 + b) * 64 + pos] = (uint8_t)(w1 >> (8 * b));
+          for (int e = 0; e < 8; ++e)
+            va[e] = __uint_as_float(
+                (uint32_t)Vs[(32 * mt + 8 * (g2 + (e >> 2)) + 4 * hh + (e & 3)) * LS + c] << 16);
+          uint32_t w0, w1;
+          e4m3x8(va, ev, w0, w1);
+          *reinterpret_cast<u32x2*>(v8t + c * 64 + 16 * pq + 4 * g2) = u32x2{w0, w1};
         }
       }
     }
@@ -298,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
     // accumulator tiles are live at a time (fewer registers: three workgroups per CU instead
     // of two, more loads in flight). Half 0 is staged over the K tile once every wave holds its
     // A fragments, half 1 over the V tile after every wave's last product.
-    constexpr bool HALVES = BLOCKS && !PISA && !FP8 && !LO && !NOSJ && NT == 4;
+    constexpr bool HALVES = BLOCKS && !PISA && !LO && !NOSJ && NT == 4;
     if constexpr (HALVES) {
       f32x16 acc2[2];
       auto product = [&](int half) __attribute__((always_inline)) {
@@ -358,11 +384,6 @@ __global__ __launch_bounds__(256, 2) void kv_summary_kernel(
         // (row c at LS elements) once every wave has read them, then 16-byte chunks per thread.
         // Lane column c = 32 nt + l32 holds rows r in runs of 4.
         __syncthreads();
-        if constexpr (FP8) {   // the V8 tile (complete after the barrier) goes out
-          uint8_t* dst = f8.v8 + ((size_t)bh * nbk + j) * D * 64;
-          for (int id = t; id < D * 64 / 16; id += 256)
-            *reinterpret_cast<u32x4*>(dst + id * 16) = *reinterpret_cast<const u32x4*>(&vt8[id * 16]);
-        }
   #pragma unroll
         for (int u = 0; u < TILES_PER_WAVE; ++u) {
           const int c = 32 * ((NT == 4) ? u : (w & 1)) + l32;
