@@ -94,11 +94,9 @@ def work(p, fp8=False):
         "complement": BH * p.nbk * d * d * 2 + BH * p.nbq * (d * d * 2 + d * 4),
     }
     dense_flops = 4 * BH * p.n_q * p.n_kv * d
-    quant_bytes = BH * (p.n_q + p.n_kv) * d * (2 + 2) + BH * p.n_kv * d * (2 + 1)
     return {"pairs": pairs, "sparse_flops": sparse_flops, "kv_summary_bytes": kv_bytes,
             "hbm_bytes": hbm, "v16_bytes": v16_bytes,
-            "dense_flops": dense_flops, "sparse_peak": sparse_flops / floor_s,
-            "quant_bytes": quant_bytes}
+            "dense_flops": dense_flops, "sparse_peak": sparse_flops / floor_s}
 
 
 # --------------------------------------------------------------------------- measured peaks
@@ -682,6 +680,13 @@ def main():
         w["hbm_bytes"] = {"kv_summary": 2 * BH * p.n_kv * d * 2 + BH * p.nbk * d * 8,
                           "route": w["hbm_bytes"]["route"]}
         w["v16_bytes"] = 0
+    if fp8:
+        # the quantised path's key/value pass writes K8 (E4M3 values held as bf16) and the V8
+        # tiles instead of the f16 copy of V; the "with_v16" figures below count those
+        BH, d = p.batch * p.heads, p.head_dim
+        k8v8 = BH * p.nbk * 64 * d * 3
+        w["kv_summary_bytes"] += k8v8 - w["v16_bytes"]
+        w["v16_bytes"] = k8v8
     for stg, nbytes in w["hbm_bytes"].items():
         t_s = stage_ms[stg] * 1e-3
         if t_s > 0 and not (pisa and stg == "complement"):
@@ -707,8 +712,8 @@ def main():
     if peaks:
         kernels["kv_summary_with_v16_frac_of_copy"] = (kernels["kv_summary_with_v16_GBps"]
                                                        / peaks["copy_GBps"])
-    if fp8:
-        kernels["quant_GBps"] = w["quant_bytes"] / (stage_ms["quant"] * 1e-3) / 1e9
+    kernels["kv_summary_operand_copies"] = ("K8 (bf16-held) and V8 tiles" if fp8 else
+                                            "none" if cache_path else "f16 copy of V")
     if pisa:
         # tail kernel (timed as the complement stage): Q K_bar^T and P Vsum over the
         # unrouted centroids, 4 d FLOP per (query row, centroid)

@@ -164,8 +164,8 @@ sla_status sla_forward_pisa(const sla_problem* p, const void* q, const void* k, 
 enum {
   SLA_STAGE_KV_SUMMARY = 0,  /* per-block phi(K)^T V, sum phi(K), pooled K, totals      */
   SLA_STAGE_ROUTE = 1,       /* pooled Q, projections, block scores, top-k              */
-  SLA_STAGE_COMPLEMENT = 2,  /* per query block: total minus the selected summaries     */
-  SLA_STAGE_QUANT = 3,       /* E4M3 quantisation of Q, K, V (fp8 only; empty otherwise) */
+  SLA_STAGE_COMPLEMENT = 2,  /* per query block: the unselected blocks' S_c and z_c     */
+  SLA_STAGE_QUANT = 3,       /* empty: K and V are quantised in KV_SUMMARY, Q in SPARSE  */
   SLA_STAGE_SPARSE = 4,      /* sparse attention + linear apply + alpha mix            */
   SLA_NUM_STAGES = 5
 };

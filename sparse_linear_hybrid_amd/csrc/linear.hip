@@ -5,7 +5,8 @@
 // kv_summary:  one pass over K and V. For every key block j: S_j = phi(K_j)^T V_j (d x d,
 //              bf16 MFMA, fp32 accumulate, stored bf16 as S_j^T[c][r]), z_j = sum phi(K_j)
 //              (fp32), the projected block mean of K (float64, for the router) and an f16
-//              copy of V for the sparse branch's P.V. The next block's loads are in flight
+//              copy of V for the bf16 exact branch's P.V (the fp8 forward writes K8 and V8
+//              instead). The next block's loads are in flight
 //              while a block is processed. Per-chunk fp32 partial totals are written for a
 //              fixed-order reduction (no atomics).
 // reduce:      z_tot = sum of the chunk partials (fixed order); S_tot only where a pass keeps
